@@ -1,0 +1,388 @@
+"""Pins of the CPU oracle against facts fixed outside it.
+
+Each test names what it checks the oracle against:
+  * library routines (torch's bf16 widening, scipy's softmax / logsumexp,
+    torch.topk, numpy.argmax),
+  * closed forms from the speculative-sampling proof on "CS3602_FINAL_SpeDec"
+    (section 2): the residual normaliser is 1 - beta with
+    beta = sum_x min(p(x), q(x)), and accept-or-resample emits x with
+    probability exactly p(x),
+  * exhaustive enumeration of every 24-bit uniform on tiny vocabularies,
+  * chi-square tests over 10^5..10^6 seeded trials,
+  * special cases with known answers.
+A plausible slip in the oracle (p and q swapped, a dropped temperature, an
+off-by-one row, <= instead of <, a missing normaliser) fails at least one.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import special, stats
+
+import workloads as W
+
+GRID = 2**24
+
+
+def _softmax(l, T, top_k=0):
+    """Independent reference: scipy softmax over the top-k kept set (ties kept)."""
+    l = np.asarray(l, dtype=np.float64)
+    keep = np.ones_like(l, dtype=bool)
+    if 0 < top_k < l.shape[-1]:
+        kth = np.sort(l)[::-1][top_k - 1]
+        keep = l >= kth
+    z = np.where(keep, l / T, -np.inf)
+    return special.softmax(z)
+
+
+def _probs_rows(rows, T, top_k=0):
+    return np.stack([_softmax(r, T, top_k) for r in rows])
+
+
+# --------------------------------------------------------------------------
+# decoding, row statistics, argmax
+# --------------------------------------------------------------------------
+def test_bf16_decode_matches_torch(orc):
+    bits = np.arange(65536, dtype=np.uint16)
+    f = W.bf16_bits_to_f32(bits)
+    keep = ~np.isnan(f)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    for i in np.flatnonzero(keep)[::97]:
+        assert orc._load().orc_decode(bits[i:i + 1].ctypes.data, 1, 0) == ref[i]
+    # generator-side RNE cast agrees with torch's float -> bf16 rounding
+    x = np.random.default_rng(0).standard_normal(100000).astype(np.float32) * 7
+    mine = W.f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, theirs)
+
+
+@pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 5.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_probs_vs_scipy(orc, T, dtype):
+    rng = np.random.default_rng(7)
+    l = (rng.standard_normal(3001) * 3).astype(np.float32)
+    row = l if dtype == "f32" else W.f32_to_bf16_bits(l)
+    lf = l if dtype == "f32" else W.bf16_bits_to_f32(row)
+    prob, st = orc.row_probs(row, dtype, T)
+    lse = special.logsumexp(lf.astype(np.float64) / T)
+    assert st["m"] == lf.max()
+    assert abs((st["m"] / T + np.log(st["S"])) - lse) < 1e-12 * max(1, abs(lse))
+    np.testing.assert_allclose(prob, special.softmax(lf.astype(np.float64) / T), rtol=1e-12, atol=1e-300)
+    assert abs(prob.sum() - 1) < 1e-12
+
+
+@pytest.mark.parametrize("k", [1, 5, 50, 3000])
+def test_top_k_threshold_vs_torch_topk(orc, k):
+    rng = np.random.default_rng(k)
+    l = rng.integers(-40, 40, 3001).astype(np.float32) / 4  # many ties
+    prob, st = orc.row_probs(l, "f32", 0.7, k)
+    tau = torch.topk(torch.from_numpy(l).double(), k).values[k - 1].item()
+    assert st["tau"] == tau
+    assert st["kept"] == int((l >= tau).sum()) >= k
+    assert np.all(prob[l < tau] == 0) and np.all(prob[l >= tau] > 0)
+    np.testing.assert_allclose(prob, _softmax(l, 0.7, k), rtol=1e-12, atol=1e-300)
+
+
+def test_top_k_at_or_above_vocab_is_off(orc):
+    l = np.random.default_rng(3).standard_normal(64).astype(np.float32)
+    p0, _ = orc.row_probs(l, "f32", 1.0, 0)
+    p1, st = orc.row_probs(l, "f32", 1.0, 64)
+    assert np.array_equal(p0, p1) and st["kept"] == 64
+
+
+def test_argmax_first_index_vs_numpy(orc):
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        l = rng.integers(-5, 5, 257).astype(np.float32)  # ties at the max
+        assert orc.row_argmax(l, "f32") == int(np.argmax(l))
+    l = np.full(9, -np.inf, np.float32)
+    l[[3, 6]] = 2.0
+    assert orc.row_argmax(l, "f32") == 3
+
+
+# --------------------------------------------------------------------------
+# beta identity (residual normaliser = 1 - beta) on every workload shape
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,batch", [(1, 1), (2, 1), (3, 6), (4, 2), (5, 4)])
+def test_residual_mass_is_one_minus_beta(orc, cfg, batch):
+    w = W.make_config(cfg, batch=batch)
+    r = orc.verify_workload(w, threads=4)
+    T = w.temperature
+    tf, df = w.target_f32(), w.draft_f32()
+    checked = 0
+    for b in range(w.batch):
+        n = r["num_accepted"][b]
+        K = w.draft_lens[b]
+        assert 0 <= n <= K
+        if n == K:
+            assert r["residual_mass"][b] == 0
+            continue
+        p = _softmax(tf[w.cu_draft[b] + b + n], T, w.top_k)
+        q = _softmax(df[w.cu_draft[b] + n], T, w.top_k)
+        beta = np.minimum(p, q).sum()
+        assert abs(r["residual_mass"][b] - (1 - beta)) < 1e-12
+        checked += 1
+    # per-position p(x), q(x) against scipy
+    for b in range(w.batch):
+        for k in range(w.draft_lens[b]):
+            x = w.draft_ids[w.cu_draft[b] + k]
+            p = _softmax(tf[w.cu_draft[b] + b + k], T, w.top_k)[x]
+            q = _softmax(df[w.cu_draft[b] + k], T, w.top_k)[x]
+            np.testing.assert_allclose(r["probs"][w.cu_draft[b] + k], [p, q], rtol=1e-10)
+    assert checked > 0 or cfg == 1
+
+
+# --------------------------------------------------------------------------
+# Exhaustive enumeration of the 2^24 uniforms on a tiny vocabulary
+# --------------------------------------------------------------------------
+def _enumerate_core(orc, P, Q, x, which):
+    """Run the oracle core once per 24-bit uniform value of one draw.
+
+    which = "acc": u_acc over the grid (u_res = 0); "res": u_acc forced to
+    reject (u = 1 - 2^-24 rejects unless the ratio is 1), u_res over the
+    grid; "bonus": u_acc = 0, u_bonus over the grid.
+    Returns the emitted token at position 0 (K = 1) or at K, per grid value.
+    """
+    K = P.shape[0] - 1
+    out = []
+    step = 2**22
+    for s in range(0, GRID, step):
+        u = (np.arange(s, s + step, dtype=np.float64)) / GRID
+        if which == "acc":
+            ua = np.repeat(u[:, None], K, 1)
+            ur = np.zeros((step, K))
+            ub = np.zeros(step)
+        elif which == "res":
+            ua = np.full((step, K), 1 - 1 / GRID)
+            ur = np.repeat(u[:, None], K, 1)
+            ub = np.zeros(step)
+        else:
+            ua = np.zeros((step, K))
+            ur = np.zeros((step, K))
+            ub = u
+        tok, n = orc.verify_seq_u_batch(P, Q, x, ua, ur, ub)
+        out.append((tok, n))
+    tok = np.concatenate([t for t, _ in out])
+    n = np.concatenate([m for _, m in out])
+    return tok, n
+
+
+@pytest.mark.slow
+def test_exact_law_by_exhaustive_enumeration(orc):
+    """P(emitted = v) = min(p, q)(v) + (1 - beta) p'(v) = p(v), to within V * 2^-24."""
+    V = 4
+    lt = np.array([0.3, -1.2, 1.1, 0.0])
+    ld = np.array([-0.4, 0.9, 0.2, 0.5])
+    T = 0.9
+    p = _softmax(lt, T)
+    q = _softmax(ld, T)
+    P = np.stack([p, _softmax(np.array([1.0, 0.0, -1.0, 2.0]), T)])
+    Q = q[None, :]
+    # the residual law does not depend on which guess was rejected: enumerate once
+    x_rej = int(np.argmax(q / p))  # a guess with q > p, so the forced reject is real
+    tok_r, n_r = _enumerate_core(orc, P, Q, np.array([x_rej]), "res")
+    assert np.all(n_r == 0)
+    law_res = np.bincount(tok_r[:, 0], minlength=V) / GRID
+    resid = np.maximum(p - q, 0)
+    np.testing.assert_allclose(law_res, resid / resid.sum(), atol=V / GRID)
+    law = np.zeros(V)
+    for x in range(V):
+        tok_a, n_a = _enumerate_core(orc, P, Q, np.array([x]), "acc")
+        acc = np.mean(n_a == 1)
+        # accept fraction on the 2^24 grid = ceil(min(1, p/q) * 2^24) / 2^24
+        assert acc == np.ceil(min(1.0, p[x] / q[x]) * GRID) / GRID
+        assert np.all(tok_a[n_a == 1, 0] == x)
+        law += q[x] * (acc * np.eye(V)[x] + (1 - acc) * law_res)
+    np.testing.assert_allclose(law, p, atol=2 * V / GRID)
+    # bonus: all accepted -> emitted token at position K follows p_K
+    x_acc = int(np.argmax(p / q))
+    tok_b, n_b = _enumerate_core(orc, P, Q, np.array([x_acc]), "bonus")
+    assert np.all(n_b == 1)
+    law_b = np.bincount(tok_b[:, 1], minlength=V) / GRID
+    np.testing.assert_allclose(law_b, P[1], atol=V / GRID)
+
+
+# --------------------------------------------------------------------------
+# Seeded, end-to-end statistical checks
+# --------------------------------------------------------------------------
+def _replicated_batch(lt_rows, ld_rows, ids_per_seq, dtype="f32"):
+    """B identical sequences (different uniforms through b) with given ids."""
+    B, K = ids_per_seq.shape
+    V = lt_rows.shape[1]
+    tgt = np.tile(lt_rows.astype(np.float32), (B, 1))
+    drf = np.tile(ld_rows.astype(np.float32), (B, 1)) if K else np.zeros((0, V), np.float32)
+    cu = np.arange(B + 1, dtype=np.int32) * K
+    return tgt, drf, ids_per_seq.reshape(-1).astype(np.int32), cu
+
+
+@pytest.mark.slow
+def test_chi_square_first_token_is_p(orc):
+    """10^6 trials, x ~ q drawn per trial: the first emitted token follows p_0,
+    and the bonus token (all accepted) follows p_K."""
+    rng = np.random.default_rng(2024)
+    V, K, T = 8, 2, 0.8
+    lt = rng.standard_normal((K + 1, V)) * 1.5
+    ld = lt[:K] + rng.standard_normal((K, V))
+    lt32, ld32 = lt.astype(np.float32), ld.astype(np.float32)
+    P = _probs_rows(lt32, T)
+    Q = _probs_rows(ld32, T)
+    B = 10**6
+    ids = np.stack([rng.choice(V, B, p=Q[k]) for k in range(K)], 1)
+    tgt, drf, x, cu = _replicated_batch(lt32, ld32, ids)
+    r = orc.verify_sample(tgt, drf, x, cu, V, "f32", T, 0, seed=99, offset=5, threads=8)
+    tok = r["tokens"].reshape(B, K + 1)
+    first = tok[:, 0]
+    assert np.all(first >= 0)
+    obs = np.bincount(first, minlength=V)
+    assert stats.chisquare(obs, P[0] * B).pvalue > 1e-3
+    allacc = r["num_accepted"] == K
+    obs_b = np.bincount(tok[allacc, K], minlength=V)
+    assert stats.chisquare(obs_b, P[K] * allacc.sum()).pvalue > 1e-3
+    # averaged over x ~ q the acceptance rate of position 0 is beta_0
+    beta0 = np.minimum(P[0], Q[0]).sum()
+    acc0 = np.mean(r["num_accepted"] >= 1)
+    assert abs(acc0 - beta0) < 5 * np.sqrt(beta0 * (1 - beta0) / B)
+
+
+@pytest.mark.slow
+def test_accept_count_law(orc):
+    """Fixed inputs: P(n >= j) = prod_{k<j} min(1, p_k(x_k)/q_k(x_k))."""
+    rng = np.random.default_rng(5)
+    V, K, T = 6, 4, 1.0
+    lt = (rng.standard_normal((K + 1, V)) * 1.2).astype(np.float32)
+    ld = (lt[:K] + rng.standard_normal((K, V)) * 0.8).astype(np.float32)
+    P, Q = _probs_rows(lt, T), _probs_rows(ld, T)
+    x = np.array([int(np.argmax(Q[k])) for k in range(K)])
+    B = 10**5
+    tgt, drf, ids, cu = _replicated_batch(lt, ld, np.tile(x, (B, 1)))
+    r = orc.verify_sample(tgt, drf, ids, cu, V, "f32", T, 0, seed=7, offset=0, threads=8)
+    ratio = np.minimum(1, P[np.arange(K), x] / Q[np.arange(K), x])
+    law = np.array([np.prod(ratio[:j]) * (1 - ratio[j]) for j in range(K)] + [np.prod(ratio)])
+    obs = np.bincount(r["num_accepted"], minlength=K + 1)
+    keep = law * B > 5
+    exp_ = law[keep] * B
+    obs_k = obs[keep]
+    assert obs[~keep].sum() <= max(10, 10 * law[~keep].sum() * B)
+    assert stats.chisquare(obs_k, exp_ * obs_k.sum() / exp_.sum()).pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Greedy: target argmax at every emitted position
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,batch", [(1, 1), (4, 3), (5, 5)])
+def test_greedy_is_target_argmax(orc, cfg, batch):
+    w = W.make_config(cfg, batch=batch)
+    ids = w.draft_ids.copy()
+    tf = w.target_f32()
+    # make some sequences fully accepted and some partially, by planting argmaxes
+    for b in range(w.batch):
+        for k in range(w.draft_lens[b]):
+            if b % 2 == 0 or k < w.draft_lens[b] // 2:
+                ids[w.cu_draft[b] + k] = int(np.argmax(tf[w.cu_draft[b] + b + k]))
+    r = orc.verify_greedy(w.target, ids, w.cu_draft, w.vocab, w.dtype)
+    for b in range(w.batch):
+        K = w.draft_lens[b]
+        a = [int(np.argmax(tf[w.cu_draft[b] + b + k])) for k in range(K + 1)]
+        x = ids[w.cu_draft[b]:w.cu_draft[b + 1]]
+        n = next((k for k in range(K) if x[k] != a[k]), K)
+        want = list(x[:n]) + [a[n]] + [-1] * (K - n)
+        got = r["tokens"][w.cu_draft[b] + b: w.cu_draft[b] + b + K + 1]
+        assert r["num_accepted"][b] == n
+        assert list(got) == want
+
+
+# --------------------------------------------------------------------------
+# Special cases with known answers
+# --------------------------------------------------------------------------
+def test_draft_equals_target_accepts_everything(orc):
+    rng = np.random.default_rng(1)
+    B, K, V = 200, 5, 33
+    lt = (rng.standard_normal((K + 1, V)) * 2).astype(np.float32)
+    ids = np.stack([rng.integers(0, V, K) for _ in range(B)])
+    tgt, drf, x, cu = _replicated_batch(lt, lt[:K], ids)
+    r = orc.verify_sample(tgt, drf, x, cu, V, "f32", 0.9, 0, seed=3, offset=1)
+    assert np.all(r["num_accepted"] == K)
+    assert np.all(r["residual_mass"] == 0)
+    tok = r["tokens"].reshape(B, K + 1)
+    assert np.array_equal(tok[:, :K], ids)
+
+
+def test_disjoint_top_k_supports_reject_at_zero(orc):
+    V, K = 20, 3
+    lt = np.zeros((K + 1, V), np.float32)
+    ld = np.zeros((K, V), np.float32)
+    lt[:, :5] = np.arange(5, 0, -1)  # target keeps ids 0..4 (top-5)
+    ld[:, 10:15] = np.arange(5, 0, -1)  # draft keeps ids 10..14
+    ids = np.array([[10, 11, 12]])
+    tgt, drf, x, cu = _replicated_batch(lt, ld, ids)
+    r = orc.verify_sample(tgt, drf, x, cu, V, "f32", 1.0, 5, seed=0, offset=0)
+    assert r["num_accepted"][0] == 0
+    assert r["probs"][0, 0] == 0 and r["probs"][0, 1] > 0
+    assert abs(r["residual_mass"][0] - 1.0) < 1e-15  # residual is p_0 itself
+    assert 0 <= r["tokens"][0] < 5
+    assert list(r["tokens"][1:]) == [-1, -1, -1]
+
+
+def test_vocab_of_one(orc):
+    B, K = 10, 4
+    tgt, drf, x, cu = _replicated_batch(np.zeros((K + 1, 1)), np.ones((K, 1)), np.zeros((B, K), int))
+    r = orc.verify_sample(tgt, drf, x, cu, 1, "f32", 1.0, 0, seed=1, offset=0)
+    assert np.all(r["num_accepted"] == K) and np.all(r["tokens"] == 0)
+
+
+def test_point_mass_draft(orc):
+    """q = delta_x: accept probability p(x), residual p with x removed, Z = 1 - p(x)."""
+    rng = np.random.default_rng(9)
+    V, K, T = 12, 1, 1.0
+    lt = rng.standard_normal((K + 1, V)).astype(np.float32)
+    ld = np.full((K, V), -np.inf, np.float32)
+    ld[0, 4] = 0.0
+    p = _softmax(lt[0], T)
+    B = 200000
+    tgt, drf, ids, cu = _replicated_batch(lt, ld, np.full((B, 1), 4))
+    r = orc.verify_sample(tgt, drf, ids, cu, V, "f32", T, 0, seed=12, offset=0, threads=8)
+    rej = r["num_accepted"] == 0
+    assert abs(np.mean(~rej) - p[4]) < 5 * np.sqrt(p[4] * (1 - p[4]) / B)
+    np.testing.assert_allclose(r["residual_mass"][rej], 1 - p[4], rtol=1e-12)
+    first = r["tokens"].reshape(B, 2)[rej, 0]
+    assert not np.any(first == 4)
+    want = np.where(np.arange(V) == 4, 0, p) / (1 - p[4])
+    obs = np.bincount(first, minlength=V)
+    m = want > 0
+    assert stats.chisquare(obs[m], want[m] * rej.sum()).pvalue > 1e-3
+
+
+def test_zero_residual_falls_back_to_p(orc):
+    """A guess outside both top-k sets has p = q = 0 and is rejected; with equal
+    rows the residual has no mass and the token is drawn from p_n."""
+    V = 10
+    l = np.arange(V, dtype=np.float32)[::-1].copy()
+    tgt, drf, ids, cu = _replicated_batch(np.stack([l, l]), l[None], np.array([[9]]))
+    r = orc.verify_sample(tgt, drf, ids, cu, V, "f32", 1.0, 3, seed=0, offset=0)
+    assert r["num_accepted"][0] == 0
+    assert r["flags"][0] & orc.FLAG_ZERO_RESIDUAL
+    assert r["residual_mass"][0] == 0
+    assert 0 <= r["tokens"][0] < 3
+
+
+def test_hand_worked_example(orc):
+    """V = 3, T = 1, p = (0.5, 0.3, 0.2), q = (0.2, 0.5, 0.3), guess x = 1.
+    Ratio p/q = 0.6: u = 0.59 accepts, u = 0.6 rejects (strict <).  The
+    residual max(0, p - q) = (0.3, 0, 0) has mass 0.3 = 1 - beta
+    (beta = 0.2 + 0.3 + 0.2 = 0.7), so a rejection always emits id 0.
+    Bonus row p_1 = (1/8, 5/8, 1/4) (edges 0.125 and 0.75 are exact in
+    binary): u = 0.05 -> 0, 0.125 -> 1 (the running mass must exceed u),
+    0.74 -> 1, 0.75 -> 2."""
+    P = np.array([[0.5, 0.3, 0.2], [0.125, 0.625, 0.25]])
+    Q = np.array([[0.2, 0.5, 0.3]])
+    r = orc.verify_seq_u(P, Q, [1], [0.59], [0.0], 0.05)
+    assert r["n"] == 1 and list(r["tokens"]) == [1, 0]
+    assert abs(r["d_acc"][0] - 0.01) < 1e-12
+    r = orc.verify_seq_u(P, Q, [1], [0.6], [0.999], 0.05)
+    assert r["n"] == 0 and list(r["tokens"]) == [0, -1]
+    assert abs(r["z"] - 0.3) < 1e-15
+    for ub, want in [(0.05, 0), (0.125, 1), (0.74, 1), (0.75, 2), (0.999, 2)]:
+        r = orc.verify_seq_u(P, Q, [1], [0.0], [0.0], ub)
+        assert r["tokens"][1] == want, (ub, r)
+    # the eps-window around a CDF edge spans both neighbours
+    r = orc.verify_seq_u(P, Q, [1], [0.0], [0.0], 0.75 - 1e-8, eps=1e-6)
+    assert (r["tok_lo"], r["tok_hi"]) == (1, 2) and r["d_fin"] < 1e-6
