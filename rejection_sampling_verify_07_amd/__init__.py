@@ -1,0 +1,15 @@
+"""specverify: the verify step of speculative sampling on AMD Instinct MI355X.
+
+The work runs in the HIP library libspecverify.so (C ABI in
+include/specverify.h); this package holds its sources (csrc/), the build
+script and a thin ctypes binding.
+"""
+from .binding import (  # noqa: F401
+    HipEvents,
+    SpecVerifyError,
+    load_library,
+    status_string,
+    verify_greedy,
+    verify_sample,
+    workspace_bytes,
+)

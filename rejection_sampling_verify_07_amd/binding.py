@@ -1,0 +1,266 @@
+"""ctypes binding of libspecverify (the C ABI in include/specverify.h).
+
+Argument marshalling only: torch supplies device memory and the stream;
+every step of the verify path runs in the HIP kernels of the library.  There
+is no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK = 0
+SV_ERR_INVALID_ARGUMENT = 1
+SV_ERR_UNSUPPORTED = 2
+SV_ERR_WORKSPACE_TOO_SMALL = 3
+SV_ERR_HIP = 4
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+MAX_VOCAB = 1 << 20
+MAX_DRAFT = 128
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class ShapeT(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32),
+        ("max_draft", C.c_int32),
+        ("total_draft", C.c_int32),
+        ("vocab", C.c_int32),
+        ("dtype", C.c_int32),
+        ("target_row_stride", C.c_int64),
+        ("draft_row_stride", C.c_int64),
+        ("cu_draft", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libspecverify.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = C.CDLL(p)
+    VP = C.c_void_p
+    lib.spec_verify_sample.restype = C.c_int
+    lib.spec_verify_sample.argtypes = [
+        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32,
+        VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP,
+    ]
+    lib.spec_verify_greedy.restype = C.c_int
+    lib.spec_verify_greedy.argtypes = [C.POINTER(ShapeT), VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP]
+    lib.spec_verify_status_string.restype = C.c_char_p
+    lib.spec_verify_status_string.argtypes = [C.c_int]
+    lib.spec_verify_set_profile_events.restype = C.c_int
+    lib.spec_verify_set_profile_events.argtypes = [VP, VP, C.c_int32]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().spec_verify_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != SV_OK:
+        raise SpecVerifyError(status, where)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    return t.stride(0)
+
+
+def make_shape(target: torch.Tensor, draft: Optional[torch.Tensor], batch: int, max_draft: int,
+               total_draft: int, cu_draft: Optional[torch.Tensor]) -> ShapeT:
+    vocab = target.shape[1]
+    ts = _rows(target, "target_logits")
+    ds = _rows(draft, "draft_logits") if (draft is not None and draft.numel() > 0) else vocab
+    return ShapeT(
+        batch=batch, max_draft=max_draft, total_draft=total_draft, vocab=vocab, dtype=_dtype_code(target),
+        target_row_stride=ts, draft_row_stride=ds,
+        cu_draft=(cu_draft.data_ptr() if cu_draft is not None else None),
+    )
+
+
+def _batch_geometry(target, draft_ids, cu_draft, max_draft):
+    total = draft_ids.numel()
+    if cu_draft is None:
+        batch = target.shape[0] - total  # rows_t = sum(K_b) + B
+        if batch <= 0 or total % batch != 0:
+            raise ValueError("target rows must be B*(K+1) for B*K draft ids; pass cu_draft for ragged K")
+        k = total // batch
+        if max_draft is not None and max_draft != k:
+            raise ValueError("max_draft does not match the uniform draft length")
+        return batch, k, total
+    if cu_draft.dtype != torch.int32 or cu_draft.dim() != 1:
+        raise ValueError("cu_draft must be a 1-D int32 tensor")
+    batch = cu_draft.numel() - 1
+    if max_draft is None:
+        max_draft = int((cu_draft[1:] - cu_draft[:-1]).max().item()) if batch > 0 else 0
+    return batch, max_draft, total
+
+
+def _stream_handle(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_ids: torch.Tensor,
+                  cu_draft: Optional[torch.Tensor] = None, temperature: float = 1.0, top_k: int = 0,
+                  seed: int = 0, offset: int = 0, max_draft: Optional[int] = None, return_probs: bool = True,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, stream=None) -> dict:
+    """Speculative-sampling verify on the GPU (spec_verify_sample).
+
+    target_logits [sum(K_b+1), V] and draft_logits [sum(K_b), V], float32 or
+    bfloat16, rows packed as in include/specverify.h; draft_ids int32
+    [sum(K_b)]; cu_draft int32 [B+1] prefix sums or None (uniform K).
+    Returns tokens [sum(K_b+1)], num_accepted [B], probs [sum(K_b), 2] and
+    residual_mass [B] (the last two when return_probs).
+    """
+    lib = load_library()
+    batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+    if draft_ids.dtype != torch.int32:
+        raise TypeError("draft_ids must be int32")
+    shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
+    dev = target_logits.device
+    need = C.c_size_t(0)
+    _check(lib.spec_verify_sample(C.byref(shape), None, None, None, float(temperature), int(top_k), int(seed),
+                                  int(offset), None, None, None, None, None, C.byref(need), None),
+           "spec_verify_sample(workspace query)")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = dict(
+            tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
+            num_accepted=torch.empty(batch, dtype=torch.int32, device=dev),
+        )
+        if return_probs:
+            out["probs"] = torch.empty((max(total, 1), 2), dtype=torch.float32, device=dev)[:total]
+            out["residual_mass"] = torch.empty(batch, dtype=torch.float32, device=dev)
+    have = C.c_size_t(workspace.numel())
+    st = lib.spec_verify_sample(
+        C.byref(shape), target_logits.data_ptr(), draft_logits.data_ptr() if draft_logits.numel() else None,
+        draft_ids.data_ptr() if draft_ids.numel() else None, float(temperature), int(top_k), int(seed), int(offset),
+        out["tokens"].data_ptr(), out["num_accepted"].data_ptr(),
+        out["probs"].data_ptr() if out.get("probs") is not None and total > 0 else None,
+        out["residual_mass"].data_ptr() if out.get("residual_mass") is not None else None,
+        workspace.data_ptr(), C.byref(have), C.c_void_p(_stream_handle(stream)))
+    _check(st, "spec_verify_sample")
+    return out
+
+
+def verify_greedy(target_logits: torch.Tensor, draft_ids: torch.Tensor, cu_draft: Optional[torch.Tensor] = None,
+                  max_draft: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[dict] = None, stream=None) -> dict:
+    """Greedy argmax-compare verify on the GPU (spec_verify_greedy)."""
+    lib = load_library()
+    batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+    if draft_ids.dtype != torch.int32:
+        raise TypeError("draft_ids must be int32")
+    shape = make_shape(target_logits, None, batch, kmax, total, cu_draft)
+    dev = target_logits.device
+    need = C.c_size_t(0)
+    _check(lib.spec_verify_greedy(C.byref(shape), None, None, None, None, None, C.byref(need), None),
+           "spec_verify_greedy(workspace query)")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = dict(
+            tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
+            num_accepted=torch.empty(batch, dtype=torch.int32, device=dev),
+        )
+    have = C.c_size_t(workspace.numel())
+    st = lib.spec_verify_greedy(C.byref(shape), target_logits.data_ptr(),
+                                draft_ids.data_ptr() if draft_ids.numel() else None, out["tokens"].data_ptr(),
+                                out["num_accepted"].data_ptr(), workspace.data_ptr(), C.byref(have),
+                                C.c_void_p(_stream_handle(stream)))
+    _check(st, "spec_verify_greedy")
+    return out
+
+
+def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k=0, max_draft=None,
+                    greedy=False) -> int:
+    lib = load_library()
+    batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+    shape = make_shape(target_logits, None if greedy else draft_logits, batch, kmax, total, cu_draft)
+    need = C.c_size_t(0)
+    if greedy:
+        st = lib.spec_verify_greedy(C.byref(shape), None, None, None, None, None, C.byref(need), None)
+    else:
+        st = lib.spec_verify_sample(C.byref(shape), None, None, None, 1.0, int(top_k), 0, 0, None, None, None,
+                                    None, None, C.byref(need), None)
+    _check(st, "workspace query")
+    return need.value
+
+
+class HipEvents:
+    """n pairs of raw HIP events (created eagerly) for the profiling hook."""
+
+    def __init__(self, n: int):
+        self._hip = C.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.n = n
+        self.starts = (C.c_void_p * n)()
+        self.stops = (C.c_void_p * n)()
+        for i in range(n):
+            for arr in (self.starts, self.stops):
+                h = C.c_void_p()
+                if self._hip.hipEventCreate(C.byref(h)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = h
+
+    def arm(self):
+        """The next n library calls record their streaming kernel into these events."""
+        _check(load_library().spec_verify_set_profile_events(self.starts, self.stops, self.n), "profile events")
+
+    @staticmethod
+    def disarm():
+        _check(load_library().spec_verify_set_profile_events(None, None, 0), "profile events")
+
+    def elapsed_ms(self):
+        """Per-call durations (ms) of the streaming kernel; call after a device sync."""
+        out = []
+        for i in range(self.n):
+            ms = C.c_float(0)
+            if self._hip.hipEventElapsedTime(C.byref(ms), self.starts[i], self.stops[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for i in range(self.n):
+            self._hip.hipEventDestroy(self.starts[i])
+            self._hip.hipEventDestroy(self.stops[i])
+        self.n = 0

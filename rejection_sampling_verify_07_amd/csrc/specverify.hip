@@ -1,0 +1,311 @@
+// specverify C ABI: argument checks, workspace layout and kernel launches.
+// The operation and the conventions are documented in include/specverify.h.
+#include "specverify.h"
+
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sv_common.hpp"
+#include "sv_stats.hpp"
+#include "sv_topk.hpp"
+#include "sv_verify.hpp"
+
+static_assert(SV_MAX_DRAFT == sv::kMaxDraft, "draft limit mismatch");
+static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
+
+namespace {
+
+constexpr int kLoads = 4;            // 16-byte loads per thread per chunk in the streaming passes
+constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
+constexpr size_t kAlign = 256;
+
+enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
+
+struct Plan {
+    PlanMode mode;
+    int32_t rows_t, rows_d, rows;
+    int32_t nchunk;
+    size_t off_partials, off_counts, off_cands, off_descs, off_kept, bytes;
+};
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int vec_of(sv_dtype_t dt) { return dt == SV_DTYPE_F32 ? 4 : 8; }
+size_t esize_of(sv_dtype_t dt) { return dt == SV_DTYPE_F32 ? 4 : 2; }
+
+// Chunks per row of the streaming passes: a row with start misalignment up
+// to VEC-1 elements touches at most ceil((V + VEC - 1) / VEC) blocks.
+int32_t chunks_for(int32_t vocab, int vec)
+{
+    const int64_t nblk = ((int64_t)vocab + 2 * vec - 2) / vec;
+    const int64_t per = (int64_t)sv::kThreads * kLoads;
+    return (int32_t)((nblk + per - 1) / per);
+}
+
+// ---- profiling hook (benchmarks only; not thread-safe)
+hipEvent_t* g_prof_start = nullptr;
+hipEvent_t* g_prof_stop = nullptr;
+int32_t g_prof_n = 0;
+int32_t g_prof_i = 0;
+
+void prof_begin(hipStream_t s)
+{
+    if (g_prof_start != nullptr && g_prof_i < g_prof_n) (void)hipEventRecord(g_prof_start[g_prof_i], s);
+}
+void prof_end(hipStream_t s)
+{
+    if (g_prof_stop != nullptr && g_prof_i < g_prof_n) {
+        (void)hipEventRecord(g_prof_stop[g_prof_i], s);
+        ++g_prof_i;
+    }
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+sv_status_t check_shape(const sv_shape_t* sh, bool need_draft_rows)
+{
+    if (sh == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    if (sh->batch < 1 || sh->vocab < 1 || sh->max_draft < 0 || sh->total_draft < 0)
+        return SV_ERR_INVALID_ARGUMENT;
+    if (sh->dtype != SV_DTYPE_F32 && sh->dtype != SV_DTYPE_BF16) return SV_ERR_INVALID_ARGUMENT;
+    if (sh->cu_draft == nullptr && (int64_t)sh->total_draft != (int64_t)sh->batch * sh->max_draft)
+        return SV_ERR_INVALID_ARGUMENT;
+    if (sh->cu_draft != nullptr && !aligned(sh->cu_draft, 4)) return SV_ERR_INVALID_ARGUMENT;
+    if ((int64_t)sh->total_draft > (int64_t)sh->batch * sh->max_draft) return SV_ERR_INVALID_ARGUMENT;
+    if (sh->target_row_stride < sh->vocab) return SV_ERR_INVALID_ARGUMENT;
+    if (need_draft_rows && sh->total_draft > 0 && sh->draft_row_stride < sh->vocab)
+        return SV_ERR_INVALID_ARGUMENT;
+    if (sh->vocab > SV_MAX_VOCAB || sh->max_draft > SV_MAX_DRAFT) return SV_ERR_UNSUPPORTED;
+    const int64_t rows_t = (int64_t)sh->total_draft + sh->batch;
+    if (rows_t > INT32_MAX / 2) return SV_ERR_UNSUPPORTED;
+    return SV_OK;
+}
+
+Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
+{
+    Plan p{};
+    p.rows_t = sh->total_draft + sh->batch;
+    p.rows_d = greedy ? 0 : sh->total_draft;
+    p.rows = p.rows_t + p.rows_d;
+    p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype));
+    const bool topk = !greedy && top_k > 0 && top_k < sh->vocab;
+    if (greedy) {
+        p.mode = PLAN_GREEDY;
+    } else if (!topk) {
+        p.mode = PLAN_FULL;
+    } else {
+        p.mode = top_k <= sv::kTopkFastMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
+    }
+    size_t off = 0;
+    const size_t slots = (size_t)p.rows * (size_t)p.nchunk;
+    if (p.mode == PLAN_FULL) {
+        p.off_partials = off;
+        off = align_up(off + slots * sizeof(sv::PartialFull));
+    } else if (p.mode == PLAN_GREEDY) {
+        p.off_partials = off;
+        off = align_up(off + slots * sizeof(sv::PartialArg));
+    } else {
+        if (p.mode == PLAN_TOPK_FAST) {
+            p.off_counts = off;
+            off = align_up(off + slots * sizeof(int32_t));
+            p.off_cands = off;
+            off = align_up(off + slots * (size_t)kCandCap * sizeof(sv::KeptEntry));
+        }
+        p.off_descs = off;
+        off = align_up(off + (size_t)p.rows * sizeof(sv::RowDesc));
+        p.off_kept = off;
+        off = align_up(off + (size_t)p.rows * sv::kKeepCap * sizeof(sv::KeptEntry));
+    }
+    p.bytes = off == 0 ? kAlign : off;
+    return p;
+}
+
+template <class T>
+T* ws_at(void* ws, size_t off)
+{
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+sv_status_t launch_status()
+{
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+template <int DT>
+sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
+                       const int32_t* ids, float c, int32_t top_k, uint64_t seed, uint32_t offset,
+                       int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
+                       hipStream_t stream)
+{
+    const size_t es = esize_of(sh->dtype);
+    sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
+                  (int64_t)(sh->target_row_stride * (int64_t)es), (int64_t)(sh->draft_row_stride * (int64_t)es),
+                  p.rows_t};
+    const uint32_t grid_stream = (uint32_t)((int64_t)p.rows * p.nchunk);
+
+    sv::VerifyArgs va{};
+    va.rs = rs;
+    va.cu = sh->cu_draft;
+    va.batch = sh->batch;
+    va.kmax = sh->max_draft;
+    va.total_draft = sh->total_draft;
+    va.vocab = sh->vocab;
+    va.ids = ids;
+    va.c = c;
+    va.seed = seed;
+    va.offset = offset;
+    va.nchunk = p.nchunk;
+    va.out_tokens = out_tokens;
+    va.out_nacc = out_nacc;
+    va.out_probs = out_probs;
+    va.out_zmass = out_z;
+
+    if (p.mode == PLAN_FULL) {
+        sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
+        prof_begin(stream);
+        hipLaunchKernelGGL((sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, false>), dim3(grid_stream),
+                           dim3(sv::kThreads), 0, stream, rs, sh->vocab, p.nchunk, c, (void*)part);
+        prof_end(stream);
+        if (launch_status() != SV_OK) return SV_ERR_HIP;
+        va.partials = part;
+        hipLaunchKernelGGL((sv::verify_kernel<DT, false>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
+        return launch_status();
+    }
+
+    sv::RowDesc* descs = ws_at<sv::RowDesc>(ws, p.off_descs);
+    sv::KeptEntry* kept = ws_at<sv::KeptEntry>(ws, p.off_kept);
+    int32_t* counts = nullptr;
+    sv::KeptEntry* cands = nullptr;
+    if (p.mode == PLAN_TOPK_FAST) {
+        counts = ws_at<int32_t>(ws, p.off_counts);
+        cands = ws_at<sv::KeptEntry>(ws, p.off_cands);
+        prof_begin(stream);
+        hipLaunchKernelGGL((sv::topk_cand_kernel<DT, kLoads, false>), dim3(grid_stream), dim3(sv::kThreads), 0,
+                           stream, rs, sh->vocab, p.nchunk, top_k, kCandCap, counts, cands);
+        prof_end(stream);
+        if (launch_status() != SV_OK) return SV_ERR_HIP;
+    }
+    hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
+                       p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)(p.mode == PLAN_TOPK_FAST),
+                       (int32_t)sv::kKeepCap, descs, kept);
+    if (launch_status() != SV_OK) return SV_ERR_HIP;
+    va.descs = descs;
+    va.kept = kept;
+    hipLaunchKernelGGL((sv::verify_kernel<DT, true>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
+    return launch_status();
+}
+
+template <int DT>
+sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, const int32_t* ids,
+                       int32_t* out_tokens, int32_t* out_nacc, void* ws, hipStream_t stream)
+{
+    const size_t es = esize_of(sh->dtype);
+    sv::RowSet rs{static_cast<const char*>(tgt), nullptr, (int64_t)(sh->target_row_stride * (int64_t)es), 0,
+                  p.rows_t};
+    sv::PartialArg* part = ws_at<sv::PartialArg>(ws, p.off_partials);
+    const uint32_t grid_stream = (uint32_t)((int64_t)p.rows_t * p.nchunk);
+    prof_begin(stream);
+    hipLaunchKernelGGL((sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, false>), dim3(grid_stream),
+                       dim3(sv::kThreads), 0, stream, rs, sh->vocab, p.nchunk, 0.0f, (void*)part);
+    prof_end(stream);
+    if (launch_status() != SV_OK) return SV_ERR_HIP;
+    sv::GreedyArgs ga{sh->cu_draft, sh->batch, sh->max_draft, sh->total_draft, sh->vocab, ids, part, p.nchunk,
+                      out_tokens, out_nacc};
+    hipLaunchKernelGGL(sv::greedy_kernel, dim3((sh->batch + sv::kWaves - 1) / sv::kWaves), dim3(sv::kThreads), 0,
+                       stream, ga);
+    return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream)
+{
+    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    sv_status_t st = check_shape(shape, true);
+    if (st != SV_OK) return st;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
+    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, false, top_k);
+    if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    if (workspace == nullptr) {
+        *workspace_bytes = p.bytes;
+        return SV_OK;
+    }
+    const size_t es = esize_of(shape->dtype);
+    if (target_logits == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    if (shape->total_draft > 0 && (draft_logits == nullptr || draft_ids == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(target_logits, es) || (draft_logits != nullptr && !aligned(draft_logits, es)))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) || (draft_ids && !aligned(draft_ids, 4)) ||
+        (out_probs && !aligned(out_probs, 4)) || (out_residual_mass && !aligned(out_residual_mass, 4)))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
+    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+
+    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    if (shape->dtype == SV_DTYPE_F32)
+        return run_sample<sv::DT_F32>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
+                                      out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream);
+    return run_sample<sv::DT_BF16>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
+                                   out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream);
+}
+
+sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,
+                               int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream)
+{
+    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    sv_status_t st = check_shape(shape, false);
+    if (st != SV_OK) return st;
+    const Plan p = make_plan(shape, true, 0);
+    if ((int64_t)p.rows_t * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    if (workspace == nullptr) {
+        *workspace_bytes = p.bytes;
+        return SV_OK;
+    }
+    const size_t es = esize_of(shape->dtype);
+    if (target_logits == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    if (shape->total_draft > 0 && draft_ids == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(target_logits, es) || !aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) ||
+        (draft_ids && !aligned(draft_ids, 4)))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
+    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (shape->dtype == SV_DTYPE_F32)
+        return run_greedy<sv::DT_F32>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
+                                      stream);
+    return run_greedy<sv::DT_BF16>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
+                                   stream);
+}
+
+const char* spec_verify_status_string(sv_status_t status)
+{
+    switch (status) {
+        case SV_OK: return "SV_OK";
+        case SV_ERR_INVALID_ARGUMENT: return "SV_ERR_INVALID_ARGUMENT";
+        case SV_ERR_UNSUPPORTED: return "SV_ERR_UNSUPPORTED";
+        case SV_ERR_WORKSPACE_TOO_SMALL: return "SV_ERR_WORKSPACE_TOO_SMALL";
+        case SV_ERR_HIP: return "SV_ERR_HIP";
+    }
+    return "SV_ERR_UNKNOWN";
+}
+
+sv_status_t spec_verify_set_profile_events(hipEvent_t* starts, hipEvent_t* stops, int32_t n)
+{
+    if (n < 0 || (n > 0 && (starts == nullptr || stops == nullptr))) return SV_ERR_INVALID_ARGUMENT;
+    g_prof_start = n > 0 ? starts : nullptr;
+    g_prof_stop = n > 0 ? stops : nullptr;
+    g_prof_n = n;
+    g_prof_i = 0;
+    return SV_OK;
+}
+
+}  // extern "C"

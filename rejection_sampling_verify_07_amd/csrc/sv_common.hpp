@@ -1,0 +1,254 @@
+// Device-side building blocks shared by the specverify kernels (gfx950).
+//
+// Wavefronts are 64 lanes; every kernel runs 256-thread workgroups (4 waves,
+// one per SIMD of a CU).  Logit rows are read in 16-byte vector loads
+// (8 bf16 or 4 fp32 values); bf16 widens to fp32 exactly (the bf16 bits are
+// the top half of the fp32 word).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+template <int DT>
+struct Dt;
+template <>
+struct Dt<DT_F32> {
+    static constexpr int kSize = 4;
+    static constexpr int kVec = 4;
+};
+template <>
+struct Dt<DT_BF16> {
+    static constexpr int kSize = 2;
+    static constexpr int kVec = 8;
+};
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+// ---------------------------------------------------------------------------
+// Loads
+// ---------------------------------------------------------------------------
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p)
+{
+    if constexpr (NT) {
+        return __builtin_nontemporal_load(p);
+    } else {
+        return *p;
+    }
+}
+
+// Widen one 16-byte block to kVec fp32 values.
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 w, float* f)
+{
+    if constexpr (DT == DT_F32) {
+        f[0] = __uint_as_float(w.x);
+        f[1] = __uint_as_float(w.y);
+        f[2] = __uint_as_float(w.z);
+        f[3] = __uint_as_float(w.w);
+    } else {
+        f[0] = __uint_as_float(w.x << 16);
+        f[1] = __uint_as_float(w.x & 0xffff0000u);
+        f[2] = __uint_as_float(w.y << 16);
+        f[3] = __uint_as_float(w.y & 0xffff0000u);
+        f[4] = __uint_as_float(w.z << 16);
+        f[5] = __uint_as_float(w.z & 0xffff0000u);
+        f[6] = __uint_as_float(w.w << 16);
+        f[7] = __uint_as_float(w.w & 0xffff0000u);
+    }
+}
+
+// One element of a row, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float load_one(const char* row, int64_t i)
+{
+    if constexpr (DT == DT_F32) {
+        return reinterpret_cast<const float*>(row)[i];
+    } else {
+        const uint32_t b = reinterpret_cast<const uint16_t*>(row)[i];
+        return __uint_as_float(b << 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Monotone map float -> uint32 (a < b  <=>  key(a) < key(b), for non-NaN).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k)
+{
+    const uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(b);
+}
+
+// ---------------------------------------------------------------------------
+// Wave primitives (64 lanes).  Reductions run a fixed butterfly, so the
+// result is the same on every run; consumers take lane 0's copy.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return __shfl(v, 0, kWave);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Inclusive prefix sum over the lanes (Hillis-Steele, fixed order).
+__device__ __forceinline__ double wave_incl_scan(double v)
+{
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double t = __shfl_up(v, o, kWave);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int v)
+{
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(v, o, kWave);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+// (value, index) arg-max with the lower index winning ties.
+__device__ __forceinline__ void argmax_merge(float& v, int32_t& i, float ov, int32_t oi)
+{
+    if (ov > v || (ov == v && oi < i)) {
+        v = ov;
+        i = oi;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int32_t& i)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(v, o, kWave);
+        const int32_t oi = __shfl_xor(i, o, kWave);
+        argmax_merge(v, i, ov, oi);
+    }
+}
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of the
+// two-multiplier S-box over a 4-word counter with a Weyl-incremented 2-word
+// key.  Only output word 0 is needed here.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                                 uint32_t k0, uint32_t k1)
+{
+    constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
+    constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t a_hi = __umulhi(kMulA, x0), a_lo = kMulA * x0;
+        const uint32_t b_hi = __umulhi(kMulB, x2), b_lo = kMulB * x2;
+        const uint32_t y0 = b_hi ^ x1 ^ k0;
+        const uint32_t y2 = a_hi ^ x3 ^ k1;
+        x0 = y0;
+        x1 = b_lo;
+        x2 = y2;
+        x3 = a_lo;
+        k0 += kWeylA;
+        k1 += kWeylB;
+    }
+    return x0;
+}
+
+// U(seq, pos, purpose) in [0, 1): 24 high bits of word 0, exact in fp32/fp64.
+__device__ __forceinline__ double uniform24(uint64_t seed, uint32_t seq, uint32_t pos,
+                                            uint32_t purpose, uint32_t offset)
+{
+    const uint32_t w = philox_word0(seq, pos, purpose, offset, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32));
+    return (double)(w >> 8) * (1.0 / 16777216.0);
+}
+
+// ---------------------------------------------------------------------------
+// Row addressing: rows [0, rows_t) are target rows, the rest draft rows.
+// ---------------------------------------------------------------------------
+struct RowSet {
+    const char* tgt;
+    const char* drf;
+    int64_t t_stride_bytes;
+    int64_t d_stride_bytes;
+    int32_t rows_t;
+};
+
+__device__ __forceinline__ const char* row_ptr(const RowSet& rs, int32_t row)
+{
+    return row < rs.rows_t ? rs.tgt + (int64_t)row * rs.t_stride_bytes
+                           : rs.drf + (int64_t)(row - rs.rows_t) * rs.d_stride_bytes;
+}
+
+// Per-(row, chunk) results of the streaming pass.
+struct PartialFull {  // sampling: chunk max and sum of exp2(l*c - mcc) at the chunk's own max
+    float m;
+    float mcc;
+    double s;
+};
+struct PartialArg {  // greedy: chunk max and its lowest index (row-relative)
+    float m;
+    int32_t idx;
+};
+
+// Per-row description used by the accept/resample pass.
+struct RowDesc {
+    float tau;      // kept set = { v : l_v >= tau } (-inf keeps every id)
+    float m;        // largest kept logit
+    float mcc;      // fl32(m * c), c = log2(e) / T in fp32
+    int32_t kept;   // >= 0: number of entries in the row's kept list; -1: full row masked by tau
+    double s;       // sum over kept v of exp2(fl32(l_v * c - mcc))
+    int32_t flags;  // bit 0: candidate overflow took the exact full-row path
+    int32_t pad;
+};
+
+struct KeptEntry {
+    int32_t idx;
+    float val;
+};
+
+}  // namespace sv

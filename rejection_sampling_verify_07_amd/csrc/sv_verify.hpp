@@ -1,0 +1,517 @@
+// Accept / first rejection / residual or extra-token draw, one workgroup per
+// sequence.  Follows the acceptance rule, residual and proof of
+// "CS3602_FINAL_SpeDec" (section 2: accept x ~ q with min(1, p(x)/q(x)), on
+// rejection draw from norm(max(0, p - q)) whose normaliser is 1 - beta) and
+// the loop shape of "Text Generation via Speculative Sampling, KV Caching,
+// and OpenVINO" ("Prepare speculative sampling", steps 3 and 4: one uniform
+// per guess, stop at the first rejection, one extra token from the last
+// target position when every guess is accepted).
+//
+// Phases (one 256-thread workgroup per sequence b):
+//  A  per-row statistics of the sequence's K_b+1 target and K_b draft rows,
+//     merged from the streaming pass's chunk partials (m, S) or read from the
+//     top-k select pass's row descriptors;
+//  B  every guess at once: p_k(x_k), q_k(x_k) in fp64 from the gathered
+//     logits, u_k = U(b, k, 0), accept iff u_k < min(1, p/q); n = the first
+//     rejected position (LDS atomic min) or K_b;
+//  C  one inverse-CDF draw in ascending id order: the residual
+//     max(0, p_n - q_n) with U(b, n, 1), or p_{K_b} with U(b, K_b, 2).  Over a
+//     full row it runs as 512-id segments (fp32 weights, fp64 sums, one
+//     wave-scan per segment), a workgroup scan of the segment sums, and a
+//     re-walk of the one segment that holds the crossing.  Over a top-k kept
+//     list (at most 1024 ids, sorted by id) one wave does it in registers;
+//  D  tokens, accepted count, residual mass.
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+constexpr int kMaxDraft = 128;       // largest K (rows per sequence 2K+1)
+constexpr int kSegElems = 8;         // ids per lane per segment
+constexpr int kSeg = kWave * kSegElems;   // 512 ids per segment
+constexpr int kMaxSeg = (1 << 20) / kSeg;  // vocabularies up to 2^20
+constexpr int kSegUnroll = 4;        // segments per wave with loads in flight together
+constexpr int kKeepCap = 1024;       // kept-list capacity per row
+
+struct VerifyArgs {
+    RowSet rs;
+    const int32_t* cu;  // device [B+1] or null
+    int32_t batch;
+    int32_t kmax;
+    int32_t total_draft;
+    int32_t vocab;
+    const int32_t* ids;
+    float c;  // log2(e) / T, fp32
+    uint64_t seed;
+    uint32_t offset;
+    // statistics source: chunk partials (no top-k) or row descriptors (top-k)
+    const PartialFull* partials;
+    int32_t nchunk;
+    const RowDesc* descs;
+    const KeptEntry* kept;
+    // outputs
+    int32_t* out_tokens;
+    int32_t* out_nacc;
+    float* out_probs;
+    float* out_zmass;
+};
+
+struct RowLds {
+    float tau;
+    float mcc;
+    float inv_s;   // fl32(1 / S)
+    int32_t kept;  // list length, or -1 for a full row
+    double s;
+};
+
+// Weights of the inverse-CDF draw, in probability units (fp32).
+struct ResidualW {
+    float tau_t, mcc_t, inv_t, tau_d, mcc_d, inv_d, c;
+    __device__ __forceinline__ float operator()(float lt, float ld) const
+    {
+        const float et = lt >= tau_t ? __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) : 0.0f;
+        const float ed = ld >= tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d)) : 0.0f;
+        return fmaxf(et * inv_t - ed * inv_d, 0.0f);
+    }
+};
+struct BonusW {
+    float tau_t, mcc_t, inv_t, c;
+    __device__ __forceinline__ float operator()(float lt, float) const
+    {
+        return lt >= tau_t ? __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) * inv_t : 0.0f;
+    }
+};
+
+// Weights of one lane's kSegElems ids of segment s (0 outside the row).
+template <int DT, bool TWO, class W>
+__device__ __forceinline__ void seg_weights(const char* ra, const char* rb, int32_t vocab, bool vec,
+                                            int32_t s, const W& wfn, float* w)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int NV = kSegElems / VEC;  // 16-byte loads per lane per row
+    const int32_t v0 = s * kSeg + lane_id() * kSegElems;
+    if (vec && v0 + kSegElems <= vocab) {
+        const u32x4* pa = reinterpret_cast<const u32x4*>(ra) + v0 / VEC;
+        const u32x4* pb = reinterpret_cast<const u32x4*>(rb) + v0 / VEC;
+        u32x4 wa[NV], wb[NV];
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            wa[q] = pa[q];
+            if constexpr (TWO) wb[q] = pb[q];
+        }
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            float fa[VEC], fb[VEC];
+            unpack<DT>(wa[q], fa);
+            if constexpr (TWO) unpack<DT>(wb[q], fb);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) w[q * VEC + e] = wfn(fa[e], TWO ? fb[e] : 0.0f);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kSegElems; ++e) {
+            const int32_t v = v0 + e;
+            w[e] = (v < vocab) ? wfn(load_one<DT>(ra, v), TWO ? load_one<DT>(rb, v) : 0.0f) : 0.0f;
+        }
+    }
+}
+
+// Inverse CDF over a full row (or row pair).  All threads call it; all get
+// the token and the total.
+template <int DT, bool TWO, class W>
+__device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, const W& wfn, double u,
+                                 double* s_seg, double* s_wd, int32_t* s_i, double* s_dd,
+                                 int32_t* token, double* total)
+{
+    const int32_t nseg = (vocab + kSeg - 1) / kSeg;
+    const bool vec = ((uintptr_t)ra & 15u) == 0 && (!TWO || ((uintptr_t)rb & 15u) == 0);
+    const int lane = lane_id();
+
+    // pass 1: per-segment sums (lane sums in fp64, then a wave inclusive scan)
+    for (int32_t s0 = wave_id(); s0 < nseg; s0 += kWaves * kSegUnroll) {
+        float w[kSegUnroll][kSegElems];
+#pragma unroll
+        for (int uu = 0; uu < kSegUnroll; ++uu) {
+            const int32_t s = s0 + uu * kWaves;
+            if (s < nseg) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
+        }
+#pragma unroll
+        for (int uu = 0; uu < kSegUnroll; ++uu) {
+            const int32_t s = s0 + uu * kWaves;
+            if (s < nseg) {
+                double ls = 0.0;
+#pragma unroll
+                for (int e = 0; e < kSegElems; ++e) ls += (double)w[uu][e];
+                const double incl = wave_incl_scan(ls);
+                if (lane == kWave - 1) s_seg[s] = incl;
+            }
+        }
+    }
+    __syncthreads();
+
+    // workgroup inclusive scan of the segment sums, in place
+    const int32_t per = (nseg + kThreads - 1) / kThreads;
+    const int32_t lo = min(nseg, (int32_t)threadIdx.x * per), hi = min(nseg, lo + per);
+    double run = 0.0;
+    for (int32_t s = lo; s < hi; ++s) {
+        run += s_seg[s];
+        s_seg[s] = run;
+    }
+    const double tincl = wave_incl_scan(run);
+    double texcl = __shfl_up(tincl, 1, kWave);
+    if (lane == 0) texcl = 0.0;
+    if (lane == kWave - 1) s_wd[wave_id()] = tincl;
+    __syncthreads();
+    double off = 0.0;
+    for (int w = 0; w < wave_id(); ++w) off += s_wd[w];
+    off += texcl;
+    for (int32_t s = lo; s < hi; ++s) s_seg[s] += off;
+    if (threadIdx.x == 0) s_i[0] = nseg;
+    __syncthreads();
+    const double z = s_seg[nseg - 1];
+    const double t = u * z;
+    for (int32_t s = lo; s < hi; ++s) {
+        if (s_seg[s] > t) {
+            atomicMin(&s_i[0], s);
+            break;
+        }
+    }
+    __syncthreads();
+
+    // pass 2: re-walk the segment holding the crossing (wave 0)
+    if (wave_id() == 0) {
+        int32_t s = s_i[0];
+        if (s >= nseg) s = nseg - 1;
+        int32_t tok = -1;
+        for (; s >= 0 && tok < 0; --s) {
+            float w[kSegElems];
+            seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w);
+            double ls = 0.0;
+#pragma unroll
+            for (int e = 0; e < kSegElems; ++e) ls += (double)w[e];
+            const double incl = wave_incl_scan(ls);
+            double excl = __shfl_up(incl, 1, kWave);
+            if (lane == 0) excl = 0.0;
+            double cum = (s > 0 ? s_seg[s - 1] : 0.0) + excl;
+            int hit = -1, lastpos = -1;
+#pragma unroll
+            for (int e = 0; e < kSegElems; ++e) {
+                cum += (double)w[e];
+                if (hit < 0 && cum > t) hit = e;
+                if (w[e] > 0.0f) lastpos = e;
+            }
+            const uint64_t bh = __ballot(hit >= 0);
+            if (bh != 0) {
+                const int src = __builtin_ctzll(bh);
+                tok = s * kSeg + src * kSegElems + __shfl(hit, src, kWave);
+            } else {
+                // rounding put the target past this segment's walk: its last positive id
+                const uint64_t bp = __ballot(lastpos >= 0);
+                if (bp != 0) {
+                    const int src = 63 - __builtin_clzll(bp);
+                    tok = s * kSeg + src * kSegElems + __shfl(lastpos, src, kWave);
+                }
+            }
+        }
+        if (lane == 0) {
+            s_i[1] = tok;
+            s_dd[0] = z;
+        }
+    }
+    __syncthreads();
+    *token = s_i[1];
+    *total = s_dd[0];
+    __syncthreads();
+}
+
+// Inverse CDF over a kept list (ascending ids), wave 0 only.
+template <int DT, bool RESID>
+__device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* drow, const ResidualW& rw,
+                                 double u, int32_t* token, double* total)
+{
+    constexpr int PER = kKeepCap / kWave;  // entries per lane
+    const int lane = lane_id();
+    const int32_t per = (n + kWave - 1) / kWave;
+    const int32_t lo = min(n, lane * per), hi = min(n, lo + per);
+    float w[PER];
+    int32_t ix[PER];
+    double ls = 0.0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int32_t i = lo + q;
+        w[q] = 0.0f;
+        ix[q] = -1;
+        if (i < hi) {
+            const KeptEntry e = list[i];
+            ix[q] = e.idx;
+            const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
+            if constexpr (RESID) {
+                const float ld = load_one<DT>(drow, e.idx);
+                const float ed =
+                    ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
+                w[q] = fmaxf(et - ed, 0.0f);
+            } else {
+                w[q] = et;
+            }
+            ls += (double)w[q];
+        }
+    }
+    const double incl = wave_incl_scan(ls);
+    double excl = __shfl_up(incl, 1, kWave);
+    if (lane == 0) excl = 0.0;
+    const double z = __shfl(incl, kWave - 1, kWave);
+    const double t = u * z;
+    double cum = excl;
+    int hit = -1, lastpos = -1;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        cum += (double)w[q];
+        if (hit < 0 && ix[q] >= 0 && cum > t) hit = ix[q];
+        if (w[q] > 0.0f) lastpos = ix[q];
+    }
+    int32_t tok = -1;
+    const uint64_t bh = __ballot(hit >= 0);
+    if (bh != 0) {
+        tok = __shfl(hit, __builtin_ctzll(bh), kWave);
+    } else {
+        const uint64_t bp = __ballot(lastpos >= 0);
+        if (bp != 0) tok = __shfl(lastpos, 63 - __builtin_clzll(bp), kWave);
+    }
+    *token = tok;
+    *total = z;
+}
+
+template <int DT, bool FROM_DESC>
+__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
+{
+    __shared__ RowLds s_row[2 * kMaxDraft + 1];
+    __shared__ double s_seg[kMaxSeg];
+    __shared__ double s_wd[kWaves];
+    __shared__ double s_dd[2];
+    __shared__ int32_t s_i[4];
+    __shared__ int32_t s_n, s_bad;
+
+    const int32_t b = blockIdx.x;
+    int32_t k0, kb;
+    if (a.cu != nullptr) {
+        k0 = a.cu[b];
+        const int32_t k1 = a.cu[b + 1];
+        kb = k1 - k0;
+        if (k0 < 0 || kb < 0 || kb > a.kmax || k1 > a.total_draft) {
+            if (threadIdx.x == 0) a.out_nacc[b] = -1;
+            return;
+        }
+    } else {
+        k0 = b * a.kmax;
+        kb = a.kmax;
+    }
+    const int32_t trow0 = k0 + b;  // first target row of the sequence
+    const int32_t drow0 = k0;      // first draft row
+    const int32_t nrows = 2 * kb + 1;
+    const int32_t rows_t = a.rs.rows_t;
+    auto grow = [&](int32_t r) {  // sequence row r -> global row (target rows first)
+        return r <= kb ? trow0 + r : rows_t + drow0 + (r - kb - 1);
+    };
+
+    if (threadIdx.x == 0) {
+        s_n = kb;
+        s_bad = 0;
+    }
+
+    // ---- A: row statistics
+    if constexpr (FROM_DESC) {
+        for (int32_t r = threadIdx.x; r < nrows; r += kThreads) {
+            const RowDesc d = a.descs[grow(r)];
+            s_row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
+        }
+    } else {
+        for (int32_t r = wave_id(); r < nrows; r += kWaves) {
+            const PartialFull* pp = a.partials + (int64_t)grow(r) * a.nchunk;
+            float m = neg_inf();
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
+            m = __shfl(wave_max(m), 0, kWave);
+            const float mcc = m * a.c;
+            double s = 0.0;
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
+                const PartialFull q = pp[ch];
+                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
+            }
+            s = wave_sum(s);
+            if (lane_id() == 0) s_row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+        }
+    }
+    __syncthreads();
+
+    // ---- B: accept test at every draft position
+    const char* tbase = a.rs.tgt;
+    const char* dbase = a.rs.drf;
+    for (int32_t k = threadIdx.x; k < kb; k += kThreads) {
+        const int32_t x = a.ids[drow0 + k];
+        if (x < 0 || x >= a.vocab) {
+            atomicOr(&s_bad, 1);
+            continue;
+        }
+        const float lt = load_one<DT>(tbase + (int64_t)(trow0 + k) * a.rs.t_stride_bytes, x);
+        const float ld = load_one<DT>(dbase + (int64_t)(drow0 + k) * a.rs.d_stride_bytes, x);
+        const RowLds& rt = s_row[k];
+        const RowLds& rd = s_row[kb + 1 + k];
+        const double cd = (double)a.c;
+        const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
+        const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
+        if (a.out_probs != nullptr) {
+            a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
+            a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
+        }
+        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)k, 0u, a.offset);
+        const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+        if (!(u < ratio)) atomicMin(&s_n, k);
+    }
+    __syncthreads();
+    if (s_bad != 0) {
+        if (threadIdx.x == 0) a.out_nacc[b] = -1;
+        return;
+    }
+    const int32_t n = s_n;
+
+    // ---- C: residual or extra-token draw
+    int32_t token = -1;
+    double z = 0.0;
+    const RowLds rt = s_row[n];
+    const char* trow = tbase + (int64_t)(trow0 + n) * a.rs.t_stride_bytes;
+    if (n < kb) {
+        const RowLds rd = s_row[kb + 1 + n];
+        const char* drow = dbase + (int64_t)(drow0 + n) * a.rs.d_stride_bytes;
+        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)n, 1u, a.offset);
+        const ResidualW wfn{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
+        if (FROM_DESC && rt.kept >= 0) {
+            if (wave_id() == 0) {
+                inverse_cdf_list<DT, true>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, drow, wfn, u, &token, &z);
+                if (lane_id() == 0) {
+                    s_i[2] = token;
+                    s_dd[1] = z;
+                }
+            }
+            __syncthreads();
+            token = s_i[2];
+            z = s_dd[1];
+        } else {
+            inverse_cdf_full<DT, true>(trow, drow, a.vocab, wfn, u, s_seg, s_wd, s_i, s_dd, &token, &z);
+        }
+        if (token < 0) {
+            // no positive residual mass (rounding only): draw from p_n with the same uniform
+            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+            double z2;
+            if (FROM_DESC && rt.kept >= 0) {
+                if (wave_id() == 0) {
+                    const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+                    inverse_cdf_list<DT, false>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, nullptr, lw, u,
+                                                &token, &z2);
+                    if (lane_id() == 0) s_i[2] = token;
+                }
+                __syncthreads();
+                token = s_i[2];
+            } else {
+                inverse_cdf_full<DT, false>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &z2);
+            }
+        }
+    } else {
+        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)kb, 2u, a.offset);
+        if (FROM_DESC && rt.kept >= 0) {
+            if (wave_id() == 0) {
+                const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+                double zz;
+                inverse_cdf_list<DT, false>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, nullptr, lw, u, &token,
+                                            &zz);
+                if (lane_id() == 0) s_i[2] = token;
+            }
+            __syncthreads();
+            token = s_i[2];
+        } else {
+            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+            double zz;
+            inverse_cdf_full<DT, false>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &zz);
+        }
+        z = 0.0;
+    }
+
+    // ---- D: outputs
+    for (int32_t j = threadIdx.x; j <= kb; j += kThreads) {
+        a.out_tokens[trow0 + j] = j < n ? a.ids[drow0 + j] : (j == n ? token : -1);
+    }
+    if (threadIdx.x == 0) {
+        a.out_nacc[b] = n;
+        if (a.out_zmass != nullptr) a.out_zmass[b] = (float)z;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Greedy argmax-compare: one wave per sequence merges the argmax partials of
+// its K_b + 1 target rows and compares them with the guesses.
+// ---------------------------------------------------------------------------
+struct GreedyArgs {
+    const int32_t* cu;
+    int32_t batch;
+    int32_t kmax;
+    int32_t total_draft;
+    int32_t vocab;
+    const int32_t* ids;
+    const PartialArg* partials;
+    int32_t nchunk;
+    int32_t* out_tokens;
+    int32_t* out_nacc;
+};
+
+__global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs a)
+{
+    const int32_t b = blockIdx.x * kWaves + wave_id();
+    if (b >= a.batch) return;
+    int32_t k0, kb;
+    if (a.cu != nullptr) {
+        k0 = a.cu[b];
+        const int32_t k1 = a.cu[b + 1];
+        kb = k1 - k0;
+        if (k0 < 0 || kb < 0 || kb > a.kmax || k1 > a.total_draft) {
+            if (lane_id() == 0) a.out_nacc[b] = -1;
+            return;
+        }
+    } else {
+        k0 = b * a.kmax;
+        kb = a.kmax;
+    }
+    const int32_t trow0 = k0 + b;
+    int32_t n = kb, an = -1;
+    bool bad = false;
+    for (int32_t k = 0; k <= kb; ++k) {
+        const PartialArg* pp = a.partials + (int64_t)(trow0 + k) * a.nchunk;
+        float v = neg_inf();
+        int32_t ix = INT32_MAX;
+        for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) argmax_merge(v, ix, pp[ch].m, pp[ch].idx);
+        wave_argmax(v, ix);
+        ix = __shfl(ix, 0, kWave);
+        if (k == kb) {
+            an = ix;
+            break;
+        }
+        const int32_t x = a.ids[k0 + k];
+        if (x < 0 || x >= a.vocab) {
+            bad = true;
+            break;
+        }
+        if (x != ix) {
+            n = k;
+            an = ix;
+            break;
+        }
+    }
+    if (bad) {
+        if (lane_id() == 0) a.out_nacc[b] = -1;
+        return;
+    }
+    for (int32_t j = lane_id(); j <= kb; j += kWave) {
+        a.out_tokens[trow0 + j] = j < n ? a.ids[k0 + j] : (j == n ? an : -1);
+    }
+    if (lane_id() == 0) a.out_nacc[b] = n;
+}
+
+}  // namespace sv

@@ -1,0 +1,129 @@
+"""Helpers of the GPU parity tests: run a workload through the C ABI (via
+the binding) and compare it with the oracle under the boundary policy."""
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import rejection_sampling_verify_07_amd as sv
+
+EPS_BOUNDARY = 1e-6  # a draw whose uniform lies this close to a threshold is a boundary draw
+RTOL = {"f32": 1e-5, "bf16": 2e-3}  # probability tolerance by input dtype
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(w, dev="cuda:0"):
+    if w.dtype == "f32":
+        tgt = torch.from_numpy(np.ascontiguousarray(w.target)).to(dev)
+        drf = torch.from_numpy(np.ascontiguousarray(w.draft)).to(dev)
+    else:
+        tgt = torch.from_numpy(np.ascontiguousarray(w.target).view(np.int16)).to(dev).view(torch.bfloat16)
+        drf = torch.from_numpy(np.ascontiguousarray(w.draft).view(np.int16)).to(dev).view(torch.bfloat16)
+    ids = torch.from_numpy(w.draft_ids.astype(np.int32)).to(dev)
+    cu = torch.from_numpy(w.cu_draft.astype(np.int32)).to(dev) if w.ragged else None
+    return tgt, drf, ids, cu
+
+
+def gpu_sample(w, tensors=None, **kw):
+    tgt, drf, ids, cu = tensors or to_device(w)
+    out = sv.verify_sample(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
+                           offset=w.offset, max_draft=w.k_max if cu is not None else None, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def gpu_greedy(w, tensors=None, ids_override=None):
+    tgt, drf, ids, cu = tensors or to_device(w)
+    if ids_override is not None:
+        ids = torch.from_numpy(ids_override.astype(np.int32)).to(tgt.device)
+    out = sv.verify_greedy(tgt, ids, cu_draft=cu, max_draft=w.k_max if cu is not None else None)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@dataclasses.dataclass
+class Report:
+    sequences: int = 0
+    exact: int = 0
+    boundary_accept: int = 0
+    boundary_final: int = 0
+    max_rel_p: float = 0.0
+    max_rel_z: float = 0.0
+
+    def __str__(self):
+        return (f"{self.sequences} sequences: {self.exact} compared bit-exactly, boundary draws: "
+                f"{self.boundary_accept} accept / {self.boundary_final} final; max rel err p,q {self.max_rel_p:.2e}, "
+                f"Z {self.max_rel_z:.2e}")
+
+
+def compare_sample(w, g, o, seqs=None, rtol=None):
+    """Assert GPU outputs g match oracle outputs o under the boundary policy."""
+    rtol = rtol if rtol is not None else RTOL[w.dtype]
+    rep = Report()
+    seqs = range(w.batch) if seqs is None else seqs
+    cu = w.cu_draft
+    for b in seqs:
+        K = int(w.draft_lens[b])
+        t0 = int(cu[b]) + b
+        d0 = int(cu[b])
+        n_o = int(o["num_accepted"][b])
+        n_g = int(g["num_accepted"][b])
+        tok_o = o["tokens"][t0:t0 + K + 1]
+        tok_g = g["tokens"][t0:t0 + K + 1]
+        ids = w.draft_ids[d0:d0 + K]
+        rep.sequences += 1
+        assert n_o >= 0, f"oracle rejected sequence {b}"
+        # probabilities of every guess
+        if "probs" in g and K > 0:
+            pg = g["probs"][d0:d0 + K].astype(np.float64)
+            po = o["probs"][d0:d0 + K]
+            err = np.abs(pg - po)
+            lim = rtol * np.abs(po) + 1e-37
+            assert np.all(err <= lim), f"seq {b}: p,q gpu {pg.tolist()} oracle {po.tolist()}"
+            rel = err / np.maximum(np.abs(po), 1e-30)
+            rep.max_rel_p = max(rep.max_rel_p, float(rel[np.abs(po) > 1e-30].max(initial=0)))
+        # evaluated accept draws and their boundary distances
+        evaluated = range(min(n_o + 1, K))
+        kstar = next((k for k in evaluated if o["d_acc"][d0 + k] < EPS_BOUNDARY), None)
+        final_boundary = o["d_fin"][b] < EPS_BOUNDARY
+        # GPU output must always be well formed
+        assert 0 <= n_g <= K, f"seq {b}: num_accepted {n_g}"
+        assert np.array_equal(tok_g[:n_g], ids[:n_g]), f"seq {b}: accepted prefix"
+        assert 0 <= tok_g[n_g] < w.vocab, f"seq {b}: new token {tok_g[n_g]}"
+        assert np.all(tok_g[n_g + 1:] == -1), f"seq {b}: padding"
+        if kstar is not None:
+            rep.boundary_accept += 1
+            assert n_g >= kstar, f"seq {b}: GPU rejected at {n_g} before the boundary draw {kstar}"
+            continue
+        assert n_g == n_o, f"seq {b}: num_accepted gpu {n_g} oracle {n_o} (no boundary draw)"
+        if final_boundary:
+            rep.boundary_final += 1
+            lo, hi = int(o["tok_lo"][b]), int(o["tok_hi"][b])
+            assert lo <= tok_g[n_g] <= hi, f"seq {b}: token {tok_g[n_g]} outside the eps-window [{lo}, {hi}]"
+        else:
+            assert np.array_equal(tok_g, tok_o), f"seq {b}: tokens gpu {tok_g.tolist()} oracle {tok_o.tolist()}"
+            rep.exact += 1
+        if "residual_mass" in g:
+            zg, zo = float(g["residual_mass"][b]), float(o["residual_mass"][b])
+            if n_o < K:
+                assert abs(zg - zo) <= rtol * abs(zo) + 1e-6, f"seq {b}: Z gpu {zg} oracle {zo}"
+                if zo > 1e-6:
+                    rep.max_rel_z = max(rep.max_rel_z, abs(zg - zo) / zo)
+            else:
+                assert zg == 0.0
+    return rep
+
+
+def compare_greedy(w, g, o, seqs=None):
+    seqs = range(w.batch) if seqs is None else seqs
+    for b in seqs:
+        K = int(w.draft_lens[b])
+        t0 = int(w.cu_draft[b]) + b
+        assert g["num_accepted"][b] == o["num_accepted"][b], f"seq {b}"
+        assert np.array_equal(g["tokens"][t0:t0 + K + 1], o["tokens"][t0:t0 + K + 1]), f"seq {b}"

@@ -1,0 +1,170 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/specverify.h declares, rejects bad arguments before launching
+anything, and answers workspace queries."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rejection_sampling_verify_07_amd import binding
+
+    if not os.path.exists(binding.LIB_PATH):
+        from rejection_sampling_verify_07_amd import build
+
+        build.build()
+    return binding.load_library()
+
+
+@pytest.fixture(scope="module")
+def B():
+    from rejection_sampling_verify_07_amd import binding
+
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SV_API\s+[\w\s\*]+?\b(spec_verify_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert "spec_verify_sample" in names and "spec_verify_greedy" in names
+    assert "spec_verify_status_string" in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from rejection_sampling_verify_07_amd import binding
+
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    # the header is plain C: compile a translation unit that includes it
+    src = '#include "specverify.h"\nint main(void){ sv_shape_t s; (void)s; return SV_OK; }\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c11", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def _shape(B, **kw):
+    d = dict(batch=2, max_draft=4, total_draft=8, vocab=1000, dtype=B.SV_DTYPE_BF16, target_row_stride=1000,
+             draft_row_stride=1000, cu_draft=None)
+    d.update(kw)
+    return B.ShapeT(**d)
+
+
+def _query(lib, sh, T=1.0, top_k=0, greedy=False):
+    need = C.c_size_t(0)
+    if greedy:
+        st = lib.spec_verify_greedy(C.byref(sh), None, None, None, None, None, C.byref(need), None)
+    else:
+        st = lib.spec_verify_sample(C.byref(sh), None, None, None, T, top_k, 0, 0, None, None, None, None, None,
+                                    C.byref(need), None)
+    return st, need.value
+
+
+def test_status_strings(lib, B):
+    for code, name in [(0, "SV_OK"), (1, "SV_ERR_INVALID_ARGUMENT"), (2, "SV_ERR_UNSUPPORTED"),
+                       (3, "SV_ERR_WORKSPACE_TOO_SMALL"), (4, "SV_ERR_HIP")]:
+        assert B.status_string(code) == name
+
+
+def test_workspace_query(lib, B):
+    st, n = _query(lib, _shape(B))
+    assert st == B.SV_OK and n > 0 and n % 256 == 0
+    st, n_topk = _query(lib, _shape(B), top_k=50)
+    assert st == B.SV_OK and n_topk > n
+    st, n_exact = _query(lib, _shape(B), top_k=600)
+    assert st == B.SV_OK and 0 < n_exact < n_topk
+    st, ng = _query(lib, _shape(B), greedy=True)
+    assert st == B.SV_OK and 0 < ng <= n
+    # top_k = V is "off": the same plan as top_k = 0
+    assert _query(lib, _shape(B), top_k=1000) == (B.SV_OK, n)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 1),
+    (dict(vocab=0), 1),
+    (dict(max_draft=-1), 1),
+    (dict(total_draft=7), 1),                       # != B*K without cu_draft
+    (dict(target_row_stride=999), 1),
+    (dict(draft_row_stride=999), 1),
+    (dict(dtype=7), 1),
+    (dict(vocab=(1 << 20) + 1, target_row_stride=1 << 21, draft_row_stride=1 << 21), 2),
+    (dict(max_draft=129, total_draft=258), 2),
+])
+def test_invalid_shapes(lib, B, kw, code):
+    assert _query(lib, _shape(B, **kw))[0] == code
+
+
+@pytest.mark.parametrize("T,top_k,code", [(0.0, 0, 1), (-1.0, 0, 1), (float("inf"), 0, 1), (float("nan"), 0, 1),
+                                          (1.0, -1, 1), (1.0, 1001, 1), (0.05, 1, 0), (5.0, 1000, 0)])
+def test_temperature_and_top_k(lib, B, T, top_k, code):
+    assert _query(lib, _shape(B), T=T, top_k=top_k)[0] == code
+
+
+def test_null_and_misaligned_pointers_and_small_workspace(lib, B):
+    sh = _shape(B)
+    st, need = _query(lib, sh)
+    fake = 1 << 40  # never dereferenced: every check below fails before a launch
+    have = C.c_size_t(need)
+
+    def call(tgt=fake, drf=fake, ids=fake, tok=fake, nacc=fake, ws=fake, have_=have):
+        return lib.spec_verify_sample(C.byref(sh), tgt, drf, ids, 1.0, 0, 0, 0, tok, nacc, None, None, ws,
+                                      C.byref(have_), None)
+
+    assert call(tgt=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(drf=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(ids=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tok=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(nacc=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tgt=fake + 1) == B.SV_ERR_INVALID_ARGUMENT   # bf16 needs 2-byte alignment
+    assert call(ids=fake + 2) == B.SV_ERR_INVALID_ARGUMENT   # int32 needs 4-byte alignment
+    assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT   # workspace 256-byte aligned
+    assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.spec_verify_sample(C.byref(sh), fake, fake, fake, 1.0, 0, 0, 0, fake, fake, None, None, fake, None,
+                                  None) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_verify_sample(None, fake, fake, fake, 1.0, 0, 0, 0, fake, fake, None, None, None,
+                                  C.byref(have), None) == B.SV_ERR_INVALID_ARGUMENT
+    # greedy
+    st, needg = _query(lib, sh, greedy=True)
+    haveg = C.c_size_t(needg - 1)
+    assert lib.spec_verify_greedy(C.byref(sh), fake, fake, fake, fake, fake, C.byref(haveg),
+                                  None) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.spec_verify_greedy(C.byref(sh), None, fake, fake, fake, fake, C.byref(haveg),
+                                  None) == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_ragged_shape_needs_consistent_totals(lib, B):
+    sh = _shape(B, cu_draft=4096, total_draft=5)        # ragged: total <= B*K is allowed
+    assert _query(lib, sh)[0] == B.SV_OK
+    sh = _shape(B, cu_draft=4096, total_draft=9)        # more than B*K
+    assert _query(lib, sh)[0] == B.SV_ERR_INVALID_ARGUMENT
+    sh = _shape(B, cu_draft=4098)                        # misaligned device pointer
+    assert _query(lib, sh)[0] == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_profile_hook_arguments(lib, B):
+    assert lib.spec_verify_set_profile_events(None, None, 3) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_verify_set_profile_events(None, None, -1) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_verify_set_profile_events(None, None, 0) == B.SV_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path, B):
+    with pytest.raises(FileNotFoundError):
+        B.load_library(str(tmp_path / "missing.so"))
