@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-sampling verify step on one MI355X.
+
+A step is one spec_verify_sample (or spec_verify_greedy) call over one batch
+of synthetic logits resident in HBM: the whole hot path (streaming pass,
+per-row select or merge, accept / residual / extra-token draw, outputs).
+The timed loop rotates over enough copies of the inputs (>= 512 MB by
+default) that they cannot stay in the 256 MB last-level cache, so it
+measures HBM reads.
+
+Prints one JSON line:
+  value         verified positions per second (sum_b (K_b + 1) per step)
+  roofline      the streaming kernel: algorithmic bytes per launch (every
+                logit once) / its average duration from HIP events recorded
+                around each launch in a profiled pass of the same loop,
+                against the 8 TB/s HBM peak
+  cpu_baseline  the fp64 CPU oracle on the same workload, on this host
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B×(K+1)×V logits"
+STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_sha() -> str:
+    """Hash of the HIP sources; a stored counter reading is used only if it matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rejection_sampling_verify_07_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, mode: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"{workload}/{mode}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, mode, seconds):
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.verify_workload(w, mode, threads=threads)  # warm (page in, build)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.verify_workload(w, mode, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": reps * w.positions() / el,
+        "unit": "positions/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the full batch of the same workload ({w.batch} sequences, {w.positions()} positions), "
+                  f"{reps} repetitions in {el:.1f} s, sequences split over {threads} host threads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: V=151936, top-k 50)")
+    ap.add_argument("--mode", choices=["sample", "greedy"], default="sample")
+    ap.add_argument("--rotate-mb", type=float, default=512.0, help="total size of the rotated input copies")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile-pass", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
+                    help="also run a plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU; the verify step shards by sequence with no exchange "
+              "(see DESIGN.md), and no multi-GPU figure is produced", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_07_amd as sv
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    w = W.make_config(args.config)
+    mode = args.mode
+    if mode not in w.modes:
+        print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
+        sys.exit(2)
+    kind = "greedy" if mode == "greedy" else ("sample_topk" if w.top_k > 0 else "sample")
+    bytes_step = w.algorithmic_bytes(mode)
+    copies = max(1, int(np.ceil(args.rotate_mb * 1e6 / bytes_step)))
+
+    def to_dev(a):
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tgt0, drf0 = to_dev(w.target), to_dev(w.draft)
+    ids = torch.from_numpy(w.draft_ids).to(dev)
+    cu = torch.from_numpy(w.cu_draft).to(dev) if w.ragged else None
+    kmax = w.k_max if cu is not None else None
+    plans = []
+    ws = None
+    for i in range(copies):
+        tgt = tgt0 if i == 0 else tgt0.clone()
+        drf = drf0 if i == 0 else drf0.clone()
+        if mode == "greedy":
+            p = sv.GreedyPlan(tgt, ids, cu_draft=cu, max_draft=kmax, workspace=ws)
+        else:
+            p = sv.SamplePlan(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
+                              offset=w.offset, max_draft=kmax, workspace=ws)
+        ws = p.workspace
+        plans.append(p)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        plans[i % copies]()
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(K):
+        plans[i % copies]()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / K
+    positions = w.positions()
+    value = positions / (ms_step * 1e-3)
+
+    # ---- profiled pass: HIP events around each streaming-kernel launch
+    roof = None
+    if not args.no_profile_pass:
+        ev = sv.HipEvents(K)
+        ev.arm()
+        torch.cuda.synchronize()
+        for i in range(K):
+            plans[i % copies]()
+        torch.cuda.synchronize()
+        sv.HipEvents.disarm()
+        dur = np.array(ev.elapsed_ms()) * 1e-3
+        ev.close()
+        avg = float(dur.mean())
+        achieved = bytes_step / avg / 1e9
+        traffic = stored_traffic(w.name, mode)
+        roof = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": STREAM_KERNEL[kind], "bytes_per_launch": bytes_step,
+            "avg_us": round(avg * 1e6, 3), "median_us": round(float(np.median(dur)) * 1e6, 3),
+        }
+
+    if args.copy_calibration_mb > 0:
+        n = int(args.copy_calibration_mb * 1e6) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, mode, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "mode": mode, "batch": w.batch, "positions_per_step": positions,
+            "draft_tokens_per_step": w.rows_draft, "vocab": w.vocab, "input_dtype": w.dtype,
+            "temperature": w.temperature, "top_k": w.top_k, "bytes_per_step": bytes_step,
+            "rotated_copies": copies, "hbm_gbs_whole_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 1),
+            "wall_s": round(wall, 4),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

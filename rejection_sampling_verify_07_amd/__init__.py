@@ -5,6 +5,8 @@ include/specverify.h); this package holds its sources (csrc/), the build
 script and a thin ctypes binding.
 """
 from .binding import (  # noqa: F401
+    GreedyPlan,
+    SamplePlan,
     HipEvents,
     SpecVerifyError,
     load_library,

@@ -53,7 +53,7 @@ def load_library(path: Optional[str] = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("SPECVERIFY_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise FileNotFoundError(
             f"{p} is missing: build the HIP library first (python -c 'import __graft_entry__ as g; g.build()')")
@@ -264,3 +264,75 @@ class HipEvents:
             self._hip.hipEventDestroy(self.starts[i])
             self._hip.hipEventDestroy(self.stops[i])
         self.n = 0
+
+
+class SamplePlan:
+    """spec_verify_sample with every argument marshalled once (for tight loops).
+
+    Holds references to the tensors it was built from; __call__ enqueues one
+    verify on `stream` (default: the current stream at construction).
+    """
+
+    def __init__(self, target_logits, draft_logits, draft_ids, cu_draft=None, temperature=1.0, top_k=0, seed=0,
+                 offset=0, max_draft=None, out=None, workspace=None, stream=None, probs=True):
+        self.lib = load_library()
+        batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+        self.shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
+        dev = target_logits.device
+        need = C.c_size_t(0)
+        _check(self.lib.spec_verify_sample(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
+                                           int(seed), int(offset), None, None, None, None, None, C.byref(need),
+                                           None), "workspace query")
+        self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
+            torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.out = out or dict(tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
+                               num_accepted=torch.empty(batch, dtype=torch.int32, device=dev),
+                               probs=torch.empty((max(total, 1), 2), dtype=torch.float32, device=dev),
+                               residual_mass=torch.empty(batch, dtype=torch.float32, device=dev))
+        self.have = C.c_size_t(self.workspace.numel())
+        self._keep = (target_logits, draft_logits, draft_ids, cu_draft)
+        self.args = (C.byref(self.shape), C.c_void_p(target_logits.data_ptr()),
+                     C.c_void_p(draft_logits.data_ptr() if draft_logits.numel() else None),
+                     C.c_void_p(draft_ids.data_ptr() if draft_ids.numel() else None), C.c_float(temperature),
+                     C.c_int32(top_k), C.c_uint64(seed), C.c_uint32(offset),
+                     C.c_void_p(self.out["tokens"].data_ptr()), C.c_void_p(self.out["num_accepted"].data_ptr()),
+                     C.c_void_p(self.out["probs"].data_ptr() if (probs and total > 0) else None),
+                     C.c_void_p(self.out["residual_mass"].data_ptr() if probs else None),
+                     C.c_void_p(self.workspace.data_ptr()), C.byref(self.have),
+                     C.c_void_p(_stream_handle(stream)))
+        self.fn = self.lib.spec_verify_sample
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "spec_verify_sample")
+
+
+class GreedyPlan:
+    """spec_verify_greedy with every argument marshalled once."""
+
+    def __init__(self, target_logits, draft_ids, cu_draft=None, max_draft=None, out=None, workspace=None,
+                 stream=None):
+        self.lib = load_library()
+        batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+        self.shape = make_shape(target_logits, None, batch, kmax, total, cu_draft)
+        dev = target_logits.device
+        need = C.c_size_t(0)
+        _check(self.lib.spec_verify_greedy(C.byref(self.shape), None, None, None, None, None, C.byref(need), None),
+               "workspace query")
+        self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
+            torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.out = out or dict(tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
+                               num_accepted=torch.empty(batch, dtype=torch.int32, device=dev))
+        self.have = C.c_size_t(self.workspace.numel())
+        self._keep = (target_logits, draft_ids, cu_draft)
+        self.args = (C.byref(self.shape), C.c_void_p(target_logits.data_ptr()),
+                     C.c_void_p(draft_ids.data_ptr() if draft_ids.numel() else None),
+                     C.c_void_p(self.out["tokens"].data_ptr()), C.c_void_p(self.out["num_accepted"].data_ptr()),
+                     C.c_void_p(self.workspace.data_ptr()), C.byref(self.have), C.c_void_p(_stream_handle(stream)))
+        self.fn = self.lib.spec_verify_greedy
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "spec_verify_greedy")

@@ -21,16 +21,18 @@ def hipcc_path() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the HIP sources into rejection_sampling_verify_07_amd/libspecverify.so."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the HIP sources into rejection_sampling_verify_07_amd/libspecverify.so
+    (or `out`, with extra -D defines, for tuning builds)."""
     src = os.path.join(CSRC, "specverify.hip")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc_path(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-I",
+           CSRC, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -2,6 +2,8 @@
 // The operation and the conventions are documented in include/specverify.h.
 #include "specverify.h"
 
+#include <hip/hip_ext.h>
+
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -16,7 +18,24 @@ static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
 
 namespace {
 
-constexpr int kLoads = 4;            // 16-byte loads per thread per chunk in the streaming passes
+// 16-byte loads per thread per chunk in the streaming passes, and whether
+// they bypass the caches (nontemporal); both chosen by measurement.
+#ifndef SV_STREAM_LOADS
+#define SV_STREAM_LOADS 4
+#endif
+#ifndef SV_CAND_LOADS
+#define SV_CAND_LOADS 8
+#endif
+#ifndef SV_STREAM_NT
+#define SV_STREAM_NT 1
+#endif
+#ifndef SV_STREAM_PIPE
+#define SV_STREAM_PIPE 0
+#endif
+constexpr int kLoads = SV_STREAM_LOADS;      // row statistics (sampling and greedy)
+constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
+constexpr bool kNT = SV_STREAM_NT != 0;
+constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instead of one tile per workgroup
 constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
 constexpr size_t kAlign = 256;
 
@@ -36,10 +55,10 @@ size_t esize_of(sv_dtype_t dt) { return dt == SV_DTYPE_F32 ? 4 : 2; }
 
 // Chunks per row of the streaming passes: a row with start misalignment up
 // to VEC-1 elements touches at most ceil((V + VEC - 1) / VEC) blocks.
-int32_t chunks_for(int32_t vocab, int vec)
+int32_t chunks_for(int32_t vocab, int vec, int loads)
 {
     const int64_t nblk = ((int64_t)vocab + 2 * vec - 2) / vec;
-    const int64_t per = (int64_t)sv::kThreads * kLoads;
+    const int64_t per = (int64_t)sv::kThreads * loads;
     return (int32_t)((nblk + per - 1) / per);
 }
 
@@ -49,15 +68,44 @@ hipEvent_t* g_prof_stop = nullptr;
 int32_t g_prof_n = 0;
 int32_t g_prof_i = 0;
 
-void prof_begin(hipStream_t s)
+// Workgroups of `kernel` the current device keeps resident at once: the
+// grid of the persistent streaming passes.  Cached per kernel and device.
+template <class K>
+uint32_t resident_grid(K kernel)
 {
-    if (g_prof_start != nullptr && g_prof_i < g_prof_n) (void)hipEventRecord(g_prof_start[g_prof_i], s);
+    struct Entry {
+        const void* fn;
+        int dev;
+        uint32_t grid;
+    };
+    static Entry cache[32];
+    static int n_cache = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    for (int i = 0; i < n_cache; ++i)
+        if (cache[i].fn == (const void*)kernel && cache[i].dev == dev) return cache[i].grid;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, sv::kThreads, 0) != hipSuccess) return 0;
+    const uint32_t g = (uint32_t)(cus > 0 ? cus : 1) * (uint32_t)(per_cu > 0 ? per_cu : 1);
+    if (n_cache < 32) cache[n_cache++] = Entry{(const void*)kernel, dev, g};
+    return g;
 }
-void prof_end(hipStream_t s)
+
+// Launch a streaming-pass kernel over `ntiles` tiles with a resident grid;
+// while the hook is armed, the launch itself records the kernel's start and
+// end into the caller's events.
+template <class K, class... Args>
+void launch_stream(K kernel, uint32_t ntiles, hipStream_t s, Args... args)
 {
-    if (g_prof_stop != nullptr && g_prof_i < g_prof_n) {
-        (void)hipEventRecord(g_prof_stop[g_prof_i], s);
+    uint32_t grid = kPipe ? resident_grid(kernel) : ntiles;
+    if (grid == 0 || grid > ntiles) grid = ntiles;
+    if (g_prof_start != nullptr && g_prof_i < g_prof_n) {
+        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(sv::kThreads), 0, s, g_prof_start[g_prof_i],
+                              g_prof_stop[g_prof_i], 0, args...);
         ++g_prof_i;
+    } else {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(sv::kThreads), 0, s, args...);
     }
 }
 
@@ -88,7 +136,6 @@ Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
     p.rows_t = sh->total_draft + sh->batch;
     p.rows_d = greedy ? 0 : sh->total_draft;
     p.rows = p.rows_t + p.rows_d;
-    p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype));
     const bool topk = !greedy && top_k > 0 && top_k < sh->vocab;
     if (greedy) {
         p.mode = PLAN_GREEDY;
@@ -97,6 +144,7 @@ Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
     } else {
         p.mode = top_k <= sv::kTopkFastMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
     }
+    p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype), p.mode == PLAN_TOPK_FAST ? kCandLoads : kLoads);
     size_t off = 0;
     const size_t slots = (size_t)p.rows * (size_t)p.nchunk;
     if (p.mode == PLAN_FULL) {
@@ -164,10 +212,8 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
 
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
-        prof_begin(stream);
-        hipLaunchKernelGGL((sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, false>), dim3(grid_stream),
-                           dim3(sv::kThreads), 0, stream, rs, sh->vocab, p.nchunk, c, (void*)part);
-        prof_end(stream);
+        launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab,
+                      p.nchunk, (int32_t)grid_stream, c, (void*)part);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         va.partials = part;
         hipLaunchKernelGGL((sv::verify_kernel<DT, false>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
@@ -181,10 +227,8 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     if (p.mode == PLAN_TOPK_FAST) {
         counts = ws_at<int32_t>(ws, p.off_counts);
         cands = ws_at<sv::KeptEntry>(ws, p.off_cands);
-        prof_begin(stream);
-        hipLaunchKernelGGL((sv::topk_cand_kernel<DT, kLoads, false>), dim3(grid_stream), dim3(sv::kThreads), 0,
-                           stream, rs, sh->vocab, p.nchunk, top_k, kCandCap, counts, cands);
-        prof_end(stream);
+        launch_stream(sv::topk_cand_kernel<DT, kCandLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab, p.nchunk,
+                      (int32_t)grid_stream, top_k, kCandCap, counts, cands);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
     }
     hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
@@ -206,10 +250,8 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
                   p.rows_t};
     sv::PartialArg* part = ws_at<sv::PartialArg>(ws, p.off_partials);
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows_t * p.nchunk);
-    prof_begin(stream);
-    hipLaunchKernelGGL((sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, false>), dim3(grid_stream),
-                       dim3(sv::kThreads), 0, stream, rs, sh->vocab, p.nchunk, 0.0f, (void*)part);
-    prof_end(stream);
+    launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab,
+                  p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
     if (launch_status() != SV_OK) return SV_ERR_HIP;
     sv::GreedyArgs ga{sh->cu_draft, sh->batch, sh->max_draft, sh->total_draft, sh->vocab, ids, part, p.nchunk,
                       out_tokens, out_nacc};

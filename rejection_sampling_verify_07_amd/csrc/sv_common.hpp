@@ -35,15 +35,21 @@ struct Dt<DT_BF16> {
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
 // ---------------------------------------------------------------------------
-// Loads
+// Loads.  Row pointers reach the kernels inside by-value structs, where the
+// compiler can no longer tell they are global memory and would emit FLAT
+// instructions (which also occupy the LDS counter, so LDS work waits on HBM
+// loads).  Casting to the global address space keeps them GLOBAL loads.
 // ---------------------------------------------------------------------------
+#define SV_GLOBAL __attribute__((address_space(1)))
+
 template <bool NT>
 __device__ __forceinline__ u32x4 load16(const u32x4* p)
 {
+    const SV_GLOBAL u32x4* g = (const SV_GLOBAL u32x4*)p;
     if constexpr (NT) {
-        return __builtin_nontemporal_load(p);
+        return __builtin_nontemporal_load(g);
     } else {
-        return *p;
+        return *g;
     }
 }
 
@@ -73,9 +79,9 @@ template <int DT>
 __device__ __forceinline__ float load_one(const char* row, int64_t i)
 {
     if constexpr (DT == DT_F32) {
-        return reinterpret_cast<const float*>(row)[i];
+        return ((const SV_GLOBAL float*)row)[i];
     } else {
-        const uint32_t b = reinterpret_cast<const uint16_t*>(row)[i];
+        const uint32_t b = ((const SV_GLOBAL uint16_t*)row)[i];
         return __uint_as_float(b << 16);
     }
 }

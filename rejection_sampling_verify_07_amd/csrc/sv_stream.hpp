@@ -1,0 +1,116 @@
+// Persistent, software-pipelined walk over the (row, chunk) tiles of the
+// streaming passes.
+//
+// A chunk is kThreads * LOADS aligned 16-byte blocks of one row; tile c is
+// chunk (c mod nchunk) of row (c / nchunk).  The grid holds as many
+// workgroups as the chip keeps resident; workgroup g handles tiles g,
+// g + G, g + 2G, ... and issues the loads of its next tile before it works
+// on the current one, so the reduction, barrier and compaction work of a
+// tile overlaps the HBM latency of the next.  Two register sets alternate
+// (the walk is unrolled by two) so no copies are needed.
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+// Every field is uniform across the workgroup (kept in scalar registers);
+// a thread's first block is cb0 + threadIdx.x.
+struct Tile {
+    int32_t index;  // global tile index (row * nchunk + chunk)
+    int32_t row;
+    int32_t cb0;    // the tile's first block (aligned 16-byte units from the row's first block)
+    int32_t mis;    // row start offset inside its first block, in elements
+    int32_t nblk;   // blocks touched by the row
+};
+
+__device__ __forceinline__ int32_t tile_b0(const Tile& t) { return t.cb0 + (int32_t)threadIdx.x; }
+
+template <int DT>
+__device__ __forceinline__ Tile make_tile(const RowSet& rs, int32_t vocab, int32_t nchunk, int32_t c, int loads,
+                                          const u32x4** base)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int ES = Dt<DT>::kSize;
+    Tile t;
+    t.index = c;
+    t.row = (int32_t)((uint32_t)c / (uint32_t)nchunk);
+    const int32_t chunk = c - t.row * nchunk;
+    const uintptr_t addr = (uintptr_t)row_ptr(rs, t.row);
+    t.mis = (int32_t)((addr & 15u) / ES);
+    *base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
+    t.nblk = (t.mis + vocab + VEC - 1) / VEC;
+    t.cb0 = chunk * (kThreads * loads);
+    return t;
+}
+
+template <int DT, int LOADS, bool NT>
+__device__ __forceinline__ void issue_tile(const Tile& t, const u32x4* base, u32x4* raw)
+{
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int32_t j = tile_b0(t) + i * kThreads;
+        raw[i] = (j < t.nblk) ? load16<NT>(base + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// body(tile, raw) is called once per tile (raw: the thread's LOADS words,
+// which the body may overwrite), by every thread of the workgroup (it may contain barriers; it must end with the workgroup's LDS
+// free for the next tile).  PIPELINE = false: one tile per workgroup
+// (grid = ntiles), no prefetch register set.
+template <int DT, int LOADS, bool NT, bool PIPELINE, class Body>
+__device__ __forceinline__ void walk_tiles(const RowSet& rs, int32_t vocab, int32_t nchunk, int32_t ntiles,
+                                           Body&& body)
+{
+    int32_t c = (int32_t)blockIdx.x;
+    if (c >= ntiles) return;
+    const u32x4* base;
+    u32x4 ra[LOADS];
+    Tile ta = make_tile<DT>(rs, vocab, nchunk, c, LOADS, &base);
+    issue_tile<DT, LOADS, NT>(ta, base, ra);
+    if constexpr (!PIPELINE) {
+        body(ta, ra);
+    } else {
+        const int32_t stride = (int32_t)gridDim.x;
+        u32x4 rb[LOADS];
+        while (true) {
+            // tile in ra is in flight; start the next one into rb
+            const int32_t cb = c + stride;
+            Tile tb;
+            if (cb < ntiles) {
+                tb = make_tile<DT>(rs, vocab, nchunk, cb, LOADS, &base);
+                issue_tile<DT, LOADS, NT>(tb, base, rb);
+            }
+            body(ta, ra);
+            if (cb >= ntiles) break;
+            const int32_t ca = cb + stride;
+            if (ca < ntiles) {
+                ta = make_tile<DT>(rs, vocab, nchunk, ca, LOADS, &base);
+                issue_tile<DT, LOADS, NT>(ta, base, ra);
+            }
+            body(tb, rb);
+            if (ca >= ntiles) break;
+            c = ca;
+        }
+    }
+}
+
+// Widen block i of a tile to fp32 and replace elements outside the row by
+// `fill`.  The checks are branch-free selects (measured faster here than a
+// per-block branch around them).
+template <int DT>
+__device__ __forceinline__ void tile_block(const Tile& t, const u32x4* raw, int i, int32_t vocab, float fill,
+                                           float* f)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    const int32_t j = tile_b0(t) + i * kThreads;
+    unpack<DT>(raw[i], f);
+    const int32_t r0 = j * VEC - t.mis;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const uint32_t r = (uint32_t)(r0 + e);
+        f[e] = ((j < t.nblk) & (r < (uint32_t)vocab)) ? f[e] : fill;
+    }
+}
+
+}  // namespace sv

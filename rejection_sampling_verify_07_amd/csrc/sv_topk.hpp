@@ -5,10 +5,9 @@
 // largest logit counted with multiplicity (ties at tau are all kept).
 //
 // Pass 1 (topk_cand_kernel, streaming, one workgroup per (row, chunk)):
-//   Each wave finds, with a 16-step ballot radix select, the j-th largest
-//   (j = ceil(top_k / 4)) of its 64 lane maxima; the smallest of the four
-//   wave results is a lower bound of the chunk's top_k-th largest logit
-//   (at least 4 * j >= top_k distinct elements reach it), hence of the row's
+//   a 16-step ballot radix select finds the top_k-th largest of the
+//   workgroup's 256 lane maxima; top_k distinct elements reach it, so it is
+//   a lower bound of the chunk's top_k-th largest logit, hence of the row's
 //   tau.  Every chunk element >= that bound is written out as a candidate.
 //   The candidate set of a row therefore contains its whole kept set.
 // Pass 2 (topk_select_kernel, one workgroup per row):
@@ -19,117 +18,29 @@
 //   than the list capacity is described as "full row masked by tau".
 #pragma once
 
+#include <type_traits>
+
 #include "sv_common.hpp"
+#include "sv_stream.hpp"
 
 namespace sv {
 
 constexpr int kSelCap = 4096;  // candidates a row can hold in LDS
-constexpr int kTopkFastMax = 4 * kWave;  // largest top_k pass 1 supports
-
-template <int DT, int LOADS, bool NT>
-__global__ __launch_bounds__(kThreads) void topk_cand_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
-                                                             int32_t top_k, int32_t cap,
-                                                             int32_t* __restrict__ counts,
-                                                             KeptEntry* __restrict__ cands)
-{
-    constexpr int VEC = Dt<DT>::kVec;
-    constexpr int ES = Dt<DT>::kSize;
-    __shared__ uint32_t s_h[kWaves];
-    __shared__ int32_t s_cnt;
-
-    const int32_t row = (int32_t)(blockIdx.x / (uint32_t)nchunk);
-    const int32_t chunk = (int32_t)blockIdx.x - row * nchunk;
-    const uintptr_t addr = (uintptr_t)row_ptr(rs, row);
-    const int32_t mis = (int32_t)((addr & 15u) / ES);
-    const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
-    const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
-    const int32_t b0 = chunk * (kThreads * LOADS) + (int32_t)threadIdx.x;
-
-    u32x4 raw[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int32_t j = b0 + i * kThreads;
-        raw[i] = (j < nblk) ? load16<NT>(base + j) : u32x4{0u, 0u, 0u, 0u};
-    }
-    auto block = [&](int i, float* f) {
-        const int32_t j = b0 + i * kThreads;
-        unpack<DT>(raw[i], f);
-        const int32_t r0 = j * VEC - mis;
-        if (j >= nblk || r0 < 0 || r0 + VEC > vocab) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const int32_t r = r0 + e;
-                if (j >= nblk || r < 0 || r >= vocab) f[e] = neg_inf();
-            }
-        }
-    };
-
-    float tm = neg_inf();
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        float f[VEC];
-        block(i, f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) tm = fmaxf(tm, f[e]);
-    }
-
-    // j-th largest of the 64 lane maxima on the top 16 key bits
-    const int jw = (top_k + kWaves - 1) / kWaves;
-    const uint32_t key16 = order_key(tm) >> 16;
-    uint32_t h = 0;
-#pragma unroll
-    for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t cand = h | (1u << bit);
-        const uint64_t bal = __ballot(key16 >= cand);
-        if (__popcll(bal) >= jw) h = cand;
-    }
-    if (lane_id() == 0) s_h[wave_id()] = h;
-    if (threadIdx.x == 0) s_cnt = 0;
-    __syncthreads();
-    uint32_t hmin = s_h[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) hmin = min(hmin, s_h[w]);
-    // smallest float whose key has these top bits; the -inf bucket maps to -inf
-    const float bound = (hmin <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(hmin << 16);
-
-    KeptEntry* out = cands + (int64_t)blockIdx.x * cap;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        float f[VEC];
-        block(i, f);
-        const int32_t j = b0 + i * kThreads;
-        const int32_t r0 = j * VEC - mis;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const bool pred = f[e] >= bound;
-            if (__ballot(pred) != 0) {
-                const int32_t r = r0 + e;
-                const bool take = pred && j < nblk && r >= 0 && r < vocab;
-                const uint64_t m2 = __ballot(take);
-                if (m2 != 0) {
-                    int slot0 = 0;
-                    if (lane_id() == 0) slot0 = atomicAdd(&s_cnt, (int)__popcll(m2));
-                    slot0 = __shfl(slot0, 0, kWave);
-                    if (take) {
-                        const int slot = slot0 + lanes_below(m2);
-                        if (slot < cap) out[slot] = KeptEntry{r, f[e]};
-                    }
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) counts[blockIdx.x] = s_cnt;
-}
+constexpr int kTopkFastMax = kThreads;   // largest top_k pass 1 supports (one lane maximum each)
+constexpr int kMaxChunks = 512;          // chunks per row the select pass can index
 
 // ---------------------------------------------------------------------------
 // Pass 2 helpers
 // ---------------------------------------------------------------------------
 
-// Visit every element of a full row (ascending blocks, 16-byte loads); fn(r, v)
-// gets the row index r and the value, and is called only for r in [0, vocab).
-// Iteration `it` covers blocks it*256 + tid, so a workgroup-wide scan per
-// iteration yields ascending-id order.
+// Visit every element of a full row in ascending 16-byte blocks.  Each
+// thread keeps kRowUnroll loads in flight; fn(step, r0, f, ok) is then called
+// once per block, in the same step for all threads, where step s covers
+// blocks s*256 .. s*256+255 (so a workgroup scan per step yields ascending
+// id order); r0 is the row index of the block's first element and ok[e]
+// tells which of its elements lie inside the row.
+constexpr int kRowUnroll = 8;
+
 template <int DT, class F>
 __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, F&& fn)
 {
@@ -139,20 +50,28 @@ __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, 
     const int32_t mis = (int32_t)((addr & 15u) / ES);
     const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
     const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
-    const int32_t iters = (nblk + kThreads - 1) / kThreads;
+    const int32_t iters = (nblk + kThreads * kRowUnroll - 1) / (kThreads * kRowUnroll);
     for (int32_t it = 0; it < iters; ++it) {
-        const int32_t j = it * kThreads + (int32_t)threadIdx.x;
-        float f[VEC];
-        bool ok[VEC];
-        if (j < nblk) {
-            unpack<DT>(load16<false>(base + j), f);
+        u32x4 raw[kRowUnroll];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const int32_t j = (it * kRowUnroll + u) * kThreads + (int32_t)threadIdx.x;
+            raw[u] = (j < nblk) ? load16<false>(base + j) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int32_t r = j * VEC - mis + e;
-            ok[e] = j < nblk && r >= 0 && r < vocab;
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const int32_t step = it * kRowUnroll + u;
+            const int32_t j = step * kThreads + (int32_t)threadIdx.x;
+            float f[VEC];
+            bool ok[VEC];
+            unpack<DT>(raw[u], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int32_t r = j * VEC - mis + e;
+                ok[e] = j < nblk && r >= 0 && r < vocab;
+            }
+            fn(step, j * VEC - mis, f, ok);
         }
-        fn(it, j * VEC - mis, f, ok);
     }
 }
 
@@ -253,6 +172,174 @@ __device__ uint32_t block_radix_select(Visit&& visit, int32_t k, int low_shift, 
     return prefix;
 }
 
+// LDS staging of one chunk's candidates before they go to global memory:
+// each wave owns kWaveLds slots, so no atomics are needed.
+constexpr int kWaveLds = 512;
+constexpr int kChunkLds = kWaves * kWaveLds;
+
+// Eight waves per SIMD (at most 64 VGPRs): this pass is latency bound, and
+// resident waves are what hides the HBM latency.  Only the raw words stay
+// live across the barrier; values are widened where they are used.
+//
+// bf16: a 32-bit word holds two elements.  Its high element is compared
+// through the raw word read as fp32: the top 16 bits are the element and the
+// low 16 bits (its neighbour) move it by less than one bf16 step (toward
+// -inf for negatives, +inf for positives); every threshold used here is the
+// smallest fp32 of some bf16 order class, so `word >= t` and `element >= t`
+// agree.  The low element needs a shift.  The lane maxima that set the bound
+// are taken over all elements.
+template <int DT, int LOADS, bool NT, bool PIPE>
+__global__ __launch_bounds__(kThreads) void topk_cand_kernel(
+    RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
+    int32_t* __restrict__ counts, KeptEntry* __restrict__ cands)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
+    constexpr bool BF = DT == DT_BF16;
+    __shared__ float s_val[kChunkLds];
+    __shared__ int32_t s_ix[kChunkLds];
+    __shared__ uint32_t s_lk[kThreads];
+    __shared__ int32_t s_wc[kWaves];
+    __shared__ uint32_t s_hist[256];
+    __shared__ int32_t s_misc[8];
+
+    walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
+        // Edge tiles (a block reaching outside the row) first overwrite the
+        // out-of-row slots of their raw words with a NaN pattern: NaN is never
+        // selected and fmaxf ignores it, so one body serves every tile.
+        const bool interior = t.cb0 * VEC >= t.mis && (t.cb0 + kThreads * LOADS) * VEC <= t.mis + vocab;
+        u32x4* rw = raw;
+        if (!interior) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                const int32_t r0 = (tile_b0(t) + i * kThreads) * VEC - t.mis;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    uint32_t w = rw[i][q];
+                    if constexpr (BF) {
+                        if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | 0x7fc0u;
+                        if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | 0x7fc00000u;
+                    } else {
+                        if ((uint32_t)(r0 + q) >= (uint32_t)vocab) w = 0x7fc00000u;
+                    }
+                    rw[i][q] = w;
+                }
+            }
+        }
+        int wcount = 0;  // wave-uniform count of this wave's candidates
+        const int wbase = wave_id() * kWaveLds;
+        {
+            float tm = neg_inf();
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = raw[i][q];
+                    if constexpr (BF) {
+                        tm = fmaxf(tm, fmaxf(__uint_as_float(w << 16), __uint_as_float(w)));
+                    } else {
+                        tm = fmaxf(tm, __uint_as_float(w));
+                    }
+                }
+            }
+
+            // Recompute the widened values in the compaction pass instead of
+            // keeping all of them live across the barrier (an empty asm that
+            // claims to update the raw words stops the compiler from reusing
+            // them; it emits no instruction).
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) asm volatile("" : "+v"(rw[i]));
+
+            // the top_k-th largest of the workgroup's 256 lane maxima (on the top
+            // 16 key bits): every wave runs the same ballot radix select over all
+            // of them, four per lane
+            s_lk[threadIdx.x] = order_key(tm) >> 16;
+            __syncthreads();
+            uint32_t k4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) k4[q] = s_lk[lane_id() + q * kWave];
+            uint32_t h = 0;
+#pragma unroll
+            for (int bit = 15; bit >= 0; --bit) {
+                const uint32_t cand = h | (1u << bit);
+                int cnt = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) cnt += (int)__popcll(__ballot(k4[q] >= cand));
+                if (cnt >= top_k) h = cand;
+            }
+            // smallest float whose key has these top bits; the -inf bucket maps to -inf
+            const float bound = (h <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(h << 16);
+
+            // candidates into this wave's LDS region, in (load, element, lane)
+            // order; the exact value and the row index are formed only on the
+            // rare taken branch
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const int q = BF ? e / 2 : e;
+                    const uint32_t w = raw[i][q];
+                    const int32_t rr = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
+                    const float cmp = BF ? __uint_as_float((e & 1) ? w : (w << 16)) : __uint_as_float(w);
+                    const bool pred = cmp >= bound;
+                    const uint64_t m = __ballot(pred);
+                    if (m != 0) {
+                        const int pos = wcount + lanes_below(m);
+                        if (pred & (pos < kWaveLds)) {
+                            const uint32_t bits = BF ? ((e & 1) ? (w & 0xffff0000u) : (w << 16)) : w;
+                            s_val[wbase + pos] = __uint_as_float(bits);
+                            s_ix[wbase + pos] = rr;
+                        }
+                        wcount += (int)__popcll(m);
+                    }
+                }
+            }
+        }
+        if (lane_id() == 0) s_wc[wave_id()] = wcount;
+        __syncthreads();
+        int32_t total = 0, wover = 0, woff = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            if (w < wave_id()) woff += s_wc[w];
+            total += s_wc[w];
+            wover |= s_wc[w] > kWaveLds;
+        }
+        KeptEntry* out = cands + (int64_t)t.index * cap;
+        int32_t written = total;
+        if (!wover && total <= cap) {
+            for (int32_t q = lane_id(); q < wcount; q += kWave)
+                out[woff + q] = KeptEntry{s_ix[wbase + q], s_val[wbase + q]};
+        } else if (!wover) {
+            // too many for the slots: keep only the tile's own top_k (ties kept)
+            int32_t greater, equal;
+            const uint32_t tkey = block_radix_select(
+                [&](auto&& fn) {
+                    for (int w = 0; w < kWaves; ++w)
+                        for (int32_t q = threadIdx.x; q < s_wc[w]; q += kThreads) fn(order_key(s_val[w * kWaveLds + q]));
+                },
+                top_k, LOW, s_hist, s_misc + 2, &greater, &equal);
+            written = greater + equal;
+            if (written <= cap) {
+                if (threadIdx.x == 0) s_misc[1] = 0;
+                __syncthreads();
+                for (int w = 0; w < kWaves; ++w) {
+                    for (int32_t q = threadIdx.x; q < s_wc[w]; q += kThreads) {
+                        const float v = s_val[w * kWaveLds + q];
+                        if (order_key(v) >= tkey) {
+                            const int32_t slot = atomicAdd(&s_misc[1], 1);
+                            out[slot] = KeptEntry{s_ix[w * kWaveLds + q], v};
+                        }
+                    }
+                }
+            }
+        } else {
+            written = cap + 1;  // a wave overflowed its staging slots
+        }
+        if (threadIdx.x == 0) counts[t.index] = written;  // > cap marks an overflow
+        __syncthreads();  // LDS is reused by the next tile
+    });
+}
+
 // Block-wide max / sum (fixed order); every thread gets the result.
 __device__ __forceinline__ float block_max_float(float v, float* s_f)
 {
@@ -310,36 +397,47 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     KeptEntry* klist = kept + (int64_t)row * keep_cap;
 
     // ---- gather the candidates of this row (if pass 1 ran and nothing overflowed)
+    __shared__ int32_t s_choff[kMaxChunks + 1];
     int32_t total = 0;
     bool fast = use_cands != 0;
     if (fast) {
-        if (threadIdx.x == 0) {
-            int32_t t = 0, bad = 0;
-            for (int32_t ch = 0; ch < nchunk; ++ch) {
-                const int32_t n = counts[(int64_t)row * nchunk + ch];
-                if (n > cap) bad = 1;
-                t += min(n, cap);
-            }
-            s_misc[0] = t;
-            s_misc[1] = bad || t > kSelCap || t < top_k;
+        // per-chunk counts read in parallel; exclusive offsets by a block scan
+        const int32_t per = (nchunk + kThreads - 1) / kThreads;
+        const int32_t lo = min(nchunk, (int32_t)threadIdx.x * per), hi = min(nchunk, lo + per);
+        int mine = 0, bad = 0;
+        for (int32_t ch = lo; ch < hi; ++ch) {
+            const int32_t n = counts[(int64_t)row * nchunk + ch];
+            bad |= n > cap;
+            s_choff[ch] = min(n, cap);
+            mine += min(n, cap);
         }
+        int tot;
+        int off = block_excl_scan_int(mine, s_w, &tot);
+        for (int32_t ch = lo; ch < hi; ++ch) {
+            const int32_t n = s_choff[ch];
+            s_choff[ch] = off;
+            off += n;
+        }
+        if (threadIdx.x == 0) s_misc[1] = 0;
         __syncthreads();
-        total = s_misc[0];
-        fast = s_misc[1] == 0;
+        if (bad) atomicOr(&s_misc[1], 1);
+        if (threadIdx.x == 0) s_choff[nchunk] = tot;
+        __syncthreads();
+        total = tot;
+        fast = s_misc[1] == 0 && total <= kSelCap && total >= top_k;
         __syncthreads();
     }
     if (fast) {
-        int32_t off = 0;
-        for (int32_t ch = 0; ch < nchunk; ++ch) {
+        for (int32_t ch = wave_id(); ch < nchunk; ch += kWaves) {
             const int64_t g = (int64_t)row * nchunk + ch;
-            const int32_t n = counts[g];
+            const int32_t off = s_choff[ch];
+            const int32_t n = s_choff[ch + 1] - off;
             const KeptEntry* src = cands + g * cap;
-            for (int32_t t = threadIdx.x; t < n; t += kThreads) {
+            for (int32_t t = lane_id(); t < n; t += kWave) {
                 const KeptEntry e = src[t];
                 s_key[off + t] = order_key(e.val);
                 s_idx[off + t] = e.idx;
             }
-            off += n;
         }
         __syncthreads();
     }

@@ -97,8 +97,8 @@ __device__ __forceinline__ void seg_weights(const char* ra, const char* rb, int3
         u32x4 wa[NV], wb[NV];
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
-            wa[q] = pa[q];
-            if constexpr (TWO) wb[q] = pb[q];
+            wa[q] = load16<false>(pa + q);
+            if constexpr (TWO) wb[q] = load16<false>(pb + q);
         }
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
