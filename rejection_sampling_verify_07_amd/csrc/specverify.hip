@@ -11,10 +11,12 @@
 #include "sv_common.hpp"
 #include "sv_stats.hpp"
 #include "sv_topk.hpp"
+#include "sv_select.hpp"
 #include "sv_verify.hpp"
 
 static_assert(SV_MAX_DRAFT == sv::kMaxDraft, "draft limit mismatch");
 static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
+static_assert(sv::kKeepCap == sv::kKeepCapList, "kept-list capacity mismatch");
 
 namespace {
 
@@ -231,9 +233,15 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
                       (int32_t)grid_stream, top_k, kCandCap, counts, cands);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
     }
-    hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
-                       p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)(p.mode == PLAN_TOPK_FAST),
-                       (int32_t)sv::kKeepCap, descs, kept);
+    if (p.mode == PLAN_TOPK_FAST) {
+        // one wave per row; rows whose chunks overflowed take the exact path inside
+        hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,
+                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)1, descs, kept);
+    } else {
+        hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
+                           p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)0, (int32_t)sv::kKeepCap, descs,
+                           kept);
+    }
     if (launch_status() != SV_OK) return SV_ERR_HIP;
     va.descs = descs;
     va.kept = kept;

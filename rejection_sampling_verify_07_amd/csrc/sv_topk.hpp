@@ -28,6 +28,7 @@ namespace sv {
 constexpr int kSelCap = 4096;  // candidates a row can hold in LDS
 constexpr int kTopkFastMax = kThreads;   // largest top_k pass 1 supports (one lane maximum each)
 constexpr int kMaxChunks = 512;          // chunks per row the select pass can index
+constexpr int kKeepCapList = 1024;       // kept-list capacity per row (ids kept by top-k)
 
 // ---------------------------------------------------------------------------
 // Pass 2 helpers
@@ -258,9 +259,19 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             uint32_t k4[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) k4[q] = s_lk[lane_id() + q * kWave];
-            uint32_t h = 0;
+            // bits above the highest one where the largest and smallest key differ
+            // are common to all 256 keys: start the select below them
+            uint32_t kmax = max(max(k4[0], k4[1]), max(k4[2], k4[3]));
+            uint32_t kmin = min(min(k4[0], k4[1]), min(k4[2], k4[3]));
 #pragma unroll
-            for (int bit = 15; bit >= 0; --bit) {
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
+                kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
+            }
+            const uint32_t diff = __builtin_amdgcn_readfirstlane(kmax ^ kmin);
+            const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+            uint32_t h = __builtin_amdgcn_readfirstlane(kmax) & ~((2u << top) - 1u);  // the common prefix
+            for (int bit = top; bit >= 0; --bit) {
                 const uint32_t cand = h | (1u << bit);
                 int cnt = 0;
 #pragma unroll
@@ -272,23 +283,23 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
 
             // candidates into this wave's LDS region, in (load, element, lane)
             // order; the exact value and the row index are formed only on the
-            // rare taken branch
+            // rare taken branch.  Slots past the region are clamped (the tile is
+            // then reported as overflowed and its staging is not used).
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
                     const int q = BF ? e / 2 : e;
                     const uint32_t w = raw[i][q];
-                    const int32_t rr = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
                     const float cmp = BF ? __uint_as_float((e & 1) ? w : (w << 16)) : __uint_as_float(w);
                     const bool pred = cmp >= bound;
                     const uint64_t m = __ballot(pred);
                     if (m != 0) {
-                        const int pos = wcount + lanes_below(m);
-                        if (pred & (pos < kWaveLds)) {
+                        if (pred) {
+                            const int pos = min(wcount + lanes_below(m), kWaveLds - 1);
                             const uint32_t bits = BF ? ((e & 1) ? (w & 0xffff0000u) : (w << 16)) : w;
                             s_val[wbase + pos] = __uint_as_float(bits);
-                            s_ix[wbase + pos] = rr;
+                            s_ix[wbase + pos] = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
                         }
                         wcount += (int)__popcll(m);
                     }
@@ -377,6 +388,195 @@ __device__ float block_row_max(const char* rowp, int32_t vocab, float* s_f)
     return block_max_float(lm, s_f);
 }
 
+// ---------------------------------------------------------------------------
+// Fast select of one row by a single wave (no workgroup barriers): used when
+// no chunk overflowed and the row's candidates fit a kept list.  Candidates
+// go to LDS in one round of loads, an LDS-histogram radix select finds the
+// top_k-th largest key, the kept ids are compacted with ballots and sorted
+// by id (in registers when at most 64 are kept), and the max and the exp2
+// sum are wave reductions in a fixed order.
+// s_choff must hold nchunk + 1 ints; s_key / s_idx kKeepCap entries;
+// s_kidx / s_kval kKeepCap entries.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ void select_row_wave(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+                                const int32_t* __restrict__ counts, const KeptEntry* __restrict__ cands,
+                                int32_t total, int32_t keep_cap, RowDesc* __restrict__ descs,
+                                KeptEntry* __restrict__ kept, int32_t* s_choff, uint32_t* s_key, int32_t* s_idx,
+                                uint32_t* s_hist, int32_t* s_kidx, float* s_kval)
+{
+    constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
+    constexpr int PER = kKeepCapList / kWave;
+    const int lane = lane_id();
+
+    // candidates of every chunk into LDS (entry i lives in the chunk whose
+    // offset range holds it), all loads issued before any store
+    KeptEntry e[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int32_t i = lane + j * kWave;
+        if (i < total) {
+            int32_t lo = 0, hi = nchunk;
+            while (hi - lo > 1) {
+                const int32_t mid = (lo + hi) >> 1;
+                if (s_choff[mid] <= i) lo = mid; else hi = mid;
+            }
+            e[j] = cands[((int64_t)row * nchunk + lo) * cap + (i - s_choff[lo])];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int32_t i = lane + j * kWave;
+        if (i < total) {
+            s_key[i] = order_key(e[j].val);
+            s_idx[i] = e[j].idx;
+        }
+    }
+
+    // radix select of the top_k-th largest key (8-bit digits from the top)
+    uint32_t prefix = 0, pmask = 0;
+    int32_t kk = top_k, eq = 0;
+    for (int shift = 24; shift >= LOW; shift -= 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_hist[lane * 4 + q] = 0;
+        __builtin_amdgcn_wave_barrier();
+        for (int32_t i = lane; i < total; i += kWave) {
+            const uint32_t key = s_key[i];
+            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
+        }
+        __builtin_amdgcn_wave_barrier();
+        int c4[4], lsum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c4[q] = (int)s_hist[255 - 4 * lane - q];
+            lsum += c4[q];
+        }
+        const int incl = wave_incl_scan_int(lsum);
+        const int excl = incl - lsum;
+        int found = -1, above = 0, cnt = 0;
+        if (excl < kk && incl >= kk) {
+            int cc = excl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (found < 0 && cc + c4[q] >= kk) {
+                    found = 255 - 4 * lane - q;
+                    above = cc;
+                    cnt = c4[q];
+                }
+                cc += c4[q];
+            }
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = bal ? __builtin_ctzll(bal) : 0;
+        found = __shfl(found, src, kWave);
+        above = __shfl(above, src, kWave);
+        cnt = __shfl(cnt, src, kWave);
+        if (bal == 0) {
+            found = 0;
+            cnt = 0;
+        }
+        prefix |= (uint32_t)found << shift;
+        pmask |= 0xffu << shift;
+        kk -= above;
+        eq = cnt;
+        __builtin_amdgcn_wave_barrier();
+    }
+    if (LOW > 0) prefix |= (prefix & 0x80000000u) ? 0u : ((1u << LOW) - 1u);
+    const uint32_t tau_key = prefix;
+    (void)eq;
+
+    // kept ids (key >= tau_key), compacted in candidate order
+    int32_t nk = 0;
+    for (int32_t b = 0; b < total; b += kWave) {
+        const int32_t i = b + lane;
+        const bool pred = i < total && s_key[i] >= tau_key;
+        const uint64_t m = __ballot(pred);
+        if (pred) {
+            const int32_t pos = nk + lanes_below(m);
+            s_kidx[pos] = s_idx[i];
+            s_kval[pos] = key_to_float(s_key[i]);
+        }
+        nk += (int32_t)__popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // sort by id
+    KeptEntry* klist = kept + (int64_t)row * keep_cap;
+    float lm = neg_inf();
+    double ls = 0.0;
+    if (nk <= kWave) {
+        int32_t ix = lane < nk ? s_kidx[lane] : INT32_MAX;
+        float v = lane < nk ? s_kval[lane] : neg_inf();
+#pragma unroll
+        for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                const int32_t pix = __shfl_xor(ix, stride, kWave);
+                const float pv = __shfl_xor(v, stride, kWave);
+                const bool up = (lane & size) == 0;
+                const bool lower = (lane & stride) == 0;
+                const bool take = (lower == up) ? (pix < ix) : (pix > ix);
+                if (take) {
+                    ix = pix;
+                    v = pv;
+                }
+            }
+        }
+        if (lane < nk) klist[lane] = KeptEntry{ix, v};
+        lm = wave_max(v);
+        lm = __shfl(lm, 0, kWave);
+        const float mcc = lm * c;
+        ls = lane < nk ? (double)__builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mcc)) : 0.0;
+    } else {
+        int32_t npad = kWave;
+        while (npad < nk) npad <<= 1;
+        for (int32_t i = nk + lane; i < npad; i += kWave) {
+            s_kidx[i] = INT32_MAX;
+            s_kval[i] = neg_inf();
+        }
+        __builtin_amdgcn_wave_barrier();
+        for (int32_t size = 2; size <= npad; size <<= 1) {
+            for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int32_t i = lane; i < npad; i += kWave) {
+                    const int32_t p = i ^ stride;
+                    if (p > i) {
+                        const bool up = (i & size) == 0;
+                        const int32_t a = s_kidx[i], bb = s_kidx[p];
+                        if ((a > bb) == up) {
+                            s_kidx[i] = bb;
+                            s_kidx[p] = a;
+                            const float tv = s_kval[i];
+                            s_kval[i] = s_kval[p];
+                            s_kval[p] = tv;
+                        }
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+        for (int32_t i = lane; i < nk; i += kWave) {
+            klist[i] = KeptEntry{s_kidx[i], s_kval[i]};
+            lm = fmaxf(lm, s_kval[i]);
+        }
+        lm = __shfl(wave_max(lm), 0, kWave);
+        const float mcc = lm * c;
+        for (int32_t i = lane; i < nk; i += kWave)
+            ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(s_kval[i], c, -mcc));
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) {
+        RowDesc d;
+        d.tau = key_to_float(tau_key);
+        d.m = lm;
+        d.mcc = lm * c;
+        d.kept = nk;
+        d.s = ls;
+        d.flags = 0;
+        d.pad = 0;
+        descs[row] = d;
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t top_k, int32_t cap, float c,
@@ -395,9 +595,35 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     const int32_t row = blockIdx.x;
     const char* rowp = row_ptr(rs, row);
     KeptEntry* klist = kept + (int64_t)row * keep_cap;
+    __shared__ int32_t s_kidx[kKeepCapList];
+    __shared__ float s_kval[kKeepCapList];
+    __shared__ int32_t s_choff[kMaxChunks + 1];
+
+    // Every wave reads the chunk counts and reaches the same decision; on the
+    // fast path waves 1..3 leave and wave 0 selects the row without barriers.
+    if (use_cands != 0) {
+        int32_t base = 0, bad = 0;
+        for (int32_t g = 0; g < nchunk; g += kWave) {
+            const int32_t ch = g + lane_id();
+            const int32_t n = ch < nchunk ? counts[(int64_t)row * nchunk + ch] : 0;
+            bad |= n > cap;
+            const int32_t nc = min(n, cap);
+            const int incl = wave_incl_scan_int(nc);
+            if (wave_id() == 0 && ch < nchunk) s_choff[ch] = base + incl - nc;
+            base += __shfl(incl, kWave - 1, kWave);
+        }
+        const bool any_bad = __ballot(bad != 0) != 0;
+        if (!any_bad && base >= top_k && base <= kKeepCapList && keep_cap >= kKeepCapList) {
+            if (wave_id() != 0) return;
+            if (lane_id() == 0) s_choff[nchunk] = base;
+            __builtin_amdgcn_wave_barrier();
+            select_row_wave<DT>(row, nchunk, top_k, cap, c, counts, cands, base, keep_cap, descs, kept, s_choff,
+                                s_key, (int32_t*)s_idx, s_hist, s_kidx, s_kval);
+            return;
+        }
+    }
 
     // ---- gather the candidates of this row (if pass 1 ran and nothing overflowed)
-    __shared__ int32_t s_choff[kMaxChunks + 1];
     int32_t total = 0;
     bool fast = use_cands != 0;
     if (fast) {
@@ -474,8 +700,6 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
             // compact the candidates >= tau, then sort them by id (bitonic)
             if (threadIdx.x == 0) s_misc[4] = 0;
             __syncthreads();
-            __shared__ int32_t s_kidx[1024];
-            __shared__ float s_kval[1024];
             for (int32_t i = threadIdx.x; i < total; i += kThreads) {
                 if (s_key[i] >= tau_key) {
                     const int32_t slot = atomicAdd(&s_misc[4], 1);

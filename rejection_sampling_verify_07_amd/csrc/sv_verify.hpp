@@ -32,7 +32,7 @@ constexpr int kSegElems = 8;         // ids per lane per segment
 constexpr int kSeg = kWave * kSegElems;   // 512 ids per segment
 constexpr int kMaxSeg = (1 << 20) / kSeg;  // vocabularies up to 2^20
 constexpr int kSegUnroll = 4;        // segments per wave with loads in flight together
-constexpr int kKeepCap = 1024;       // kept-list capacity per row
+constexpr int kKeepCap = 1024;       // kept-list capacity per row (same as the select passes')
 
 struct VerifyArgs {
     RowSet rs;
