@@ -94,7 +94,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build measures one GPU; the verify step shards by sequence with no exchange "
-              "(see DESIGN.md), and no multi-GPU figure is produced", file=sys.stderr)
+              "across GPUs, so a single-GPU figure is the measured one and no multi-GPU figure is produced", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -24,7 +24,7 @@
  *    "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11 (the Philox
  *    S-box: two 32x32->64 multiplications per round, Weyl key schedule).
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  p = target, q = draft; both are softmaxes at the same temperature T;
  *  top-k keeps every id whose raw logit is >= the k-th largest (ties kept),
  *  applied to each row on its own; accept iff u < min(1, p/q) with u in
