@@ -35,10 +35,13 @@ namespace {
 #define SV_STREAM_PIPE 0
 #endif
 constexpr int kLoads = SV_STREAM_LOADS;      // row statistics (sampling and greedy)
+constexpr int kLoadsBig = 8;                 // row statistics over grids much larger than the chip
+constexpr int64_t kBigGridTiles = 16384;     // 4-load tiles beyond which kLoadsBig is used (8x the resident slots)
 constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
 constexpr bool kNT = SV_STREAM_NT != 0;
 constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instead of one tile per workgroup
 constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
+constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
 constexpr size_t kAlign = 256;
 
 enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
@@ -47,6 +50,7 @@ struct Plan {
     PlanMode mode;
     int32_t rows_t, rows_d, rows;
     int32_t nchunk;
+    int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
     size_t off_partials, off_counts, off_cands, off_descs, off_kept, bytes;
 };
 
@@ -146,7 +150,16 @@ Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
     } else {
         p.mode = top_k <= sv::kTopkFastMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
     }
-    p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype), p.mode == PLAN_TOPK_FAST ? kCandLoads : kLoads);
+    // Streaming tiles: measured on MI355X, 8 loads per thread beat 4 once the
+    // grid holds many times more tiles than the chip keeps resident, and lose
+    // below that (fewer, longer tiles leave the last wave of tiles thin).
+    if (p.mode == PLAN_TOPK_FAST) {
+        p.loads = kCandLoads;
+    } else {
+        const int64_t rows_stream = greedy ? p.rows_t : p.rows;
+        p.loads = rows_stream * chunks_for(sh->vocab, vec_of(sh->dtype), kLoads) > kBigGridTiles ? kLoadsBig : kLoads;
+    }
+    p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype), p.loads);
     size_t off = 0;
     const size_t slots = (size_t)p.rows * (size_t)p.nchunk;
     if (p.mode == PLAN_FULL) {
@@ -214,11 +227,17 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
 
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
-        launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab,
-                      p.nchunk, (int32_t)grid_stream, c, (void*)part);
+        if (p.loads == kLoadsBig) {
+            launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoadsBig, kNT, kPipe, true>, grid_stream, stream, rs,
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
+        } else {
+            launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT, kPipe>, grid_stream, stream, rs,
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
+        }
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         va.partials = part;
-        hipLaunchKernelGGL((sv::verify_kernel<DT, false>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
+        hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
+                           stream, va);
         return launch_status();
     }
 
@@ -245,7 +264,7 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     if (launch_status() != SV_OK) return SV_ERR_HIP;
     va.descs = descs;
     va.kept = kept;
-    hipLaunchKernelGGL((sv::verify_kernel<DT, true>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
+    hipLaunchKernelGGL((sv::verify_kernel<DT, true, sv::kThreads>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
     return launch_status();
 }
 
@@ -258,8 +277,13 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
                   p.rows_t};
     sv::PartialArg* part = ws_at<sv::PartialArg>(ws, p.off_partials);
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows_t * p.nchunk);
-    launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab,
-                  p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
+    if (p.loads == kLoadsBig) {
+        launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoadsBig, kNT, kPipe>, grid_stream, stream, rs,
+                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
+    } else {
+        launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT, kPipe>, grid_stream, stream, rs,
+                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
+    }
     if (launch_status() != SV_OK) return SV_ERR_HIP;
     sv::GreedyArgs ga{sh->cu_draft, sh->batch, sh->max_draft, sh->total_draft, sh->vocab, ids, part, p.nchunk,
                       out_tokens, out_nacc};

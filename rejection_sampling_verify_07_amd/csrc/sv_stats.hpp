@@ -6,14 +6,14 @@
 // "Prepare autoregressive sampling" and "Prepare speculative sampling") is
 // reduced here to per-chunk statistics; the accept pass merges them.
 //
-// Tiles of 256 * LOADS aligned 16-byte blocks per (row, chunk), walked by a
-// persistent pipelined grid (sv_stream.hpp).  Every thread keeps its LOADS
-// raw words in registers and walks them twice:
+// Tiles of 256 * LOADS aligned 16-byte blocks per (row, chunk), one tile per
+// workgroup (sv_stream.hpp).  Every thread keeps its LOADS raw words in
+// registers and walks them twice:
 //   MODE_FULL   chunk max m_c, then S_c = sum exp2(fl32(l * c - fl32(m_c * c)))
 //               (fp32 terms, fp64 accumulation across blocks and lanes);
-//   MODE_ARGMAX chunk max and the lowest row index that holds it.
-// Rows need not be 16-byte aligned: the blocks that straddle a row edge are
-// masked element by element.
+//   MODE_ARGMAX chunk max, then the lowest row index that holds it.
+// Rows need not be 16-byte aligned: the out-of-row slots of the blocks that
+// straddle a row edge are overwritten with -inf before either walk.
 #pragma once
 
 #include "sv_common.hpp"
@@ -23,7 +23,98 @@ namespace sv {
 
 enum { MODE_FULL = 0, MODE_ARGMAX = 1 };
 
-template <int DT, int MODE, int LOADS, bool NT, bool PIPE>
+// Edge tiles (a block reaching outside the row) overwrite the out-of-row
+// slots of their raw words with -inf first: -inf never raises a maximum and
+// exp2(-inf) = 0, so the element loops below need no masks.
+template <int DT, int LOADS>
+__device__ __forceinline__ void sanitize_edge(const Tile& t, int32_t vocab, u32x4* rw)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    const bool interior = t.cb0 * VEC >= t.mis && (t.cb0 + kThreads * LOADS) * VEC <= t.mis + vocab;
+    if (interior) return;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int32_t r0 = (tile_b0(t) + i * kThreads) * VEC - t.mis;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            uint32_t w = rw[i][q];
+            if constexpr (DT == DT_BF16) {
+                if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | 0xff80u;
+                if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | 0xff800000u;
+            } else {
+                if ((uint32_t)(r0 + q) >= (uint32_t)vocab) w = 0xff800000u;
+            }
+            rw[i][q] = w;
+        }
+    }
+}
+
+template <int DT, int LOADS>
+__device__ __forceinline__ float lane_max(const u32x4* raw)
+{
+    float tm = neg_inf();
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        float f[Dt<DT>::kVec];
+        unpack<DT>(raw[i], f);
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) tm = fmaxf(tm, f[e]);
+    }
+    return tm;
+}
+
+// MODE_FULL with every element masked in place of the -inf fill of edge
+// tiles.  Same results; on MI355X this form sustains more HBM bandwidth than
+// the masked-free one over grids far larger than the chip (1.1 GB of logits
+// at 8 loads per thread: about 157 us against 170-175 us), and less over
+// grids of a few resident waves of tiles, so the plan picks per grid size.
+template <int DT, int LOADS>
+__device__ __forceinline__ void full_masked(const Tile& t, const u32x4* raw, int32_t vocab, float c,
+                                            void* __restrict__ partials, float* s_m, double* s_s)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    float mx = neg_inf();
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        float f[VEC];
+        tile_block<DT>(t, raw, i, vocab, neg_inf(), f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) mx = fmaxf(mx, f[e]);
+    }
+    mx = wave_max(mx);
+    if (lane_id() == 0) s_m[wave_id()] = mx;
+    __syncthreads();
+    float m = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w]);
+    const float mcc = m * c;
+    double acc = 0.0;
+    if (m != neg_inf()) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            float f[VEC];
+            tile_block<DT>(t, raw, i, vocab, neg_inf(), f);
+            float s = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+            acc += (double)s;
+        }
+    }
+    acc = wave_sum(acc);
+    if (lane_id() == 0) s_s[wave_id()] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double s = s_s[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) s += s_s[w];
+        PartialFull* out = reinterpret_cast<PartialFull*>(partials) + t.index;
+        out->m = m;
+        out->mcc = mcc;
+        out->s = s;
+    }
+}
+
+template <int DT, int MODE, int LOADS, bool NT, bool PIPE, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                              int32_t ntiles, float c, void* __restrict__ partials)
 {
@@ -32,63 +123,66 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t 
     __shared__ int32_t s_i[kWaves];
     __shared__ double s_s[kWaves];
 
-    walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, const u32x4* raw) {
+    walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
+        if constexpr (MODE == MODE_FULL && MASKED) {
+            full_masked<DT, LOADS>(t, raw, vocab, c, partials, s_m, s_s);
+            return;
+        }
+        sanitize_edge<DT, LOADS>(t, vocab, raw);
+        const float tm = lane_max<DT, LOADS>(raw);
+        // With 8 loads per thread, widen again after the barrier rather than
+        // keep every widened value live across it (an empty asm that claims
+        // to update the raw words; it emits no instruction), which keeps the
+        // pass within 64 VGPRs.  With 4 the widened values fit and are kept.
+        if constexpr (LOADS > 4) {
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) asm volatile("" : "+v"(raw[i]));
+        }
+        const float wm = wave_max(tm);
+        if (lane_id() == 0) s_m[wave_id()] = wm;
+        __syncthreads();
+        float m = s_m[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w]);
+
         if constexpr (MODE == MODE_ARGMAX) {
-            float best = neg_inf();
-            // lowest valid row index this thread covers (ties at -inf resolve to it)
-            int32_t bidx = (tile_b0(t) < t.nblk) ? max(tile_b0(t) * VEC - t.mis, 0) : INT32_MAX;
+            // the lowest row index holding m: only lanes whose own maximum is m
+            // look for it (-inf also matches the fill, so indexes are range-checked)
+            int32_t idx = INT32_MAX;
+            if (tm == m) {
 #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                float f[VEC];
-                tile_block<DT>(t, raw, i, vocab, neg_inf(), f);
-                const int32_t r0 = (tile_b0(t) + i * kThreads) * VEC - t.mis;
+                for (int i = LOADS - 1; i >= 0; --i) {  // backwards: the last hit is the lowest index
+                    float f[VEC];
+                    unpack<DT>(raw[i], f);
+                    const int32_t r0 = (tile_b0(t) + i * kThreads) * VEC - t.mis;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    if (f[e] > best) {
-                        best = f[e];
-                        bidx = r0 + e;
+                    for (int e = VEC - 1; e >= 0; --e) {
+                        const int32_t r = r0 + e;
+                        idx = (f[e] == m && (uint32_t)r < (uint32_t)vocab) ? r : idx;
                     }
                 }
             }
-            wave_argmax(best, bidx);
-            if (lane_id() == 0) {
-                s_m[wave_id()] = best;
-                s_i[wave_id()] = bidx;
-            }
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) idx = min(idx, __shfl_xor(idx, o, kWave));
+            if (lane_id() == 0) s_i[wave_id()] = idx;
             __syncthreads();
             if (threadIdx.x == 0) {
-                float v = s_m[0];
                 int32_t ix = s_i[0];
 #pragma unroll
-                for (int w = 1; w < kWaves; ++w) argmax_merge(v, ix, s_m[w], s_i[w]);
+                for (int w = 1; w < kWaves; ++w) ix = min(ix, s_i[w]);
                 PartialArg* out = reinterpret_cast<PartialArg*>(partials) + t.index;
-                out->m = v;
+                out->m = m;
                 out->idx = ix;
             }
             __syncthreads();  // s_m / s_i are rewritten by the next tile
         } else {
-            float mx = neg_inf();
-#pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                float f[VEC];
-                tile_block<DT>(t, raw, i, vocab, neg_inf(), f);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) mx = fmaxf(mx, f[e]);
-            }
-            mx = wave_max(mx);
-            if (lane_id() == 0) s_m[wave_id()] = mx;
-            __syncthreads();
-            float m = s_m[0];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_m[w]);
-
             const float mcc = m * c;
             double acc = 0.0;
             if (m != neg_inf()) {
 #pragma unroll
                 for (int i = 0; i < LOADS; ++i) {
                     float f[VEC];
-                    tile_block<DT>(t, raw, i, vocab, neg_inf(), f);
+                    unpack<DT>(raw[i], f);
                     float s = 0.0f;
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));

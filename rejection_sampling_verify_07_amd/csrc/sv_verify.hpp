@@ -7,7 +7,9 @@
 // per guess, stop at the first rejection, one extra token from the last
 // target position when every guess is accepted).
 //
-// Phases (one 256-thread workgroup per sequence b):
+// Phases (one workgroup per sequence b: 1024 threads when the draws walk full
+// rows, so that enough loads are in flight for the residual's two-row
+// re-read; 256 when they walk top-k kept lists):
 //  A  per-row statistics of the sequence's K_b+1 target and K_b draft rows,
 //     merged from the streaming pass's chunk partials (m, S) or read from the
 //     top-k select pass's row descriptors;
@@ -119,7 +121,7 @@ __device__ __forceinline__ void seg_weights(const char* ra, const char* rb, int3
 
 // Inverse CDF over a full row (or row pair).  All threads call it; all get
 // the token and the total.
-template <int DT, bool TWO, class W>
+template <int DT, bool TWO, int NT, class W>
 __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, const W& wfn, double u,
                                  double* s_seg, double* s_wd, int32_t* s_i, double* s_dd,
                                  int32_t* token, double* total)
@@ -129,16 +131,16 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
     const int lane = lane_id();
 
     // pass 1: per-segment sums (lane sums in fp64, then a wave inclusive scan)
-    for (int32_t s0 = wave_id(); s0 < nseg; s0 += kWaves * kSegUnroll) {
+    for (int32_t s0 = wave_id(); s0 < nseg; s0 += (NT / kWave) * kSegUnroll) {
         float w[kSegUnroll][kSegElems];
 #pragma unroll
         for (int uu = 0; uu < kSegUnroll; ++uu) {
-            const int32_t s = s0 + uu * kWaves;
+            const int32_t s = s0 + uu * (NT / kWave);
             if (s < nseg) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
         }
 #pragma unroll
         for (int uu = 0; uu < kSegUnroll; ++uu) {
-            const int32_t s = s0 + uu * kWaves;
+            const int32_t s = s0 + uu * (NT / kWave);
             if (s < nseg) {
                 double ls = 0.0;
 #pragma unroll
@@ -151,7 +153,7 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
     __syncthreads();
 
     // workgroup inclusive scan of the segment sums, in place
-    const int32_t per = (nseg + kThreads - 1) / kThreads;
+    const int32_t per = (nseg + NT - 1) / NT;
     const int32_t lo = min(nseg, (int32_t)threadIdx.x * per), hi = min(nseg, lo + per);
     double run = 0.0;
     for (int32_t s = lo; s < hi; ++s) {
@@ -282,12 +284,12 @@ __device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* d
     *total = z;
 }
 
-template <int DT, bool FROM_DESC>
-__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
+template <int DT, bool FROM_DESC, int NT>
+__global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
 {
     __shared__ RowLds s_row[2 * kMaxDraft + 1];
     __shared__ double s_seg[kMaxSeg];
-    __shared__ double s_wd[kWaves];
+    __shared__ double s_wd[(NT / kWave)];
     __shared__ double s_dd[2];
     __shared__ int32_t s_i[4];
     __shared__ int32_t s_n, s_bad;
@@ -321,12 +323,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
 
     // ---- A: row statistics
     if constexpr (FROM_DESC) {
-        for (int32_t r = threadIdx.x; r < nrows; r += kThreads) {
+        for (int32_t r = threadIdx.x; r < nrows; r += NT) {
             const RowDesc d = a.descs[grow(r)];
             s_row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
         }
     } else {
-        for (int32_t r = wave_id(); r < nrows; r += kWaves) {
+        for (int32_t r = wave_id(); r < nrows; r += (NT / kWave)) {
             const PartialFull* pp = a.partials + (int64_t)grow(r) * a.nchunk;
             float m = neg_inf();
             for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     // ---- B: accept test at every draft position
     const char* tbase = a.rs.tgt;
     const char* dbase = a.rs.drf;
-    for (int32_t k = threadIdx.x; k < kb; k += kThreads) {
+    for (int32_t k = threadIdx.x; k < kb; k += NT) {
         const int32_t x = a.ids[drow0 + k];
         if (x < 0 || x >= a.vocab) {
             atomicOr(&s_bad, 1);
@@ -396,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             token = s_i[2];
             z = s_dd[1];
         } else {
-            inverse_cdf_full<DT, true>(trow, drow, a.vocab, wfn, u, s_seg, s_wd, s_i, s_dd, &token, &z);
+            inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wfn, u, s_seg, s_wd, s_i, s_dd, &token, &z);
         }
         if (token < 0) {
             // no positive residual mass (rounding only): draw from p_n with the same uniform
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                 __syncthreads();
                 token = s_i[2];
             } else {
-                inverse_cdf_full<DT, false>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &z2);
+                inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &z2);
             }
         }
     } else {
@@ -430,13 +432,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
         } else {
             const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
             double zz;
-            inverse_cdf_full<DT, false>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &zz);
+            inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &zz);
         }
         z = 0.0;
     }
 
     // ---- D: outputs
-    for (int32_t j = threadIdx.x; j <= kb; j += kThreads) {
+    for (int32_t j = threadIdx.x; j <= kb; j += NT) {
         a.out_tokens[trow0 + j] = j < n ? a.ids[drow0 + j] : (j == n ? token : -1);
     }
     if (threadIdx.x == 0) {
