@@ -41,6 +41,7 @@ constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
 constexpr bool kNT = SV_STREAM_NT != 0;
 constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instead of one tile per workgroup
 constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
+static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads past a chunk's candidate slots");
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
 constexpr size_t kAlign = 256;
 
@@ -51,7 +52,7 @@ struct Plan {
     int32_t rows_t, rows_d, rows;
     int32_t nchunk;
     int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
-    size_t off_partials, off_counts, off_cands, off_descs, off_kept, bytes;
+    size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, bytes;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -172,6 +173,8 @@ Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
         if (p.mode == PLAN_TOPK_FAST) {
             p.off_counts = off;
             off = align_up(off + slots * sizeof(int32_t));
+            p.off_bounds = off;
+            off = align_up(off + slots * sizeof(float));
             p.off_cands = off;
             off = align_up(off + slots * (size_t)kCandCap * sizeof(sv::KeptEntry));
         }
@@ -244,18 +247,20 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     sv::RowDesc* descs = ws_at<sv::RowDesc>(ws, p.off_descs);
     sv::KeptEntry* kept = ws_at<sv::KeptEntry>(ws, p.off_kept);
     int32_t* counts = nullptr;
+    float* bounds = nullptr;
     sv::KeptEntry* cands = nullptr;
     if (p.mode == PLAN_TOPK_FAST) {
         counts = ws_at<int32_t>(ws, p.off_counts);
+        bounds = ws_at<float>(ws, p.off_bounds);
         cands = ws_at<sv::KeptEntry>(ws, p.off_cands);
         launch_stream(sv::topk_cand_kernel<DT, kCandLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab, p.nchunk,
-                      (int32_t)grid_stream, top_k, kCandCap, counts, cands);
+                      (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
     }
     if (p.mode == PLAN_TOPK_FAST) {
         // one wave per row; rows whose chunks overflowed take the exact path inside
         hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,
-                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)1, descs, kept);
+                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, (int32_t)1, descs, kept);
     } else {
         hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
                            p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)0, (int32_t)sv::kKeepCap, descs,

@@ -171,6 +171,58 @@ __device__ __forceinline__ void wave_argmax(float& v, int32_t& i)
     }
 }
 
+// ---------------------------------------------------------------------------
+// DPP reductions: data moves between lanes inside the VALU (quad permutes,
+// row mirrors, row broadcasts) instead of through the LDS crossbar, which
+// matters for the latency-bound one-wave-per-row passes.  The combine order
+// is fixed; the result is read from lane 63 and returned wave-uniform.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_mov(int old, int v)
+{
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror, row_bcast:15 (into rows 1 and 3), row_bcast:31 (into rows 2, 3).
+enum { kDppQuad1032 = 0xB1, kDppQuad2301 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+       kDppBcast15 = 0x142, kDppBcast31 = 0x143 };
+
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    const int ninf = __float_as_int(neg_inf());
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuad1032>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppQuad2301>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppHalfMirror>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppMirror>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppBcast15, 0xa>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_mov<kDppBcast31, 0xc>(ninf, __float_as_int(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ double dpp_mov_f64(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const int lo = dpp_mov<CTRL, ROW_MASK>(0, (int)(uint32_t)b);
+    const int hi = dpp_mov<CTRL, ROW_MASK>(0, (int)(uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double wave_sum_dpp(double v)
+{
+    v += dpp_mov_f64<kDppQuad1032>(v);
+    v += dpp_mov_f64<kDppQuad2301>(v);
+    v += dpp_mov_f64<kDppHalfMirror>(v);
+    v += dpp_mov_f64<kDppMirror>(v);
+    v += dpp_mov_f64<kDppBcast15, 0xa>(v);
+    v += dpp_mov_f64<kDppBcast31, 0xc>(v);
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, kWave - 1);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), kWave - 1);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask)
 {

@@ -44,82 +44,47 @@ struct SelKey {
     }
 };
 
-// Sort (id, value) pairs held one per lane (lanes >= n hold INT32_MAX) by id.
-__device__ __forceinline__ void wave_bitonic_by_id(int32_t& ix, float& v)
-{
-    const int lane = lane_id();
-#pragma unroll
-    for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int32_t pix = __shfl_xor(ix, stride, kWave);
-            const float pv = __shfl_xor(v, stride, kWave);
-            const bool up = (lane & size) == 0;
-            const bool lower = (lane & stride) == 0;
-            const bool take = (lower == up) ? (pix < ix) : (pix > ix);
-            if (take) {
-                ix = pix;
-                v = pv;
-            }
-        }
-    }
-}
-
 // LDS scratch of one wave.
-struct WaveSelLds {
+struct alignas(16) WaveSelLds {
     int32_t kidx[kKeepCapList];
     float kval[kKeepCapList];
     uint32_t hist[256];
 };
 
-template <int DT>
-__device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
-                                 const int32_t* __restrict__ counts, const KeptEntry* __restrict__ cands,
-                                 RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
-                                 const int32_t* choff, int32_t total)
+// The select proper, from NJ candidate slots per lane in registers (idx
+// INT32_MAX marks an empty slot): tau by a ballot radix select, the kept
+// entries compacted and sorted by id, their max and sum, the descriptor.
+// NJ is a template argument so that every per-slot loop is unrolled without
+// branches; select_tail picks the smallest NJ that holds the candidates.
+template <int DT, int NJ>
+__device__ void select_tail_n(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+                              KeptEntry* __restrict__ kept, WaveSelLds& L, const KeptEntry* e)
 {
     using K = SelKey<DT>;
     const int lane = lane_id();
-    const int32_t nj = (total + kWave - 1) / kWave;  // wave-uniform
-
-    // candidates into registers, all loads issued first
-    KeptEntry e[kSelPer];
+    uint32_t key[NJ];
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) {
-        const int32_t i = lane + j * kWave;
-        e[j] = KeptEntry{INT32_MAX, neg_inf()};
-        if (j < nj && i < total) {
-            int32_t lo = 0, hi = nchunk;
-            while (hi - lo > 1) {
-                const int32_t mid = (lo + hi) >> 1;
-                if (choff[mid] <= i) lo = mid; else hi = mid;
-            }
-            e[j] = cands[((int64_t)row * nchunk + lo) * cap + (i - choff[lo])];
-        }
-    }
-    uint32_t key[kSelPer];
-#pragma unroll
-    for (int j = 0; j < kSelPer; ++j) key[j] = (e[j].idx != INT32_MAX) ? K::of(e[j].val) : 0u;
+    for (int j = 0; j < NJ; ++j) key[j] = (e[j].idx != INT32_MAX) ? K::of(e[j].val) : 0u;
 
     // ballot radix select: the largest h with #{key >= h} >= top_k
     uint32_t h = 0;
+#pragma unroll
     for (int bit = K::kBits - 1; bit >= 0; --bit) {
         const uint32_t cand = h | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < kSelPer; ++j)
-            if (j < nj) cnt += (int)__popcll(__ballot(key[j] >= cand));
-        if (cnt >= top_k) h = cand;
+        for (int j = 0; j < NJ; ++j) cnt += (int)__popcll(__ballot(key[j] >= cand));
+        h = cnt >= top_k ? cand : h;
     }
 
     // kept entries (key >= h), compacted in candidate order
     int32_t nk = 0;
     float lm = neg_inf();
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) {
-        if (j < nj) {
-            const bool pred = key[j] >= h && e[j].idx != INT32_MAX;
-            const uint64_t m = __ballot(pred);
+    for (int j = 0; j < NJ; ++j) {
+        const bool pred = key[j] >= h && e[j].idx != INT32_MAX;
+        const uint64_t m = __ballot(pred);
+        if (m != 0) {
             if (pred) {
                 const int32_t pos = nk + lanes_below(m);
                 L.kidx[pos] = e[j].idx;
@@ -129,21 +94,32 @@ __device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int
             nk += (int32_t)__popcll(m);
         }
     }
-    lm = __shfl(wave_max(lm), 0, kWave);
+    lm = wave_max_dpp(lm);
     const float mcc = lm * c;
-    __builtin_amdgcn_wave_barrier();
 
     KeptEntry* klist = kept + (int64_t)row * kKeepCapList;
     double ls = 0.0;
     if (nk <= kWave) {
-        int32_t ix = lane < nk ? L.kidx[lane] : INT32_MAX;
-        float v = lane < nk ? L.kval[lane] : neg_inf();
-        wave_bitonic_by_id(ix, v);
+        // one kept entry per lane; its place in the id-sorted list is the
+        // number of kept ids below its own (ids are distinct), counted from
+        // 16 broadcast LDS reads of four ids each (slots past nk hold INT32_MAX)
+        if (lane >= nk) L.kidx[lane] = INT32_MAX;
+        __builtin_amdgcn_wave_barrier();
+        const int32_t ix = L.kidx[lane];
+        const float v = lane < nk ? L.kval[lane] : neg_inf();
+        const int4* k4 = reinterpret_cast<const int4*>(L.kidx);
+        int4 q[kWave / 4];
+#pragma unroll
+        for (int j = 0; j < kWave / 4; ++j) q[j] = k4[j];
+        int32_t rank = 0;
+#pragma unroll
+        for (int j = 0; j < kWave / 4; ++j) rank += (q[j].x < ix) + (q[j].y < ix) + (q[j].z < ix) + (q[j].w < ix);
         if (lane < nk) {
-            klist[lane] = KeptEntry{ix, v};
+            klist[rank] = KeptEntry{ix, v};
             ls = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mcc));
         }
     } else {
+        __builtin_amdgcn_wave_barrier();
         int32_t npad = kWave;
         while (npad < nk) npad <<= 1;
         for (int32_t i = nk + lane; i < npad; i += kWave) {
@@ -175,7 +151,7 @@ __device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int
             ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(L.kval[i], c, -mcc));
         }
     }
-    ls = wave_sum(ls);
+    ls = wave_sum_dpp(ls);
     if (lane == 0) {
         RowDesc d;
         d.tau = K::value(h);
@@ -187,6 +163,134 @@ __device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int
         d.pad = 0;
         descs[row] = d;
     }
+}
+
+// e[0 .. nj) hold the candidates (nj wave-uniform, at most kSelPer).
+template <int DT>
+__device__ void select_tail(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+                            KeptEntry* __restrict__ kept, WaveSelLds& L, const KeptEntry* e, int32_t nj)
+{
+    if (nj <= 1) {
+        select_tail_n<DT, 1>(row, top_k, c, descs, kept, L, e);
+    } else if (nj <= 2) {
+        select_tail_n<DT, 2>(row, top_k, c, descs, kept, L, e);
+    } else if (nj <= 4) {
+        select_tail_n<DT, 4>(row, top_k, c, descs, kept, L, e);
+    } else if (nj <= 8) {
+        select_tail_n<DT, 8>(row, top_k, c, descs, kept, L, e);
+    } else {
+        select_tail_n<DT, kSelPer>(row, top_k, c, descs, kept, L, e);
+    }
+}
+
+// Candidates by global position: the row's chunks hold counts[ch] entries
+// each, choff their exclusive prefix sums (in LDS); candidate i is found by a
+// binary search over choff.
+template <int DT>
+__device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+                                 const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
+                                 KeptEntry* __restrict__ kept, WaveSelLds& L, const int32_t* choff, int32_t total)
+{
+    const int lane = lane_id();
+    const int32_t nj = (total + kWave - 1) / kWave;  // wave-uniform
+    KeptEntry e[kSelPer];
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) {
+        const int32_t i = lane + j * kWave;
+        e[j] = KeptEntry{INT32_MAX, neg_inf()};
+        if (j < nj && i < total) {
+            int32_t lo = 0, hi = nchunk;
+            while (hi - lo > 1) {
+                const int32_t mid = (lo + hi) >> 1;
+                if (choff[mid] <= i) lo = mid; else hi = mid;
+            }
+            e[j] = cands[((int64_t)row * nchunk + lo) * cap + (i - choff[lo])];
+        }
+    }
+    select_tail<DT>(row, top_k, c, descs, kept, L, e, nj);
+}
+
+// Speculative path for rows of at most kSpecChunks chunks whose chunks hold at
+// most kSpecSlots * 64 candidates each: the counts, the chunk bounds and the
+// first kSpecSlots * 64 slots of every chunk are loaded at once.  Every chunk
+// bound is a lower bound of the row's tau, so only candidates >= their
+// maximum can be kept; those few are compacted (in LDS) before the select.
+// Returns false, having written nothing, when the row does not qualify.
+constexpr int kSpecChunks = 16;
+constexpr int kSpecSlots = 2;
+
+// The select over n candidates staged in L.kidx / L.kval (n <= NJ * 64).
+template <int DT, int NJ>
+__device__ void select_from_lds(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+                                KeptEntry* __restrict__ kept, WaveSelLds& L, int32_t n)
+{
+    KeptEntry r[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int32_t i = lane_id() + j * kWave;
+        r[j] = i < n ? KeptEntry{L.kidx[i], L.kval[i]} : KeptEntry{INT32_MAX, neg_inf()};
+    }
+    __builtin_amdgcn_wave_barrier();
+    select_tail_n<DT, NJ>(row, top_k, c, descs, kept, L, r);
+}
+
+template <int DT>
+__device__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+                                 const int32_t* __restrict__ counts, const float* __restrict__ bounds,
+                                 const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
+                                 KeptEntry* __restrict__ kept, WaveSelLds& L)
+{
+    const int lane = lane_id();
+    const int64_t t0 = (int64_t)row * nchunk;
+    const int32_t cnt_l = lane < nchunk ? counts[t0 + lane] : 0;
+    const float bnd_l = lane < nchunk ? bounds[t0 + lane] : neg_inf();
+    KeptEntry e[kSpecChunks][kSpecSlots];
+#pragma unroll
+    for (int ch = 0; ch < kSpecChunks; ++ch) {
+#pragma unroll
+        for (int q = 0; q < kSpecSlots; ++q) {
+            e[ch][q] = ch < nchunk ? cands[(t0 + ch) * cap + q * kWave + lane] : KeptEntry{INT32_MAX, neg_inf()};
+        }
+    }
+    if (__ballot(cnt_l > kSpecSlots * kWave) != 0) return false;
+    const float bmax = wave_max_dpp(bnd_l);
+
+    // survivors (candidate >= the largest chunk bound), compacted in chunk order
+    int32_t ns = 0;
+#pragma unroll
+    for (int ch = 0; ch < kSpecChunks; ++ch) {
+        if (ch < nchunk) {
+            const int32_t cnt = __builtin_amdgcn_readlane(cnt_l, ch);
+#pragma unroll
+            for (int q = 0; q < kSpecSlots; ++q) {
+                const bool pred = q * kWave + lane < cnt && e[ch][q].val >= bmax;
+                const uint64_t m = __ballot(pred);
+                if (m != 0) {
+                    const int32_t pos = ns + lanes_below(m);
+                    if (pred && pos < kKeepCapList) {
+                        L.kidx[pos] = e[ch][q].idx;
+                        L.kval[pos] = e[ch][q].val;
+                    }
+                    ns += (int32_t)__popcll(m);
+                }
+            }
+        }
+    }
+    if (ns < top_k || ns > kKeepCapList) return false;
+    __builtin_amdgcn_wave_barrier();
+    const int32_t nj = (ns + kWave - 1) / kWave;
+    if (nj <= 1) {
+        select_from_lds<DT, 1>(row, top_k, c, descs, kept, L, ns);
+    } else if (nj <= 2) {
+        select_from_lds<DT, 2>(row, top_k, c, descs, kept, L, ns);
+    } else if (nj <= 4) {
+        select_from_lds<DT, 4>(row, top_k, c, descs, kept, L, ns);
+    } else if (nj <= 8) {
+        select_from_lds<DT, 8>(row, top_k, c, descs, kept, L, ns);
+    } else {
+        select_from_lds<DT, kSelPer>(row, top_k, c, descs, kept, L, ns);
+    }
+    return true;
 }
 
 // Visit a full row by one wave, 16-byte loads, kRowUnroll per lane in flight;
@@ -339,6 +443,7 @@ template <int DT>
 __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                                  int32_t top_k, int32_t cap, float c,
                                                                  const int32_t* __restrict__ counts,
+                                                                 const float* __restrict__ bounds,
                                                                  const KeptEntry* __restrict__ cands,
                                                                  int32_t use_cands, RowDesc* __restrict__ descs,
                                                                  KeptEntry* __restrict__ kept)
@@ -346,6 +451,9 @@ __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int3
     __shared__ WaveSelLds L;
     __shared__ int32_t s_choff[kMaxChunks + 1];
     const int32_t row = blockIdx.x;
+    if (use_cands != 0 && nchunk <= kSpecChunks &&
+        wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L))
+        return;
     if (use_cands != 0) {
         int32_t base = 0, bad = 0;
         for (int32_t g = 0; g < nchunk; g += kWave) {
@@ -360,7 +468,7 @@ __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int3
         if (lane_id() == 0) s_choff[nchunk] = base;
         __builtin_amdgcn_wave_barrier();
         if (__ballot(bad != 0) == 0 && base >= top_k && base <= kKeepCapList) {
-            wave_select_fast<DT>(row, nchunk, top_k, cap, c, counts, cands, descs, kept, L, s_choff, base);
+            wave_select_fast<DT>(row, nchunk, top_k, cap, c, cands, descs, kept, L, s_choff, base);
             return;
         }
     }

@@ -192,7 +192,7 @@ constexpr int kChunkLds = kWaves * kWaveLds;
 template <int DT, int LOADS, bool NT, bool PIPE>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
-    int32_t* __restrict__ counts, KeptEntry* __restrict__ cands)
+    int32_t* __restrict__ counts, float* __restrict__ bounds, KeptEntry* __restrict__ cands)
 {
     constexpr int VEC = Dt<DT>::kVec;
     constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
         }
         int wcount = 0;  // wave-uniform count of this wave's candidates
         const int wbase = wave_id() * kWaveLds;
+        float bound;  // the tile's lower bound of the row's tau
         {
             float tm = neg_inf();
 #pragma unroll
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 if (cnt >= top_k) h = cand;
             }
             // smallest float whose key has these top bits; the -inf bucket maps to -inf
-            const float bound = (h <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(h << 16);
+            bound = (h <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(h << 16);
 
             // candidates into this wave's LDS region, in (load, element, lane)
             // order; the exact value and the row index are formed only on the
@@ -346,7 +347,10 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
         } else {
             written = cap + 1;  // a wave overflowed its staging slots
         }
-        if (threadIdx.x == 0) counts[t.index] = written;  // > cap marks an overflow
+        if (threadIdx.x == 0) {
+            counts[t.index] = written;  // > cap marks an overflow
+            bounds[t.index] = bound;
+        }
         __syncthreads();  // LDS is reused by the next tile
     });
 }
