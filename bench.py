@@ -53,6 +53,59 @@ def stored_traffic(workload: str, mode: str):
     return rec.get("bytes_per_launch")
 
 
+def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, copy_mb: float) -> dict:
+    """Per-launch HBM bytes of the streaming kernel from two rocprofv3 --pmc runs.
+
+    fetch_csv / write_csv are the counter_collection.csv files of runs with
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of this same bench command
+    with --copy-calibration-mb copy_mb.  Each counter is scaled by what it
+    reads for that plain device copy of known size (the last five copy
+    dispatches: copy_mb MB read and written each), and the result is stored
+    in profiles/traffic.json under the current kernel-source hash.
+    """
+    import csv
+
+    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else ("sample_topk" if "top" in workload else "sample")]
+
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            vals[key] = (r["Kernel_Name"], vals.get(key, ("", 0.0))[1] + float(r["Counter_Value"]))
+        return [vals[k] for k in sorted(vals)]
+
+    out = {}
+    known = copy_mb * 1e6
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = per_dispatch(path, counter)
+        copies = [v for n, v in rows if "copy" in n.lower()][-5:]
+        stream = sorted(v for n, v in rows if kind_kernel in n)
+        if len(copies) < 5 or not stream:
+            raise SystemExit(f"record-traffic: found {len(copies)} copy and {len(stream)} {kind_kernel} dispatches")
+        copy_kib = sorted(copies)[2]
+        factor = known / (copy_kib * 1024.0)
+        out[counter] = {"stream_kib_median": stream[len(stream) // 2], "copy_kib": copy_kib, "factor": factor,
+                        "bytes": stream[len(stream) // 2] * 1024.0 * factor, "dispatches": len(stream)}
+    rec = {"source_sha": kernel_source_sha(), "kernel": kind_kernel,
+           "bytes_per_launch": round(out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]),
+           "fetch_bytes": round(out["FETCH_SIZE"]["bytes"]), "write_bytes": round(out["WRITE_SIZE"]["bytes"]),
+           "calibration": {"copy_mb": copy_mb, "fetch_factor": round(out["FETCH_SIZE"]["factor"], 4),
+                           "write_factor": round(out["WRITE_SIZE"]["factor"], 4)},
+           "raw_kib": {"fetch": out["FETCH_SIZE"]["stream_kib_median"], "write": out["WRITE_SIZE"]["stream_kib_median"],
+                       "copy_fetch": out["FETCH_SIZE"]["copy_kib"], "copy_write": out["WRITE_SIZE"]["copy_kib"]}}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[f"{workload}/{mode}"] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+    return rec
+
+
 def cpu_baseline(w, mode, seconds):
     import oracle
 
@@ -89,7 +142,18 @@ def main():
     ap.add_argument("--no-profile-pass", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run a plain device copy of this size (for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store the streaming kernel's HBM bytes from two rocprofv3 --pmc runs (no GPU needed)")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        import workloads as W
+
+        name = W.CONFIGS[args.config]["name"]
+        rec = record_traffic(name, args.mode, args.record_traffic[0], args.record_traffic[1],
+                             args.copy_calibration_mb or 256.0)
+        print(json.dumps(rec))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
