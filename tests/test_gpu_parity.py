@@ -156,6 +156,36 @@ def test_constant_rows_take_the_full_row_path():
     note(f"constant rows: {rep}")
 
 
+def test_tied_head_takes_the_chunk_list_select():
+    # 200 logits tied at the row maximum, one at the start of each of the first
+    # 200 16-byte blocks (rows are 16-byte aligned here): 200 lanes of the first
+    # tile reach the maximum, so the tile's bound is that maximum and its 200
+    # ties are its candidates -- more than the speculative select loads per
+    # chunk (128), fewer than a chunk holds (256).  The kept set is the 200
+    # ties, more than one per lane of a wave.
+    w = W.make_workload(_spec(vocab=20000, batch=3, k=3, top_k=50, kind="zipf"), gen_seed=21)
+
+    def tie_head(x):
+        x = np.minimum(x, 8.0)
+        x[:, 0:1600:8] = 9.0
+        return x
+
+    w = _with_rows(w, tie_head)
+    note("tied head: 200 ties at the max in the first chunk, top_k=50")
+    g = gpu_sample(w)
+    rep = compare_sample(w, g, _oracle(w))
+    note(f"tied head: {rep}")
+    compare_greedy(w, gpu_greedy(w), _oracle(w, "greedy"))
+
+
+def test_many_chunks_bypass_the_speculative_select():
+    # V = 300000 bf16 is 19 chunks per row, more than the speculative select covers
+    w = W.make_workload(_spec(vocab=300000, batch=2, k=2, top_k=50, kind="zipf", temperature=0.7), gen_seed=22)
+    note("V=300000 bf16 top_k=50 (19 chunks per row)")
+    rep = compare_sample(w, gpu_sample(w), _oracle(w))
+    note(f"many chunks: {rep}")
+
+
 def test_candidate_overflow_takes_the_exact_path():
     # heavy ties inside one chunk overflow its candidate slots
     w = W.make_workload(_spec(vocab=30000, batch=3, k=3, top_k=50, kind="zipf"), gen_seed=3)
