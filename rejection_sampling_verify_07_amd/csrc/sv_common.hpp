@@ -223,6 +223,45 @@ __device__ __forceinline__ double wave_sum_dpp(double v)
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP (fixed order): within each
+// row of 16 the sums of 2, 3 and 4 neighbours, then shifts by 4 and 8; then
+// the row totals are carried into rows 1 and 3 (row_bcast:15) and into rows 2
+// and 3 (row_bcast:31).  Lanes whose source is outside the row add 0.
+enum { kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118,
+       kDppWaveShr1 = 0x138 };
+
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, BANK_MASK, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, BANK_MASK, true);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+__device__ __forceinline__ double wave_incl_scan_dpp(double v)
+{
+    double s = v + dpp_f64<kDppRowShr1, 0xf, 0xf>(v);
+    s = s + dpp_f64<kDppRowShr2, 0xf, 0xf>(v);
+    s = s + dpp_f64<kDppRowShr3, 0xf, 0xf>(v);
+    s = s + dpp_f64<kDppRowShr4, 0xf, 0xe>(s);
+    s = s + dpp_f64<kDppRowShr8, 0xf, 0xc>(s);
+    s = s + dpp_f64<kDppBcast15, 0xa, 0xf>(s);
+    s = s + dpp_f64<kDppBcast31, 0xc, 0xf>(s);
+    return s;
+}
+
+// The previous lane's value (0 in lane 0).
+__device__ __forceinline__ double wave_prev_dpp(double v) { return dpp_f64<kDppWaveShr1, 0xf, 0xf>(v); }
+
+__device__ __forceinline__ double readlane_f64(double v, int lane)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask)
 {

@@ -145,7 +145,7 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
                 double ls = 0.0;
 #pragma unroll
                 for (int e = 0; e < kSegElems; ++e) ls += (double)w[uu][e];
-                const double incl = wave_incl_scan(ls);
+                const double incl = wave_incl_scan_dpp(ls);
                 if (lane == kWave - 1) s_seg[s] = incl;
             }
         }
@@ -160,9 +160,8 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
         run += s_seg[s];
         s_seg[s] = run;
     }
-    const double tincl = wave_incl_scan(run);
-    double texcl = __shfl_up(tincl, 1, kWave);
-    if (lane == 0) texcl = 0.0;
+    const double tincl = wave_incl_scan_dpp(run);
+    const double texcl = wave_prev_dpp(tincl);
     if (lane == kWave - 1) s_wd[wave_id()] = tincl;
     __syncthreads();
     double off = 0.0;
@@ -192,9 +191,8 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
             double ls = 0.0;
 #pragma unroll
             for (int e = 0; e < kSegElems; ++e) ls += (double)w[e];
-            const double incl = wave_incl_scan(ls);
-            double excl = __shfl_up(incl, 1, kWave);
-            if (lane == 0) excl = 0.0;
+            const double incl = wave_incl_scan_dpp(ls);
+            const double excl = wave_prev_dpp(incl);
             double cum = (s > 0 ? s_seg[s - 1] : 0.0) + excl;
             int hit = -1, lastpos = -1;
 #pragma unroll
@@ -206,13 +204,13 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
             const uint64_t bh = __ballot(hit >= 0);
             if (bh != 0) {
                 const int src = __builtin_ctzll(bh);
-                tok = s * kSeg + src * kSegElems + __shfl(hit, src, kWave);
+                tok = s * kSeg + src * kSegElems + __builtin_amdgcn_readlane(hit, src);
             } else {
                 // rounding put the target past this segment's walk: its last positive id
                 const uint64_t bp = __ballot(lastpos >= 0);
                 if (bp != 0) {
                     const int src = 63 - __builtin_clzll(bp);
-                    tok = s * kSeg + src * kSegElems + __shfl(lastpos, src, kWave);
+                    tok = s * kSeg + src * kSegElems + __builtin_amdgcn_readlane(lastpos, src);
                 }
             }
         }
@@ -227,10 +225,11 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
     __syncthreads();
 }
 
-// Inverse CDF over a kept list (ascending ids), wave 0 only.
-template <int DT, bool RESID>
-__device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* drow, const ResidualW& rw,
-                                 double u, int32_t* token, double* total)
+// Inverse CDF over a kept list (ascending ids), one wave.  entry(i) yields the
+// list's i-th (id, logit); draft(id) the draft logit at id (RESID only).
+template <bool RESID, class Entry, class Draft>
+__device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, const ResidualW& rw, double u,
+                                    int32_t* token, double* total)
 {
     constexpr int PER = kKeepCap / kWave;  // entries per lane
     const int lane = lane_id();
@@ -245,11 +244,11 @@ __device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* d
         w[q] = 0.0f;
         ix[q] = -1;
         if (i < hi) {
-            const KeptEntry e = list[i];
+            const KeptEntry e = entry(i);
             ix[q] = e.idx;
             const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
             if constexpr (RESID) {
-                const float ld = load_one<DT>(drow, e.idx);
+                const float ld = draft(e.idx);
                 const float ed =
                     ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
                 w[q] = fmaxf(et - ed, 0.0f);
@@ -259,10 +258,9 @@ __device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* d
             ls += (double)w[q];
         }
     }
-    const double incl = wave_incl_scan(ls);
-    double excl = __shfl_up(incl, 1, kWave);
-    if (lane == 0) excl = 0.0;
-    const double z = __shfl(incl, kWave - 1, kWave);
+    const double incl = wave_incl_scan_dpp(ls);
+    const double excl = wave_prev_dpp(incl);
+    const double z = readlane_f64(incl, kWave - 1);
     const double t = u * z;
     double cum = excl;
     int hit = -1, lastpos = -1;
@@ -275,23 +273,104 @@ __device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* d
     int32_t tok = -1;
     const uint64_t bh = __ballot(hit >= 0);
     if (bh != 0) {
-        tok = __shfl(hit, __builtin_ctzll(bh), kWave);
+        tok = __builtin_amdgcn_readlane(hit, __builtin_ctzll(bh));
     } else {
         const uint64_t bp = __ballot(lastpos >= 0);
-        if (bp != 0) tok = __shfl(lastpos, 63 - __builtin_clzll(bp), kWave);
+        if (bp != 0) tok = __builtin_amdgcn_readlane(lastpos, 63 - __builtin_clzll(bp));
     }
     *token = tok;
     *total = z;
+}
+
+// The same over a kept list in global memory, the draft logits gathered from
+// the draft row.
+template <int DT, bool RESID>
+__device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* drow, const ResidualW& rw,
+                                 double u, int32_t* token, double* total)
+{
+    inverse_cdf_list_of<RESID>([&](int32_t i) { return list[i]; }, n,
+                               [&](int32_t v) { return load_one<DT>(drow, v); }, rw, u, token, total);
+}
+
+// LDS of the one-draw phase.
+template <int NT>
+struct DrawLds {
+    double seg[kMaxSeg];
+    double wd[NT / kWave];
+    double dd[2];
+    int32_t i[4];
+};
+
+// The new token of a sequence (all threads call it; all get the result):
+// the residual draw at the first rejection n < kb, else the extra-token draw
+// from target row kb.  rt / rd: statistics of target row n and draft row n.
+// u: U(b, n, 1) when n < kb, else U(b, kb, 2).
+template <int DT, bool FROM_DESC, int NT>
+__device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32_t kb, double u, const RowLds& rt,
+                           const RowLds& rd, const char* trow, const char* drow, int64_t kept_row_n,
+                           DrawLds<NT>& L, int32_t* token_out, double* z_out)
+{
+    int32_t token = -1;
+    double z = 0.0;
+    if (n < kb) {
+        const ResidualW wfn{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
+        if (FROM_DESC && rt.kept >= 0) {
+            if (wave_id() == 0) {
+                inverse_cdf_list<DT, true>(a.kept + kept_row_n * kKeepCap, rt.kept, drow, wfn, u, &token, &z);
+                if (lane_id() == 0) {
+                    L.i[2] = token;
+                    L.dd[1] = z;
+                }
+            }
+            __syncthreads();
+            token = L.i[2];
+            z = L.dd[1];
+        } else {
+            inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wfn, u, L.seg, L.wd, L.i, L.dd, &token, &z);
+        }
+        if (token < 0) {
+            // no positive residual mass (rounding only): draw from p_n with the same uniform
+            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+            double z2;
+            if (FROM_DESC && rt.kept >= 0) {
+                if (wave_id() == 0) {
+                    const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+                    inverse_cdf_list<DT, false>(a.kept + kept_row_n * kKeepCap, rt.kept, nullptr, lw, u, &token, &z2);
+                    if (lane_id() == 0) L.i[2] = token;
+                }
+                __syncthreads();
+                token = L.i[2];
+            } else {
+                inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, L.seg, L.wd, L.i, L.dd, &token, &z2);
+            }
+        }
+    } else {
+        if (FROM_DESC && rt.kept >= 0) {
+            if (wave_id() == 0) {
+                const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+                double zz;
+                inverse_cdf_list<DT, false>(a.kept + kept_row_n * kKeepCap, rt.kept, nullptr, lw, u, &token, &zz);
+                if (lane_id() == 0) L.i[2] = token;
+            }
+            __syncthreads();
+            token = L.i[2];
+        } else {
+            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+            double zz;
+            inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, L.seg, L.wd, L.i, L.dd, &token, &zz);
+        }
+        z = 0.0;
+    }
+    *token_out = token;
+    *z_out = z;
 }
 
 template <int DT, bool FROM_DESC, int NT>
 __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
 {
     __shared__ RowLds s_row[2 * kMaxDraft + 1];
-    __shared__ double s_seg[kMaxSeg];
-    __shared__ double s_wd[(NT / kWave)];
-    __shared__ double s_dd[2];
-    __shared__ int32_t s_i[4];
+    __shared__ DrawLds<NT> s_draw;
+    __shared__ double s_udraw[kMaxDraft + 1];
     __shared__ int32_t s_n, s_bad;
 
     const int32_t b = blockIdx.x;
@@ -320,6 +399,12 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
         s_n = kb;
         s_bad = 0;
     }
+    // every uniform the step can use, computed while the first loads are in
+    // flight: thread k holds U(b, k, 0); s_udraw[k] = U(b, k, 1), s_udraw[kb] = U(b, kb, 2)
+    static_assert(NT > kMaxDraft, "one thread per draft position");
+    const int32_t tk = threadIdx.x;
+    const double u_acc = uniform24(a.seed, (uint32_t)b, (uint32_t)tk, 0u, a.offset);
+    if (tk <= kb) s_udraw[tk] = uniform24(a.seed, (uint32_t)b, (uint32_t)tk, tk < kb ? 1u : 2u, a.offset);
 
     // ---- A: row statistics
     if constexpr (FROM_DESC) {
@@ -332,14 +417,14 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
             const PartialFull* pp = a.partials + (int64_t)grow(r) * a.nchunk;
             float m = neg_inf();
             for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
-            m = __shfl(wave_max(m), 0, kWave);
+            m = wave_max_dpp(m);
             const float mcc = m * a.c;
             double s = 0.0;
             for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
                 const PartialFull q = pp[ch];
                 if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
             }
-            s = wave_sum(s);
+            s = wave_sum_dpp(s);
             if (lane_id() == 0) s_row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
         }
     }
@@ -365,9 +450,8 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
             a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
             a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
         }
-        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)k, 0u, a.offset);
         const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        if (!(u < ratio)) atomicMin(&s_n, k);
+        if (!(u_acc < ratio)) atomicMin(&s_n, k);
     }
     __syncthreads();
     if (s_bad != 0) {
@@ -377,64 +461,14 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
     const int32_t n = s_n;
 
     // ---- C: residual or extra-token draw
-    int32_t token = -1;
-    double z = 0.0;
-    const RowLds rt = s_row[n];
-    const char* trow = tbase + (int64_t)(trow0 + n) * a.rs.t_stride_bytes;
-    if (n < kb) {
-        const RowLds rd = s_row[kb + 1 + n];
-        const char* drow = dbase + (int64_t)(drow0 + n) * a.rs.d_stride_bytes;
-        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)n, 1u, a.offset);
-        const ResidualW wfn{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
-        if (FROM_DESC && rt.kept >= 0) {
-            if (wave_id() == 0) {
-                inverse_cdf_list<DT, true>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, drow, wfn, u, &token, &z);
-                if (lane_id() == 0) {
-                    s_i[2] = token;
-                    s_dd[1] = z;
-                }
-            }
-            __syncthreads();
-            token = s_i[2];
-            z = s_dd[1];
-        } else {
-            inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wfn, u, s_seg, s_wd, s_i, s_dd, &token, &z);
-        }
-        if (token < 0) {
-            // no positive residual mass (rounding only): draw from p_n with the same uniform
-            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
-            double z2;
-            if (FROM_DESC && rt.kept >= 0) {
-                if (wave_id() == 0) {
-                    const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
-                    inverse_cdf_list<DT, false>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, nullptr, lw, u,
-                                                &token, &z2);
-                    if (lane_id() == 0) s_i[2] = token;
-                }
-                __syncthreads();
-                token = s_i[2];
-            } else {
-                inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &z2);
-            }
-        }
-    } else {
-        const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)kb, 2u, a.offset);
-        if (FROM_DESC && rt.kept >= 0) {
-            if (wave_id() == 0) {
-                const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
-                double zz;
-                inverse_cdf_list<DT, false>(a.kept + (int64_t)grow(n) * kKeepCap, rt.kept, nullptr, lw, u, &token,
-                                            &zz);
-                if (lane_id() == 0) s_i[2] = token;
-            }
-            __syncthreads();
-            token = s_i[2];
-        } else {
-            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
-            double zz;
-            inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, s_seg, s_wd, s_i, s_dd, &token, &zz);
-        }
-        z = 0.0;
+    int32_t token;
+    double z;
+    {
+        const RowLds rt = s_row[n];
+        const RowLds rd = s_row[n < kb ? kb + 1 + n : n];
+        const char* trow = tbase + (int64_t)(trow0 + n) * a.rs.t_stride_bytes;
+        const char* drow = n < kb ? dbase + (int64_t)(drow0 + n) * a.rs.d_stride_bytes : nullptr;
+        draw_token<DT, FROM_DESC, NT>(a, n, kb, s_udraw[n], rt, rd, trow, drow, (int64_t)grow(n), s_draw, &token, &z);
     }
 
     // ---- D: outputs
