@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t 
                 out->m = m;
                 out->idx = ix;
             }
-            __syncthreads();  // s_m / s_i are rewritten by the next tile
+            if constexpr (PIPE) __syncthreads();  // s_m / s_i are rewritten by the next tile of a persistent grid
         } else {
             const float mcc = m * c;
             double acc = 0.0;

@@ -351,7 +351,10 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             counts[t.index] = written;  // > cap marks an overflow
             bounds[t.index] = bound;
         }
-        __syncthreads();  // LDS is reused by the next tile
+        // LDS is reused by the next tile of a persistent grid.  With one tile
+        // per workgroup there is none, and a barrier here would only keep the
+        // waves resident until their candidate stores are acknowledged.
+        if constexpr (PIPE) __syncthreads();
     });
 }
 
