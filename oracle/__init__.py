@@ -85,6 +85,11 @@ def _load():
     lib.orc_verify_greedy.argtypes = [
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int32, C.c_int32, P, P,
     ]
+    lib.orc_draft_sample.restype = C.c_int
+    lib.orc_draft_sample.argtypes = [
+        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, C.c_double, C.c_int32, C.c_uint64, C.c_uint32,
+        C.c_double, C.c_int32, C.c_int32, P, P, P, P, P,
+    ]
     _lib = lib
     return lib
 
@@ -295,8 +300,44 @@ def verify_greedy(target, draft_ids, cu_draft, vocab: int, dtype: str,
     return dict(tokens=tokens, num_accepted=nacc)
 
 
+def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int, seed: int, offset: int,
+                 eps: float = 1e-6, seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+                 draft_stride: Optional[int] = None) -> dict:
+    """Seeded draft-side sampling: x(b, k) ~ q_k by the inverse CDF with U(b, k, 3).
+
+    Returns ids [R_d] and, per draft row, dist (distance of u to the chosen
+    id's interval edges), tok_lo / tok_hi (ids whose interval meets the
+    eps-window) and flags.  Rows of sequences not listed in `seqs` keep -2.
+    """
+    lib = _load()
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    B = cu.shape[0] - 1
+    R_d = int(cu[-1])
+    n = max(R_d, 1)
+    drf = _as_storage(draft, dtype) if R_d > 0 else np.zeros((1, vocab), np.float32 if dtype == "f32" else np.uint16)
+    ds = int(draft_stride or (drf.shape[-1] if drf.ndim == 2 else vocab))
+    out = dict(ids=np.full(n, -2, np.int32), dist=np.full(n, np.nan), tok_lo=np.full(n, -2, np.int32),
+               tok_hi=np.full(n, -2, np.int32), flags=np.zeros(n, np.int32))
+    o = out
+
+    def fn(rng):
+        return lib.orc_draft_sample(B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(drf), ds, float(temperature),
+                                    int(top_k), int(seed), int(offset), float(eps), rng[0], rng[1], _ptr(o["ids"]),
+                                    _ptr(o["dist"]), _ptr(o["tok_lo"]), _ptr(o["tok_hi"]), _ptr(o["flags"]))
+
+    rcs = _run(fn, _ranges(B, seqs, threads), threads)
+    if any(rc == -2 for rc in rcs):
+        raise MemoryError("oracle draft_sample")
+    for k in out:
+        out[k] = out[k][:R_d]
+    out["rc"] = min(rcs) if rcs else 0
+    return out
+
+
 def verify_workload(w, mode: str = "sample", **kw) -> dict:
-    """Convenience: run the oracle on a workloads.Workload."""
+    """Convenience: run the oracle on a workloads.Workload (mode "draft": draft-side sampling)."""
+    if mode == "draft":
+        return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset, **kw)
     if mode == "greedy":
         return verify_greedy(w.target, w.draft_ids, w.cu_draft, w.vocab, w.dtype, **kw)
     return verify_sample(w.target, w.draft, w.draft_ids, w.cu_draft, w.vocab, w.dtype,

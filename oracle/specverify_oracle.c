@@ -408,6 +408,44 @@ int orc_verify_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
 }
 
 /*
+ * Draft-side sampling, the step before verify: the draft model proposes the
+ * K guesses one position at a time ("Text Generation via Speculative
+ * Sampling, KV Caching, and OpenVINO", "Prepare speculative sampling", step
+ * 1, where it takes the argmax), and the acceptance proof of
+ * "CS3602_FINAL_SpeDec", section 2, assumes each guess is drawn from q.  So
+ * x(b, k) is the inverse-CDF draw (ascending ids) of q_k = softmax(draft row
+ * k / T) over its top-k kept set, with U(b, k, 3).  Per draft row: the id,
+ * the distance from u to the chosen id's interval edges, the ids whose
+ * interval meets [u - eps, u + eps], and flags.
+ */
+int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* draft, int64_t d_stride,
+                     double T, int32_t top_k, uint64_t seed, uint32_t offset, double eps, int32_t b_begin,
+                     int32_t b_end, int32_t* ids, double* dist, int32_t* tok_lo, int32_t* tok_hi, int32_t* flags)
+{
+    const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
+    double* q = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!q) return -2;
+    double stats[4];
+    int rc_all = 0;
+    for (int32_t b = b_begin; b < b_end && b < B; ++b) {
+        const int32_t K = cu[b + 1] - cu[b];
+        for (int32_t k = 0; k < K; ++k) {
+            const int64_t r = (int64_t)cu[b] + k;
+            const char* row = (const char*)draft + (size_t)r * (size_t)d_stride * esz;
+            int32_t fl = 0;
+            if (orc_row_probs(row, dtype, V, T, top_k, q, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            const double u = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 3u, offset);
+            double total;
+            ids[r] = (int32_t)orc_inverse_cdf(q, V, u, eps, &total, dist + r, tok_lo + r, tok_hi + r, &fl);
+            flags[r] = fl;
+            if (fl & ORC_FLAG_BAD_INPUT) rc_all = -1;
+        }
+    }
+    free(q);
+    return rc_all;
+}
+
+/*
  * Greedy argmax-compare: a_k = argmax of target row k; n = the first k with
  * x_k != a_k (K_b when none); tokens x_0..x_{n-1}, a_n, then -1.
  */

@@ -386,3 +386,59 @@ def test_hand_worked_example(orc):
     # the eps-window around a CDF edge spans both neighbours
     r = orc.verify_seq_u(P, Q, [1], [0.0], [0.0], 0.75 - 1e-8, eps=1e-6)
     assert (r["tok_lo"], r["tok_hi"]) == (1, 2) and r["d_fin"] < 1e-6
+
+
+# --------------------------------------------------------------------------
+# draft-side sampling (the guesses x ~ q that the proof assumes)
+# --------------------------------------------------------------------------
+def _one_row_per_sequence(row, B, dtype="f32"):
+    rows = np.repeat(np.asarray(row, np.float32)[None, :], B, axis=0)
+    return (rows if dtype == "f32" else W.f32_to_bf16_bits(rows)), np.arange(B + 1, dtype=np.int32)
+
+
+@pytest.mark.parametrize("top_k", [0, 5])
+def test_draft_sample_law_chi_square(orc, top_k):
+    """2*10^5 independent draws (one per sequence, distinct counters) follow
+    q = softmax(l / T) over the top-k kept set, by a chi-square test against
+    scipy's softmax."""
+    rng = np.random.default_rng(31)
+    V, T, B = 8, 0.8, 200000
+    row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    rows, cu = _one_row_per_sequence(row, B)
+    r = orc.draft_sample(rows, cu, V, "f32", T, top_k, seed=7, offset=3, threads=8)
+    q = _softmax(row, T, top_k)
+    obs = np.bincount(r["ids"], minlength=V)
+    assert obs[q == 0].sum() == 0
+    keep = q > 0
+    assert stats.chisquare(obs[keep], q[keep] * B).pvalue > 1e-3
+
+
+def test_draft_sample_top_k_1_is_argmax(orc):
+    # distinct logits: top_k = 1 keeps only the maximum, so the draw is numpy's argmax
+    rng = np.random.default_rng(5)
+    rows = (rng.standard_normal((64, 500)) * 3).astype(np.float32)
+    cu = np.array([0, 10, 10, 40, 64], np.int32)
+    r = orc.draft_sample(rows, cu, 500, "f32", 0.9, 1, seed=1, offset=0)
+    assert np.array_equal(r["ids"], np.argmax(rows, axis=1))
+    # a tied maximum is kept whole (ties at tau are kept): every draw is one of the tied ids
+    tied = rng.integers(-20, 20, (64, 500)).astype(np.float32) / 2
+    r = orc.draft_sample(tied, cu, 500, "f32", 0.9, 1, seed=1, offset=0)
+    assert np.all(tied[np.arange(64), r["ids"]] == tied.max(axis=1))
+
+
+def test_draft_sample_single_finite_logit(orc):
+    rows = np.full((6, 40), -np.inf, np.float32)
+    for i in range(6):
+        rows[i, (7 * i) % 40] = 0.5 * i
+    r = orc.draft_sample(rows, np.array([0, 6], np.int32), 40, "f32", 1.0, 0, seed=4, offset=9)
+    assert np.array_equal(r["ids"], (7 * np.arange(6)) % 40)
+
+
+def test_draft_sample_seed_and_offset_move_the_draws(orc):
+    rng = np.random.default_rng(8)
+    rows = (rng.standard_normal((200, 50)) * 0.3).astype(np.float32)  # flat: draws spread out
+    cu = np.array([0, 200], np.int32)
+    a = orc.draft_sample(rows, cu, 50, "f32", 1.0, 0, seed=1, offset=0)["ids"]
+    b = orc.draft_sample(rows, cu, 50, "f32", 1.0, 0, seed=2, offset=0)["ids"]
+    c = orc.draft_sample(rows, cu, 50, "f32", 1.0, 0, seed=1, offset=1)["ids"]
+    assert (a != b).mean() > 0.5 and (a != c).mean() > 0.5
