@@ -14,9 +14,11 @@
  *   draft position, stop at the first rejection, and draw one extra token from
  *   the last target position when every guess was accepted; section "Prepare
  *   autoregressive sampling": softmax over the vocabulary, argmax decode
- *   (the greedy mode here).
+ *   (the greedy mode here).  spec_draft_sample draws the guesses themselves
+ *   (step 1 of "Prepare speculative sampling", sampling in place of the
+ *   argmax).
  *
- * Conventions shared by both calls
+ * Conventions shared by the calls
  *   Batch layout (packed, ragged).  Sequence b has K_b >= 0 draft tokens.
  *   With cu_draft == NULL every K_b equals shape->max_draft; otherwise
  *   cu_draft is a DEVICE array of B+1 int32 prefix sums (cu_draft[0] = 0,
@@ -156,6 +158,36 @@ SV_API sv_status_t spec_verify_greedy(const sv_shape_t* shape,
                                void* workspace,
                                size_t* workspace_bytes,
                                hipStream_t stream);
+
+/*
+ * Draft-side sampling, the step before verify: every guess x(b, k) ~ q_k.
+ * The draft model proposes its K guesses one position at a time ("Text
+ * Generation via Speculative Sampling, KV Caching, and OpenVINO", section
+ * "Prepare speculative sampling", step 1, which takes the argmax); the
+ * acceptance proof of "CS3602_FINAL_SpeDec", section 2, assumes each guess
+ * is drawn from q, and that page's sampling helpers filter by top-K.
+ *   q_k = softmax(draft row k / T) over its top-k kept set, exactly as in
+ *   spec_verify_sample; x(b, k) = the first id (ascending) whose running sum
+ *   of q_k exceeds U(b, k, 3), with U as in spec_verify_sample.
+ * Arguments
+ *   shape as for spec_verify_sample; target_row_stride is ignored.
+ *   draft_logits [total_draft, draft_row_stride] in shape->dtype.
+ *   temperature > 0 and finite; top_k in [0, V].
+ *   out_ids int32 [total_draft]: x(b, k) at cu_draft[b] + k.  A sequence
+ *   whose cu_draft entries are out of range leaves its slots untouched; a
+ *   row with no finite logit in its kept set yields -1.
+ * Memory, execution, workspace and errors as for spec_verify_sample.
+ */
+SV_API sv_status_t spec_draft_sample(const sv_shape_t* shape,
+                              const void* draft_logits,
+                              float temperature,
+                              int32_t top_k,
+                              uint64_t seed,
+                              uint32_t offset,
+                              int32_t* out_ids,
+                              void* workspace,
+                              size_t* workspace_bytes,
+                              hipStream_t stream);
 
 /* A static, human-readable name for a status code. */
 SV_API const char* spec_verify_status_string(sv_status_t status);

@@ -5,11 +5,13 @@ include/specverify.h); this package holds its sources (csrc/), the build
 script and a thin ctypes binding.
 """
 from .binding import (  # noqa: F401
+    DraftPlan,
     GreedyPlan,
     SamplePlan,
     HipEvents,
     SpecVerifyError,
     load_library,
+    draft_sample,
     status_string,
     verify_greedy,
     verify_sample,

@@ -66,6 +66,10 @@ def load_library(path: Optional[str] = None):
     ]
     lib.spec_verify_greedy.restype = C.c_int
     lib.spec_verify_greedy.argtypes = [C.POINTER(ShapeT), VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP]
+    lib.spec_draft_sample.restype = C.c_int
+    lib.spec_draft_sample.argtypes = [
+        C.POINTER(ShapeT), VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32, VP, VP, C.POINTER(C.c_size_t), VP,
+    ]
     lib.spec_verify_status_string.restype = C.c_char_p
     lib.spec_verify_status_string.argtypes = [C.c_int]
     lib.spec_verify_set_profile_events.restype = C.c_int
@@ -208,6 +212,52 @@ def verify_greedy(target_logits: torch.Tensor, draft_ids: torch.Tensor, cu_draft
     return out
 
 
+def _draft_geometry(draft_logits, cu_draft, batch, max_draft):
+    total = draft_logits.shape[0]
+    if cu_draft is None:
+        if batch is None or batch <= 0 or total % batch != 0:
+            raise ValueError("pass batch (rows = batch * K) or cu_draft for ragged K")
+        k = total // batch
+        if max_draft is not None and max_draft != k:
+            raise ValueError("max_draft does not match the uniform draft length")
+        return batch, k, total
+    if cu_draft.dtype != torch.int32 or cu_draft.dim() != 1:
+        raise ValueError("cu_draft must be a 1-D int32 tensor")
+    b = cu_draft.numel() - 1
+    if max_draft is None:
+        max_draft = int((cu_draft[1:] - cu_draft[:-1]).max().item()) if b > 0 else 0
+    return b, max_draft, total
+
+
+def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = None, batch: Optional[int] = None,
+                 temperature: float = 1.0, top_k: int = 0, seed: int = 0, offset: int = 0,
+                 max_draft: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Draft-side sampling on the GPU (spec_draft_sample): x(b, k) ~ q_k.
+
+    draft_logits [sum(K_b), V] float32 or bfloat16, rows packed as for the
+    verify; cu_draft int32 [B+1] or None with `batch` (uniform K).  Returns
+    the int32 ids [sum(K_b)].
+    """
+    lib = load_library()
+    b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
+    shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
+    dev = draft_logits.device
+    need = C.c_size_t(0)
+    _check(lib.spec_draft_sample(C.byref(shape), None, float(temperature), int(top_k), int(seed), int(offset), None,
+                                 None, C.byref(need), None), "spec_draft_sample(workspace query)")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)[:total]
+    have = C.c_size_t(workspace.numel())
+    st = lib.spec_draft_sample(C.byref(shape), draft_logits.data_ptr() if total else None, float(temperature),
+                               int(top_k), int(seed), int(offset), out.data_ptr() if total else None,
+                               workspace.data_ptr(), C.byref(have), C.c_void_p(_stream_handle(stream)))
+    _check(st, "spec_draft_sample")
+    return out
+
+
 def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k=0, max_draft=None,
                     greedy=False) -> int:
     lib = load_library()
@@ -336,3 +386,31 @@ class GreedyPlan:
         st = self.fn(*self.args)
         if st != SV_OK:
             raise SpecVerifyError(st, "spec_verify_greedy")
+
+
+class DraftPlan:
+    """spec_draft_sample with every argument marshalled once."""
+
+    def __init__(self, draft_logits, cu_draft=None, batch=None, temperature=1.0, top_k=0, seed=0, offset=0,
+                 max_draft=None, out=None, workspace=None, stream=None):
+        self.lib = load_library()
+        b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
+        self.shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
+        dev = draft_logits.device
+        need = C.c_size_t(0)
+        _check(self.lib.spec_draft_sample(C.byref(self.shape), None, float(temperature), int(top_k), int(seed),
+                                          int(offset), None, None, C.byref(need), None), "workspace query")
+        self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
+            torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+        self.have = C.c_size_t(self.workspace.numel())
+        self._keep = (draft_logits, cu_draft)
+        self.args = (C.byref(self.shape), C.c_void_p(draft_logits.data_ptr()), C.c_float(temperature),
+                     C.c_int32(top_k), C.c_uint64(seed), C.c_uint32(offset), C.c_void_p(self.out.data_ptr()),
+                     C.c_void_p(self.workspace.data_ptr()), C.byref(self.have), C.c_void_p(_stream_handle(stream)))
+        self.fn = self.lib.spec_draft_sample
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "spec_draft_sample")

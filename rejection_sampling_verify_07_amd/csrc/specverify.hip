@@ -46,6 +46,7 @@ constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves kee
 constexpr size_t kAlign = 256;
 
 enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
+enum CallKind { CALL_SAMPLE = 0, CALL_GREEDY = 1, CALL_DRAFT = 2 };
 
 struct Plan {
     PlanMode mode;
@@ -118,8 +119,9 @@ void launch_stream(K kernel, uint32_t ntiles, hipStream_t s, Args... args)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-sv_status_t check_shape(const sv_shape_t* sh, bool need_draft_rows)
+sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
 {
+    const bool need_draft_rows = kind != CALL_GREEDY;
     if (sh == nullptr) return SV_ERR_INVALID_ARGUMENT;
     if (sh->batch < 1 || sh->vocab < 1 || sh->max_draft < 0 || sh->total_draft < 0)
         return SV_ERR_INVALID_ARGUMENT;
@@ -128,7 +130,7 @@ sv_status_t check_shape(const sv_shape_t* sh, bool need_draft_rows)
         return SV_ERR_INVALID_ARGUMENT;
     if (sh->cu_draft != nullptr && !aligned(sh->cu_draft, 4)) return SV_ERR_INVALID_ARGUMENT;
     if ((int64_t)sh->total_draft > (int64_t)sh->batch * sh->max_draft) return SV_ERR_INVALID_ARGUMENT;
-    if (sh->target_row_stride < sh->vocab) return SV_ERR_INVALID_ARGUMENT;
+    if (kind != CALL_DRAFT && sh->target_row_stride < sh->vocab) return SV_ERR_INVALID_ARGUMENT;
     if (need_draft_rows && sh->total_draft > 0 && sh->draft_row_stride < sh->vocab)
         return SV_ERR_INVALID_ARGUMENT;
     if (sh->vocab > SV_MAX_VOCAB || sh->max_draft > SV_MAX_DRAFT) return SV_ERR_UNSUPPORTED;
@@ -137,11 +139,15 @@ sv_status_t check_shape(const sv_shape_t* sh, bool need_draft_rows)
     return SV_OK;
 }
 
-Plan make_plan(const sv_shape_t* sh, bool greedy, int32_t top_k)
+// Rows of the streaming pass: rows [0, rows_t) are read through RowSet::tgt
+// (the target rows, or the draft rows for draft-side sampling), the rest
+// through RowSet::drf.
+Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k)
 {
+    const bool greedy = kind == CALL_GREEDY;
     Plan p{};
-    p.rows_t = sh->total_draft + sh->batch;
-    p.rows_d = greedy ? 0 : sh->total_draft;
+    p.rows_t = kind == CALL_DRAFT ? sh->total_draft : sh->total_draft + sh->batch;
+    p.rows_d = kind == CALL_SAMPLE ? sh->total_draft : 0;
     p.rows = p.rows_t + p.rows_d;
     const bool topk = !greedy && top_k > 0 && top_k < sh->vocab;
     if (greedy) {
@@ -199,35 +205,13 @@ sv_status_t launch_status()
     return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+// The streaming pass and, with top-k, the per-row select over the rows of rs:
+// fills va.partials (full rows) or va.descs / va.kept (top-k).
 template <int DT>
-sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
-                       const int32_t* ids, float c, int32_t top_k, uint64_t seed, uint32_t offset,
-                       int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
-                       hipStream_t stream)
+sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, int32_t top_k, void* ws,
+                      hipStream_t stream, sv::VerifyArgs& va)
 {
-    const size_t es = esize_of(sh->dtype);
-    sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
-                  (int64_t)(sh->target_row_stride * (int64_t)es), (int64_t)(sh->draft_row_stride * (int64_t)es),
-                  p.rows_t};
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows * p.nchunk);
-
-    sv::VerifyArgs va{};
-    va.rs = rs;
-    va.cu = sh->cu_draft;
-    va.batch = sh->batch;
-    va.kmax = sh->max_draft;
-    va.total_draft = sh->total_draft;
-    va.vocab = sh->vocab;
-    va.ids = ids;
-    va.c = c;
-    va.seed = seed;
-    va.offset = offset;
-    va.nchunk = p.nchunk;
-    va.out_tokens = out_tokens;
-    va.out_nacc = out_nacc;
-    va.out_probs = out_probs;
-    va.out_zmass = out_z;
-
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
         if (p.loads == kLoadsBig) {
@@ -237,13 +221,9 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
             launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT, kPipe>, grid_stream, stream, rs,
                           sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
         }
-        if (launch_status() != SV_OK) return SV_ERR_HIP;
         va.partials = part;
-        hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
-                           stream, va);
         return launch_status();
     }
-
     sv::RowDesc* descs = ws_at<sv::RowDesc>(ws, p.off_descs);
     sv::KeptEntry* kept = ws_at<sv::KeptEntry>(ws, p.off_kept);
     int32_t* counts = nullptr;
@@ -256,8 +236,6 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
         launch_stream(sv::topk_cand_kernel<DT, kCandLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab, p.nchunk,
                       (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
-    }
-    if (p.mode == PLAN_TOPK_FAST) {
         // one wave per row; rows whose chunks overflowed take the exact path inside
         hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,
                            sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, (int32_t)1, descs, kept);
@@ -266,10 +244,73 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
                            p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)0, (int32_t)sv::kKeepCap, descs,
                            kept);
     }
-    if (launch_status() != SV_OK) return SV_ERR_HIP;
     va.descs = descs;
     va.kept = kept;
-    hipLaunchKernelGGL((sv::verify_kernel<DT, true, sv::kThreads>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, va);
+    return launch_status();
+}
+
+sv::VerifyArgs base_args(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, uint64_t seed,
+                         uint32_t offset)
+{
+    sv::VerifyArgs va{};
+    va.rs = rs;
+    va.cu = sh->cu_draft;
+    va.batch = sh->batch;
+    va.kmax = sh->max_draft;
+    va.total_draft = sh->total_draft;
+    va.vocab = sh->vocab;
+    va.c = c;
+    va.seed = seed;
+    va.offset = offset;
+    va.nchunk = p.nchunk;
+    return va;
+}
+
+template <int DT>
+sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
+                       const int32_t* ids, float c, int32_t top_k, uint64_t seed, uint32_t offset,
+                       int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
+                       hipStream_t stream)
+{
+    const size_t es = esize_of(sh->dtype);
+    const sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
+                        (int64_t)(sh->target_row_stride * (int64_t)es), (int64_t)(sh->draft_row_stride * (int64_t)es),
+                        p.rows_t};
+    sv::VerifyArgs va = base_args(sh, p, rs, c, seed, offset);
+    va.ids = ids;
+    va.out_tokens = out_tokens;
+    va.out_nacc = out_nacc;
+    va.out_probs = out_probs;
+    va.out_zmass = out_z;
+    if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (p.mode == PLAN_FULL) {
+        hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
+                           stream, va);
+    } else {
+        hipLaunchKernelGGL((sv::verify_kernel<DT, true, sv::kThreads>), dim3(sh->batch), dim3(sv::kThreads), 0, stream,
+                           va);
+    }
+    return launch_status();
+}
+
+template <int DT>
+sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, float c, int32_t top_k, uint64_t seed,
+                      uint32_t offset, int32_t* out_ids, void* ws, hipStream_t stream)
+{
+    const size_t es = esize_of(sh->dtype);
+    // the draft rows are the streamed rows
+    const sv::RowSet rs{static_cast<const char*>(drf), nullptr, (int64_t)(sh->draft_row_stride * (int64_t)es), 0,
+                        p.rows_t};
+    sv::VerifyArgs va = base_args(sh, p, rs, c, seed, offset);
+    va.out_tokens = out_ids;
+    if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    const dim3 grid((uint32_t)sh->batch, (uint32_t)sh->max_draft);  // max_draft <= SV_MAX_DRAFT fits grid y
+    if (p.mode == PLAN_FULL) {
+        hipLaunchKernelGGL((sv::draft_draw_kernel<DT, false, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads), 0,
+                           stream, va);
+    } else {
+        hipLaunchKernelGGL((sv::draft_draw_kernel<DT, true, sv::kThreads>), grid, dim3(sv::kThreads), 0, stream, va);
+    }
     return launch_status();
 }
 
@@ -308,11 +349,11 @@ sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logit
                                hipStream_t stream)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
-    sv_status_t st = check_shape(shape, true);
+    sv_status_t st = check_shape(shape, CALL_SAMPLE);
     if (st != SV_OK) return st;
     if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
     if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
-    const Plan p = make_plan(shape, false, top_k);
+    const Plan p = make_plan(shape, CALL_SAMPLE, top_k);
     if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;
@@ -342,9 +383,9 @@ sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logit
                                size_t* workspace_bytes, hipStream_t stream)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
-    sv_status_t st = check_shape(shape, false);
+    sv_status_t st = check_shape(shape, CALL_GREEDY);
     if (st != SV_OK) return st;
-    const Plan p = make_plan(shape, true, 0);
+    const Plan p = make_plan(shape, CALL_GREEDY, 0);
     if ((int64_t)p.rows_t * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;
@@ -363,6 +404,35 @@ sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logit
                                       stream);
     return run_greedy<sv::DT_BF16>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
                                    stream);
+}
+
+sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
+                              uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
+                              size_t* workspace_bytes, hipStream_t stream)
+{
+    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    sv_status_t st = check_shape(shape, CALL_DRAFT);
+    if (st != SV_OK) return st;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
+    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, CALL_DRAFT, top_k);
+    if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    if (workspace == nullptr) {
+        *workspace_bytes = p.bytes;
+        return SV_OK;
+    }
+    if (shape->total_draft > 0 && (draft_logits == nullptr || out_ids == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+    if ((draft_logits != nullptr && !aligned(draft_logits, esize_of(shape->dtype))) ||
+        (out_ids != nullptr && !aligned(out_ids, 4)))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
+    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+    if (shape->total_draft == 0 || shape->max_draft == 0) return SV_OK;  // no draft rows: nothing to draw
+
+    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    if (shape->dtype == SV_DTYPE_F32)
+        return run_draft<sv::DT_F32>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace, stream);
+    return run_draft<sv::DT_BF16>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace, stream);
 }
 
 const char* spec_verify_status_string(sv_status_t status)

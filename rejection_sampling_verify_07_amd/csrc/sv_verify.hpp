@@ -482,6 +482,83 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Draft-side sampling, the step before verify: x(b, k) ~ q_k, the
+// inverse-CDF draw (ascending ids) with U(b, k, 3) ("Text Generation via
+// Speculative Sampling, KV Caching, and OpenVINO", "Prepare speculative
+// sampling", step 1, sampling in place of its argmax).  One workgroup per
+// (sequence b, position k): blockIdx.x = b, blockIdx.y = k.  The rows of
+// a.rs are the draft rows (rows_t = total_draft), their statistics come from
+// the same streaming passes as the verify's, and the draw is the verify's
+// extra-token draw: over the kept list after a top-k select, over the full
+// row (16 waves keep its re-read in flight) otherwise.
+// ---------------------------------------------------------------------------
+template <int DT, bool FROM_DESC, int NT>
+__global__ __launch_bounds__(NT) void draft_draw_kernel(VerifyArgs a)
+{
+    __shared__ DrawLds<NT> s_draw;
+    __shared__ RowLds s_r;
+    __shared__ int32_t s_tok;
+    const int32_t b = blockIdx.x;
+    const int32_t k = blockIdx.y;
+    int32_t k0, kb;
+    if (a.cu != nullptr) {
+        k0 = a.cu[b];
+        const int32_t k1 = a.cu[b + 1];
+        kb = k1 - k0;
+        if (k0 < 0 || kb < 0 || kb > a.kmax || k1 > a.total_draft) return;  // slots left untouched
+    } else {
+        k0 = b * a.kmax;
+        kb = a.kmax;
+    }
+    if (k >= kb) return;
+    const int32_t row = k0 + k;
+    const double u = uniform24(a.seed, (uint32_t)b, (uint32_t)k, 3u, a.offset);
+
+    if constexpr (FROM_DESC) {
+        if (threadIdx.x == 0) {
+            const RowDesc d = a.descs[row];
+            s_r = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
+        }
+    } else {
+        if (wave_id() == 0) {
+            const PartialFull* pp = a.partials + (int64_t)row * a.nchunk;
+            float m = neg_inf();
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
+            m = wave_max_dpp(m);
+            const float mcc = m * a.c;
+            double s = 0.0;
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
+                const PartialFull q = pp[ch];
+                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
+            }
+            s = wave_sum_dpp(s);
+            if (lane_id() == 0) s_r = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+        }
+    }
+    __syncthreads();
+    const RowLds rt = s_r;
+    int32_t token;
+    double z;
+    if (FROM_DESC && rt.kept >= 0) {
+        if (wave_id() == 0) {
+            const KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;
+            const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+            int32_t tok;
+            inverse_cdf_list_of<false>([&](int32_t i) { return kl[i]; }, rt.kept,
+                                       [](int32_t, int32_t) { return 0.0f; }, lw, u, &tok, &z);
+            if (lane_id() == 0) s_tok = tok;
+        }
+        __syncthreads();
+        token = s_tok;
+    } else {
+        const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+        inverse_cdf_full<DT, false, NT>(row_ptr(a.rs, row), nullptr, a.vocab, bw, u, s_draw.seg, s_draw.wd, s_draw.i,
+                                         s_draw.dd, &token, &z);
+    }
+    if (threadIdx.x == 0) a.out_tokens[row] = token;
+}
+
+// ---------------------------------------------------------------------------
 // Greedy argmax-compare: one wave per sequence merges the argmax partials of
 // its K_b + 1 target rows and compares them with the guesses.
 // ---------------------------------------------------------------------------

@@ -127,3 +127,35 @@ def compare_greedy(w, g, o, seqs=None):
         t0 = int(w.cu_draft[b]) + b
         assert g["num_accepted"][b] == o["num_accepted"][b], f"seq {b}"
         assert np.array_equal(g["tokens"][t0:t0 + K + 1], o["tokens"][t0:t0 + K + 1]), f"seq {b}"
+
+
+def gpu_draft(w, tensors=None, cu_override=None, **kw):
+    """Draft-side sampling of every draft row of w through spec_draft_sample."""
+    tgt, drf, ids, cu = tensors or to_device(w)
+    if cu_override is not None:
+        cu = cu_override
+    kw.setdefault("temperature", w.temperature)
+    kw.setdefault("top_k", w.top_k)
+    kw.setdefault("seed", w.seed)
+    kw.setdefault("offset", w.offset)
+    out = sv.draft_sample(drf, cu_draft=cu, batch=None if cu is not None else w.batch,
+                          max_draft=w.k_max if cu is not None else None, **kw)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def compare_draft(ids_gpu, ref):
+    """Draft draws: bit-exact ids except where the oracle's uniform lies within
+    EPS_BOUNDARY of the chosen id's interval edges; there the GPU id must be
+    one whose interval meets the eps-window.  Returns (rows, boundary rows)."""
+    ids_ref = ref["ids"]
+    assert ids_gpu.shape == ids_ref.shape
+    assert np.all(ref["flags"] & 4 == 0), "oracle flagged a bad row"
+    boundary = ref["dist"] < EPS_BOUNDARY
+    exact = ~boundary
+    bad = np.flatnonzero(exact & (ids_gpu != ids_ref))
+    assert bad.size == 0, f"rows {bad[:10]}: gpu {ids_gpu[bad[:10]]} oracle {ids_ref[bad[:10]]}"
+    lo, hi = ref["tok_lo"][boundary], ref["tok_hi"][boundary]
+    g = ids_gpu[boundary]
+    assert np.all((g >= lo) & (g <= hi)), "boundary draw outside the oracle's window"
+    return int(ids_ref.size), int(boundary.sum())

@@ -32,12 +32,13 @@ def B():
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"SV_API\s+[\w\s\*]+?\b(spec_verify_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"SV_API\s+[\w\s\*]+?\b(spec_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert "spec_verify_sample" in names and "spec_verify_greedy" in names
+    assert "spec_draft_sample" in names
     assert "spec_verify_status_string" in names
 
 
@@ -168,3 +169,45 @@ def test_profile_hook_arguments(lib, B):
 def test_binding_fails_loudly_without_library(tmp_path, B):
     with pytest.raises(FileNotFoundError):
         B.load_library(str(tmp_path / "missing.so"))
+
+
+def _draft_query(lib, sh, T=1.0, top_k=0):
+    need = C.c_size_t(0)
+    st = lib.spec_draft_sample(C.byref(sh), None, T, top_k, 0, 0, None, None, C.byref(need), None)
+    return st, need.value
+
+
+def test_draft_sample_arguments(lib, B):
+    # the target stride is not used by draft-side sampling
+    st, need = _draft_query(lib, _shape(B, target_row_stride=0))
+    assert st == B.SV_OK and need > 0
+    assert _draft_query(lib, _shape(B, draft_row_stride=999))[0] == B.SV_ERR_INVALID_ARGUMENT
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        assert _draft_query(lib, _shape(B), T=T)[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _draft_query(lib, _shape(B), top_k=-1)[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _draft_query(lib, _shape(B), top_k=1001)[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _draft_query(lib, _shape(B, vocab=(1 << 20) + 1, target_row_stride=(1 << 20) + 1,
+                                    draft_row_stride=(1 << 20) + 1))[0] == B.SV_ERR_UNSUPPORTED
+    sh = _shape(B)
+    st, need = _draft_query(lib, sh)
+    fake = 1 << 40  # never dereferenced: every check below fails before a launch
+    have = C.c_size_t(need)
+
+    def call(drf=fake, ids=fake, ws=fake, have_=have):
+        return lib.spec_draft_sample(C.byref(sh), drf, 1.0, 0, 0, 0, ids, ws, C.byref(have_), None)
+
+    assert call(drf=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(ids=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(drf=fake + 1) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(ids=fake + 2) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.spec_draft_sample(C.byref(sh), fake, 1.0, 0, 0, 0, fake, fake, None, None) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_draft_sample(None, fake, 1.0, 0, 0, 0, fake, fake, C.byref(have), None) == \
+        B.SV_ERR_INVALID_ARGUMENT
+    # no draft rows: a valid call that launches nothing
+    sh0 = _shape(B, max_draft=0, total_draft=0)
+    st, need0 = _draft_query(lib, sh0)
+    assert st == B.SV_OK
+    assert lib.spec_draft_sample(C.byref(sh0), None, 1.0, 0, 0, 0, None, fake,
+                                 C.byref(C.c_size_t(need0)), None) == B.SV_OK

@@ -1,0 +1,123 @@
+"""Draft-side sampling on the GPU (spec_draft_sample) against the oracle.
+
+x(b, k) ~ q_k by the inverse CDF with U(b, k, 3): the step before verify
+("Text Generation via Speculative Sampling, KV Caching, and OpenVINO",
+"Prepare speculative sampling", step 1, sampling in place of its argmax).
+"""
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+import workloads as W
+from gpu_util import compare_draft, gpu_draft, note, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, **kw):
+    return oracle.verify_workload(w, "draft", threads=16, **kw)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_draft_full_size(cfg):
+    w = W.make_config(cfg)
+    note(f"draft config {cfg} {w.name}: rows={w.rows_draft} V={w.vocab} {w.dtype} T={w.temperature} top_k={w.top_k}")
+    g = gpu_draft(w)
+    rows, nb = compare_draft(g, _oracle(w))
+    note(f"draft config {cfg}: {rows} rows, {nb} boundary draws")
+
+
+def _spec(**kw):
+    d = dict(name="draft_edge", batch=4, k=3, vocab=1001, dtype="bf16", temperature=1.0, top_k=0, kind="iid",
+             target_sigma=2.0, draft_sigma=1.0, ragged=False, modes=("sample",))
+    d.update(kw)
+    return d
+
+
+EDGE = {
+    "vocab1": _spec(vocab=1),
+    "vocab7_f32": _spec(vocab=7, dtype="f32"),
+    "misaligned_rows_bf16": _spec(),
+    "top_k_1": _spec(top_k=1, vocab=4000),
+    "top_k_v": _spec(top_k=1001),
+    "top_k_300_exact_path": _spec(top_k=300, vocab=20000),
+    "zipf_top50_ragged": _spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
+    "peaks_f32_wide": _spec(kind="peaks", target_sigma=3.0, draft_sigma=1.5, vocab=70001, dtype="f32", batch=3),
+    "k128": _spec(k=128, batch=2, vocab=300, dtype="f32"),
+    "temperature_0.05": _spec(temperature=0.05, vocab=8000, batch=8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_draft_edge_shapes(name):
+    w = W.make_workload(EDGE[name], gen_seed=zlib.crc32(name.encode()) % 1000)
+    note(f"draft edge {name}: rows={w.rows_draft} V={w.vocab} {w.dtype} top_k={w.top_k}")
+    rows, nb = compare_draft(gpu_draft(w), _oracle(w))
+    note(f"draft edge {name}: {rows} rows, {nb} boundary")
+
+
+def test_draft_ragged_with_zero_lengths_and_bad_offsets():
+    w = W.make_workload(_spec(batch=6, k=8, vocab=5000, top_k=20), gen_seed=3, draft_lens=[0, 3, 0, 1, 8, 2])
+    rows, _ = compare_draft(gpu_draft(w), _oracle(w))
+    assert rows == 14
+    # a sequence whose prefix sums run past the total leaves its slots untouched
+    tgt, drf, ids, cu = to_device(w)
+    bad = torch.from_numpy(np.array([0, 3, 3, 4, 12, 20], np.int32)).to(drf.device)  # last entry > total (14)
+    out = torch.full((w.rows_draft,), -7, dtype=torch.int32, device=drf.device)
+    import rejection_sampling_verify_07_amd as sv
+    sv.draft_sample(drf, cu_draft=bad, temperature=w.temperature, top_k=w.top_k, seed=w.seed, offset=w.offset,
+                    max_draft=8, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[12:] == -7)          # sequence 4's rows under the bad layout: untouched
+    assert np.all(got[:12] >= 0)
+
+
+def test_draft_strided_rows():
+    w = W.make_workload(_spec(vocab=3000, batch=5, k=4, top_k=40, dtype="f32"), gen_seed=9)
+    _, drf, _, _ = to_device(w)
+    wide = torch.zeros((drf.shape[0], 3000 + 37), dtype=drf.dtype, device=drf.device)
+    wide[:, 5:5 + 3000] = drf
+    view = wide[:, 5:5 + 3000]
+    import rejection_sampling_verify_07_amd as sv
+    g = sv.draft_sample(view, batch=w.batch, temperature=w.temperature, top_k=w.top_k, seed=w.seed, offset=w.offset)
+    torch.cuda.synchronize()
+    compare_draft(g.cpu().numpy(), _oracle(w))
+
+
+def test_draft_determinism_seed_and_offset():
+    w = W.make_config(5)
+    a = gpu_draft(w)
+    b = gpu_draft(w)
+    assert np.array_equal(a, b)
+    c = gpu_draft(w, seed=w.seed + 1)
+    d = gpu_draft(w, offset=w.offset + 1)
+    assert (a != c).any() and (a != d).any()
+    compare_draft(c, _oracle(dataclasses.replace(w, seed=w.seed + 1)))
+    compare_draft(d, _oracle(dataclasses.replace(w, offset=w.offset + 1)))
+
+
+@pytest.mark.parametrize("top_k", [0, 5])
+def test_draft_chi_square_on_gpu(top_k):
+    """10^6 draws from one row (one sequence each, distinct counters) follow q."""
+    rng = np.random.default_rng(77)
+    V, T, B = 12, 0.9, 10**6
+    row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    rows = torch.from_numpy(np.repeat(row[None, :], B, axis=0)).to("cuda:0")
+    import rejection_sampling_verify_07_amd as sv
+    ids = sv.draft_sample(rows, batch=B, temperature=T, top_k=top_k, seed=11, offset=2)
+    torch.cuda.synchronize()
+    obs = np.bincount(ids.cpu().numpy(), minlength=V)
+    l = row.astype(np.float64)
+    keep = np.ones(V, bool)
+    if top_k:
+        keep = l >= np.sort(l)[::-1][top_k - 1]
+    q = np.where(keep, np.exp((l - l.max()) / T), 0.0)
+    q /= q.sum()
+    assert obs[~keep].sum() == 0
+    assert stats.chisquare(obs[keep], q[keep] * B).pvalue > 1e-3
