@@ -9,7 +9,8 @@ default) that they cannot stay in the 256 MB last-level cache, so it
 measures HBM reads.
 
 Prints one JSON line:
-  value         verified positions per second (sum_b (K_b + 1) per step)
+  value         verified positions per second (sum_b (K_b + 1) per step);
+                with --mode draft, draft tokens sampled per second (sum_b K_b)
   roofline      the streaming kernel: algorithmic bytes per launch (every
                 logit once) / its average duration from HIP events recorded
                 around each launch in a profiled pass of the same loop,
@@ -28,7 +29,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B×(K+1)×V logits"
-STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel"}
+METRIC_DRAFT = "draft tokens sampled/sec + achieved HBM GB/s (% of peak), B×K×V draft logits"
+STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel",
+                 "draft_topk": "topk_cand_kernel", "draft": "row_stats_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -65,7 +68,7 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
     """
     import csv
 
-    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else ("sample_topk" if "top" in workload else "sample")]
+    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else (mode + ("_topk" if "top" in workload else ""))]
 
     def per_dispatch(path, counter):
         vals = {}
@@ -109,6 +112,8 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
 def cpu_baseline(w, mode, seconds):
     import oracle
 
+    units = w.rows_draft if mode == "draft" else w.positions()
+    unit = "draft tokens/s" if mode == "draft" else "positions/s"
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     oracle.verify_workload(w, mode, threads=threads)  # warm (page in, build)
     t0 = time.perf_counter()
@@ -120,11 +125,11 @@ def cpu_baseline(w, mode, seconds):
         if el >= seconds:
             break
     return {
-        "value": reps * w.positions() / el,
-        "unit": "positions/s",
+        "value": reps * units / el,
+        "unit": unit,
         "cores": threads,
         "kind": "oracle",
-        "sample": f"the full batch of the same workload ({w.batch} sequences, {w.positions()} positions), "
+        "sample": f"the full batch of the same workload ({w.batch} sequences, {units} {unit[:-2]}), "
                   f"{reps} repetitions in {el:.1f} s, sequences split over {threads} host threads",
     }
 
@@ -135,7 +140,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: V=151936, top-k 50)")
-    ap.add_argument("--mode", choices=["sample", "greedy"], default="sample")
+    ap.add_argument("--mode", choices=["sample", "greedy", "draft"], default="sample",
+                    help="sample / greedy: spec_verify_*; draft: spec_draft_sample over the draft rows")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="total size of the rotated input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -173,10 +179,10 @@ def main():
     dev = torch.device("cuda:0")
     w = W.make_config(args.config)
     mode = args.mode
-    if mode not in w.modes:
+    if mode != "draft" and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
         sys.exit(2)
-    kind = "greedy" if mode == "greedy" else ("sample_topk" if w.top_k > 0 else "sample")
+    kind = "greedy" if mode == "greedy" else (mode + ("_topk" if w.top_k > 0 else ""))
     bytes_step = w.algorithmic_bytes(mode)
     copies = max(1, int(np.ceil(args.rotate_mb * 1e6 / bytes_step)))
 
@@ -192,9 +198,12 @@ def main():
     plans = []
     ws = None
     for i in range(copies):
-        tgt = tgt0 if i == 0 else tgt0.clone()
-        drf = drf0 if i == 0 else drf0.clone()
-        if mode == "greedy":
+        tgt = tgt0 if (i == 0 or mode == "draft") else tgt0.clone()
+        drf = drf0 if (i == 0 or mode == "greedy") else drf0.clone()
+        if mode == "draft":
+            p = sv.DraftPlan(drf, cu_draft=cu, batch=None if cu is not None else w.batch, temperature=w.temperature,
+                             top_k=w.top_k, seed=w.seed, offset=w.offset, max_draft=kmax, workspace=ws)
+        elif mode == "greedy":
             p = sv.GreedyPlan(tgt, ids, cu_draft=cu, max_draft=kmax, workspace=ws)
         else:
             p = sv.SamplePlan(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
@@ -219,7 +228,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / K
-    positions = w.positions()
+    positions = w.rows_draft if mode == "draft" else w.positions()  # units per step
     value = positions / (ms_step * 1e-3)
 
     # ---- profiled pass: HIP events around each streaming-kernel launch
@@ -257,9 +266,9 @@ def main():
         cpu = cpu_baseline(w, mode, args.cpu_seconds)
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC_DRAFT if mode == "draft" else METRIC,
         "value": round(value, 1),
-        "unit": "positions/s",
+        "unit": "draft tokens/s" if mode == "draft" else "positions/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -270,7 +279,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "mode": mode, "batch": w.batch, "positions_per_step": positions,
+            "workload": w.name, "mode": mode, "batch": w.batch, "positions_per_step": w.positions(),
             "draft_tokens_per_step": w.rows_draft, "vocab": w.vocab, "input_dtype": w.dtype,
             "temperature": w.temperature, "top_k": w.top_k, "bytes_per_step": bytes_step,
             "rotated_copies": copies, "hbm_gbs_whole_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 1),

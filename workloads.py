@@ -100,8 +100,12 @@ class Workload:
         return 4 if self.dtype == "f32" else 2
 
     def algorithmic_bytes(self, mode: str = "sample") -> int:
-        """Bytes the method must read once: every logit of every row it uses."""
-        rows = self.rows_target + (self.rows_draft if mode == "sample" else 0)
+        """Bytes the method must read once: every logit of every row it uses
+        (sample: target and draft rows; greedy: target rows; draft: draft rows)."""
+        if mode == "draft":
+            rows = self.rows_draft
+        else:
+            rows = self.rows_target + (self.rows_draft if mode == "sample" else 0)
         return rows * self.vocab * self.elem_size
 
     def positions(self) -> int:
