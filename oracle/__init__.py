@@ -85,6 +85,11 @@ def _load():
     lib.orc_verify_greedy.argtypes = [
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int32, C.c_int32, P, P,
     ]
+    lib.orc_verify_argmax.restype = C.c_int
+    lib.orc_verify_argmax.argtypes = [
+        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, P,
+        C.c_double, C.c_int32, C.c_uint64, C.c_uint32, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P,
+    ]
     lib.orc_draft_sample.restype = C.c_int
     lib.orc_draft_sample.argtypes = [
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, C.c_double, C.c_int32, C.c_uint64, C.c_uint32,
@@ -300,6 +305,47 @@ def verify_greedy(target, draft_ids, cu_draft, vocab: int, dtype: str,
     return dict(tokens=tokens, num_accepted=nacc)
 
 
+def verify_argmax(target, draft, draft_ids, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int,
+                  seed: int, offset: int, seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+                  target_stride: Optional[int] = None, draft_stride: Optional[int] = None) -> dict:
+    """The argmax-draw variant: the sampling variant's acceptance test, then
+    the argmax of max(0, p_n - q_n) at a rejection or of p_K when all pass.
+
+    Returns tokens, num_accepted, probs, residual_mass, d_acc and, per
+    sequence, gap (relative margin of the final argmax over its runner-up),
+    second (the runner-up's id) and flags.
+    """
+    lib = _load()
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    B = cu.shape[0] - 1
+    R_d = int(cu[-1])
+    R_t = R_d + B
+    tgt = _as_storage(target, dtype)
+    drf = _as_storage(draft, dtype) if R_d > 0 else np.zeros((1, vocab), tgt.dtype)
+    ids = np.ascontiguousarray(draft_ids, dtype=np.int32) if R_d > 0 else np.zeros(1, np.int32)
+    ts = int(target_stride or (tgt.shape[-1] if tgt.ndim == 2 else vocab))
+    ds = int(draft_stride or (drf.shape[-1] if drf.ndim == 2 else vocab))
+    o = dict(tokens=np.full(R_t, -2, np.int32), num_accepted=np.full(B, -2, np.int32),
+             probs=np.full((max(R_d, 1), 2), np.nan), residual_mass=np.full(B, np.nan),
+             d_acc=np.full(max(R_d, 1), np.inf), gap=np.full(B, np.nan), second=np.full(B, -2, np.int32),
+             flags=np.zeros(B, np.int32))
+
+    def fn(rng):
+        return lib.orc_verify_argmax(
+            B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(tgt), ts, _ptr(drf), ds, _ptr(ids), float(temperature),
+            int(top_k), int(seed), int(offset), rng[0], rng[1], _ptr(o["tokens"]), _ptr(o["num_accepted"]),
+            _ptr(o["probs"]), _ptr(o["residual_mass"]), _ptr(o["d_acc"]), _ptr(o["gap"]), _ptr(o["second"]),
+            _ptr(o["flags"]))
+
+    rcs = _run(fn, _ranges(B, seqs, threads), threads)
+    if any(rc == -2 for rc in rcs):
+        raise MemoryError("oracle verify_argmax")
+    o["probs"] = o["probs"][:R_d]
+    o["d_acc"] = o["d_acc"][:R_d]
+    o["rc"] = min(rcs) if rcs else 0
+    return o
+
+
 def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int, seed: int, offset: int,
                  eps: float = 1e-6, seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
                  draft_stride: Optional[int] = None) -> dict:
@@ -335,9 +381,14 @@ def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, to
 
 
 def verify_workload(w, mode: str = "sample", **kw) -> dict:
-    """Convenience: run the oracle on a workloads.Workload (mode "draft": draft-side sampling)."""
+    """Convenience: run the oracle on a workloads.Workload.
+
+    mode: "sample", "greedy", "argmax" (argmax draws) or "draft" (draft-side sampling)."""
     if mode == "draft":
         return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset, **kw)
+    if mode == "argmax":
+        return verify_argmax(w.target, w.draft, w.draft_ids, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k,
+                             w.seed, w.offset, **kw)
     if mode == "greedy":
         return verify_greedy(w.target, w.draft_ids, w.cu_draft, w.vocab, w.dtype, **kw)
     return verify_sample(w.target, w.draft, w.draft_ids, w.cu_draft, w.vocab, w.dtype,

@@ -320,6 +320,143 @@ int orc_verify_seq_u(const double* P, const double* Q, const int32_t* x, int32_t
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Variant with argmax draws ("Text Generation via Speculative Sampling, KV  */
+/* Caching, and OpenVINO", "Prepare speculative sampling": step 3 accepts   */
+/* with the same probabilistic test but takes the argmax of                  */
+/* max_fn(q - p) (in its names; max(0, p - q) here) on a rejection, step 4  */
+/* the argmax of the last target position).                                 */
+/* ------------------------------------------------------------------------ */
+
+/* First index of the largest w[v] (w >= 0), or -1 when every w is 0.  gap:   */
+/* (best - runner-up) / best over the other ids (1 when there is none);     */
+/* second: the runner-up's id (-1 when none).                               */
+static int64_t orc_argmax_w(const double* w, int64_t V, double* gap, int32_t* second)
+{
+    int64_t best = -1, sec = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        if (!(w[v] > 0.0)) continue;
+        if (best < 0 || w[v] > w[best]) {
+            sec = best;
+            best = v;
+        } else if (sec < 0 || w[v] > w[sec]) {
+            sec = v;
+        }
+    }
+    *second = (int32_t)sec;
+    *gap = best < 0 ? 0.0 : (sec < 0 ? 1.0 : (w[best] - w[sec]) / w[best]);
+    return best;
+}
+
+int orc_verify_argmax_seq(const double* P, const double* Q, const int32_t* x, int32_t K, int64_t V,
+                          const double* u_acc, int32_t* tokens, int32_t* n_out, double* p_out, double* q_out,
+                          double* z_out, double* d_acc, double* gap, int32_t* second, int32_t* flags)
+{
+    *flags = 0;
+    for (int32_t j = 0; j <= K; ++j) tokens[j] = -1;
+    for (int32_t k = 0; k < K; ++k) {
+        if (x[k] < 0 || (int64_t)x[k] >= V) {
+            *flags |= ORC_FLAG_BAD_INPUT;
+            *n_out = -1;
+            return -1;
+        }
+    }
+    /* the acceptance test of the sampling variant */
+    int32_t n = K;
+    for (int32_t k = 0; k < K; ++k) {
+        p_out[k] = P[(int64_t)k * V + x[k]];
+        q_out[k] = Q[(int64_t)k * V + x[k]];
+        d_acc[k] = INFINITY;
+    }
+    for (int32_t k = 0; k < K; ++k) {
+        double p = p_out[k], q = q_out[k];
+        double r = q > 0.0 ? (p / q > 1.0 ? 1.0 : p / q) : (p > 0.0 ? 1.0 : 0.0);
+        d_acc[k] = fabs(u_acc[k] - r);
+        if (!(u_acc[k] < r)) { n = k; break; }
+        tokens[k] = x[k];
+    }
+    *n_out = n;
+    int64_t tok;
+    if (n < K) {
+        double* w = (double*)malloc((size_t)V * sizeof(double));
+        if (!w) return -2;
+        const double* pn = P + (int64_t)n * V;
+        const double* qn = Q + (int64_t)n * V;
+        double total = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double r = pn[v] - qn[v];
+            w[v] = r > 0.0 ? r : 0.0;
+            total += w[v];
+        }
+        *z_out = total;
+        tok = orc_argmax_w(w, V, gap, second);
+        if (tok < 0) {
+            /* no positive residual (rounding only): the argmax of p_n */
+            *flags |= ORC_FLAG_ZERO_RESIDUAL;
+            tok = orc_argmax_w(pn, V, gap, second);
+        }
+        free(w);
+    } else {
+        *z_out = 0.0;
+        tok = orc_argmax_w(P + (int64_t)K * V, V, gap, second);
+    }
+    if (tok < 0) {
+        *flags |= ORC_FLAG_BAD_INPUT;
+        return -1;
+    }
+    tokens[n] = (int32_t)tok;
+    return 0;
+}
+
+/* Batch driver of the argmax-draw variant (layout and accept uniforms as      */
+/* orc_verify_sample; gap / second per sequence describe the final argmax). */
+int orc_verify_argmax(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* target, int64_t t_stride,
+                      const void* draft, int64_t d_stride, const int32_t* ids, double T, int32_t top_k,
+                      uint64_t seed, uint32_t offset, int32_t b_begin, int32_t b_end, int32_t* tokens,
+                      int32_t* n_acc, double* probs, double* zmass, double* d_acc, double* gap, int32_t* second,
+                      int32_t* flags)
+{
+    const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
+    int rc_all = 0;
+    double stats[4];
+    for (int32_t b = b_begin; b < b_end && b < B; ++b) {
+        int32_t K = cu[b + 1] - cu[b];
+        int64_t trow0 = (int64_t)cu[b] + b;
+        int64_t drow0 = cu[b];
+        const size_t k1 = (size_t)(K > 0 ? K : 1);
+        double* P = (double*)malloc(sizeof(double) * (size_t)(K + 1) * (size_t)V);
+        double* Q = (double*)malloc(sizeof(double) * k1 * (size_t)V);
+        double* ua = (double*)malloc(sizeof(double) * k1);
+        double* pq = (double*)malloc(sizeof(double) * 2 * k1);
+        if (!P || !Q || !ua || !pq) {
+            free(P); free(Q); free(ua); free(pq);
+            return -2;
+        }
+        int bad = 0;
+        for (int32_t k = 0; k <= K; ++k) {
+            const char* row = (const char*)target + (size_t)(trow0 + k) * (size_t)t_stride * esz;
+            if (orc_row_probs(row, dtype, V, T, top_k, P + (int64_t)k * V, stats) != 0) bad = 1;
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            const char* row = (const char*)draft + (size_t)(drow0 + k) * (size_t)d_stride * esz;
+            if (orc_row_probs(row, dtype, V, T, top_k, Q + (int64_t)k * V, stats) != 0) bad = 1;
+            ua[k] = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 0u, offset);
+        }
+        int32_t fl = 0;
+        int rc = orc_verify_argmax_seq(P, Q, ids + drow0, K, V, ua, tokens + trow0, n_acc + b, pq, pq + k1,
+                                       zmass + b, d_acc + drow0, gap + b, second + b, &fl);
+        for (int32_t k = 0; k < K; ++k) {
+            probs[2 * (drow0 + k)] = pq[k];
+            probs[2 * (drow0 + k) + 1] = pq[k1 + k];
+        }
+        if (bad) fl |= ORC_FLAG_BAD_INPUT;
+        flags[b] = fl;
+        if (rc != 0 || bad) rc_all = -1;
+        free(P); free(Q); free(ua); free(pq);
+    }
+    return rc_all;
+}
+
 /* The same core over many uniform sets (for exhaustive enumeration tests):  */
 /* trial t uses u_acc[t*K..], u_res[t*K..] and u_bonus[t].                    */
 int orc_verify_seq_u_batch(const double* P, const double* Q, const int32_t* x, int32_t K,

@@ -442,3 +442,44 @@ def test_draft_sample_seed_and_offset_move_the_draws(orc):
     b = orc.draft_sample(rows, cu, 50, "f32", 1.0, 0, seed=2, offset=0)["ids"]
     c = orc.draft_sample(rows, cu, 50, "f32", 1.0, 0, seed=1, offset=1)["ids"]
     assert (a != b).mean() > 0.5 and (a != c).mean() > 0.5
+
+
+# --------------------------------------------------------------------------
+# the argmax-draw variant (OpenVINO notebook's steps 3-4)
+# --------------------------------------------------------------------------
+def test_argmax_variant_residual_and_extra_token_vs_numpy(orc):
+    """At a rejection the token is numpy's argmax of max(0, p_n - q_n) with p
+    and q from scipy's softmax; when every guess passes it is numpy's argmax
+    of p_K.  Acceptance counts equal the sampling variant's (same uniforms)."""
+    w = W.make_workload(dict(W.CONFIGS[2], name="argmax_pin"), gen_seed=3, batch=24)
+    a = orc.verify_workload(w, "argmax", threads=8)
+    s = orc.verify_workload(w, "sample", threads=8)
+    assert np.array_equal(a["num_accepted"], s["num_accepted"])
+    tf, df = w.target_f32(), w.draft_f32()
+    seen_reject = seen_bonus = 0
+    for b in range(w.batch):
+        k0, k1 = w.cu_draft[b], w.cu_draft[b + 1]
+        n = a["num_accepted"][b]
+        tok = a["tokens"][k0 + b + n]
+        if n < k1 - k0:
+            p = _softmax(tf[k0 + b + n], w.temperature, w.top_k)
+            q = _softmax(df[k0 + n], w.temperature, w.top_k)
+            r = np.maximum(p - q, 0.0)
+            assert tok == int(np.argmax(r))
+            seen_reject += 1
+        else:
+            assert tok == int(np.argmax(tf[k0 + b + n]))
+            seen_bonus += 1
+    assert seen_reject > 0
+
+
+def test_argmax_variant_draft_equals_target(orc):
+    w = W.make_workload(dict(W.CONFIGS[1], name="argmax_eq", batch=6), gen_seed=4)
+    a = orc.verify_argmax(w.target, w.target[np.concatenate([np.arange(w.cu_draft[b] + b, w.cu_draft[b + 1] + b)
+                                                            for b in range(w.batch)])],
+                          w.draft_ids, w.cu_draft, w.vocab, w.dtype, w.temperature, 0, 0, 0)
+    K = w.k_max
+    assert np.all(a["num_accepted"] == K)
+    tf = w.target_f32()
+    for b in range(w.batch):
+        assert a["tokens"][b * (K + 1) + K] == int(np.argmax(tf[b * (K + 1) + K]))
