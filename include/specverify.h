@@ -143,6 +143,33 @@ SV_API sv_status_t spec_verify_sample(const sv_shape_t* shape,
                                hipStream_t stream);
 
 /*
+ * Verify with argmax draws, the variant the OpenVINO page implements
+ * ("Text Generation via Speculative Sampling, KV Caching, and OpenVINO",
+ * "Prepare speculative sampling", steps 3 and 4): the same probabilistic
+ * acceptance test as spec_verify_sample (same uniforms U(b, k, 0)), but the
+ * new token is the argmax (lowest id among equal maxima) of
+ * max(0, p_n - q_n) at the first rejection n < K_b -- of p_n when that
+ * residual has no positive entry -- and the argmax of p_{K_b} when every
+ * guess is accepted.  Arguments, outputs and errors as for
+ * spec_verify_sample; out_residual_mass is the residual's total as there.
+ */
+SV_API sv_status_t spec_verify_argmax(const sv_shape_t* shape,
+                               const void* target_logits,
+                               const void* draft_logits,
+                               const int32_t* draft_ids,
+                               float temperature,
+                               int32_t top_k,
+                               uint64_t seed,
+                               uint32_t offset,
+                               int32_t* out_tokens,
+                               int32_t* out_num_accepted,
+                               float* out_probs,
+                               float* out_residual_mass,
+                               void* workspace,
+                               size_t* workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * Greedy argmax-compare verify (the argmax rule of the autoregressive decode
  * on the OpenVINO page).  a_k = the lowest index among the maxima of target
  * row k; n = the first k < K_b with draft_ids[k] != a_k, or K_b; the tokens

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     load_library,
     draft_sample,
     status_string,
+    verify_argmax,
     verify_greedy,
     verify_sample,
     workspace_bytes,

@@ -64,6 +64,8 @@ def load_library(path: Optional[str] = None):
         C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32,
         VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP,
     ]
+    lib.spec_verify_argmax.restype = C.c_int
+    lib.spec_verify_argmax.argtypes = lib.spec_verify_sample.argtypes
     lib.spec_verify_greedy.restype = C.c_int
     lib.spec_verify_greedy.argtypes = [C.POINTER(ShapeT), VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP]
     lib.spec_draft_sample.restype = C.c_int
@@ -142,8 +144,10 @@ def _stream_handle(stream) -> int:
 def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_ids: torch.Tensor,
                   cu_draft: Optional[torch.Tensor] = None, temperature: float = 1.0, top_k: int = 0,
                   seed: int = 0, offset: int = 0, max_draft: Optional[int] = None, return_probs: bool = True,
-                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, stream=None) -> dict:
-    """Speculative-sampling verify on the GPU (spec_verify_sample).
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, stream=None,
+                  argmax: bool = False) -> dict:
+    """Speculative-sampling verify on the GPU (spec_verify_sample, or
+    spec_verify_argmax with argmax=True: argmax draws).
 
     target_logits [sum(K_b+1), V] and draft_logits [sum(K_b), V], float32 or
     bfloat16, rows packed as in include/specverify.h; draft_ids int32
@@ -152,15 +156,16 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     residual_mass [B] (the last two when return_probs).
     """
     lib = load_library()
+    fn = lib.spec_verify_argmax if argmax else lib.spec_verify_sample
+    name = "spec_verify_argmax" if argmax else "spec_verify_sample"
     batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
     if draft_ids.dtype != torch.int32:
         raise TypeError("draft_ids must be int32")
     shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
     dev = target_logits.device
     need = C.c_size_t(0)
-    _check(lib.spec_verify_sample(C.byref(shape), None, None, None, float(temperature), int(top_k), int(seed),
-                                  int(offset), None, None, None, None, None, C.byref(need), None),
-           "spec_verify_sample(workspace query)")
+    _check(fn(C.byref(shape), None, None, None, float(temperature), int(top_k), int(seed),
+              int(offset), None, None, None, None, None, C.byref(need), None), name + "(workspace query)")
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     if out is None:
@@ -172,15 +177,20 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
             out["probs"] = torch.empty((max(total, 1), 2), dtype=torch.float32, device=dev)[:total]
             out["residual_mass"] = torch.empty(batch, dtype=torch.float32, device=dev)
     have = C.c_size_t(workspace.numel())
-    st = lib.spec_verify_sample(
+    st = fn(
         C.byref(shape), target_logits.data_ptr(), draft_logits.data_ptr() if draft_logits.numel() else None,
         draft_ids.data_ptr() if draft_ids.numel() else None, float(temperature), int(top_k), int(seed), int(offset),
         out["tokens"].data_ptr(), out["num_accepted"].data_ptr(),
         out["probs"].data_ptr() if out.get("probs") is not None and total > 0 else None,
         out["residual_mass"].data_ptr() if out.get("residual_mass") is not None else None,
         workspace.data_ptr(), C.byref(have), C.c_void_p(_stream_handle(stream)))
-    _check(st, "spec_verify_sample")
+    _check(st, name)
     return out
+
+
+def verify_argmax(*args, **kw) -> dict:
+    """spec_verify_argmax: verify_sample's acceptance test, argmax draws."""
+    return verify_sample(*args, argmax=True, **kw)
 
 
 def verify_greedy(target_logits: torch.Tensor, draft_ids: torch.Tensor, cu_draft: Optional[torch.Tensor] = None,
@@ -324,7 +334,7 @@ class SamplePlan:
     """
 
     def __init__(self, target_logits, draft_logits, draft_ids, cu_draft=None, temperature=1.0, top_k=0, seed=0,
-                 offset=0, max_draft=None, out=None, workspace=None, stream=None, probs=True):
+                 offset=0, max_draft=None, out=None, workspace=None, stream=None, probs=True, argmax=False):
         self.lib = load_library()
         batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
         self.shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
@@ -350,7 +360,7 @@ class SamplePlan:
                      C.c_void_p(self.out["residual_mass"].data_ptr() if probs else None),
                      C.c_void_p(self.workspace.data_ptr()), C.byref(self.have),
                      C.c_void_p(_stream_handle(stream)))
-        self.fn = self.lib.spec_verify_sample
+        self.fn = self.lib.spec_verify_argmax if argmax else self.lib.spec_verify_sample
 
     def __call__(self):
         st = self.fn(*self.args)

@@ -270,7 +270,7 @@ template <int DT>
 sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
                        const int32_t* ids, float c, int32_t top_k, uint64_t seed, uint32_t offset,
                        int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
-                       hipStream_t stream)
+                       hipStream_t stream, int32_t argmax_draw)
 {
     const size_t es = esize_of(sh->dtype);
     const sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
@@ -282,6 +282,7 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     va.out_nacc = out_nacc;
     va.out_probs = out_probs;
     va.out_zmass = out_z;
+    va.argmax_draw = argmax_draw;
     if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
     if (p.mode == PLAN_FULL) {
         hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
@@ -338,15 +339,11 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     return launch_status();
 }
 
-}  // namespace
-
-extern "C" {
-
-sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
-                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
-                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
-                               hipStream_t stream)
+sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                                 uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                 float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream, int32_t argmax_draw)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_SAMPLE);
@@ -373,9 +370,37 @@ sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logit
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
     if (shape->dtype == SV_DTYPE_F32)
         return run_sample<sv::DT_F32>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
-                                      out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream);
+                                      out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream,
+                                      argmax_draw);
     return run_sample<sv::DT_BF16>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
-                                   out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream);
+                                   out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream,
+                                   argmax_draw);
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream)
+{
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 0);
+}
+
+sv_status_t spec_verify_argmax(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream)
+{
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 1);
 }
 
 sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,

@@ -45,6 +45,7 @@ struct VerifyArgs {
     int32_t vocab;
     const int32_t* ids;
     float c;  // log2(e) / T, fp32
+    int32_t argmax_draw;  // 1: the new token is the argmax of the residual / of p_K instead of a draw
     uint64_t seed;
     uint32_t offset;
     // statistics source: chunk partials (no top-k) or row descriptors (top-k)
@@ -226,7 +227,7 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
 }
 
 // Inverse CDF over a kept list (ascending ids), one wave.  entry(i) yields the
-// list's i-th (id, logit); draft(id) the draft logit at id (RESID only).
+// list's i-th (id, logit); draft(i, id) the draft logit at that id (RESID only).
 template <bool RESID, class Entry, class Draft>
 __device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, const ResidualW& rw, double u,
                                     int32_t* token, double* total)
@@ -248,7 +249,7 @@ __device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, con
             ix[q] = e.idx;
             const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
             if constexpr (RESID) {
-                const float ld = draft(e.idx);
+                const float ld = draft(i, e.idx);
                 const float ed =
                     ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
                 w[q] = fmaxf(et - ed, 0.0f);
@@ -289,7 +290,7 @@ __device__ void inverse_cdf_list(const KeptEntry* list, int32_t n, const char* d
                                  double u, int32_t* token, double* total)
 {
     inverse_cdf_list_of<RESID>([&](int32_t i) { return list[i]; }, n,
-                               [&](int32_t v) { return load_one<DT>(drow, v); }, rw, u, token, total);
+                               [&](int32_t, int32_t v) { return load_one<DT>(drow, v); }, rw, u, token, total);
 }
 
 // LDS of the one-draw phase.
@@ -299,67 +300,155 @@ struct DrawLds {
     double wd[NT / kWave];
     double dd[2];
     int32_t i[4];
+    float bv[NT / kWave];
+    int32_t bi[NT / kWave];
 };
 
+// Argmax of the weights over a kept list (one wave; entry / draft as in
+// inverse_cdf_list_of): the lowest id among the largest positive weights, or
+// -1 when no weight is positive; total = their fp64 sum.
+template <bool RESID, class Entry, class Draft>
+__device__ void argmax_list_of(Entry&& entry, int32_t n, Draft&& draft, const ResidualW& rw, int32_t* token,
+                               double* total)
+{
+    const int32_t per = (n + kWave - 1) / kWave;
+    const int32_t lo = min(n, lane_id() * per), hi = min(n, lo + per);
+    float best = 0.0f;
+    int32_t bid = INT32_MAX;
+    double ls = 0.0;
+    for (int32_t i = lo; i < hi; ++i) {
+        const KeptEntry e = entry(i);
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
+        float w = et;
+        if constexpr (RESID) {
+            const float ld = draft(i, e.idx);
+            const float ed =
+                ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
+            w = fmaxf(et - ed, 0.0f);
+        }
+        ls += (double)w;
+        if (w > 0.0f) argmax_merge(best, bid, w, e.idx);
+    }
+    wave_argmax(best, bid);
+    *token = bid == INT32_MAX ? -1 : __builtin_amdgcn_readlane(bid, 0);
+    *total = wave_sum_dpp(ls);
+}
+
+// Argmax of the weights over a full row (or row pair), all threads: the
+// lowest id among the largest positive weights, or -1; total = their sum.
+template <int DT, bool TWO, int NT, class W>
+__device__ void argmax_full(const char* ra, const char* rb, int32_t vocab, const W& wfn, DrawLds<NT>& L,
+                            int32_t* token, double* total)
+{
+    constexpr int NW = NT / kWave;
+    const int32_t nseg = (vocab + kSeg - 1) / kSeg;
+    const bool vec = ((uintptr_t)ra & 15u) == 0 && (!TWO || ((uintptr_t)rb & 15u) == 0);
+    float best = 0.0f;
+    int32_t bid = INT32_MAX;
+    double ls = 0.0;
+    for (int32_t s0 = wave_id(); s0 < nseg; s0 += NW * kSegUnroll) {
+        float w[kSegUnroll][kSegElems];
+#pragma unroll
+        for (int uu = 0; uu < kSegUnroll; ++uu) {
+            const int32_t s = s0 + uu * NW;
+            if (s < nseg) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
+        }
+#pragma unroll
+        for (int uu = 0; uu < kSegUnroll; ++uu) {
+            const int32_t s = s0 + uu * NW;
+            if (s < nseg) {
+                const int32_t v0 = s * kSeg + lane_id() * kSegElems;
+#pragma unroll
+                for (int e = 0; e < kSegElems; ++e) {
+                    ls += (double)w[uu][e];
+                    if (w[uu][e] > 0.0f) argmax_merge(best, bid, w[uu][e], v0 + e);
+                }
+            }
+        }
+    }
+    wave_argmax(best, bid);
+    ls = wave_sum_dpp(ls);
+    if (lane_id() == 0) {
+        L.bv[wave_id()] = best;
+        L.bi[wave_id()] = bid;
+        L.wd[wave_id()] = ls;
+    }
+    __syncthreads();
+    float v = L.bv[0];
+    int32_t ix = L.bi[0];
+    double z = L.wd[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        argmax_merge(v, ix, L.bv[w], L.bi[w]);
+        z += L.wd[w];
+    }
+    __syncthreads();
+    *token = ix == INT32_MAX ? -1 : ix;
+    *total = z;
+}
+
 // The new token of a sequence (all threads call it; all get the result):
-// the residual draw at the first rejection n < kb, else the extra-token draw
-// from target row kb.  rt / rd: statistics of target row n and draft row n.
-// u: U(b, n, 1) when n < kb, else U(b, kb, 2).
+// at the first rejection n < kb the residual max(0, p_n - q_n), else p_kb --
+// drawn by the inverse CDF with u (U(b, n, 1), or U(b, kb, 2)), or, with
+// a.argmax_draw, its argmax.  rt / rd: statistics of target row n and draft
+// row n; kept_row_n: target row n's index in the kept lists.
 template <int DT, bool FROM_DESC, int NT>
 __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32_t kb, double u, const RowLds& rt,
-                           const RowLds& rd, const char* trow, const char* drow, int64_t kept_row_n,
-                           DrawLds<NT>& L, int32_t* token_out, double* z_out)
+                                           const RowLds& rd, const char* trow, const char* drow, int64_t kept_row_n,
+                                           DrawLds<NT>& L, int32_t* token_out, double* z_out)
 {
+    const bool list = FROM_DESC && rt.kept >= 0;
+    const KeptEntry* kl = a.kept + kept_row_n * kKeepCap;
+    auto entry = [&](int32_t i) { return kl[i]; };
+    auto dlogit = [&](int32_t, int32_t v) { return load_one<DT>(drow, v); };
+    auto none = [](int32_t, int32_t) { return 0.0f; };
+    const ResidualW pw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
+    const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+    // the token of p_n (or p_kb) alone
+    auto pick_p = [&](int32_t* tok) {
+        double zz;
+        if (list) {
+            if (wave_id() == 0) {
+                int32_t t1;
+                if (a.argmax_draw) argmax_list_of<false>(entry, rt.kept, none, pw, &t1, &zz);
+                else inverse_cdf_list_of<false>(entry, rt.kept, none, pw, u, &t1, &zz);
+                if (lane_id() == 0) L.i[2] = t1;
+            }
+            __syncthreads();
+            *tok = L.i[2];
+        } else if (a.argmax_draw) {
+            argmax_full<DT, false, NT>(trow, nullptr, a.vocab, bw, L, tok, &zz);
+        } else {
+            inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, L.seg, L.wd, L.i, L.dd, tok, &zz);
+        }
+    };
     int32_t token = -1;
     double z = 0.0;
     if (n < kb) {
         const ResidualW wfn{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
-        if (FROM_DESC && rt.kept >= 0) {
+        if (list) {
             if (wave_id() == 0) {
-                inverse_cdf_list<DT, true>(a.kept + kept_row_n * kKeepCap, rt.kept, drow, wfn, u, &token, &z);
+                int32_t t1;
+                double z1;
+                if (a.argmax_draw) argmax_list_of<true>(entry, rt.kept, dlogit, wfn, &t1, &z1);
+                else inverse_cdf_list_of<true>(entry, rt.kept, dlogit, wfn, u, &t1, &z1);
                 if (lane_id() == 0) {
-                    L.i[2] = token;
-                    L.dd[1] = z;
+                    L.i[2] = t1;
+                    L.dd[1] = z1;
                 }
             }
             __syncthreads();
             token = L.i[2];
             z = L.dd[1];
+        } else if (a.argmax_draw) {
+            argmax_full<DT, true, NT>(trow, drow, a.vocab, wfn, L, &token, &z);
         } else {
             inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wfn, u, L.seg, L.wd, L.i, L.dd, &token, &z);
         }
-        if (token < 0) {
-            // no positive residual mass (rounding only): draw from p_n with the same uniform
-            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
-            double z2;
-            if (FROM_DESC && rt.kept >= 0) {
-                if (wave_id() == 0) {
-                    const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
-                    inverse_cdf_list<DT, false>(a.kept + kept_row_n * kKeepCap, rt.kept, nullptr, lw, u, &token, &z2);
-                    if (lane_id() == 0) L.i[2] = token;
-                }
-                __syncthreads();
-                token = L.i[2];
-            } else {
-                inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, L.seg, L.wd, L.i, L.dd, &token, &z2);
-            }
-        }
+        // no positive residual mass (rounding only): p_n with the same uniform, or its argmax
+        if (token < 0) pick_p(&token);
     } else {
-        if (FROM_DESC && rt.kept >= 0) {
-            if (wave_id() == 0) {
-                const ResidualW lw{rt.tau, rt.mcc, rt.inv_s, 0.f, 0.f, 0.f, a.c};
-                double zz;
-                inverse_cdf_list<DT, false>(a.kept + kept_row_n * kKeepCap, rt.kept, nullptr, lw, u, &token, &zz);
-                if (lane_id() == 0) L.i[2] = token;
-            }
-            __syncthreads();
-            token = L.i[2];
-        } else {
-            const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
-            double zz;
-            inverse_cdf_full<DT, false, NT>(trow, nullptr, a.vocab, bw, u, L.seg, L.wd, L.i, L.dd, &token, &zz);
-        }
-        z = 0.0;
+        pick_p(&token);
     }
     *token_out = token;
     *z_out = z;
