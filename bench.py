@@ -31,7 +31,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B×(K+1)×V logits"
 METRIC_DRAFT = "draft tokens sampled/sec + achieved HBM GB/s (% of peak), B×K×V draft logits"
 STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel",
-                 "draft_topk": "topk_cand_kernel", "draft": "row_stats_kernel"}
+                 "draft_topk": "topk_cand_kernel", "draft": "row_stats_kernel",
+                 "argmax_topk": "topk_cand_kernel", "argmax": "row_stats_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -140,8 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: V=151936, top-k 50)")
-    ap.add_argument("--mode", choices=["sample", "greedy", "draft"], default="sample",
-                    help="sample / greedy: spec_verify_*; draft: spec_draft_sample over the draft rows")
+    ap.add_argument("--mode", choices=["sample", "greedy", "argmax", "draft"], default="sample",
+                    help="sample / greedy / argmax: spec_verify_*; draft: spec_draft_sample over the draft rows")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="total size of the rotated input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -179,7 +180,7 @@ def main():
     dev = torch.device("cuda:0")
     w = W.make_config(args.config)
     mode = args.mode
-    if mode != "draft" and mode not in w.modes:
+    if mode not in ("draft", "argmax") and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
         sys.exit(2)
     kind = "greedy" if mode == "greedy" else (mode + ("_topk" if w.top_k > 0 else ""))
@@ -207,7 +208,7 @@ def main():
             p = sv.GreedyPlan(tgt, ids, cu_draft=cu, max_draft=kmax, workspace=ws)
         else:
             p = sv.SamplePlan(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
-                              offset=w.offset, max_draft=kmax, workspace=ws)
+                              offset=w.offset, max_draft=kmax, workspace=ws, argmax=mode == "argmax")
         ws = p.workspace
         plans.append(p)
     torch.cuda.synchronize()

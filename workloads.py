@@ -101,11 +101,11 @@ class Workload:
 
     def algorithmic_bytes(self, mode: str = "sample") -> int:
         """Bytes the method must read once: every logit of every row it uses
-        (sample: target and draft rows; greedy: target rows; draft: draft rows)."""
+        (sample, argmax: target and draft rows; greedy: target rows; draft: draft rows)."""
         if mode == "draft":
             rows = self.rows_draft
         else:
-            rows = self.rows_target + (self.rows_draft if mode == "sample" else 0)
+            rows = self.rows_target + (self.rows_draft if mode in ("sample", "argmax") else 0)
         return rows * self.vocab * self.elem_size
 
     def positions(self) -> int:
