@@ -143,6 +143,8 @@ def main():
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: V=151936, top-k 50)")
     ap.add_argument("--mode", choices=["sample", "greedy", "argmax", "draft"], default="sample",
                     help="sample / greedy / argmax: spec_verify_*; draft: spec_draft_sample over the draft rows")
+    ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
+                    help="store a 16-bit workload's logits in this type instead (same values before rounding)")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="total size of the rotated input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -157,6 +159,8 @@ def main():
         import workloads as W
 
         name = W.CONFIGS[args.config]["name"]
+        if args.dtype is not None:
+            name = name.replace(W.CONFIGS[args.config]["dtype"], args.dtype)
         rec = record_traffic(name, args.mode, args.record_traffic[0], args.record_traffic[1],
                              args.copy_calibration_mb or 256.0)
         print(json.dumps(rec))
@@ -178,7 +182,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
-    w = W.make_config(args.config)
+    if args.dtype is not None and W.CONFIGS[args.config]["dtype"] != args.dtype:
+        if W.CONFIGS[args.config]["dtype"] == "f32":
+            print("--dtype applies to the 16-bit workloads (3, 4, 5)", file=sys.stderr)
+            sys.exit(2)
+        spec = dict(W.CONFIGS[args.config], dtype=args.dtype)
+        spec["name"] = spec["name"].replace(W.CONFIGS[args.config]["dtype"], args.dtype)
+        w = W.make_workload(spec, args.config)
+    else:
+        w = W.make_config(args.config)
     mode = args.mode
     if mode not in ("draft", "argmax") and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
@@ -190,7 +202,8 @@ def main():
     def to_dev(a):
         if w.dtype == "f32":
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        t16 = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(t16)
 
     tgt0, drf0 = to_dev(w.target), to_dev(w.draft)
     ids = torch.from_numpy(w.draft_ids).to(dev)

@@ -91,7 +91,11 @@ typedef enum {
     SV_ERR_HIP = 4
 } sv_status_t;
 
-typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 } sv_dtype_t;
+/* Logit element types.  Every type is widened exactly to fp32 on load and no
+ * probability is ever formed in 16 bits ("CS3602_FINAL_SpeDec", problem
+ * analysis, item 1: fp16 probabilities underflow).  SV_DTYPE_F16 is IEEE
+ * binary16, the precision the pages' models ran in. */
+typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1, SV_DTYPE_F16 = 2 } sv_dtype_t;
 
 typedef struct {
     int32_t batch;             /* B >= 1                                          */

@@ -30,6 +30,7 @@ _lib = None
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_F16 = 2
 FLAG_ZERO_RESIDUAL = 1
 FLAG_NO_CROSSING = 2
 FLAG_BAD_INPUT = 4
@@ -104,7 +105,7 @@ def _ptr(a: np.ndarray):
 
 
 def _dtype_code(dtype: str) -> int:
-    return DTYPE_F32 if dtype == "f32" else DTYPE_BF16
+    return {"f32": DTYPE_F32, "bf16": DTYPE_BF16, "f16": DTYPE_F16}[dtype]
 
 
 def _as_storage(a: np.ndarray, dtype: str) -> np.ndarray:

@@ -42,6 +42,7 @@
 
 #define ORC_DTYPE_F32 0
 #define ORC_DTYPE_BF16 1
+#define ORC_DTYPE_F16 2
 
 #define ORC_FLAG_ZERO_RESIDUAL 1   /* residual mass <= 0: fell back to p_n   */
 #define ORC_FLAG_NO_CROSSING 2     /* rounding: took the last positive id    */
@@ -49,12 +50,34 @@
 
 /* ------------------------------------------------------------------------ */
 /* Element decoding: bf16 is the top half of an IEEE binary32, so widening   */
-/* is exact.                                                                 */
+/* is exact.  IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10        */
+/* fraction bits) is decoded from its definition: subnormals are             */
+/* fraction * 2^-24, normals (1024 + fraction) * 2^(exponent - 25), and the  */
+/* all-ones exponent is infinity (fraction 0) or NaN.                        */
 /* ------------------------------------------------------------------------ */
+static double orc_half_to_double(uint16_t h)
+{
+    const int sign = h >> 15;
+    const int ex = (h >> 10) & 31;
+    const int fr = h & 1023;
+    double mag;
+    if (ex == 0) {
+        mag = ldexp((double)fr, -24);
+    } else if (ex == 31) {
+        mag = fr == 0 ? INFINITY : NAN;
+    } else {
+        mag = ldexp((double)(1024 + fr), ex - 25);
+    }
+    return sign ? -mag : mag;
+}
+
 double orc_decode(const void* base, int32_t dtype, int64_t i)
 {
     if (dtype == ORC_DTYPE_F32) {
         return (double)((const float*)base)[i];
+    }
+    if (dtype == ORC_DTYPE_F16) {
+        return orc_half_to_double(((const uint16_t*)base)[i]);
     }
     uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
     float f;

@@ -22,6 +22,7 @@ SV_ERR_WORKSPACE_TOO_SMALL = 3
 SV_ERR_HIP = 4
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
+SV_DTYPE_F16 = 2
 MAX_VOCAB = 1 << 20
 MAX_DRAFT = 128
 
@@ -95,7 +96,9 @@ def _dtype_code(t: torch.Tensor) -> int:
         return SV_DTYPE_F32
     if t.dtype == torch.bfloat16:
         return SV_DTYPE_BF16
-    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return SV_DTYPE_F16
+    raise TypeError(f"logits must be float32, bfloat16 or float16, got {t.dtype}")
 
 
 def _rows(t: torch.Tensor, name: str):

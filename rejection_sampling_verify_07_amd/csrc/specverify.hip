@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "sv_common.hpp"
 #include "sv_stats.hpp"
 #include "sv_topk.hpp"
@@ -60,6 +62,19 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int vec_of(sv_dtype_t dt) { return dt == SV_DTYPE_F32 ? 4 : 8; }
 size_t esize_of(sv_dtype_t dt) { return dt == SV_DTYPE_F32 ? 4 : 2; }
+
+// Calls fn with std::integral_constant<int, DT> for the element type
+// (the shape check has already rejected any other value).
+template <class F>
+sv_status_t by_dtype(sv_dtype_t dt, F&& fn)
+{
+    switch (dt) {
+        case SV_DTYPE_F32: return fn(std::integral_constant<int, sv::DT_F32>{});
+        case SV_DTYPE_BF16: return fn(std::integral_constant<int, sv::DT_BF16>{});
+        case SV_DTYPE_F16: return fn(std::integral_constant<int, sv::DT_F16>{});
+    }
+    return SV_ERR_INVALID_ARGUMENT;
+}
 
 // Chunks per row of the streaming passes: a row with start misalignment up
 // to VEC-1 elements touches at most ceil((V + VEC - 1) / VEC) blocks.
@@ -125,7 +140,8 @@ sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
     if (sh == nullptr) return SV_ERR_INVALID_ARGUMENT;
     if (sh->batch < 1 || sh->vocab < 1 || sh->max_draft < 0 || sh->total_draft < 0)
         return SV_ERR_INVALID_ARGUMENT;
-    if (sh->dtype != SV_DTYPE_F32 && sh->dtype != SV_DTYPE_BF16) return SV_ERR_INVALID_ARGUMENT;
+    if (sh->dtype != SV_DTYPE_F32 && sh->dtype != SV_DTYPE_BF16 && sh->dtype != SV_DTYPE_F16)
+        return SV_ERR_INVALID_ARGUMENT;
     if (sh->cu_draft == nullptr && (int64_t)sh->total_draft != (int64_t)sh->batch * sh->max_draft)
         return SV_ERR_INVALID_ARGUMENT;
     if (sh->cu_draft != nullptr && !aligned(sh->cu_draft, 4)) return SV_ERR_INVALID_ARGUMENT;
@@ -368,13 +384,11 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
 
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
-    if (shape->dtype == SV_DTYPE_F32)
-        return run_sample<sv::DT_F32>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
-                                      out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream,
-                                      argmax_draw);
-    return run_sample<sv::DT_BF16>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed, offset,
-                                   out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace, stream,
-                                   argmax_draw);
+    return by_dtype(shape->dtype, [&](auto dt) {
+        return run_sample<decltype(dt)::value>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed,
+                                               offset, out_tokens, out_num_accepted, out_probs, out_residual_mass,
+                                               workspace, stream, argmax_draw);
+    });
 }
 
 }  // namespace
@@ -424,11 +438,10 @@ sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logit
         return SV_ERR_INVALID_ARGUMENT;
     if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
-    if (shape->dtype == SV_DTYPE_F32)
-        return run_greedy<sv::DT_F32>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
-                                      stream);
-    return run_greedy<sv::DT_BF16>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
-                                   stream);
+    return by_dtype(shape->dtype, [&](auto dt) {
+        return run_greedy<decltype(dt)::value>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted,
+                                               workspace, stream);
+    });
 }
 
 sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
@@ -455,9 +468,10 @@ sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits,
     if (shape->total_draft == 0 || shape->max_draft == 0) return SV_OK;  // no draft rows: nothing to draw
 
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
-    if (shape->dtype == SV_DTYPE_F32)
-        return run_draft<sv::DT_F32>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace, stream);
-    return run_draft<sv::DT_BF16>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace, stream);
+    return by_dtype(shape->dtype, [&](auto dt) {
+        return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace,
+                                              stream);
+    });
 }
 
 const char* spec_verify_status_string(sv_status_t status)

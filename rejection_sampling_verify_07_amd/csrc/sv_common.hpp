@@ -17,7 +17,7 @@ constexpr int kWaves = kThreads / kWave;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 
 template <int DT>
 struct Dt;
@@ -26,11 +26,43 @@ struct Dt<DT_F32> {
     static constexpr int kSize = 4;
     static constexpr int kVec = 4;
 };
+// 16-bit types also carry the bit patterns the streaming passes write into
+// out-of-row slots: -inf (ignored by every max and weight) and a quiet NaN
+// (rejected by every compare).
 template <>
 struct Dt<DT_BF16> {
     static constexpr int kSize = 2;
     static constexpr int kVec = 8;
+    static constexpr uint32_t kNegInf = 0xff80u;
+    static constexpr uint32_t kNaN = 0x7fc0u;
 };
+template <>
+struct Dt<DT_F16> {
+    static constexpr int kSize = 2;
+    static constexpr int kVec = 8;
+    static constexpr uint32_t kNegInf = 0xfc00u;
+    static constexpr uint32_t kNaN = 0x7e00u;
+};
+
+// IEEE binary16 bits -> fp32 (exact; v_cvt_f32_f16).
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// The low and high 16-bit element of a 32-bit word, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float lo16(uint32_t w)
+{
+    if constexpr (DT == DT_BF16) return __uint_as_float(w << 16);
+    else return half_bits_to_float(w & 0xffffu);
+}
+template <int DT>
+__device__ __forceinline__ float hi16(uint32_t w)
+{
+    if constexpr (DT == DT_BF16) return __uint_as_float(w & 0xffff0000u);
+    else return half_bits_to_float(w >> 16);
+}
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -63,14 +95,14 @@ __device__ __forceinline__ void unpack(const u32x4 w, float* f)
         f[2] = __uint_as_float(w.z);
         f[3] = __uint_as_float(w.w);
     } else {
-        f[0] = __uint_as_float(w.x << 16);
-        f[1] = __uint_as_float(w.x & 0xffff0000u);
-        f[2] = __uint_as_float(w.y << 16);
-        f[3] = __uint_as_float(w.y & 0xffff0000u);
-        f[4] = __uint_as_float(w.z << 16);
-        f[5] = __uint_as_float(w.z & 0xffff0000u);
-        f[6] = __uint_as_float(w.w << 16);
-        f[7] = __uint_as_float(w.w & 0xffff0000u);
+        f[0] = lo16<DT>(w.x);
+        f[1] = hi16<DT>(w.x);
+        f[2] = lo16<DT>(w.y);
+        f[3] = hi16<DT>(w.y);
+        f[4] = lo16<DT>(w.z);
+        f[5] = hi16<DT>(w.z);
+        f[6] = lo16<DT>(w.w);
+        f[7] = hi16<DT>(w.w);
     }
 }
 
@@ -82,7 +114,7 @@ __device__ __forceinline__ float load_one(const char* row, int64_t i)
         return ((const SV_GLOBAL float*)row)[i];
     } else {
         const uint32_t b = ((const SV_GLOBAL uint16_t*)row)[i];
-        return __uint_as_float(b << 16);
+        return lo16<DT>(b);
     }
 }
 

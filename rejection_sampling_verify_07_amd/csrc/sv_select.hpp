@@ -25,19 +25,30 @@ namespace sv {
 constexpr int kSelPer = kKeepCapList / kWave;  // candidates per lane on the fast path
 
 // Keys the radix select works on: bf16 logits are fully ordered by the top
-// 16 bits of their fp32 order key; fp32 needs all 32.
+// 16 bits of their fp32 order key; fp16 logits by the same sign flip applied
+// to their own 16 bits (a widened value narrows back exactly); fp32 needs
+// all 32.
 template <int DT>
 struct SelKey {
-    static constexpr int kBits = (DT == DT_BF16) ? 16 : 32;
+    static constexpr int kBits = Dt<DT>::kSize == 2 ? 16 : 32;
     __device__ __forceinline__ static uint32_t of(float v)
     {
-        return (DT == DT_BF16) ? (order_key(v) >> 16) : order_key(v);
+        if constexpr (DT == DT_BF16) {
+            return order_key(v) >> 16;
+        } else if constexpr (DT == DT_F16) {
+            const uint32_t h = __builtin_bit_cast(uint16_t, (_Float16)v);
+            return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+        } else {
+            return order_key(v);
+        }
     }
     // the logit value of a key (bf16: the low 16 key bits follow from the sign)
     __device__ __forceinline__ static float value(uint32_t k)
     {
         if constexpr (DT == DT_BF16) {
             return key_to_float((k << 16) | ((k & 0x8000u) ? 0u : 0xffffu));
+        } else if constexpr (DT == DT_F16) {
+            return half_bits_to_float((k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu));
         } else {
             return key_to_float(k);
         }

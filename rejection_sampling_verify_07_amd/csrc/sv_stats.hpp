@@ -38,9 +38,9 @@ __device__ __forceinline__ void sanitize_edge(const Tile& t, int32_t vocab, u32x
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             uint32_t w = rw[i][q];
-            if constexpr (DT == DT_BF16) {
-                if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | 0xff80u;
-                if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | 0xff800000u;
+            if constexpr (Dt<DT>::kSize == 2) {
+                if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | Dt<DT>::kNegInf;
+                if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | (Dt<DT>::kNegInf << 16);
             } else {
                 if ((uint32_t)(r0 + q) >= (uint32_t)vocab) w = 0xff800000u;
             }

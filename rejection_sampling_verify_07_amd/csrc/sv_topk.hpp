@@ -188,7 +188,7 @@ constexpr int kChunkLds = kWaves * kWaveLds;
 // -inf for negatives, +inf for positives); every threshold used here is the
 // smallest fp32 of some bf16 order class, so `word >= t` and `element >= t`
 // agree.  The low element needs a shift.  The lane maxima that set the bound
-// are taken over all elements.
+// are taken over all elements.  fp16 elements are widened (exactly) instead.
 template <int DT, int LOADS, bool NT, bool PIPE>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     constexpr int VEC = Dt<DT>::kVec;
     constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
     constexpr bool BF = DT == DT_BF16;
+    constexpr bool H16 = DT == DT_F16;
     __shared__ float s_val[kChunkLds];
     __shared__ int32_t s_ix[kChunkLds];
     __shared__ uint32_t s_lk[kThreads];
@@ -217,9 +218,9 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     uint32_t w = rw[i][q];
-                    if constexpr (BF) {
-                        if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | 0x7fc0u;
-                        if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | 0x7fc00000u;
+                    if constexpr (Dt<DT>::kSize == 2) {
+                        if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) w = (w & 0xffff0000u) | Dt<DT>::kNaN;
+                        if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) w = (w & 0x0000ffffu) | (Dt<DT>::kNaN << 16);
                     } else {
                         if ((uint32_t)(r0 + q) >= (uint32_t)vocab) w = 0x7fc00000u;
                     }
@@ -239,6 +240,8 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                     const uint32_t w = raw[i][q];
                     if constexpr (BF) {
                         tm = fmaxf(tm, fmaxf(__uint_as_float(w << 16), __uint_as_float(w)));
+                    } else if constexpr (H16) {
+                        tm = fmaxf(tm, fmaxf(lo16<DT>(w), hi16<DT>(w)));
                     } else {
                         tm = fmaxf(tm, __uint_as_float(w));
                     }
@@ -290,15 +293,19 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             for (int i = 0; i < LOADS; ++i) {
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    const int q = BF ? e / 2 : e;
+                    const int q = Dt<DT>::kSize == 2 ? e / 2 : e;
                     const uint32_t w = raw[i][q];
-                    const float cmp = BF ? __uint_as_float((e & 1) ? w : (w << 16)) : __uint_as_float(w);
+                    const float cmp = BF    ? __uint_as_float((e & 1) ? w : (w << 16))
+                                      : H16 ? ((e & 1) ? hi16<DT>(w) : lo16<DT>(w))
+                                            : __uint_as_float(w);
                     const bool pred = cmp >= bound;
                     const uint64_t m = __ballot(pred);
                     if (m != 0) {
                         if (pred) {
                             const int pos = min(wcount + lanes_below(m), kWaveLds - 1);
-                            const uint32_t bits = BF ? ((e & 1) ? (w & 0xffff0000u) : (w << 16)) : w;
+                            const uint32_t bits = BF    ? ((e & 1) ? (w & 0xffff0000u) : (w << 16))
+                                                  : H16 ? __float_as_uint(cmp)
+                                                        : w;
                             s_val[wbase + pos] = __uint_as_float(bits);
                             s_ix[wbase + pos] = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
                         }

@@ -10,7 +10,8 @@ import oracle
 import rejection_sampling_verify_07_amd as sv
 
 EPS_BOUNDARY = 1e-6  # a draw whose uniform lies this close to a threshold is a boundary draw
-RTOL = {"f32": 1e-5, "bf16": 2e-3}  # probability tolerance by input dtype
+RTOL = {"f32": 1e-5, "bf16": 2e-3, "f16": 2e-3}  # probability tolerance by input dtype
+TORCH_16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
 
 def note(msg):
@@ -23,8 +24,8 @@ def to_device(w, dev="cuda:0"):
         tgt = torch.from_numpy(np.ascontiguousarray(w.target)).to(dev)
         drf = torch.from_numpy(np.ascontiguousarray(w.draft)).to(dev)
     else:
-        tgt = torch.from_numpy(np.ascontiguousarray(w.target).view(np.int16)).to(dev).view(torch.bfloat16)
-        drf = torch.from_numpy(np.ascontiguousarray(w.draft).view(np.int16)).to(dev).view(torch.bfloat16)
+        tgt = torch.from_numpy(np.ascontiguousarray(w.target).view(np.int16)).to(dev).view(TORCH_16[w.dtype])
+        drf = torch.from_numpy(np.ascontiguousarray(w.draft).view(np.int16)).to(dev).view(TORCH_16[w.dtype])
     ids = torch.from_numpy(w.draft_ids.astype(np.int32)).to(dev)
     cu = torch.from_numpy(w.cu_draft.astype(np.int32)).to(dev) if w.ragged else None
     return tgt, drf, ids, cu

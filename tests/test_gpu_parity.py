@@ -117,7 +117,7 @@ def test_edge_shapes(name):
 def _with_rows(w, f):
     """A copy of w with target/draft float rows transformed by f (then re-encoded)."""
     tf, df = f(w.target_f32().copy()), f(w.draft_f32().copy())
-    enc = (lambda x: x.astype(np.float32)) if w.dtype == "f32" else W.f32_to_bf16_bits
+    enc = {"f32": lambda x: x.astype(np.float32), "bf16": W.f32_to_bf16_bits, "f16": W.f32_to_f16_bits}[w.dtype]
     return dataclasses.replace(w, target=enc(tf), draft=enc(df))
 
 

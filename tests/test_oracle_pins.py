@@ -55,13 +55,28 @@ def test_bf16_decode_matches_torch(orc):
     assert np.array_equal(mine, theirs)
 
 
+def test_f16_decode_matches_numpy(orc):
+    # every binary16 pattern: zeros, subnormals, normals, infinities, NaNs
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    dec = orc._load().orc_decode
+    got = np.array([dec(bits[i:i + 1].ctypes.data, 2, 0) for i in range(65536)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # generator-side cast agrees with torch's float -> float16 rounding
+    x = np.random.default_rng(1).standard_normal(100000).astype(np.float32) * 7
+    theirs = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_f16_bits(x), theirs)
+
+
 @pytest.mark.parametrize("T", [0.05, 0.7, 1.0, 5.0])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_row_probs_vs_scipy(orc, T, dtype):
     rng = np.random.default_rng(7)
     l = (rng.standard_normal(3001) * 3).astype(np.float32)
-    row = l if dtype == "f32" else W.f32_to_bf16_bits(l)
-    lf = l if dtype == "f32" else W.bf16_bits_to_f32(row)
+    row = l if dtype == "f32" else W.f32_to_bf16_bits(l) if dtype == "bf16" else W.f32_to_f16_bits(l)
+    lf = W.decode_f32(row, dtype)
     prob, st = orc.row_probs(row, dtype, T)
     lse = special.logsumexp(lf.astype(np.float64) / T)
     assert st["m"] == lf.max()

@@ -35,6 +35,9 @@ __all__ = [
     "make_workload",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
+    "f32_to_f16_bits",
+    "f16_bits_to_f32",
+    "decode_f32",
 ]
 
 
@@ -55,6 +58,24 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return b.view(np.float32)
 
 
+# IEEE binary16: numpy's own conversion (round to nearest, ties to even)
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16; return the bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of binary16 bits to float32."""
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
+def decode_f32(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored logits (float32 values, or 16-bit patterns) widened to float32."""
+    if dtype == "f32":
+        return x
+    return bf16_bits_to_f32(x) if dtype == "bf16" else f16_bits_to_f32(x)
+
+
 # --------------------------------------------------------------------------
 # Workload container
 # --------------------------------------------------------------------------
@@ -66,7 +87,8 @@ class Workload:
     cu_draft[b] .. cu_draft[b+1]-1 and target rows cu_draft[b]+b ..
     cu_draft[b+1]+b (K_b + 1 rows, the last one is the bonus position).
     Logits are row-major [rows, vocab]; dtype "f32" holds float32 values,
-    dtype "bf16" holds the raw bfloat16 bit patterns as uint16.
+    dtype "bf16" and "f16" hold the raw bfloat16 / IEEE binary16 bit patterns
+    as uint16.
     """
 
     name: str
@@ -113,10 +135,10 @@ class Workload:
         return self.rows_target
 
     def target_f32(self) -> np.ndarray:
-        return self.target if self.dtype == "f32" else bf16_bits_to_f32(self.target)
+        return decode_f32(self.target, self.dtype)
 
     def draft_f32(self) -> np.ndarray:
-        return self.draft if self.dtype == "f32" else bf16_bits_to_f32(self.draft)
+        return decode_f32(self.draft, self.dtype)
 
 
 # --------------------------------------------------------------------------
@@ -181,11 +203,13 @@ def _target_rows(rng, kind, n_rows, vocab, sigma):
 
 
 def _encode(x, dtype):
-    return x.astype(np.float32) if dtype == "f32" else f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return x.astype(np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else f32_to_f16_bits(x)
 
 
 def _decode(x, dtype):
-    return x if dtype == "f32" else bf16_bits_to_f32(x)
+    return decode_f32(x, dtype)
 
 
 def _gumbel_draw(rng, logits_f32, temperature, top_k):
