@@ -152,8 +152,8 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     """Speculative-sampling verify on the GPU (spec_verify_sample, or
     spec_verify_argmax with argmax=True: argmax draws).
 
-    target_logits [sum(K_b+1), V] and draft_logits [sum(K_b), V], float32 or
-    bfloat16, rows packed as in include/specverify.h; draft_ids int32
+    target_logits [sum(K_b+1), V] and draft_logits [sum(K_b), V], float32,
+    bfloat16 or float16, rows packed as in include/specverify.h; draft_ids int32
     [sum(K_b)]; cu_draft int32 [B+1] prefix sums or None (uniform K).
     Returns tokens [sum(K_b+1)], num_accepted [B], probs [sum(K_b), 2] and
     residual_mass [B] (the last two when return_probs).
@@ -248,7 +248,7 @@ def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = 
                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Draft-side sampling on the GPU (spec_draft_sample): x(b, k) ~ q_k.
 
-    draft_logits [sum(K_b), V] float32 or bfloat16, rows packed as for the
+    draft_logits [sum(K_b), V] float32, bfloat16 or float16, rows packed as for the
     verify; cu_draft int32 [B+1] or None with `batch` (uniform K).  Returns
     the int32 ids [sum(K_b)].
     """
