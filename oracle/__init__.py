@@ -96,6 +96,11 @@ def _load():
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, C.c_double, C.c_int32, C.c_uint64, C.c_uint32,
         C.c_double, C.c_int32, C.c_int32, P, P, P, P, P,
     ]
+    lib.orc_token_likelihood.restype = C.c_int
+    lib.orc_token_likelihood.argtypes = [
+        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, C.c_double, C.c_int32, P,
+        C.c_int32, C.c_int32, P, P, P, P,
+    ]
     _lib = lib
     return lib
 
@@ -381,10 +386,61 @@ def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, to
     return out
 
 
+def token_likelihood(target, draft, tokens, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int,
+                     seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+                     target_stride: Optional[int] = None, draft_stride: Optional[int] = None) -> dict:
+    """Per-token speculative likelihood of tokens[r] at row r of both tensors
+    (position (b, k) is row cu_draft[b] + k).
+
+    Returns accept [R] = q(y) min(1, p(y)/q(y)), reject [R] = (1 - beta) p'(y),
+    p [R] = p(y), beta [R] = sum_v min(p, q), and per sequence nll [B] =
+    -sum_k log(accept + reject) and flags.
+    """
+    lib = _load()
+    cu = np.ascontiguousarray(cu_draft, dtype=np.int32)
+    B = cu.shape[0] - 1
+    R = int(cu[-1])
+    n = max(R, 1)
+    empty = np.zeros((1, vocab), np.float32 if dtype == "f32" else np.uint16)
+    tgt = _as_storage(target, dtype) if R > 0 else empty
+    drf = _as_storage(draft, dtype) if R > 0 else empty
+    tok = np.ascontiguousarray(tokens, dtype=np.int32) if R > 0 else np.zeros(1, np.int32)
+    ts = int(target_stride or (tgt.shape[-1] if tgt.ndim == 2 else vocab))
+    ds = int(draft_stride or (drf.shape[-1] if drf.ndim == 2 else vocab))
+    terms = np.full((n, 3), np.nan)
+    beta = np.full(n, np.nan)
+    nll = np.full(B, np.nan)
+    flags = np.zeros(B, np.int32)
+
+    def fn(rng):
+        return lib.orc_token_likelihood(B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(tgt), ts, _ptr(drf), ds,
+                                        float(temperature), int(top_k), _ptr(tok), rng[0], rng[1], _ptr(terms),
+                                        _ptr(beta), _ptr(nll), _ptr(flags))
+
+    rcs = _run(fn, _ranges(B, seqs, threads), threads)
+    if any(rc == -2 for rc in rcs):
+        raise MemoryError("oracle token_likelihood")
+    return dict(accept=terms[:R, 0], reject=terms[:R, 1], p=terms[:R, 2], beta=beta[:R], nll=nll, flags=flags,
+                rc=min(rcs) if rcs else 0)
+
+
+def likelihood_rows(w):
+    """A verify workload's rows in the likelihood layout: target rows k < K_b of
+    every sequence (row cu_draft[b] + k), its draft rows, and its guesses as
+    the scored tokens."""
+    keep = np.concatenate([np.arange(int(w.cu_draft[b]) + b, int(w.cu_draft[b + 1]) + b) for b in range(w.batch)]
+                          + [np.zeros(0, np.int64)]).astype(np.int64)
+    return np.ascontiguousarray(w.target[keep]), w.draft, w.draft_ids
+
+
 def verify_workload(w, mode: str = "sample", **kw) -> dict:
     """Convenience: run the oracle on a workloads.Workload.
 
-    mode: "sample", "greedy", "argmax" (argmax draws) or "draft" (draft-side sampling)."""
+    mode: "sample", "greedy", "argmax" (argmax draws), "draft" (draft-side sampling) or
+    "likelihood" (per-token speculative likelihood of the guesses, rows from likelihood_rows)."""
+    if mode == "likelihood":
+        tgt, drf, tok = likelihood_rows(w)
+        return token_likelihood(tgt, drf, tok, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, **kw)
     if mode == "draft":
         return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset, **kw)
     if mode == "argmax":

@@ -606,6 +606,86 @@ int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, con
 }
 
 /*
+ * Per-token speculative likelihood: the probability that one speculative
+ * step emits a given token y, split as in the proof of
+ * "CS3602_FINAL_SpeDec", section 2, and used for that report's perplexity
+ * check (its problem analysis, item 1):
+ *   beta             = sum_v min(p(v), q(v))                (acceptance mass)
+ *   accept part      = q(y) * min(1, p(y) / q(y))           (guess y accepted)
+ *   reject part      = (1 - beta) * p'(y),  p' = norm(max(0, p - q))
+ *                                                           (guess rejected, y drawn)
+ *   P(y)             = accept part + reject part
+ * with p = softmax(target row / T) and q = softmax(draft row / T), each over
+ * its top-k kept set.  The sum over the vocabulary is taken as written (no
+ * shortcut through the identity reject part = p(y) - min(p(y), q(y))); a
+ * residual with no positive mass gives a zero reject part.  Position (b, k),
+ * k < K_b, is row cu[b] + k of both tensors; nll[b] = -sum_k log P(y_k).
+ * Outputs per position: terms[3 r + 0..2] = accept part, reject part, p(y);
+ * beta[r].  A sequence with a bad row or a token outside [0, V) gets the
+ * bad-input flag and nll = NaN (its terms for such a token are NaN).
+ */
+int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* target,
+                         int64_t t_stride, const void* draft, int64_t d_stride, double T, int32_t top_k,
+                         const int32_t* tokens, int32_t b_begin, int32_t b_end, double* terms, double* beta,
+                         double* nll, int32_t* flags)
+{
+    const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
+    double* P = (double*)malloc(sizeof(double) * (size_t)V);
+    double* Q = (double*)malloc(sizeof(double) * (size_t)V);
+    if (!P || !Q) {
+        free(P);
+        free(Q);
+        return -2;
+    }
+    double stats[4];
+    int rc_all = 0;
+    for (int32_t b = b_begin; b < b_end && b < B; ++b) {
+        const int32_t K = cu[b + 1] - cu[b];
+        int32_t fl = 0;
+        double s_nll = 0.0;
+        for (int32_t k = 0; k < K; ++k) {
+            const int64_t r = (int64_t)cu[b] + k;
+            const char* trow = (const char*)target + (size_t)r * (size_t)t_stride * esz;
+            const char* drow = (const char*)draft + (size_t)r * (size_t)d_stride * esz;
+            if (orc_row_probs(trow, dtype, V, T, top_k, P, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            if (orc_row_probs(drow, dtype, V, T, top_k, Q, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            double bsum = 0.0, zsum = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                bsum += P[v] < Q[v] ? P[v] : Q[v];
+                zsum += P[v] > Q[v] ? P[v] - Q[v] : 0.0;
+            }
+            beta[r] = bsum;
+            const int32_t y = tokens[r];
+            if (y < 0 || (int64_t)y >= V) {
+                fl |= ORC_FLAG_BAD_INPUT;
+                terms[3 * r] = terms[3 * r + 1] = terms[3 * r + 2] = NAN;
+                continue;
+            }
+            const double py = P[y], qy = Q[y];
+            double acc;
+            if (qy > 0.0) {
+                const double ratio = py / qy;
+                acc = qy * (ratio < 1.0 ? ratio : 1.0);
+            } else {
+                acc = 0.0;
+            }
+            const double rdens = py > qy ? py - qy : 0.0;   /* max(0, p - q) at y */
+            const double rej = zsum > 0.0 ? (1.0 - bsum) * (rdens / zsum) : 0.0;
+            terms[3 * r] = acc;
+            terms[3 * r + 1] = rej;
+            terms[3 * r + 2] = py;
+            s_nll -= log(acc + rej);
+        }
+        nll[b] = (fl & ORC_FLAG_BAD_INPUT) ? NAN : s_nll;
+        flags[b] = fl;
+        if (fl & ORC_FLAG_BAD_INPUT) rc_all = -1;
+    }
+    free(P);
+    free(Q);
+    return rc_all;
+}
+
+/*
  * Greedy argmax-compare: a_k = argmax of target row k; n = the first k with
  * x_k != a_k (K_b when none); tokens x_0..x_{n-1}, a_n, then -1.
  */

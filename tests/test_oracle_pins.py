@@ -498,3 +498,120 @@ def test_argmax_variant_draft_equals_target(orc):
     tf = w.target_f32()
     for b in range(w.batch):
         assert a["tokens"][b * (K + 1) + K] == int(np.argmax(tf[b * (K + 1) + K]))
+
+
+# --------------------------------------------------------------------------
+# per-token speculative likelihood (the perplexity check of
+# "CS3602_FINAL_SpeDec": accept part + reject part of an observed token)
+# --------------------------------------------------------------------------
+def _lik_rows(seed, R, V, dtype, scale=2.0):
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((R, V)) * scale).astype(np.float32)
+    d = (t + rng.standard_normal((R, V)).astype(np.float32)).astype(np.float32)
+    enc = {"f32": lambda x: x, "bf16": W.f32_to_bf16_bits, "f16": W.f32_to_f16_bits}[dtype]
+    return enc(t), enc(d)
+
+
+@pytest.mark.parametrize("dtype,top_k,T", [("f32", 0, 1.0), ("bf16", 0, 0.7), ("bf16", 20, 1.3), ("f16", 5, 0.5)])
+def test_likelihood_terms_vs_scipy(orc, dtype, top_k, T):
+    """Against scipy's softmax: the accept part is min(p, q)(y); the reject part
+    is max(0, p - q)(y) (the proof's identity (1 - beta) p'(y) = p(y) - min);
+    their sum is p(y), the proof's claim that accept-or-resample emits y with
+    probability p(y); beta = 1 - sum max(0, p - q); and the sequence's NLL
+    equals the target's own, -sum log p(y) from scipy's log_softmax."""
+    R, V = 12, 400
+    tgt, drf = _lik_rows(3, R, V, dtype)
+    cu = np.array([0, 5, 5, 12], np.int32)   # three sequences, one empty
+    rng = np.random.default_rng(4)
+    tf, df = W.decode_f32(tgt, dtype), W.decode_f32(drf, dtype)
+    P, Q = _probs_rows(tf, T, top_k), _probs_rows(df, T, top_k)
+    # tokens inside the target's support (else p(y) = 0 and the NLL is infinite)
+    tok = np.array([rng.choice(np.flatnonzero(P[r] > 0)) for r in range(R)], np.int32)
+    o = orc.token_likelihood(tgt, drf, tok, cu, V, dtype, T, top_k)
+    py, qy = P[np.arange(R), tok], Q[np.arange(R), tok]
+    np.testing.assert_allclose(o["p"], py, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(o["accept"], np.minimum(py, qy), rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(o["reject"], np.maximum(py - qy, 0), rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(o["accept"] + o["reject"], py, rtol=1e-12, atol=1e-300)
+    np.testing.assert_allclose(o["beta"], 1 - np.maximum(P - Q, 0).sum(axis=1), rtol=0, atol=1e-13)
+    assert np.all(o["flags"] == 0)
+    for b in range(3):
+        ks = slice(cu[b], cu[b + 1])
+        lsm = np.array([special.log_softmax(np.where(P[r] > 0, tf[r].astype(np.float64) / T, -np.inf))[tok[r]]
+                        for r in range(cu[b], cu[b + 1])])
+        want = -lsm.sum() if lsm.size else 0.0
+        assert abs(o["nll"][b] - want) <= 1e-11 * max(1.0, abs(want)), (b, o["nll"][b], want)
+        assert np.all(np.isfinite(o["accept"][ks]))
+
+
+def test_likelihood_hand_worked_example(orc):
+    """V = 4, T = 1, p = (1/2, 1/4, 1/8, 1/8), q = (1/4, 1/4, 1/4, 1/4):
+    beta = 1/4 + 1/4 + 1/8 + 1/8 = 3/4 and the residual max(0, p - q) =
+    (1/4, 0, 0, 0) has mass 1/4 = 1 - beta.  y = 0: accepted with 1/4,
+    emitted after a rejection with (1 - 3/4) * 1 = 1/4, total 1/2 = p(0).
+    y = 1: 1/4 + 0.  y = 2: 1/8 + 0.  NLL of (0, 1, 2) = ln 2 + ln 4 + ln 8."""
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    q = np.full(4, 0.25)
+    tgt = np.log(np.repeat(p[None], 3, 0)).astype(np.float32)
+    drf = np.log(np.repeat(q[None], 3, 0)).astype(np.float32)
+    o = orc.token_likelihood(tgt, drf, np.array([0, 1, 2], np.int32), np.array([0, 3], np.int32), 4, "f32",
+                             1.0, 0)
+    np.testing.assert_allclose(o["beta"], 0.75, atol=1e-7)
+    np.testing.assert_allclose(o["accept"], [0.25, 0.25, 0.125], atol=1e-7)
+    np.testing.assert_allclose(o["reject"], [0.25, 0.0, 0.0], atol=1e-7)
+    assert abs(o["nll"][0] - np.log(64.0)) < 1e-6
+
+
+def test_likelihood_beta_is_the_acceptance_rate(orc):
+    """beta is the probability that a guess x ~ q passes the acceptance test:
+    sum_x q(x) min(1, p(x)/q(x)).  The oracle's own verify step, run over
+    20000 sequences with the same row pair, guesses drawn from q with
+    numpy and a different Philox stream per sequence, accepts the first
+    guess at a rate within 4.5 binomial sigma of the likelihood's beta."""
+    V, N, T = 40, 20000, 0.9
+    rng = np.random.default_rng(9)
+    lt = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    ld = (lt + rng.standard_normal(V) * 1.2).astype(np.float32)
+    lik = orc.token_likelihood(lt[None], ld[None], np.zeros(1, np.int32), np.array([0, 1], np.int32), V, "f32",
+                               T, 0)
+    beta = float(lik["beta"][0])
+    q = _softmax(ld, T)
+    x = rng.choice(V, size=N, p=q).astype(np.int32)
+    tgt = np.repeat(np.stack([lt, lt])[None], N, 0).reshape(2 * N, V)  # target rows k = 0, 1 per sequence
+    drf = np.repeat(ld[None], N, 0)
+    cu = np.arange(N + 1, dtype=np.int32)
+    o = orc.verify_sample(tgt, drf, x, cu, V, "f32", T, 0, 1234, 0, threads=8)
+    rate = float(np.mean(o["num_accepted"] >= 1))
+    sigma = np.sqrt(beta * (1 - beta) / N)
+    assert abs(rate - beta) < 4.5 * sigma, (rate, beta, sigma)
+
+
+def test_likelihood_special_cases(orc):
+    V = 300
+    tgt, drf = _lik_rows(5, 4, V, "f32")
+    tok = np.array([3, 7, 11, 299], np.int32)
+    cu = np.array([0, 4], np.int32)
+    # draft = target: every guess is accepted, nothing comes from the residual
+    o = orc.token_likelihood(tgt, tgt, tok, cu, V, "f32", 1.0, 0)
+    np.testing.assert_allclose(o["beta"], 1.0, atol=1e-13)
+    assert np.all(o["reject"] == 0) and np.allclose(o["accept"], o["p"], rtol=1e-15)
+    # disjoint top-k supports: beta = 0, every emitted token comes from the residual
+    t2 = np.full((1, 10), -5.0, np.float32)
+    d2 = np.full((1, 10), -5.0, np.float32)
+    t2[0, :3] = [3.0, 2.0, 1.0]
+    d2[0, 5:8] = [3.0, 2.0, 1.0]
+    o = orc.token_likelihood(t2, d2, np.array([1], np.int32), np.array([0, 1], np.int32), 10, "f32", 1.0, 3)
+    assert o["beta"][0] == 0.0 and o["accept"][0] == 0.0
+    assert abs(o["reject"][0] - _softmax(t2[0], 1.0, 3)[1]) < 1e-15
+    # V = 1: p = q = 1, NLL 0
+    o = orc.token_likelihood(np.zeros((2, 1), np.float32), np.ones((2, 1), np.float32), np.zeros(2, np.int32),
+                             np.array([0, 2], np.int32), 1, "f32", 1.0, 0)
+    assert np.all(o["beta"] == 1.0) and np.all(o["accept"] == 1.0) and o["nll"][0] == 0.0
+    # a token outside the vocabulary flags its sequence and leaves NaN
+    o = orc.token_likelihood(tgt, drf, np.array([3, V, 1, 2], np.int32), np.array([0, 2, 4], np.int32), V, "f32",
+                             1.0, 0)
+    assert o["flags"][0] != 0 and np.isnan(o["nll"][0]) and np.isnan(o["accept"][1])
+    assert o["flags"][1] == 0 and np.isfinite(o["nll"][1])
+    # a token outside the target's top-k kept set has likelihood 0
+    o = orc.token_likelihood(t2, d2, np.array([9], np.int32), np.array([0, 1], np.int32), 10, "f32", 1.0, 3)
+    assert o["accept"][0] == 0.0 and o["reject"][0] == 0.0 and o["nll"][0] == np.inf
