@@ -621,8 +621,9 @@ int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, con
  * residual with no positive mass gives a zero reject part.  Position (b, k),
  * k < K_b, is row cu[b] + k of both tensors; nll[b] = -sum_k log P(y_k).
  * Outputs per position: terms[3 r + 0..2] = accept part, reject part, p(y);
- * beta[r].  A sequence with a bad row or a token outside [0, V) gets the
- * bad-input flag and nll = NaN (its terms for such a token are NaN).
+ * beta[r].  A sequence with a bad row (no finite kept logit) or a token
+ * outside [0, V) gets the bad-input flag and nll = NaN; such a position's
+ * terms are NaN, and so is a bad row's beta.
  */
 int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* target,
                          int64_t t_stride, const void* draft, int64_t d_stride, double T, int32_t top_k,
@@ -647,8 +648,15 @@ int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
             const int64_t r = (int64_t)cu[b] + k;
             const char* trow = (const char*)target + (size_t)r * (size_t)t_stride * esz;
             const char* drow = (const char*)draft + (size_t)r * (size_t)d_stride * esz;
-            if (orc_row_probs(trow, dtype, V, T, top_k, P, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
-            if (orc_row_probs(drow, dtype, V, T, top_k, Q, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            const int bad_t = orc_row_probs(trow, dtype, V, T, top_k, P, stats) != 0;
+            const int bad_d = orc_row_probs(drow, dtype, V, T, top_k, Q, stats) != 0;
+            if (bad_t || bad_d) {
+                /* a row with no finite kept logit defines no distribution */
+                fl |= ORC_FLAG_BAD_INPUT;
+                beta[r] = NAN;
+                terms[3 * r] = terms[3 * r + 1] = terms[3 * r + 2] = NAN;
+                continue;
+            }
             double bsum = 0.0, zsum = 0.0;
             for (int64_t v = 0; v < V; ++v) {
                 bsum += P[v] < Q[v] ? P[v] : Q[v];
