@@ -16,7 +16,8 @@
  *   autoregressive sampling": softmax over the vocabulary, argmax decode
  *   (the greedy mode here).  spec_draft_sample draws the guesses themselves
  *   (step 1 of "Prepare speculative sampling", sampling in place of the
- *   argmax).
+ *   argmax), and spec_token_likelihood scores given tokens under the
+ *   speculative step (the perplexity check of "CS3602_FINAL_SpeDec").
  *
  * Conventions shared by the calls
  *   Batch layout (packed, ragged).  Sequence b has K_b >= 0 draft tokens.
@@ -216,6 +217,50 @@ SV_API sv_status_t spec_draft_sample(const sv_shape_t* shape,
                               uint64_t seed,
                               uint32_t offset,
                               int32_t* out_ids,
+                              void* workspace,
+                              size_t* workspace_bytes,
+                              hipStream_t stream);
+
+/*
+ * Per-token speculative likelihood, the quantity behind the perplexity
+ * check of "CS3602_FINAL_SpeDec" (section 2's proof, used by that report's
+ * problem analysis, item 1, to score speculative output without summing
+ * over the vocabulary).  For position (b, k), k < K_b, with p = the target
+ * row's and q = the draft row's softmax at temperature T (each over its
+ * top-k kept set, exactly as in spec_verify_sample) and y = tokens[r]:
+ *   accept part  P(guess accepted, x = y) = q(y) min(1, p(y)/q(y)) = min(p(y), q(y))
+ *   reject part  P(guess rejected, x = y) = (1 - beta) p'(y)       = p(y) - min(p(y), q(y))
+ *   beta         = sum_v min(p(v), q(v))   (the position's acceptance mass)
+ *   nll[b]       = -sum_k log(accept part + reject part)
+ * The two parts add to p(y): one speculative step emits y with the target's
+ * probability.
+ * Arguments
+ *   shape: batch, vocab, dtype, strides and cu_draft as for
+ *   spec_verify_sample, but position (b, k) is row r = cu_draft[b] + k of
+ *   BOTH tensors (total_draft rows each; max_draft, the largest K_b, has no
+ *   upper limit here).
+ *   target_logits [total_draft, target_row_stride], draft_logits
+ *   [total_draft, draft_row_stride] in shape->dtype; tokens int32
+ *   [total_draft].  temperature > 0 and finite; top_k in [0, V].
+ *   out_terms (nullable) float [total_draft][2] = accept part, reject part;
+ *   out_beta (nullable) float [total_draft]; out_nll (nullable) double [B].
+ *   At least one output must be non-NULL.  beta over full rows costs a
+ *   second read of both rows; leave out_beta NULL when it is not needed.
+ *   A token outside [0, V), or a row with no finite logit in its kept set,
+ *   gives NaN parts (and NaN beta for such a row); p(y) = 0 gives an infinite
+ *   nll.  A sequence whose cu_draft entries are out of range gets nll = NaN
+ *   and leaves its other slots untouched.
+ * Memory, execution, workspace and errors as for spec_verify_sample.
+ */
+SV_API sv_status_t spec_token_likelihood(const sv_shape_t* shape,
+                              const void* target_logits,
+                              const void* draft_logits,
+                              const int32_t* tokens,
+                              float temperature,
+                              int32_t top_k,
+                              float* out_terms,
+                              float* out_beta,
+                              double* out_nll,
                               void* workspace,
                               size_t* workspace_bytes,
                               hipStream_t stream);

@@ -424,22 +424,13 @@ def token_likelihood(target, draft, tokens, cu_draft, vocab: int, dtype: str, te
                 rc=min(rcs) if rcs else 0)
 
 
-def likelihood_rows(w):
-    """A verify workload's rows in the likelihood layout: target rows k < K_b of
-    every sequence (row cu_draft[b] + k), its draft rows, and its guesses as
-    the scored tokens."""
-    keep = np.concatenate([np.arange(int(w.cu_draft[b]) + b, int(w.cu_draft[b + 1]) + b) for b in range(w.batch)]
-                          + [np.zeros(0, np.int64)]).astype(np.int64)
-    return np.ascontiguousarray(w.target[keep]), w.draft, w.draft_ids
-
-
 def verify_workload(w, mode: str = "sample", **kw) -> dict:
     """Convenience: run the oracle on a workloads.Workload.
 
     mode: "sample", "greedy", "argmax" (argmax draws), "draft" (draft-side sampling) or
-    "likelihood" (per-token speculative likelihood of the guesses, rows from likelihood_rows)."""
+    "likelihood" (per-token speculative likelihood of the guesses, rows from w.likelihood_rows())."""
     if mode == "likelihood":
-        tgt, drf, tok = likelihood_rows(w)
+        tgt, drf, tok = w.likelihood_rows()
         return token_likelihood(tgt, drf, tok, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, **kw)
     if mode == "draft":
         return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset, **kw)

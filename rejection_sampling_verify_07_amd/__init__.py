@@ -7,12 +7,14 @@ script and a thin ctypes binding.
 from .binding import (  # noqa: F401
     DraftPlan,
     GreedyPlan,
+    LikelihoodPlan,
     SamplePlan,
     HipEvents,
     SpecVerifyError,
     load_library,
     draft_sample,
     status_string,
+    token_likelihood,
     verify_argmax,
     verify_greedy,
     verify_sample,

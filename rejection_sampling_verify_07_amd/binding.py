@@ -73,6 +73,10 @@ def load_library(path: Optional[str] = None):
     lib.spec_draft_sample.argtypes = [
         C.POINTER(ShapeT), VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32, VP, VP, C.POINTER(C.c_size_t), VP,
     ]
+    lib.spec_token_likelihood.restype = C.c_int
+    lib.spec_token_likelihood.argtypes = [
+        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP,
+    ]
     lib.spec_verify_status_string.restype = C.c_char_p
     lib.spec_verify_status_string.argtypes = [C.c_int]
     lib.spec_verify_set_profile_events.restype = C.c_int
@@ -271,6 +275,60 @@ def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = 
     return out
 
 
+def _likelihood_outputs(total, batch, dev, terms, beta, nll):
+    out = {}
+    if terms:
+        out["terms"] = torch.empty((max(total, 1), 2), dtype=torch.float32, device=dev)[:total]
+    if beta:
+        out["beta"] = torch.empty(max(total, 1), dtype=torch.float32, device=dev)[:total]
+    if nll:
+        out["nll"] = torch.empty(batch, dtype=torch.float64, device=dev)
+    if not out:
+        raise ValueError("ask for at least one of terms, beta, nll")
+    return out
+
+
+def _ptr_or_none(out, key):
+    t = out.get(key)
+    return t.data_ptr() if t is not None and t.numel() > 0 else None
+
+
+def token_likelihood(target_logits: torch.Tensor, draft_logits: torch.Tensor, tokens: torch.Tensor,
+                     cu_draft: Optional[torch.Tensor] = None, batch: Optional[int] = None, temperature: float = 1.0,
+                     top_k: int = 0, max_draft: Optional[int] = None, terms: bool = True, beta: bool = True,
+                     nll: bool = True, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Per-token speculative likelihood on the GPU (spec_token_likelihood).
+
+    target_logits and draft_logits [sum(K_b), V] (float32, bfloat16 or
+    float16; position (b, k) is row cu_draft[b] + k of both), tokens int32
+    [sum(K_b)]; cu_draft int32 [B+1] or None with `batch` (uniform K).
+    Returns terms [sum(K_b), 2] (accept part, reject part), beta [sum(K_b)]
+    and nll [B] (float64), each when asked for.
+    """
+    lib = load_library()
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be int32")
+    if target_logits.shape[0] != draft_logits.shape[0] or target_logits.shape[0] != tokens.numel():
+        raise ValueError("target_logits, draft_logits and tokens need one row per position")
+    b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
+    shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
+    dev = target_logits.device
+    need = C.c_size_t(0)
+    _check(lib.spec_token_likelihood(C.byref(shape), None, None, None, float(temperature), int(top_k), None, None,
+                                     None, None, C.byref(need), None), "spec_token_likelihood(workspace query)")
+    if workspace is None or workspace.numel() < need.value:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    out = _likelihood_outputs(total, b, dev, terms, beta, nll)
+    have = C.c_size_t(workspace.numel())
+    st = lib.spec_token_likelihood(
+        C.byref(shape), target_logits.data_ptr() if total else None, draft_logits.data_ptr() if total else None,
+        tokens.data_ptr() if total else None, float(temperature), int(top_k), _ptr_or_none(out, "terms"),
+        _ptr_or_none(out, "beta"), _ptr_or_none(out, "nll"), workspace.data_ptr(), C.byref(have),
+        C.c_void_p(_stream_handle(stream)))
+    _check(st, "spec_token_likelihood")
+    return out
+
+
 def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k=0, max_draft=None,
                     greedy=False) -> int:
     lib = load_library()
@@ -399,6 +457,37 @@ class GreedyPlan:
         st = self.fn(*self.args)
         if st != SV_OK:
             raise SpecVerifyError(st, "spec_verify_greedy")
+
+
+class LikelihoodPlan:
+    """spec_token_likelihood with every argument marshalled once."""
+
+    def __init__(self, target_logits, draft_logits, tokens, cu_draft=None, batch=None, temperature=1.0, top_k=0,
+                 max_draft=None, terms=True, beta=True, nll=True, workspace=None, stream=None):
+        self.lib = load_library()
+        b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
+        self.shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
+        dev = target_logits.device
+        need = C.c_size_t(0)
+        _check(self.lib.spec_token_likelihood(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
+                                              None, None, None, None, C.byref(need), None), "workspace query")
+        self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
+            torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+        self.out = _likelihood_outputs(total, b, dev, terms, beta, nll)
+        self.have = C.c_size_t(self.workspace.numel())
+        self._keep = (target_logits, draft_logits, tokens, cu_draft)
+        self.args = (C.byref(self.shape), C.c_void_p(target_logits.data_ptr()), C.c_void_p(draft_logits.data_ptr()),
+                     C.c_void_p(tokens.data_ptr()), C.c_float(temperature), C.c_int32(top_k),
+                     C.c_void_p(_ptr_or_none(self.out, "terms")), C.c_void_p(_ptr_or_none(self.out, "beta")),
+                     C.c_void_p(_ptr_or_none(self.out, "nll")), C.c_void_p(self.workspace.data_ptr()),
+                     C.byref(self.have), C.c_void_p(_stream_handle(stream)))
+        self.fn = self.lib.spec_token_likelihood
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, "spec_token_likelihood")
+        return self.out
 
 
 class DraftPlan:

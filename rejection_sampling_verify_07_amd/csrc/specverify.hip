@@ -15,6 +15,7 @@
 #include "sv_topk.hpp"
 #include "sv_select.hpp"
 #include "sv_verify.hpp"
+#include "sv_likelihood.hpp"
 
 static_assert(SV_MAX_DRAFT == sv::kMaxDraft, "draft limit mismatch");
 static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
@@ -48,14 +49,15 @@ constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves kee
 constexpr size_t kAlign = 256;
 
 enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
-enum CallKind { CALL_SAMPLE = 0, CALL_GREEDY = 1, CALL_DRAFT = 2 };
+enum CallKind { CALL_SAMPLE = 0, CALL_GREEDY = 1, CALL_DRAFT = 2, CALL_LIKE = 3 };
 
 struct Plan {
     PlanMode mode;
     int32_t rows_t, rows_d, rows;
     int32_t nchunk;
     int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
-    size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, bytes;
+    int32_t nchunk2;  // tiles per row pair of the likelihood's pair pass (full rows)
+    size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, off_pair, bytes;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -149,7 +151,8 @@ sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
     if (kind != CALL_DRAFT && sh->target_row_stride < sh->vocab) return SV_ERR_INVALID_ARGUMENT;
     if (need_draft_rows && sh->total_draft > 0 && sh->draft_row_stride < sh->vocab)
         return SV_ERR_INVALID_ARGUMENT;
-    if (sh->vocab > SV_MAX_VOCAB || sh->max_draft > SV_MAX_DRAFT) return SV_ERR_UNSUPPORTED;
+    if (sh->vocab > SV_MAX_VOCAB) return SV_ERR_UNSUPPORTED;
+    if (kind != CALL_LIKE && sh->max_draft > SV_MAX_DRAFT) return SV_ERR_UNSUPPORTED;
     const int64_t rows_t = (int64_t)sh->total_draft + sh->batch;
     if (rows_t > INT32_MAX / 2) return SV_ERR_UNSUPPORTED;
     return SV_OK;
@@ -162,8 +165,8 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k)
 {
     const bool greedy = kind == CALL_GREEDY;
     Plan p{};
-    p.rows_t = kind == CALL_DRAFT ? sh->total_draft : sh->total_draft + sh->batch;
-    p.rows_d = kind == CALL_SAMPLE ? sh->total_draft : 0;
+    p.rows_t = (kind == CALL_DRAFT || kind == CALL_LIKE) ? sh->total_draft : sh->total_draft + sh->batch;
+    p.rows_d = (kind == CALL_SAMPLE || kind == CALL_LIKE) ? sh->total_draft : 0;
     p.rows = p.rows_t + p.rows_d;
     const bool topk = !greedy && top_k > 0 && top_k < sh->vocab;
     if (greedy) {
@@ -188,6 +191,11 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k)
     if (p.mode == PLAN_FULL) {
         p.off_partials = off;
         off = align_up(off + slots * sizeof(sv::PartialFull));
+        if (kind == CALL_LIKE) {
+            p.nchunk2 = chunks_for(sh->vocab, vec_of(sh->dtype), sv::kPairLoads);
+            p.off_pair = off;
+            off = align_up(off + (size_t)p.rows_t * (size_t)p.nchunk2 * sizeof(double));
+        }
     } else if (p.mode == PLAN_GREEDY) {
         p.off_partials = off;
         off = align_up(off + slots * sizeof(sv::PartialArg));
@@ -332,6 +340,53 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
 }
 
 template <int DT>
+sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
+                           const int32_t* tokens, float c, int32_t top_k, float* out_terms, float* out_beta,
+                           double* out_nll, void* ws, hipStream_t stream)
+{
+    const size_t es = esize_of(sh->dtype);
+    const sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
+                        (int64_t)(sh->target_row_stride * (int64_t)es), (int64_t)(sh->draft_row_stride * (int64_t)es),
+                        p.rows_t};
+    sv::LikArgs la{};
+    la.rs = rs;
+    la.cu = sh->cu_draft;
+    la.batch = sh->batch;
+    la.kmax = sh->max_draft;
+    la.rows = sh->total_draft;
+    la.vocab = sh->vocab;
+    la.tokens = tokens;
+    la.c = c;
+    la.nchunk = p.nchunk;
+    la.nchunk2 = p.nchunk2;
+    la.out_terms = out_terms;
+    la.out_beta = out_beta;
+    la.out_nll = out_nll;
+    if (sh->total_draft > 0) {
+        sv::VerifyArgs va = base_args(sh, p, rs, c, 0, 0);
+        if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+        la.partials = va.partials;
+        la.descs = va.descs;
+        la.kept = va.kept;
+        if (p.mode == PLAN_FULL && out_beta != nullptr) {
+            double* pair = ws_at<double>(ws, p.off_pair);
+            const sv::PairArgs pa{rs, sh->vocab, sh->total_draft, va.partials, p.nchunk, p.nchunk2, c, pair};
+            const uint32_t grid = (uint32_t)((int64_t)sh->total_draft * p.nchunk2);
+            hipLaunchKernelGGL((sv::pair_min_kernel<DT, sv::kPairLoads>), dim3(grid), dim3(sv::kThreads), 0, stream,
+                               pa);
+            if (launch_status() != SV_OK) return SV_ERR_HIP;
+            la.pair = pair;
+        }
+    }
+    if (p.mode == PLAN_FULL) {
+        hipLaunchKernelGGL((sv::likelihood_kernel<DT, false>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, la);
+    } else {
+        hipLaunchKernelGGL((sv::likelihood_kernel<DT, true>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, la);
+    }
+    return launch_status();
+}
+
+template <int DT>
 sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, const int32_t* ids,
                        int32_t* out_tokens, int32_t* out_nacc, void* ws, hipStream_t stream)
 {
@@ -471,6 +526,41 @@ sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits,
     return by_dtype(shape->dtype, [&](auto dt) {
         return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace,
                                               stream);
+    });
+}
+
+sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                                  const int32_t* tokens, float temperature, int32_t top_k, float* out_terms,
+                                  float* out_beta, double* out_nll, void* workspace, size_t* workspace_bytes,
+                                  hipStream_t stream)
+{
+    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    sv_status_t st = check_shape(shape, CALL_LIKE);
+    if (st != SV_OK) return st;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
+    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, CALL_LIKE, top_k);
+    if ((int64_t)p.rows * p.nchunk > INT32_MAX || (int64_t)p.rows_t * (p.nchunk2 > 0 ? p.nchunk2 : 1) > INT32_MAX)
+        return SV_ERR_UNSUPPORTED;
+    if (workspace == nullptr) {
+        *workspace_bytes = p.bytes;
+        return SV_OK;
+    }
+    if (out_terms == nullptr && out_beta == nullptr && out_nll == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    const size_t es = esize_of(shape->dtype);
+    if (shape->total_draft > 0 && (target_logits == nullptr || draft_logits == nullptr || tokens == nullptr))
+        return SV_ERR_INVALID_ARGUMENT;
+    if ((target_logits && !aligned(target_logits, es)) || (draft_logits && !aligned(draft_logits, es)) ||
+        (tokens && !aligned(tokens, 4)) || (out_terms && !aligned(out_terms, 4)) ||
+        (out_beta && !aligned(out_beta, 4)) || (out_nll && !aligned(out_nll, 8)))
+        return SV_ERR_INVALID_ARGUMENT;
+    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
+    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+
+    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    return by_dtype(shape->dtype, [&](auto dt) {
+        return run_likelihood<decltype(dt)::value>(shape, p, target_logits, draft_logits, tokens, c, top_k,
+                                                   out_terms, out_beta, out_nll, workspace, stream);
     });
 }
 

@@ -189,3 +189,65 @@ def compare_argmax(w, g, o):
     o2["d_fin"] = np.where(o["gap"] < GAP_BOUNDARY, 0.0, 1.0)
     tok_o = {b: int(o["tokens"][int(w.cu_draft[b]) + b + int(o["num_accepted"][b])]) for b in range(w.batch)}
     return compare_sample(w, g, o2, final_ok=lambda b, t: t in (tok_o[b], int(o["second"][b])))
+
+
+BETA_ATOL = 1e-5  # beta: fp32 min(p, q) terms, fp64 sums (relative error of each term below 2^-20)
+
+
+def lik_to_device(w, rows=None, dev="cuda:0"):
+    tgt, drf, tok = rows if rows is not None else w.likelihood_rows()
+
+    def put(a):
+        if w.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(TORCH_16[w.dtype])
+
+    cu = torch.from_numpy(w.cu_draft.astype(np.int32)).to(dev) if w.ragged else None
+    return put(tgt), put(drf), torch.from_numpy(np.ascontiguousarray(tok, dtype=np.int32)).to(dev), cu
+
+
+def gpu_likelihood(w, tensors=None, **kw):
+    tgt, drf, tok, cu = tensors or lik_to_device(w)
+    out = sv.token_likelihood(tgt, drf, tok, cu_draft=cu, batch=None if cu is not None else w.batch,
+                              temperature=w.temperature, top_k=w.top_k,
+                              max_draft=w.k_max if cu is not None else None, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def compare_likelihood(w, g, o):
+    """Per-token likelihood against the oracle.  The accept part (a min of two
+    probabilities) within 2 rtol of itself, the reject part (a difference)
+    within 2 rtol of p(y), their sum within rtol of p(y) (rtol: 1e-5 for
+    fp32 inputs, 2e-3 for 16-bit ones); beta within BETA_ATOL; each
+    sequence's NLL within rtol per position.  NaN and infinity must match."""
+    rtol = RTOL[w.dtype]
+    R = int(w.cu_draft[-1])
+    rep = dict(positions=R)
+    if "terms" in g:
+        a, r = g["terms"][:, 0].astype(np.float64), g["terms"][:, 1].astype(np.float64)
+        ao, ro, po = o["accept"], o["reject"], o["p"]
+        nan = np.isnan(ao)
+        assert np.array_equal(np.isnan(a), nan) and np.array_equal(np.isnan(r), nan), "NaN pattern differs"
+        ok = ~nan
+        assert np.all(np.abs(a - ao)[ok] <= 2 * rtol * ao[ok] + 1e-30), "accept part"
+        assert np.all(np.abs(r - ro)[ok] <= 2 * rtol * po[ok] + 1e-30), "reject part"
+        assert np.all(np.abs(a + r - po)[ok] <= rtol * po[ok] + 1e-30), "accept + reject != p(y)"
+        rep["max_rel_p"] = float(np.max(np.abs(a + r - po)[ok] / np.maximum(po[ok], 1e-300), initial=0.0))
+    if "beta" in g:
+        bg, bo = g["beta"].astype(np.float64), o["beta"]
+        nan = np.isnan(bo)
+        assert np.array_equal(np.isnan(bg), nan), "beta NaN pattern differs"
+        err = np.abs(bg - bo)[~nan]
+        assert np.all(err <= BETA_ATOL), f"beta off by {err.max()}"
+        rep["max_abs_beta"] = float(err.max(initial=0.0))
+    if "nll" in g:
+        ng, no = g["nll"], o["nll"]
+        fin = np.isfinite(no)
+        assert np.array_equal(np.isnan(ng), np.isnan(no)), "nll NaN pattern differs"
+        assert np.array_equal(np.isposinf(ng), np.isposinf(no)), "nll infinity pattern differs"
+        ks = w.draft_lens.astype(np.float64)
+        err = np.abs(ng[fin] - no[fin])
+        assert np.all(err <= rtol * ks[fin] + 1e-12), "nll"
+        rep["max_abs_nll"] = float(np.max(err, initial=0.0))
+    return rep

@@ -38,7 +38,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert "spec_verify_sample" in names and "spec_verify_greedy" in names
-    assert "spec_draft_sample" in names
+    assert "spec_draft_sample" in names and "spec_verify_argmax" in names
+    assert "spec_token_likelihood" in names
     assert "spec_verify_status_string" in names
 
 
@@ -211,3 +212,47 @@ def test_draft_sample_arguments(lib, B):
     assert st == B.SV_OK
     assert lib.spec_draft_sample(C.byref(sh0), None, 1.0, 0, 0, 0, None, fake,
                                  C.byref(C.c_size_t(need0)), None) == B.SV_OK
+
+
+def _lik_query(lib, sh, T=1.0, top_k=0):
+    need = C.c_size_t(0)
+    st = lib.spec_token_likelihood(C.byref(sh), None, None, None, T, top_k, None, None, None, None, C.byref(need),
+                                   None)
+    return st, need.value
+
+
+def test_token_likelihood_arguments(lib, B):
+    st, need = _lik_query(lib, _shape(B))
+    assert st == B.SV_OK and need > 0
+    # both tensors use the draft-row layout; both strides must cover V
+    assert _lik_query(lib, _shape(B, target_row_stride=999))[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _lik_query(lib, _shape(B, draft_row_stride=999))[0] == B.SV_ERR_INVALID_ARGUMENT
+    # positions per sequence are not limited to the verify's SV_MAX_DRAFT
+    long = _shape(B, batch=2, max_draft=4096, total_draft=8192)
+    assert _lik_query(lib, long)[0] == B.SV_OK
+    for T in (0.0, -1.0, float("inf"), float("nan")):
+        assert _lik_query(lib, _shape(B), T=T)[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _lik_query(lib, _shape(B), top_k=-1)[0] == B.SV_ERR_INVALID_ARGUMENT
+    assert _lik_query(lib, _shape(B), top_k=1001)[0] == B.SV_ERR_INVALID_ARGUMENT
+    # a top-k plan and a full-row plan differ in size (kept lists vs pair partials)
+    assert _lik_query(lib, _shape(B), top_k=50)[1] != need
+    sh = _shape(B)
+    fake = 1 << 40  # never dereferenced: every check below fails before a launch
+    have = C.c_size_t(need)
+
+    def call(tgt=fake, drf=fake, tok=fake, terms=fake, beta=fake, nll=fake, ws=fake, have_=have):
+        return lib.spec_token_likelihood(C.byref(sh), tgt, drf, tok, 1.0, 0, terms, beta, nll, ws, C.byref(have_),
+                                         None)
+
+    assert call(terms=None, beta=None, nll=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tgt=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(drf=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tok=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tgt=fake + 1) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(tok=fake + 2) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(nll=fake + 4) == B.SV_ERR_INVALID_ARGUMENT   # doubles need 8-byte alignment
+    assert call(beta=fake + 2) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.spec_token_likelihood(None, fake, fake, fake, 1.0, 0, fake, fake, fake, fake, C.byref(have),
+                                     None) == B.SV_ERR_INVALID_ARGUMENT

@@ -1,0 +1,177 @@
+"""Per-token speculative likelihood on the GPU (spec_token_likelihood)
+against the oracle: the accept part min(p, q)(y), the reject part
+(1 - beta) p'(y) = p(y) - min(p, q)(y), the acceptance mass beta and each
+sequence's -sum log P(y) ("CS3602_FINAL_SpeDec", section 2's proof and the
+perplexity check of its problem analysis, item 1).  Position (b, k) is row
+cu_draft[b] + k of both tensors."""
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import compare_likelihood, gpu_likelihood, lik_to_device, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_07_amd as sv
+
+    sv.load_library()
+
+
+def _oracle(w, rows=None):
+    tgt, drf, tok = rows if rows is not None else w.likelihood_rows()
+    return oracle.token_likelihood(tgt, drf, tok, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, threads=16)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_likelihood_full_size(cfg):
+    w = W.make_config(cfg)
+    note(f"likelihood config {cfg} {w.name}: positions={w.rows_draft} V={w.vocab} {w.dtype} top_k={w.top_k}")
+    rep = compare_likelihood(w, gpu_likelihood(w), _oracle(w))
+    note(f"likelihood config {cfg}: {rep}")
+
+
+def test_outputs_can_be_left_out():
+    w = W.make_config(3)
+    o = _oracle(w)
+    for kw in (dict(beta=False), dict(terms=False, nll=False), dict(terms=False, beta=False)):
+        note(f"likelihood outputs {kw}")
+        g = gpu_likelihood(w, **kw)
+        assert set(g) == {"terms", "beta", "nll"} - {k for k, v in kw.items() if not v}
+        compare_likelihood(w, g, o)
+
+
+def _spec(**kw):
+    d = dict(name="lik_edge", batch=4, k=3, vocab=1001, dtype="bf16", temperature=1.0, top_k=0, kind="iid",
+             target_sigma=2.0, draft_sigma=1.0, ragged=False, modes=("sample",))
+    d.update(kw)
+    return d
+
+
+def _with_rows(w, f):
+    tf, df = f(w.target_f32().copy()), f(w.draft_f32().copy())
+    enc = {"f32": lambda x: x.astype(np.float32), "bf16": W.f32_to_bf16_bits, "f16": W.f32_to_f16_bits}[w.dtype]
+    return dataclasses.replace(w, target=enc(tf), draft=enc(df))
+
+
+EDGE = {
+    "vocab1": (_spec(vocab=1, batch=3), None, {}),
+    "vocab7_f32": (_spec(vocab=7, dtype="f32", batch=5, k=2), None, {}),
+    "vocab1001_misaligned_rows": (_spec(), None, {}),
+    "vocab1001_f16": (_spec(dtype="f16"), None, {}),
+    "ragged_with_zero_lengths": (_spec(batch=6, k=8, vocab=5000), None, dict(draft_lens=[0, 3, 0, 1, 8, 2])),
+    "long_sequences_k300": (_spec(batch=3, k=300, vocab=2000, dtype="f32"), None, {}),
+    "top_k_1": (_spec(top_k=1, vocab=4000, batch=6), None, {}),
+    "top_k_300_exact_path": (_spec(top_k=300, vocab=20000), None, {}),
+    "top_k_v": (_spec(top_k=1001), None, {}),
+    "zipf_top50_ragged": (_spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
+                          None, {}),
+    "temperature_0.05": (_spec(temperature=0.05, vocab=8000, batch=8), None, {}),
+    "peaks_f32_wide": (_spec(kind="peaks", target_sigma=3.0, draft_sigma=1.5, vocab=70001, dtype="f32", batch=3),
+                       None, {}),
+    "ties_top50": (_spec(vocab=9000, batch=8, k=4, top_k=50), lambda x: np.round(x * 2) / 2, {}),
+    # every logit ties: the top-50 kept set is the whole row, past the kept lists
+    "constant_rows_top50": (_spec(vocab=5000, batch=3, k=2, top_k=50, kind="flat"), None, {}),
+    "neg_inf_masks_top50": (_spec(vocab=6000, batch=8, k=4, top_k=50),
+                            lambda x: np.where((np.arange(x.shape[1]) % 7 == 0) | (np.arange(x.shape[1]) >= 3000),
+                                               -np.inf, x), {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_likelihood_edge_shapes(name):
+    spec, f, kw = EDGE[name]
+    w = W.make_workload(spec, gen_seed=zlib.crc32(name.encode()) % 1000, **kw)
+    if f is not None:
+        w = _with_rows(w, f)
+    note(f"likelihood edge {name}: B={w.batch} K={w.draft_lens.tolist()[:8]} V={w.vocab} {w.dtype} "
+         f"T={w.temperature} top_k={w.top_k}")
+    rep = compare_likelihood(w, gpu_likelihood(w), _oracle(w))
+    note(f"likelihood edge {name}: {rep}")
+
+
+def test_draft_equals_target_and_disjoint_supports():
+    w = W.make_workload(_spec(vocab=3000, batch=4, k=3), gen_seed=21)
+    tgt, _, tok = w.likelihood_rows()
+    rows = (tgt, tgt.copy(), tok)
+    note("likelihood draft = target")
+    g = gpu_likelihood(w, tensors=lik_to_device(w, rows))
+    compare_likelihood(w, g, _oracle(w, rows))
+    assert np.all(np.abs(g["beta"] - 1.0) < 1e-5) and np.all(g["terms"][:, 1] == 0)
+    # top-3 kept sets that never meet: beta = 0 and the accept part vanishes
+    w2 = dataclasses.replace(w, top_k=3)
+    tf = np.full((tgt.shape[0], 3000), -4.0, np.float32)
+    df = tf.copy()
+    tf[:, :3] = [3.0, 2.0, 1.0]
+    df[:, 10:13] = [3.0, 2.0, 1.0]
+    rows2 = (W.f32_to_bf16_bits(tf), W.f32_to_bf16_bits(df), np.zeros(tgt.shape[0], np.int32))
+    note("likelihood disjoint top-3 supports")
+    g = gpu_likelihood(w2, tensors=lik_to_device(w2, rows2))
+    compare_likelihood(w2, g, _oracle(w2, rows2))
+    assert np.all(g["beta"] == 0) and np.all(g["terms"][:, 0] == 0)
+
+
+@pytest.mark.parametrize("top_k", [0, 50])
+def test_bad_rows_tokens_and_offsets(top_k):
+    w = W.make_workload(_spec(vocab=4000, batch=5, k=4, top_k=top_k), gen_seed=31,
+                        draft_lens=[2, 4, 1, 3, 4])
+    tgt, drf, tok = w.likelihood_rows()
+    tok = tok.copy()
+    tok[int(w.cu_draft[1]) + 1] = 4000      # sequence 1: a token past the vocabulary
+    tok[int(w.cu_draft[3])] = -1            # sequence 3: a negative token
+    tf = W.bf16_bits_to_f32(tgt).copy()
+    tf[int(w.cu_draft[4]) + 2] = -np.inf    # sequence 4: a target row with no finite logit
+    rows = (W.f32_to_bf16_bits(tf), drf, tok)
+    note(f"likelihood bad tokens and rows, top_k={top_k}")
+    g = gpu_likelihood(w, tensors=lik_to_device(w, rows))
+    o = _oracle(w, rows)
+    compare_likelihood(w, g, o)
+    assert np.isnan(g["nll"][[1, 3, 4]]).all() and not np.isnan(g["nll"][[0, 2]]).any()
+    # out-of-range cu_draft entries: NaN nll, the sequence's other slots untouched
+    t, d, k, _ = lik_to_device(w, rows)
+    cu = torch.tensor([0, 2, 6, 99, 10, 14], dtype=torch.int32, device="cuda:0")
+    import rejection_sampling_verify_07_amd as sv
+    out = sv.token_likelihood(t, d, k, cu_draft=cu, temperature=w.temperature, top_k=top_k, max_draft=4)
+    torch.cuda.synchronize()
+    nll = out["nll"].cpu().numpy()
+    assert np.isnan(nll[2]) and np.isnan(nll[3])            # offsets out of range
+    assert np.isnan(nll[1]) and np.isnan(nll[4])            # bad token, bad row (as before)
+    assert nll[0] == o["nll"][0] or abs(nll[0] - o["nll"][0]) <= 2e-3 * 2   # rows 0..2 still scored
+
+
+def test_strided_rows_on_different_phases():
+    # target and draft rows on different 16-byte phases: the pair pass's element path
+    w = W.make_workload(_spec(vocab=2003, batch=5, k=3, dtype="bf16"), gen_seed=41)
+    tgt, drf, tok = w.likelihood_rows()
+    dev = "cuda:0"
+
+    def padded(a, pad, shift):
+        buf = np.zeros((a.shape[0], a.shape[1] + pad), dtype=np.uint16)
+        buf[:, shift:shift + a.shape[1]] = a
+        full = torch.from_numpy(buf.view(np.int16)).to(dev).view(torch.bfloat16)
+        return full[:, shift:shift + a.shape[1]]
+
+    t = padded(tgt, 5, 1)
+    d = padded(drf, 11, 6)
+    k = torch.from_numpy(tok.astype(np.int32)).to(dev)
+    note("likelihood strided rows, different phases")
+    g = gpu_likelihood(w, tensors=(t, d, k, None))
+    compare_likelihood(w, g, _oracle(w))
+
+
+def test_likelihood_determinism():
+    w = W.make_config(4, batch=64)
+    tens = lik_to_device(w)
+    a = gpu_likelihood(w, tensors=tens)
+    b = gpu_likelihood(w, tensors=tens)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key

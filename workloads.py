@@ -123,9 +123,12 @@ class Workload:
 
     def algorithmic_bytes(self, mode: str = "sample") -> int:
         """Bytes the method must read once: every logit of every row it uses
-        (sample, argmax: target and draft rows; greedy: target rows; draft: draft rows)."""
+        (sample, argmax: target and draft rows; greedy: target rows; draft: draft rows;
+        likelihood: the draft rows and as many target rows)."""
         if mode == "draft":
             rows = self.rows_draft
+        elif mode == "likelihood":
+            rows = 2 * self.rows_draft
         else:
             rows = self.rows_target + (self.rows_draft if mode in ("sample", "argmax") else 0)
         return rows * self.vocab * self.elem_size
@@ -133,6 +136,14 @@ class Workload:
     def positions(self) -> int:
         """Verified positions per call: sum over sequences of K_b + 1."""
         return self.rows_target
+
+    def likelihood_rows(self):
+        """The rows in the likelihood layout, where position (b, k), k < K_b, is
+        row cu_draft[b] + k of both tensors: target rows k < K_b of every
+        sequence, the draft rows, and the guesses as the scored tokens."""
+        keep = [np.arange(int(self.cu_draft[b]) + b, int(self.cu_draft[b + 1]) + b) for b in range(self.batch)]
+        keep = np.concatenate(keep + [np.zeros(0, np.int64)]).astype(np.int64)
+        return np.ascontiguousarray(self.target[keep]), self.draft, self.draft_ids
 
     def target_f32(self) -> np.ndarray:
         return decode_f32(self.target, self.dtype)
