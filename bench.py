@@ -30,9 +30,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B×(K+1)×V logits"
 METRIC_DRAFT = "draft tokens sampled/sec + achieved HBM GB/s (% of peak), B×K×V draft logits"
+METRIC_LIK = "positions scored/sec (speculative likelihood: both parts, beta, NLL) + achieved HBM GB/s, 2×B×K×V logits"
 STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel",
                  "draft_topk": "topk_cand_kernel", "draft": "row_stats_kernel",
-                 "argmax_topk": "topk_cand_kernel", "argmax": "row_stats_kernel"}
+                 "argmax_topk": "topk_cand_kernel", "argmax": "row_stats_kernel",
+                 "likelihood_topk": "topk_cand_kernel", "likelihood": "row_stats_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -113,7 +115,7 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
 def cpu_baseline(w, mode, seconds):
     import oracle
 
-    units = w.rows_draft if mode == "draft" else w.positions()
+    units = w.rows_draft if mode in ("draft", "likelihood") else w.positions()
     unit = "draft tokens/s" if mode == "draft" else "positions/s"
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     oracle.verify_workload(w, mode, threads=threads)  # warm (page in, build)
@@ -141,7 +143,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", type=int, default=5, help="workload 1..5 (default 5: V=151936, top-k 50)")
-    ap.add_argument("--mode", choices=["sample", "greedy", "argmax", "draft"], default="sample",
+    ap.add_argument("--mode", choices=["sample", "greedy", "argmax", "draft", "likelihood"], default="sample",
                     help="sample / greedy / argmax: spec_verify_*; draft: spec_draft_sample over the draft rows")
     ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
                     help="store a 16-bit workload's logits in this type instead (same values before rounding)")
@@ -192,7 +194,7 @@ def main():
     else:
         w = W.make_config(args.config)
     mode = args.mode
-    if mode not in ("draft", "argmax") and mode not in w.modes:
+    if mode not in ("draft", "argmax", "likelihood") and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
         sys.exit(2)
     kind = "greedy" if mode == "greedy" else (mode + ("_topk" if w.top_k > 0 else ""))
@@ -205,7 +207,7 @@ def main():
         t16 = torch.bfloat16 if w.dtype == "bf16" else torch.float16
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(t16)
 
-    tgt0, drf0 = to_dev(w.target), to_dev(w.draft)
+    tgt0, drf0 = to_dev(w.likelihood_rows()[0] if mode == "likelihood" else w.target), to_dev(w.draft)
     ids = torch.from_numpy(w.draft_ids).to(dev)
     cu = torch.from_numpy(w.cu_draft).to(dev) if w.ragged else None
     kmax = w.k_max if cu is not None else None
@@ -214,7 +216,10 @@ def main():
     for i in range(copies):
         tgt = tgt0 if (i == 0 or mode == "draft") else tgt0.clone()
         drf = drf0 if (i == 0 or mode == "greedy") else drf0.clone()
-        if mode == "draft":
+        if mode == "likelihood":
+            p = sv.LikelihoodPlan(tgt, drf, ids, cu_draft=cu, batch=None if cu is not None else w.batch,
+                                  temperature=w.temperature, top_k=w.top_k, max_draft=kmax, workspace=ws)
+        elif mode == "draft":
             p = sv.DraftPlan(drf, cu_draft=cu, batch=None if cu is not None else w.batch, temperature=w.temperature,
                              top_k=w.top_k, seed=w.seed, offset=w.offset, max_draft=kmax, workspace=ws)
         elif mode == "greedy":
@@ -242,7 +247,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / K
-    positions = w.rows_draft if mode == "draft" else w.positions()  # units per step
+    positions = w.rows_draft if mode in ("draft", "likelihood") else w.positions()  # units per step
     value = positions / (ms_step * 1e-3)
 
     # ---- profiled pass: HIP events around each streaming-kernel launch
@@ -280,7 +285,7 @@ def main():
         cpu = cpu_baseline(w, mode, args.cpu_seconds)
 
     line = {
-        "metric": METRIC_DRAFT if mode == "draft" else METRIC,
+        "metric": {"draft": METRIC_DRAFT, "likelihood": METRIC_LIK}.get(mode, METRIC),
         "value": round(value, 1),
         "unit": "draft tokens/s" if mode == "draft" else "positions/s",
         "n_gpus": 1,
