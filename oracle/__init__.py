@@ -65,6 +65,8 @@ def _load():
     lib.orc_uniform.argtypes = [C.c_uint64, C.c_uint32, C.c_uint32, C.c_uint32, C.c_uint32]
     lib.orc_row_probs.restype = C.c_int
     lib.orc_row_probs.argtypes = [P, C.c_int32, C.c_int64, C.c_double, C.c_int32, P, P]
+    lib.orc_row_probs_p.restype = C.c_int
+    lib.orc_row_probs_p.argtypes = [P, C.c_int32, C.c_int64, C.c_double, C.c_int32, C.c_double, P, P]
     lib.orc_row_argmax.restype = C.c_int64
     lib.orc_row_argmax.argtypes = [P, C.c_int32, C.c_int64]
     lib.orc_verify_seq_u.restype = C.c_int
@@ -79,8 +81,8 @@ def _load():
     lib.orc_verify_sample.restype = C.c_int
     lib.orc_verify_sample.argtypes = [
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, P,
-        C.c_double, C.c_int32, C.c_uint64, C.c_uint32, C.c_double,
-        C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P,
+        C.c_double, C.c_int32, C.c_double, C.c_uint64, C.c_uint32, C.c_double,
+        C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P,
     ]
     lib.orc_verify_greedy.restype = C.c_int
     lib.orc_verify_greedy.argtypes = [
@@ -89,17 +91,18 @@ def _load():
     lib.orc_verify_argmax.restype = C.c_int
     lib.orc_verify_argmax.argtypes = [
         C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, P,
-        C.c_double, C.c_int32, C.c_uint64, C.c_uint32, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P,
+        C.c_double, C.c_int32, C.c_double, C.c_uint64, C.c_uint32, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P,
+        P,
     ]
     lib.orc_draft_sample.restype = C.c_int
     lib.orc_draft_sample.argtypes = [
-        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, C.c_double, C.c_int32, C.c_uint64, C.c_uint32,
-        C.c_double, C.c_int32, C.c_int32, P, P, P, P, P,
+        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, C.c_double, C.c_int32, C.c_double, C.c_uint64,
+        C.c_uint32, C.c_double, C.c_int32, C.c_int32, P, P, P, P, P, P,
     ]
     lib.orc_token_likelihood.restype = C.c_int
     lib.orc_token_likelihood.argtypes = [
-        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, C.c_double, C.c_int32, P,
-        C.c_int32, C.c_int32, P, P, P, P,
+        C.c_int32, P, C.c_int64, C.c_int32, P, C.c_int64, P, C.c_int64, C.c_double, C.c_int32, C.c_double, P,
+        C.c_int32, C.c_int32, P, P, P, P, P,
     ]
     _lib = lib
     return lib
@@ -137,21 +140,22 @@ def uniform(seed: int, seq: int, pos: int, purpose: int, offset: int) -> float:
 # --------------------------------------------------------------------------
 # Rows
 # --------------------------------------------------------------------------
-def row_probs(row: np.ndarray, dtype: str, temperature: float, top_k: int = 0):
-    """Temperature softmax of one logit row over its top-k kept set.
+def row_probs(row: np.ndarray, dtype: str, temperature: float, top_k: int = 0, top_p: float = 1.0):
+    """Temperature softmax of one logit row over its top-k kept set, then the
+    top-p nucleus of that distribution (top_p < 1).
 
-    Returns (prob[V] float64, dict(m, S, tau, kept)).
+    Returns (prob[V] float64, dict(m, S, tau, kept, tau_p, margin)).
     """
     lib = _load()
     r = _as_storage(row, dtype)
     V = r.shape[0]
     prob = np.zeros(V, dtype=np.float64)
-    st = np.zeros(4, dtype=np.float64)
-    rc = lib.orc_row_probs(_ptr(r), _dtype_code(dtype), V, float(temperature), int(top_k),
-                           _ptr(prob), _ptr(st))
+    st = np.zeros(6, dtype=np.float64)
+    rc = lib.orc_row_probs_p(_ptr(r), _dtype_code(dtype), V, float(temperature), int(top_k), float(top_p),
+                             _ptr(prob), _ptr(st))
     if rc == -2:
         raise MemoryError("oracle row_probs")
-    return prob, dict(m=st[0], S=st[1], tau=st[2], kept=int(st[3]), ok=(rc == 0))
+    return prob, dict(m=st[0], S=st[1], tau=st[2], kept=int(st[3]), tau_p=st[4], margin=st[5], ok=(rc == 0))
 
 
 def row_argmax(row: np.ndarray, dtype: str) -> int:
@@ -239,14 +243,15 @@ def verify_sample(target, draft, draft_ids, cu_draft, vocab: int, dtype: str,
                   temperature: float, top_k: int, seed: int, offset: int,
                   eps: float = 1e-6, seqs: Optional[Sequence[int]] = None,
                   threads: Optional[int] = None, target_stride: Optional[int] = None,
-                  draft_stride: Optional[int] = None) -> dict:
+                  draft_stride: Optional[int] = None, top_p: float = 1.0) -> dict:
     """Seeded speculative verify over a batch; mirrors the library's outputs.
 
     Returns tokens [R_t], num_accepted [B], probs [R_d, 2] (p, q of each
     draft id), residual_mass [B], plus diagnostics: d_acc [R_d] (distance
     of each evaluated accept draw to its threshold, inf if not evaluated),
     d_fin [B] (distance of the final draw to its interval edges), tok_lo /
-    tok_hi [B] (ids whose interval meets the eps-window) and flags [B].
+    tok_hi [B] (ids whose interval meets the eps-window), flags [B] and
+    p_margin [B] (the sequence's smallest top-p margin; inf without top-p).
     Sequences not listed in `seqs` keep sentinel values (-2 / nan).
     """
     lib = _load()
@@ -269,16 +274,17 @@ def verify_sample(target, draft, draft_ids, cu_draft, vocab: int, dtype: str,
         tok_lo=np.full(B, -2, np.int32),
         tok_hi=np.full(B, -2, np.int32),
         flags=np.zeros(B, np.int32),
+        p_margin=np.full(B, np.nan),
     )
     o = out
 
     def fn(rng):
         return lib.orc_verify_sample(
             B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(tgt), ts, _ptr(drf), ds, _ptr(ids),
-            float(temperature), int(top_k), int(seed), int(offset), float(eps), rng[0], rng[1],
+            float(temperature), int(top_k), float(top_p), int(seed), int(offset), float(eps), rng[0], rng[1],
             _ptr(o["tokens"]), _ptr(o["num_accepted"]), _ptr(o["probs"]),
             _ptr(o["residual_mass"]), _ptr(o["d_acc"]), _ptr(o["d_fin"]), _ptr(o["tok_lo"]),
-            _ptr(o["tok_hi"]), _ptr(o["flags"]))
+            _ptr(o["tok_hi"]), _ptr(o["flags"]), _ptr(o["p_margin"]))
 
     rcs = _run(fn, _ranges(B, seqs, threads), threads)
     if any(rc == -2 for rc in rcs):
@@ -313,7 +319,8 @@ def verify_greedy(target, draft_ids, cu_draft, vocab: int, dtype: str,
 
 def verify_argmax(target, draft, draft_ids, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int,
                   seed: int, offset: int, seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
-                  target_stride: Optional[int] = None, draft_stride: Optional[int] = None) -> dict:
+                  target_stride: Optional[int] = None, draft_stride: Optional[int] = None,
+                  top_p: float = 1.0) -> dict:
     """The argmax-draw variant: the sampling variant's acceptance test, then
     the argmax of max(0, p_n - q_n) at a rejection or of p_K when all pass.
 
@@ -334,14 +341,14 @@ def verify_argmax(target, draft, draft_ids, cu_draft, vocab: int, dtype: str, te
     o = dict(tokens=np.full(R_t, -2, np.int32), num_accepted=np.full(B, -2, np.int32),
              probs=np.full((max(R_d, 1), 2), np.nan), residual_mass=np.full(B, np.nan),
              d_acc=np.full(max(R_d, 1), np.inf), gap=np.full(B, np.nan), second=np.full(B, -2, np.int32),
-             flags=np.zeros(B, np.int32))
+             flags=np.zeros(B, np.int32), p_margin=np.full(B, np.nan))
 
     def fn(rng):
         return lib.orc_verify_argmax(
             B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(tgt), ts, _ptr(drf), ds, _ptr(ids), float(temperature),
-            int(top_k), int(seed), int(offset), rng[0], rng[1], _ptr(o["tokens"]), _ptr(o["num_accepted"]),
-            _ptr(o["probs"]), _ptr(o["residual_mass"]), _ptr(o["d_acc"]), _ptr(o["gap"]), _ptr(o["second"]),
-            _ptr(o["flags"]))
+            int(top_k), float(top_p), int(seed), int(offset), rng[0], rng[1], _ptr(o["tokens"]),
+            _ptr(o["num_accepted"]), _ptr(o["probs"]), _ptr(o["residual_mass"]), _ptr(o["d_acc"]), _ptr(o["gap"]),
+            _ptr(o["second"]), _ptr(o["flags"]), _ptr(o["p_margin"]))
 
     rcs = _run(fn, _ranges(B, seqs, threads), threads)
     if any(rc == -2 for rc in rcs):
@@ -354,7 +361,7 @@ def verify_argmax(target, draft, draft_ids, cu_draft, vocab: int, dtype: str, te
 
 def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int, seed: int, offset: int,
                  eps: float = 1e-6, seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
-                 draft_stride: Optional[int] = None) -> dict:
+                 draft_stride: Optional[int] = None, top_p: float = 1.0) -> dict:
     """Seeded draft-side sampling: x(b, k) ~ q_k by the inverse CDF with U(b, k, 3).
 
     Returns ids [R_d] and, per draft row, dist (distance of u to the chosen
@@ -369,13 +376,14 @@ def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, to
     drf = _as_storage(draft, dtype) if R_d > 0 else np.zeros((1, vocab), np.float32 if dtype == "f32" else np.uint16)
     ds = int(draft_stride or (drf.shape[-1] if drf.ndim == 2 else vocab))
     out = dict(ids=np.full(n, -2, np.int32), dist=np.full(n, np.nan), tok_lo=np.full(n, -2, np.int32),
-               tok_hi=np.full(n, -2, np.int32), flags=np.zeros(n, np.int32))
+               tok_hi=np.full(n, -2, np.int32), flags=np.zeros(n, np.int32), p_margin=np.full(n, np.nan))
     o = out
 
     def fn(rng):
         return lib.orc_draft_sample(B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(drf), ds, float(temperature),
-                                    int(top_k), int(seed), int(offset), float(eps), rng[0], rng[1], _ptr(o["ids"]),
-                                    _ptr(o["dist"]), _ptr(o["tok_lo"]), _ptr(o["tok_hi"]), _ptr(o["flags"]))
+                                    int(top_k), float(top_p), int(seed), int(offset), float(eps), rng[0], rng[1],
+                                    _ptr(o["ids"]), _ptr(o["dist"]), _ptr(o["tok_lo"]), _ptr(o["tok_hi"]),
+                                    _ptr(o["flags"]), _ptr(o["p_margin"]))
 
     rcs = _run(fn, _ranges(B, seqs, threads), threads)
     if any(rc == -2 for rc in rcs):
@@ -388,7 +396,8 @@ def draft_sample(draft, cu_draft, vocab: int, dtype: str, temperature: float, to
 
 def token_likelihood(target, draft, tokens, cu_draft, vocab: int, dtype: str, temperature: float, top_k: int,
                      seqs: Optional[Sequence[int]] = None, threads: Optional[int] = None,
-                     target_stride: Optional[int] = None, draft_stride: Optional[int] = None) -> dict:
+                     target_stride: Optional[int] = None, draft_stride: Optional[int] = None,
+                     top_p: float = 1.0) -> dict:
     """Per-token speculative likelihood of tokens[r] at row r of both tensors
     (position (b, k) is row cu_draft[b] + k).
 
@@ -411,17 +420,18 @@ def token_likelihood(target, draft, tokens, cu_draft, vocab: int, dtype: str, te
     beta = np.full(n, np.nan)
     nll = np.full(B, np.nan)
     flags = np.zeros(B, np.int32)
+    pm = np.full(n, np.nan)
 
     def fn(rng):
         return lib.orc_token_likelihood(B, _ptr(cu), vocab, _dtype_code(dtype), _ptr(tgt), ts, _ptr(drf), ds,
-                                        float(temperature), int(top_k), _ptr(tok), rng[0], rng[1], _ptr(terms),
-                                        _ptr(beta), _ptr(nll), _ptr(flags))
+                                        float(temperature), int(top_k), float(top_p), _ptr(tok), rng[0], rng[1],
+                                        _ptr(terms), _ptr(beta), _ptr(nll), _ptr(flags), _ptr(pm))
 
     rcs = _run(fn, _ranges(B, seqs, threads), threads)
     if any(rc == -2 for rc in rcs):
         raise MemoryError("oracle token_likelihood")
     return dict(accept=terms[:R, 0], reject=terms[:R, 1], p=terms[:R, 2], beta=beta[:R], nll=nll, flags=flags,
-                rc=min(rcs) if rcs else 0)
+                p_margin=pm[:R], rc=min(rcs) if rcs else 0)
 
 
 def verify_workload(w, mode: str = "sample", **kw) -> dict:
@@ -431,13 +441,15 @@ def verify_workload(w, mode: str = "sample", **kw) -> dict:
     "likelihood" (per-token speculative likelihood of the guesses, rows from w.likelihood_rows())."""
     if mode == "likelihood":
         tgt, drf, tok = w.likelihood_rows()
-        return token_likelihood(tgt, drf, tok, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, **kw)
+        return token_likelihood(tgt, drf, tok, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k,
+                                top_p=w.top_p, **kw)
     if mode == "draft":
-        return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset, **kw)
+        return draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed, w.offset,
+                            top_p=w.top_p, **kw)
     if mode == "argmax":
         return verify_argmax(w.target, w.draft, w.draft_ids, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k,
-                             w.seed, w.offset, **kw)
+                             w.seed, w.offset, top_p=w.top_p, **kw)
     if mode == "greedy":
         return verify_greedy(w.target, w.draft_ids, w.cu_draft, w.vocab, w.dtype, **kw)
     return verify_sample(w.target, w.draft, w.draft_ids, w.cu_draft, w.vocab, w.dtype,
-                         w.temperature, w.top_k, w.seed, w.offset, **kw)
+                         w.temperature, w.top_k, w.seed, w.offset, top_p=w.top_p, **kw)

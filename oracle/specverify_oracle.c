@@ -138,12 +138,64 @@ static int orc_cmp_desc(const void* a, const void* b)
  * prob[v] = softmax(l / T) over the kept set, 0 elsewhere.  The kept set is
  * every id when top_k <= 0 or top_k >= V; otherwise every id whose logit is
  * >= tau, the top_k-th largest logit counted with multiplicity (so ties at
- * tau are all kept).  stats = {m, S, tau, kept_count}, where m is the largest
+ * tau are all kept).  Then, when top_p < 1, the nucleus (top-p) filter on
+ * that distribution, the other sampling filter the SpeDec report's helpers
+ * name next to top-K: the kept set shrinks to every id whose logit is >=
+ * tau_p, the largest logit value t for which the probability of
+ * {v : l_v >= t} reaches top_p (so the smallest such set of highest-logit
+ * ids, with ties at tau_p kept), and is renormalised.
+ * stats = {m, S, tau, kept_count, tau_p, margin}, where m is the largest
  * kept logit and S = sum over kept v of exp((l_v - m) / T), summed in
- * ascending v.  Returns 0, or -1 when the kept set has no finite logit.
+ * ascending v (both over the final kept set); margin is the distance of
+ * top_p from the cumulative probabilities on either side of tau_p (infinity
+ * without top-p).  Returns 0, or -1 when the kept set has no finite logit.
  */
-int orc_row_probs(const void* row, int32_t dtype, int64_t V, double T, int32_t top_k,
-                  double* prob, double* stats)
+typedef struct {
+    double val;
+    int64_t idx;
+} OrcValIdx;
+
+static int orc_cmp_vi_desc(const void* a, const void* b)
+{
+    const double x = ((const OrcValIdx*)a)->val, y = ((const OrcValIdx*)b)->val;
+    return (x < y) - (x > y);
+}
+
+/* The nucleus threshold of prob (kept ids have prob > 0): tau_p and the margin. */
+static int orc_nucleus(const double* vals, const double* prob, int64_t V, double top_p, double* tau_p,
+                       double* margin)
+{
+    int64_t n = 0;
+    for (int64_t v = 0; v < V; ++v) n += prob[v] > 0.0;
+    OrcValIdx* a = (OrcValIdx*)malloc(sizeof(OrcValIdx) * (size_t)(n > 0 ? n : 1));
+    if (!a) return -2;
+    n = 0;
+    for (int64_t v = 0; v < V; ++v)
+        if (prob[v] > 0.0) a[n++] = (OrcValIdx){vals[v], v};
+    qsort(a, (size_t)n, sizeof(OrcValIdx), orc_cmp_vi_desc);
+    /* walk groups of equal logits from the top; cum = P(l >= group value) */
+    double cum = 0.0, prev = 0.0;
+    *tau_p = n > 0 ? a[n - 1].val : -INFINITY;
+    *margin = INFINITY;
+    for (int64_t i = 0; i < n;) {
+        int64_t j = i;
+        double g = 0.0;
+        while (j < n && a[j].val == a[i].val) g += prob[a[j++].idx];
+        prev = cum;
+        cum += g;
+        if (cum >= top_p) {
+            *tau_p = a[i].val;
+            *margin = fmin(cum - top_p, top_p - prev);
+            break;
+        }
+        i = j;
+    }
+    free(a);
+    return 0;
+}
+
+int orc_row_probs_p(const void* row, int32_t dtype, int64_t V, double T, int32_t top_k, double top_p,
+                    double* prob, double* stats)
 {
     double* vals = (double*)malloc((size_t)V * sizeof(double));
     if (!vals) return -2;
@@ -170,6 +222,7 @@ int orc_row_probs(const void* row, int32_t dtype, int64_t V, double T, int32_t t
     if (!(m > -INFINITY) || isinf(m)) {
         for (int64_t v = 0; v < V; ++v) prob[v] = 0.0;
         stats[0] = m; stats[1] = 0.0; stats[2] = tau; stats[3] = (double)kept;
+        stats[4] = tau; stats[5] = INFINITY;
         free(vals);
         return -1;
     }
@@ -181,9 +234,32 @@ int orc_row_probs(const void* row, int32_t dtype, int64_t V, double T, int32_t t
         S += w;
     }
     for (int64_t v = 0; v < V; ++v) prob[v] /= S;
+    stats[4] = tau;
+    stats[5] = INFINITY;
+    if (top_p < 1.0) {
+        double tau_p, margin;
+        if (orc_nucleus(vals, prob, V, top_p, &tau_p, &margin) != 0) { free(vals); return -2; }
+        /* the same softmax over the nucleus (m, the largest logit, is in it) */
+        S = 0.0;
+        kept = 0;
+        for (int64_t v = 0; v < V; ++v) {
+            double w = (vals[v] >= tau && vals[v] >= tau_p) ? exp((vals[v] - m) / T) : 0.0;
+            kept += (vals[v] >= tau && vals[v] >= tau_p);
+            prob[v] = w;
+            S += w;
+        }
+        for (int64_t v = 0; v < V; ++v) prob[v] /= S;
+        stats[4] = tau_p;
+        stats[5] = margin;
+    }
     stats[0] = m; stats[1] = S; stats[2] = tau; stats[3] = (double)kept;
     free(vals);
     return 0;
+}
+
+int orc_row_probs(const void* row, int32_t dtype, int64_t V, double T, int32_t top_k, double* prob, double* stats)
+{
+    return orc_row_probs_p(row, dtype, V, T, top_k, 1.0, prob, stats);
 }
 
 /* The lowest index among the maxima of the raw logits. */
@@ -435,13 +511,13 @@ int orc_verify_argmax_seq(const double* P, const double* Q, const int32_t* x, in
 /* orc_verify_sample; gap / second per sequence describe the final argmax). */
 int orc_verify_argmax(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* target, int64_t t_stride,
                       const void* draft, int64_t d_stride, const int32_t* ids, double T, int32_t top_k,
-                      uint64_t seed, uint32_t offset, int32_t b_begin, int32_t b_end, int32_t* tokens,
+                      double top_p, uint64_t seed, uint32_t offset, int32_t b_begin, int32_t b_end, int32_t* tokens,
                       int32_t* n_acc, double* probs, double* zmass, double* d_acc, double* gap, int32_t* second,
-                      int32_t* flags)
+                      int32_t* flags, double* p_margin)
 {
     const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
     int rc_all = 0;
-    double stats[4];
+    double stats[6];
     for (int32_t b = b_begin; b < b_end && b < B; ++b) {
         int32_t K = cu[b + 1] - cu[b];
         int64_t trow0 = (int64_t)cu[b] + b;
@@ -456,15 +532,19 @@ int orc_verify_argmax(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, co
             return -2;
         }
         int bad = 0;
+        double pm = INFINITY;  /* the sequence's smallest top-p margin */
         for (int32_t k = 0; k <= K; ++k) {
             const char* row = (const char*)target + (size_t)(trow0 + k) * (size_t)t_stride * esz;
-            if (orc_row_probs(row, dtype, V, T, top_k, P + (int64_t)k * V, stats) != 0) bad = 1;
+            if (orc_row_probs_p(row, dtype, V, T, top_k, top_p, P + (int64_t)k * V, stats) != 0) bad = 1;
+            pm = fmin(pm, stats[5]);
         }
         for (int32_t k = 0; k < K; ++k) {
             const char* row = (const char*)draft + (size_t)(drow0 + k) * (size_t)d_stride * esz;
-            if (orc_row_probs(row, dtype, V, T, top_k, Q + (int64_t)k * V, stats) != 0) bad = 1;
+            if (orc_row_probs_p(row, dtype, V, T, top_k, top_p, Q + (int64_t)k * V, stats) != 0) bad = 1;
+            pm = fmin(pm, stats[5]);
             ua[k] = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 0u, offset);
         }
+        if (p_margin) p_margin[b] = pm;
         int32_t fl = 0;
         int rc = orc_verify_argmax_seq(P, Q, ids + drow0, K, V, ua, tokens + trow0, n_acc + b, pq, pq + k1,
                                        zmass + b, d_acc + drow0, gap + b, second + b, &fl);
@@ -514,15 +594,15 @@ int orc_verify_seq_u_batch(const double* P, const double* Q, const int32_t* x, i
 int orc_verify_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
                       const void* target, int64_t t_stride,
                       const void* draft, int64_t d_stride, const int32_t* ids,
-                      double T, int32_t top_k, uint64_t seed, uint32_t offset, double eps,
+                      double T, int32_t top_k, double top_p, uint64_t seed, uint32_t offset, double eps,
                       int32_t b_begin, int32_t b_end,
                       int32_t* tokens, int32_t* n_acc, double* probs, double* zmass,
                       double* d_acc, double* d_fin, int32_t* tok_lo, int32_t* tok_hi,
-                      int32_t* flags)
+                      int32_t* flags, double* p_margin)
 {
     const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
     int rc_all = 0;
-    double stats[4];
+    double stats[6];
     for (int32_t b = b_begin; b < b_end && b < B; ++b) {
         int32_t K = cu[b + 1] - cu[b];
         int64_t trow0 = (int64_t)cu[b] + b;
@@ -537,19 +617,23 @@ int orc_verify_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
             return -2;
         }
         int bad = 0;
+        double pm = INFINITY;  /* the sequence's smallest top-p margin */
         for (int32_t k = 0; k <= K; ++k) {
             const char* row = (const char*)target + (size_t)(trow0 + k) * (size_t)t_stride * esz;
-            if (orc_row_probs(row, dtype, V, T, top_k, P + (int64_t)k * V, stats) != 0) bad = 1;
+            if (orc_row_probs_p(row, dtype, V, T, top_k, top_p, P + (int64_t)k * V, stats) != 0) bad = 1;
+            pm = fmin(pm, stats[5]);
         }
         for (int32_t k = 0; k < K; ++k) {
             const char* row = (const char*)draft + (size_t)(drow0 + k) * (size_t)d_stride * esz;
-            if (orc_row_probs(row, dtype, V, T, top_k, Q + (int64_t)k * V, stats) != 0) bad = 1;
+            if (orc_row_probs_p(row, dtype, V, T, top_k, top_p, Q + (int64_t)k * V, stats) != 0) bad = 1;
+            pm = fmin(pm, stats[5]);
             ua[k] = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 0u, offset);
         }
         for (int32_t k = 0; k < K; ++k)
             ur[k] = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 1u, offset);
         double u_bonus = orc_uniform(seed, (uint32_t)b, (uint32_t)K, 2u, offset);
 
+        if (p_margin) p_margin[b] = pm;
         int32_t fl = 0;
         double* dk = d_acc + drow0;
         int rc = orc_verify_seq_u(P, Q, ids + drow0, K, V, ua, ur, u_bonus, eps,
@@ -579,13 +663,14 @@ int orc_verify_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
  * interval meets [u - eps, u + eps], and flags.
  */
 int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* draft, int64_t d_stride,
-                     double T, int32_t top_k, uint64_t seed, uint32_t offset, double eps, int32_t b_begin,
-                     int32_t b_end, int32_t* ids, double* dist, int32_t* tok_lo, int32_t* tok_hi, int32_t* flags)
+                     double T, int32_t top_k, double top_p, uint64_t seed, uint32_t offset, double eps,
+                     int32_t b_begin, int32_t b_end, int32_t* ids, double* dist, int32_t* tok_lo, int32_t* tok_hi,
+                     int32_t* flags, double* p_margin)
 {
     const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
     double* q = (double*)malloc(sizeof(double) * (size_t)V);
     if (!q) return -2;
-    double stats[4];
+    double stats[6];
     int rc_all = 0;
     for (int32_t b = b_begin; b < b_end && b < B; ++b) {
         const int32_t K = cu[b + 1] - cu[b];
@@ -593,7 +678,8 @@ int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, con
             const int64_t r = (int64_t)cu[b] + k;
             const char* row = (const char*)draft + (size_t)r * (size_t)d_stride * esz;
             int32_t fl = 0;
-            if (orc_row_probs(row, dtype, V, T, top_k, q, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            if (orc_row_probs_p(row, dtype, V, T, top_k, top_p, q, stats) != 0) fl |= ORC_FLAG_BAD_INPUT;
+            if (p_margin) p_margin[r] = stats[5];
             const double u = orc_uniform(seed, (uint32_t)b, (uint32_t)k, 3u, offset);
             double total;
             ids[r] = (int32_t)orc_inverse_cdf(q, V, u, eps, &total, dist + r, tok_lo + r, tok_hi + r, &fl);
@@ -627,8 +713,8 @@ int orc_draft_sample(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, con
  */
 int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype, const void* target,
                          int64_t t_stride, const void* draft, int64_t d_stride, double T, int32_t top_k,
-                         const int32_t* tokens, int32_t b_begin, int32_t b_end, double* terms, double* beta,
-                         double* nll, int32_t* flags)
+                         double top_p, const int32_t* tokens, int32_t b_begin, int32_t b_end, double* terms,
+                         double* beta, double* nll, int32_t* flags, double* p_margin)
 {
     const size_t esz = dtype == ORC_DTYPE_F32 ? 4 : 2;
     double* P = (double*)malloc(sizeof(double) * (size_t)V);
@@ -638,7 +724,7 @@ int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
         free(Q);
         return -2;
     }
-    double stats[4];
+    double stats[6];
     int rc_all = 0;
     for (int32_t b = b_begin; b < b_end && b < B; ++b) {
         const int32_t K = cu[b + 1] - cu[b];
@@ -648,8 +734,10 @@ int orc_token_likelihood(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
             const int64_t r = (int64_t)cu[b] + k;
             const char* trow = (const char*)target + (size_t)r * (size_t)t_stride * esz;
             const char* drow = (const char*)draft + (size_t)r * (size_t)d_stride * esz;
-            const int bad_t = orc_row_probs(trow, dtype, V, T, top_k, P, stats) != 0;
-            const int bad_d = orc_row_probs(drow, dtype, V, T, top_k, Q, stats) != 0;
+            const int bad_t = orc_row_probs_p(trow, dtype, V, T, top_k, top_p, P, stats) != 0;
+            const double pm_t = stats[5];
+            const int bad_d = orc_row_probs_p(drow, dtype, V, T, top_k, top_p, Q, stats) != 0;
+            if (p_margin) p_margin[r] = fmin(pm_t, stats[5]);
             if (bad_t || bad_d) {
                 /* a row with no finite kept logit defines no distribution */
                 fl |= ORC_FLAG_BAD_INPUT;

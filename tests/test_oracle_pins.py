@@ -615,3 +615,87 @@ def test_likelihood_special_cases(orc):
     # a token outside the target's top-k kept set has likelihood 0
     o = orc.token_likelihood(t2, d2, np.array([9], np.int32), np.array([0, 1], np.int32), 10, "f32", 1.0, 3)
     assert o["accept"][0] == 0.0 and o["reject"][0] == 0.0 and o["nll"][0] == np.inf
+
+
+# --------------------------------------------------------------------------
+# top-p (nucleus) filter after top-k
+# --------------------------------------------------------------------------
+def test_top_p_one_is_no_filter(orc):
+    rng = np.random.default_rng(12)
+    l = (rng.standard_normal(500) * 2).astype(np.float32)
+    for top_k in (0, 40):
+        a, _ = orc.row_probs(l, "f32", 0.8, top_k)
+        b, st = orc.row_probs(l, "f32", 0.8, top_k, top_p=1.0)
+        assert np.array_equal(a, b) and st["margin"] == np.inf
+
+
+def test_top_p_tiny_keeps_the_maxima(orc):
+    # any top_p below the largest probability keeps exactly the tied maxima
+    l = np.array([1.0, 3.0, -2.0, 3.0, 0.5, 3.0], np.float32)
+    prob, st = orc.row_probs(l, "f32", 1.0, 0, top_p=1e-9)
+    np.testing.assert_allclose(prob, [0, 1 / 3, 0, 1 / 3, 0, 1 / 3], atol=1e-15)
+    assert st["tau_p"] == 3.0
+
+
+def test_top_p_hand_worked_example(orc):
+    """p = (1/2, 1/4, 1/8, 1/8) (logits ln p, T = 1).  top_p = 0.6: {0} holds
+    0.5 < 0.6, {0, 1} holds 0.75, so the nucleus is {0, 1} renormalised to
+    (2/3, 1/3).  top_p = 0.8: ids 2 and 3 tie at 1/8; 0.75 < 0.8, and adding
+    the tied pair reaches 1, so both are kept (no arbitrary half of a tie)."""
+    l = np.log(np.array([0.5, 0.25, 0.125, 0.125])).astype(np.float32)
+    prob, st = orc.row_probs(l, "f32", 1.0, 0, top_p=0.6)
+    np.testing.assert_allclose(prob, [2 / 3, 1 / 3, 0, 0], atol=1e-7)
+    assert abs(st["margin"] - 0.1) < 1e-6   # 0.6 - 0.5 = 0.1 and 0.75 - 0.6 = 0.15: the smaller
+    prob, st = orc.row_probs(l, "f32", 1.0, 0, top_p=0.8)
+    np.testing.assert_allclose(prob, [0.5, 0.25, 0.125, 0.125], atol=1e-7)
+    assert st["kept"] == 4
+    # "reaches": a top_p equal to the mass of the two largest keeps exactly those two
+    p1, _ = orc.row_probs(l, "f32", 1.0, 0)
+    prob, st = orc.row_probs(l, "f32", 1.0, 0, top_p=float(p1[0] + p1[1]))
+    assert st["kept"] == 2 and st["margin"] == 0.0
+
+
+@pytest.mark.parametrize("top_k,top_p,T", [(0, 0.9, 1.0), (0, 0.5, 0.7), (50, 0.8, 1.0), (20, 0.95, 1.5),
+                                           (0, 0.3, 2.0)])
+def test_top_p_is_the_smallest_high_logit_set(orc, top_k, top_p, T):
+    """Against scipy's softmax of the top-k set: the kept set is upward closed
+    in the logit (every id above a kept one is kept), it holds at least top_p
+    of the mass, dropping its lowest logit value takes it below top_p (so it
+    is the smallest such set, ties kept whole), and the result is that
+    softmax renormalised on the set.  Nested as top_p grows."""
+    rng = np.random.default_rng(int(top_p * 100) + top_k)
+    l = np.round(rng.standard_normal(3000) * 4, 1).astype(np.float32)   # many ties
+    base = _softmax(l, T, top_k)
+    prob, st = orc.row_probs(l, "f32", T, top_k, top_p=top_p)
+    kept = prob > 0
+    lo = l[kept].min()
+    assert np.array_equal(kept, (base > 0) & (l >= lo))               # upward closed, ties whole
+    assert base[kept].sum() >= top_p - 1e-12
+    assert base[kept & (l > lo)].sum() < top_p + 1e-12                 # minimal
+    np.testing.assert_allclose(prob[kept], base[kept] / base[kept].sum(), rtol=1e-12)
+    assert st["tau_p"] == lo
+    m = min(base[kept].sum() - top_p, top_p - base[kept & (l > lo)].sum())
+    assert abs(st["margin"] - m) < 1e-12
+    bigger, _ = orc.row_probs(l, "f32", T, top_k, top_p=min(1.0, top_p + 0.05))
+    assert np.all(bigger[kept] > 0)
+
+
+def test_draft_sample_law_with_top_p(orc):
+    """Draws from the nucleus distribution: chi-square of 10^6 draft-side
+    samples against the renormalised nucleus of scipy's softmax."""
+    V, T, top_p = 60, 0.9, 0.85
+    rng = np.random.default_rng(17)
+    l = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    base = _softmax(l, T)
+    order = np.argsort(-l, kind="stable")
+    cum = np.cumsum(base[order])
+    cut = l[order][np.searchsorted(cum, top_p)]        # logit at which the mass reaches top_p
+    keep = l >= cut
+    want = np.where(keep, base, 0) / base[keep].sum()
+    N = 1_000_000
+    rows, cu = _one_row_per_sequence(l, N)
+    o = orc.draft_sample(rows, cu, V, "f32", T, 0, 0, 0, threads=8, top_p=top_p)
+    assert np.all(keep[o["ids"]])
+    counts = np.bincount(o["ids"], minlength=V)[keep]
+    chi = stats.chisquare(counts, want[keep] * N)
+    assert chi.pvalue > 1e-4, chi

@@ -108,6 +108,7 @@ class Workload:
     draft: np.ndarray  # [R_d, V] float32 or uint16
     draft_ids: np.ndarray  # int32 [R_d]
     info: dict = dataclasses.field(default_factory=dict)
+    top_p: float = 1.0  # nucleus filter after top-k; 1 keeps everything
 
     @property
     def rows_target(self) -> int:
@@ -329,6 +330,7 @@ def make_workload(
         draft=draft,
         draft_ids=ids,
         info=dict(draft_sigma=sigmas, gen_seed=int(gen_seed)),
+        top_p=float(spec.get("top_p", 1.0)),
     )
 
 
