@@ -184,8 +184,9 @@ static int orc_nucleus(const double* vals, const double* prob, int64_t V, double
         prev = cum;
         cum += g;
         if (cum >= top_p) {
+            /* the first group is always kept: below it there is no other choice */
             *tau_p = a[i].val;
-            *margin = fmin(cum - top_p, top_p - prev);
+            *margin = fmin(cum - top_p, i > 0 ? top_p - prev : INFINITY);
             break;
         }
         i = j;
