@@ -113,7 +113,12 @@ typedef struct {
  * Speculative sampling verify.
  *   p_k = softmax(target row k / T) and q_k = softmax(draft row k / T), each
  *   restricted to its own top-k kept set when top_k > 0 (every id whose raw
- *   logit is >= the top_k-th largest, ties kept; top_k = 0 or V keeps all).
+ *   logit is >= the top_k-th largest, ties kept; top_k = 0 or V keeps all),
+ *   then, when top_p < 1, to its own top-p nucleus: every id whose logit is
+ *   >= tau_p, the largest logit value t for which the probability of
+ *   {v : l_v >= t} reaches top_p (ties kept), renormalised.  Top-K and
+ *   Top-P are the two filters the sampling helpers of "CS3602_FINAL_SpeDec"
+ *   name (its module list; problem analysis, item 2).
  *   Position k accepts iff u_k < min(1, p_k(x_k) / q_k(x_k)) (q = 0 accepts
  *   iff p > 0), u_k = U(b, k, 0).  n = the first rejected position, or K_b.
  *   If n < K_b the new token is the first id (ascending) whose running sum
@@ -125,7 +130,9 @@ typedef struct {
  * Arguments
  *   target_logits [rows_t, stride] and draft_logits [rows_d, stride] in
  *   shape->dtype; draft_ids int32 [total_draft] in [0, V).
- *   temperature > 0 and finite.  top_k in [0, V].
+ *   temperature > 0 and finite.  top_k in [0, V].  top_p in (0, 1]; 1 is
+ *   off.  top-p over full rows costs several extra reads of each row (a
+ *   mass-weighted radix select); after top-k it works on the kept lists.
  *   out_tokens int32 [total_draft + B]; out_num_accepted int32 [B];
  *   out_probs (nullable) float [total_draft][2] = p_k(x_k), q_k(x_k) for
  *   every draft position; out_residual_mass (nullable) float [B] = the
@@ -137,6 +144,7 @@ SV_API sv_status_t spec_verify_sample(const sv_shape_t* shape,
                                const int32_t* draft_ids,
                                float temperature,
                                int32_t top_k,
+                               float top_p,
                                uint64_t seed,
                                uint32_t offset,
                                int32_t* out_tokens,
@@ -164,6 +172,7 @@ SV_API sv_status_t spec_verify_argmax(const sv_shape_t* shape,
                                const int32_t* draft_ids,
                                float temperature,
                                int32_t top_k,
+                               float top_p,
                                uint64_t seed,
                                uint32_t offset,
                                int32_t* out_tokens,
@@ -198,13 +207,13 @@ SV_API sv_status_t spec_verify_greedy(const sv_shape_t* shape,
  * "Prepare speculative sampling", step 1, which takes the argmax); the
  * acceptance proof of "CS3602_FINAL_SpeDec", section 2, assumes each guess
  * is drawn from q, and that page's sampling helpers filter by top-K.
- *   q_k = softmax(draft row k / T) over its top-k kept set, exactly as in
- *   spec_verify_sample; x(b, k) = the first id (ascending) whose running sum
+ *   q_k = softmax(draft row k / T) over its top-k kept set and top-p
+ *   nucleus, exactly as in spec_verify_sample; x(b, k) = the first id (ascending) whose running sum
  *   of q_k exceeds U(b, k, 3), with U as in spec_verify_sample.
  * Arguments
  *   shape as for spec_verify_sample; target_row_stride is ignored.
  *   draft_logits [total_draft, draft_row_stride] in shape->dtype.
- *   temperature > 0 and finite; top_k in [0, V].
+ *   temperature > 0 and finite; top_k in [0, V]; top_p in (0, 1].
  *   out_ids int32 [total_draft]: x(b, k) at cu_draft[b] + k.  A sequence
  *   whose cu_draft entries are out of range leaves its slots untouched; a
  *   row with no finite logit in its kept set yields -1.
@@ -214,6 +223,7 @@ SV_API sv_status_t spec_draft_sample(const sv_shape_t* shape,
                               const void* draft_logits,
                               float temperature,
                               int32_t top_k,
+                              float top_p,
                               uint64_t seed,
                               uint32_t offset,
                               int32_t* out_ids,
@@ -227,7 +237,8 @@ SV_API sv_status_t spec_draft_sample(const sv_shape_t* shape,
  * problem analysis, item 1, to score speculative output without summing
  * over the vocabulary).  For position (b, k), k < K_b, with p = the target
  * row's and q = the draft row's softmax at temperature T (each over its
- * top-k kept set, exactly as in spec_verify_sample) and y = tokens[r]:
+ * top-k kept set and top-p nucleus, exactly as in spec_verify_sample) and
+ * y = tokens[r]:
  *   accept part  P(guess accepted, x = y) = q(y) min(1, p(y)/q(y)) = min(p(y), q(y))
  *   reject part  P(guess rejected, x = y) = (1 - beta) p'(y)       = p(y) - min(p(y), q(y))
  *   beta         = sum_v min(p(v), q(v))   (the position's acceptance mass)
@@ -241,7 +252,8 @@ SV_API sv_status_t spec_draft_sample(const sv_shape_t* shape,
  *   upper limit here).
  *   target_logits [total_draft, target_row_stride], draft_logits
  *   [total_draft, draft_row_stride] in shape->dtype; tokens int32
- *   [total_draft].  temperature > 0 and finite; top_k in [0, V].
+ *   [total_draft].  temperature > 0 and finite; top_k in [0, V]; top_p in
+ *   (0, 1].
  *   out_terms (nullable) float [total_draft][2] = accept part, reject part;
  *   out_beta (nullable) float [total_draft]; out_nll (nullable) double [B].
  *   At least one output must be non-NULL.  beta over full rows costs a
@@ -258,6 +270,7 @@ SV_API sv_status_t spec_token_likelihood(const sv_shape_t* shape,
                               const int32_t* tokens,
                               float temperature,
                               int32_t top_k,
+                              float top_p,
                               float* out_terms,
                               float* out_beta,
                               double* out_nll,

@@ -62,7 +62,7 @@ def load_library(path: Optional[str] = None):
     VP = C.c_void_p
     lib.spec_verify_sample.restype = C.c_int
     lib.spec_verify_sample.argtypes = [
-        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32,
+        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_float, C.c_uint64, C.c_uint32,
         VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP,
     ]
     lib.spec_verify_argmax.restype = C.c_int
@@ -71,11 +71,13 @@ def load_library(path: Optional[str] = None):
     lib.spec_verify_greedy.argtypes = [C.POINTER(ShapeT), VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP]
     lib.spec_draft_sample.restype = C.c_int
     lib.spec_draft_sample.argtypes = [
-        C.POINTER(ShapeT), VP, C.c_float, C.c_int32, C.c_uint64, C.c_uint32, VP, VP, C.POINTER(C.c_size_t), VP,
+        C.POINTER(ShapeT), VP, C.c_float, C.c_int32, C.c_float, C.c_uint64, C.c_uint32, VP, VP,
+        C.POINTER(C.c_size_t), VP,
     ]
     lib.spec_token_likelihood.restype = C.c_int
     lib.spec_token_likelihood.argtypes = [
-        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP,
+        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_float, VP, VP, VP, VP, C.POINTER(C.c_size_t),
+        VP,
     ]
     lib.spec_verify_status_string.restype = C.c_char_p
     lib.spec_verify_status_string.argtypes = [C.c_int]
@@ -152,7 +154,7 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
                   cu_draft: Optional[torch.Tensor] = None, temperature: float = 1.0, top_k: int = 0,
                   seed: int = 0, offset: int = 0, max_draft: Optional[int] = None, return_probs: bool = True,
                   workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None, stream=None,
-                  argmax: bool = False) -> dict:
+                  argmax: bool = False, top_p: float = 1.0) -> dict:
     """Speculative-sampling verify on the GPU (spec_verify_sample, or
     spec_verify_argmax with argmax=True: argmax draws).
 
@@ -171,7 +173,7 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
     dev = target_logits.device
     need = C.c_size_t(0)
-    _check(fn(C.byref(shape), None, None, None, float(temperature), int(top_k), int(seed),
+    _check(fn(C.byref(shape), None, None, None, float(temperature), int(top_k), float(top_p), int(seed),
               int(offset), None, None, None, None, None, C.byref(need), None), name + "(workspace query)")
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
@@ -186,7 +188,8 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     have = C.c_size_t(workspace.numel())
     st = fn(
         C.byref(shape), target_logits.data_ptr(), draft_logits.data_ptr() if draft_logits.numel() else None,
-        draft_ids.data_ptr() if draft_ids.numel() else None, float(temperature), int(top_k), int(seed), int(offset),
+        draft_ids.data_ptr() if draft_ids.numel() else None, float(temperature), int(top_k), float(top_p), int(seed),
+        int(offset),
         out["tokens"].data_ptr(), out["num_accepted"].data_ptr(),
         out["probs"].data_ptr() if out.get("probs") is not None and total > 0 else None,
         out["residual_mass"].data_ptr() if out.get("residual_mass") is not None else None,
@@ -249,7 +252,7 @@ def _draft_geometry(draft_logits, cu_draft, batch, max_draft):
 def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = None, batch: Optional[int] = None,
                  temperature: float = 1.0, top_k: int = 0, seed: int = 0, offset: int = 0,
                  max_draft: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                 out: Optional[torch.Tensor] = None, stream=None, top_p: float = 1.0) -> torch.Tensor:
     """Draft-side sampling on the GPU (spec_draft_sample): x(b, k) ~ q_k.
 
     draft_logits [sum(K_b), V] float32, bfloat16 or float16, rows packed as for the
@@ -261,15 +264,15 @@ def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = 
     shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
     dev = draft_logits.device
     need = C.c_size_t(0)
-    _check(lib.spec_draft_sample(C.byref(shape), None, float(temperature), int(top_k), int(seed), int(offset), None,
-                                 None, C.byref(need), None), "spec_draft_sample(workspace query)")
+    _check(lib.spec_draft_sample(C.byref(shape), None, float(temperature), int(top_k), float(top_p), int(seed),
+                                 int(offset), None, None, C.byref(need), None), "spec_draft_sample(workspace query)")
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     if out is None:
         out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)[:total]
     have = C.c_size_t(workspace.numel())
     st = lib.spec_draft_sample(C.byref(shape), draft_logits.data_ptr() if total else None, float(temperature),
-                               int(top_k), int(seed), int(offset), out.data_ptr() if total else None,
+                               int(top_k), float(top_p), int(seed), int(offset), out.data_ptr() if total else None,
                                workspace.data_ptr(), C.byref(have), C.c_void_p(_stream_handle(stream)))
     _check(st, "spec_draft_sample")
     return out
@@ -296,7 +299,8 @@ def _ptr_or_none(out, key):
 def token_likelihood(target_logits: torch.Tensor, draft_logits: torch.Tensor, tokens: torch.Tensor,
                      cu_draft: Optional[torch.Tensor] = None, batch: Optional[int] = None, temperature: float = 1.0,
                      top_k: int = 0, max_draft: Optional[int] = None, terms: bool = True, beta: bool = True,
-                     nll: bool = True, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                     nll: bool = True, workspace: Optional[torch.Tensor] = None, stream=None,
+                     top_p: float = 1.0) -> dict:
     """Per-token speculative likelihood on the GPU (spec_token_likelihood).
 
     target_logits and draft_logits [sum(K_b), V] (float32, bfloat16 or
@@ -314,15 +318,16 @@ def token_likelihood(target_logits: torch.Tensor, draft_logits: torch.Tensor, to
     shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
     dev = target_logits.device
     need = C.c_size_t(0)
-    _check(lib.spec_token_likelihood(C.byref(shape), None, None, None, float(temperature), int(top_k), None, None,
-                                     None, None, C.byref(need), None), "spec_token_likelihood(workspace query)")
+    _check(lib.spec_token_likelihood(C.byref(shape), None, None, None, float(temperature), int(top_k), float(top_p),
+                                     None, None, None, None, C.byref(need), None),
+           "spec_token_likelihood(workspace query)")
     if workspace is None or workspace.numel() < need.value:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     out = _likelihood_outputs(total, b, dev, terms, beta, nll)
     have = C.c_size_t(workspace.numel())
     st = lib.spec_token_likelihood(
         C.byref(shape), target_logits.data_ptr() if total else None, draft_logits.data_ptr() if total else None,
-        tokens.data_ptr() if total else None, float(temperature), int(top_k), _ptr_or_none(out, "terms"),
+        tokens.data_ptr() if total else None, float(temperature), int(top_k), float(top_p), _ptr_or_none(out, "terms"),
         _ptr_or_none(out, "beta"), _ptr_or_none(out, "nll"), workspace.data_ptr(), C.byref(have),
         C.c_void_p(_stream_handle(stream)))
     _check(st, "spec_token_likelihood")
@@ -338,7 +343,7 @@ def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k
     if greedy:
         st = lib.spec_verify_greedy(C.byref(shape), None, None, None, None, None, C.byref(need), None)
     else:
-        st = lib.spec_verify_sample(C.byref(shape), None, None, None, 1.0, int(top_k), 0, 0, None, None, None,
+        st = lib.spec_verify_sample(C.byref(shape), None, None, None, 1.0, int(top_k), 1.0, 0, 0, None, None, None,
                                     None, None, C.byref(need), None)
     _check(st, "workspace query")
     return need.value
@@ -395,15 +400,16 @@ class SamplePlan:
     """
 
     def __init__(self, target_logits, draft_logits, draft_ids, cu_draft=None, temperature=1.0, top_k=0, seed=0,
-                 offset=0, max_draft=None, out=None, workspace=None, stream=None, probs=True, argmax=False):
+                 offset=0, max_draft=None, out=None, workspace=None, stream=None, probs=True, argmax=False,
+                 top_p=1.0):
         self.lib = load_library()
         batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
         self.shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
         dev = target_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_verify_sample(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
-                                           int(seed), int(offset), None, None, None, None, None, C.byref(need),
-                                           None), "workspace query")
+                                           float(top_p), int(seed), int(offset), None, None, None, None, None,
+                                           C.byref(need), None), "workspace query")
         self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
             torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
         self.out = out or dict(tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
@@ -415,7 +421,7 @@ class SamplePlan:
         self.args = (C.byref(self.shape), C.c_void_p(target_logits.data_ptr()),
                      C.c_void_p(draft_logits.data_ptr() if draft_logits.numel() else None),
                      C.c_void_p(draft_ids.data_ptr() if draft_ids.numel() else None), C.c_float(temperature),
-                     C.c_int32(top_k), C.c_uint64(seed), C.c_uint32(offset),
+                     C.c_int32(top_k), C.c_float(top_p), C.c_uint64(seed), C.c_uint32(offset),
                      C.c_void_p(self.out["tokens"].data_ptr()), C.c_void_p(self.out["num_accepted"].data_ptr()),
                      C.c_void_p(self.out["probs"].data_ptr() if (probs and total > 0) else None),
                      C.c_void_p(self.out["residual_mass"].data_ptr() if probs else None),
@@ -463,21 +469,22 @@ class LikelihoodPlan:
     """spec_token_likelihood with every argument marshalled once."""
 
     def __init__(self, target_logits, draft_logits, tokens, cu_draft=None, batch=None, temperature=1.0, top_k=0,
-                 max_draft=None, terms=True, beta=True, nll=True, workspace=None, stream=None):
+                 max_draft=None, terms=True, beta=True, nll=True, workspace=None, stream=None, top_p=1.0):
         self.lib = load_library()
         b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
         self.shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
         dev = target_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_token_likelihood(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
-                                              None, None, None, None, C.byref(need), None), "workspace query")
+                                              float(top_p), None, None, None, None, C.byref(need), None),
+               "workspace query")
         self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
             torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
         self.out = _likelihood_outputs(total, b, dev, terms, beta, nll)
         self.have = C.c_size_t(self.workspace.numel())
         self._keep = (target_logits, draft_logits, tokens, cu_draft)
         self.args = (C.byref(self.shape), C.c_void_p(target_logits.data_ptr()), C.c_void_p(draft_logits.data_ptr()),
-                     C.c_void_p(tokens.data_ptr()), C.c_float(temperature), C.c_int32(top_k),
+                     C.c_void_p(tokens.data_ptr()), C.c_float(temperature), C.c_int32(top_k), C.c_float(top_p),
                      C.c_void_p(_ptr_or_none(self.out, "terms")), C.c_void_p(_ptr_or_none(self.out, "beta")),
                      C.c_void_p(_ptr_or_none(self.out, "nll")), C.c_void_p(self.workspace.data_ptr()),
                      C.byref(self.have), C.c_void_p(_stream_handle(stream)))
@@ -494,21 +501,22 @@ class DraftPlan:
     """spec_draft_sample with every argument marshalled once."""
 
     def __init__(self, draft_logits, cu_draft=None, batch=None, temperature=1.0, top_k=0, seed=0, offset=0,
-                 max_draft=None, out=None, workspace=None, stream=None):
+                 max_draft=None, out=None, workspace=None, stream=None, top_p=1.0):
         self.lib = load_library()
         b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
         self.shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
         dev = draft_logits.device
         need = C.c_size_t(0)
-        _check(self.lib.spec_draft_sample(C.byref(self.shape), None, float(temperature), int(top_k), int(seed),
-                                          int(offset), None, None, C.byref(need), None), "workspace query")
+        _check(self.lib.spec_draft_sample(C.byref(self.shape), None, float(temperature), int(top_k), float(top_p),
+                                          int(seed), int(offset), None, None, C.byref(need), None), "workspace query")
         self.workspace = workspace if workspace is not None and workspace.numel() >= need.value else \
             torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
         self.out = out if out is not None else torch.empty(max(total, 1), dtype=torch.int32, device=dev)
         self.have = C.c_size_t(self.workspace.numel())
         self._keep = (draft_logits, cu_draft)
         self.args = (C.byref(self.shape), C.c_void_p(draft_logits.data_ptr()), C.c_float(temperature),
-                     C.c_int32(top_k), C.c_uint64(seed), C.c_uint32(offset), C.c_void_p(self.out.data_ptr()),
+                     C.c_int32(top_k), C.c_float(top_p), C.c_uint64(seed), C.c_uint32(offset),
+                     C.c_void_p(self.out.data_ptr()),
                      C.c_void_p(self.workspace.data_ptr()), C.byref(self.have), C.c_void_p(_stream_handle(stream)))
         self.fn = self.lib.spec_draft_sample
 

@@ -16,6 +16,7 @@
 #include "sv_select.hpp"
 #include "sv_verify.hpp"
 #include "sv_likelihood.hpp"
+#include "sv_nucleus.hpp"
 
 static_assert(SV_MAX_DRAFT == sv::kMaxDraft, "draft limit mismatch");
 static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
@@ -57,6 +58,10 @@ struct Plan {
     int32_t nchunk;
     int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
     int32_t nchunk2;  // tiles per row pair of the likelihood's pair pass (full rows)
+    int32_t top_k;
+    float top_p;
+    bool topp;  // top_p < 1: the nucleus pass runs after the statistics
+    bool desc;  // the consumers read row descriptors (top-k and/or top-p), not chunk partials
     size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, off_pair, bytes;
 };
 
@@ -161,10 +166,13 @@ sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
 // Rows of the streaming pass: rows [0, rows_t) are read through RowSet::tgt
 // (the target rows, or the draft rows for draft-side sampling), the rest
 // through RowSet::drf.
-Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k)
+Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p = 1.0f)
 {
     const bool greedy = kind == CALL_GREEDY;
     Plan p{};
+    p.top_k = top_k;
+    p.top_p = top_p;
+    p.topp = !greedy && top_p < 1.0f;
     p.rows_t = (kind == CALL_DRAFT || kind == CALL_LIKE) ? sh->total_draft : sh->total_draft + sh->batch;
     p.rows_d = (kind == CALL_SAMPLE || kind == CALL_LIKE) ? sh->total_draft : 0;
     p.rows = p.rows_t + p.rows_d;
@@ -186,15 +194,22 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k)
         p.loads = rows_stream * chunks_for(sh->vocab, vec_of(sh->dtype), kLoads) > kBigGridTiles ? kLoadsBig : kLoads;
     }
     p.nchunk = chunks_for(sh->vocab, vec_of(sh->dtype), p.loads);
+    p.desc = (p.mode == PLAN_TOPK_FAST || p.mode == PLAN_TOPK_EXACT) || p.topp;
     size_t off = 0;
     const size_t slots = (size_t)p.rows * (size_t)p.nchunk;
     if (p.mode == PLAN_FULL) {
         p.off_partials = off;
         off = align_up(off + slots * sizeof(sv::PartialFull));
-        if (kind == CALL_LIKE) {
+        if (kind == CALL_LIKE && !p.topp) {
             p.nchunk2 = chunks_for(sh->vocab, vec_of(sh->dtype), sv::kPairLoads);
             p.off_pair = off;
             off = align_up(off + (size_t)p.rows_t * (size_t)p.nchunk2 * sizeof(double));
+        }
+        if (p.topp) {  // the nucleus pass writes descriptors and kept lists
+            p.off_descs = off;
+            off = align_up(off + (size_t)p.rows * sizeof(sv::RowDesc));
+            p.off_kept = off;
+            off = align_up(off + (size_t)p.rows * sv::kKeepCap * sizeof(sv::KeptEntry));
         }
     } else if (p.mode == PLAN_GREEDY) {
         p.off_partials = off;
@@ -232,9 +247,10 @@ sv_status_t launch_status()
 // The streaming pass and, with top-k, the per-row select over the rows of rs:
 // fills va.partials (full rows) or va.descs / va.kept (top-k).
 template <int DT>
-sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, int32_t top_k, void* ws,
-                      hipStream_t stream, sv::VerifyArgs& va)
+sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, void* ws,
+                           hipStream_t stream, sv::VerifyArgs& va)
 {
+    const int32_t top_k = p.top_k;
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows * p.nchunk);
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
@@ -273,6 +289,27 @@ sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs,
     return launch_status();
 }
 
+// The streaming pass, the top-k select when top-k is on, and the top-p
+// nucleus pass when top_p < 1 (which turns full-row partials into row
+// descriptors too).
+template <int DT>
+sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, void* ws,
+                      hipStream_t stream, sv::VerifyArgs& va)
+{
+    if (run_stats_topk<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (!p.topp) return SV_OK;
+    sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p, va.partials, p.nchunk,
+                   ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
+    if (p.mode == PLAN_FULL) {
+        hipLaunchKernelGGL((sv::nucleus_kernel<DT, false>), dim3(p.rows), dim3(sv::kThreads), 0, stream, na);
+    } else {
+        hipLaunchKernelGGL((sv::nucleus_kernel<DT, true>), dim3(p.rows), dim3(sv::kThreads), 0, stream, na);
+    }
+    va.descs = na.descs;
+    va.kept = na.kept;
+    return launch_status();
+}
+
 sv::VerifyArgs base_args(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, uint64_t seed,
                          uint32_t offset)
 {
@@ -292,7 +329,7 @@ sv::VerifyArgs base_args(const sv_shape_t* sh, const Plan& p, const sv::RowSet& 
 
 template <int DT>
 sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
-                       const int32_t* ids, float c, int32_t top_k, uint64_t seed, uint32_t offset,
+                       const int32_t* ids, float c, uint64_t seed, uint32_t offset,
                        int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
                        hipStream_t stream, int32_t argmax_draw)
 {
@@ -307,9 +344,12 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     va.out_probs = out_probs;
     va.out_zmass = out_z;
     va.argmax_draw = argmax_draw;
-    if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
-    if (p.mode == PLAN_FULL) {
+    if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (!p.desc) {
         hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
+                           stream, va);
+    } else if (p.mode == PLAN_FULL) {  // top-p over full rows: a nucleus may still be a masked full row
+        hipLaunchKernelGGL((sv::verify_kernel<DT, true, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
                            stream, va);
     } else {
         hipLaunchKernelGGL((sv::verify_kernel<DT, true, sv::kThreads>), dim3(sh->batch), dim3(sv::kThreads), 0, stream,
@@ -319,8 +359,8 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
 }
 
 template <int DT>
-sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, float c, int32_t top_k, uint64_t seed,
-                      uint32_t offset, int32_t* out_ids, void* ws, hipStream_t stream)
+sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, float c, uint64_t seed, uint32_t offset,
+                      int32_t* out_ids, void* ws, hipStream_t stream)
 {
     const size_t es = esize_of(sh->dtype);
     // the draft rows are the streamed rows
@@ -328,10 +368,13 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
                         p.rows_t};
     sv::VerifyArgs va = base_args(sh, p, rs, c, seed, offset);
     va.out_tokens = out_ids;
-    if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
     const dim3 grid((uint32_t)sh->batch, (uint32_t)sh->max_draft);  // max_draft <= SV_MAX_DRAFT fits grid y
-    if (p.mode == PLAN_FULL) {
+    if (!p.desc) {
         hipLaunchKernelGGL((sv::draft_draw_kernel<DT, false, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads), 0,
+                           stream, va);
+    } else if (p.mode == PLAN_FULL) {
+        hipLaunchKernelGGL((sv::draft_draw_kernel<DT, true, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads), 0,
                            stream, va);
     } else {
         hipLaunchKernelGGL((sv::draft_draw_kernel<DT, true, sv::kThreads>), grid, dim3(sv::kThreads), 0, stream, va);
@@ -341,7 +384,7 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
 
 template <int DT>
 sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
-                           const int32_t* tokens, float c, int32_t top_k, float* out_terms, float* out_beta,
+                           const int32_t* tokens, float c, float* out_terms, float* out_beta,
                            double* out_nll, void* ws, hipStream_t stream)
 {
     const size_t es = esize_of(sh->dtype);
@@ -364,11 +407,11 @@ sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt,
     la.out_nll = out_nll;
     if (sh->total_draft > 0) {
         sv::VerifyArgs va = base_args(sh, p, rs, c, 0, 0);
-        if (run_stats<DT>(sh, p, rs, c, top_k, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+        if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
         la.partials = va.partials;
         la.descs = va.descs;
         la.kept = va.kept;
-        if (p.mode == PLAN_FULL && out_beta != nullptr) {
+        if (!p.desc && out_beta != nullptr) {
             double* pair = ws_at<double>(ws, p.off_pair);
             const sv::PairArgs pa{rs, sh->vocab, sh->total_draft, va.partials, p.nchunk, p.nchunk2, c, pair};
             const uint32_t grid = (uint32_t)((int64_t)sh->total_draft * p.nchunk2);
@@ -378,7 +421,7 @@ sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt,
             la.pair = pair;
         }
     }
-    if (p.mode == PLAN_FULL) {
+    if (!p.desc) {
         hipLaunchKernelGGL((sv::likelihood_kernel<DT, false>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, la);
     } else {
         hipLaunchKernelGGL((sv::likelihood_kernel<DT, true>), dim3(sh->batch), dim3(sv::kThreads), 0, stream, la);
@@ -410,8 +453,15 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     return launch_status();
 }
 
+// Temperature, top-k and top-p arguments shared by the sampling calls.
+bool filters_ok(const sv_shape_t* sh, float temperature, int32_t top_k, float top_p)
+{
+    return temperature > 0.0f && isfinite(temperature) && top_k >= 0 && top_k <= sh->vocab && top_p > 0.0f &&
+           top_p <= 1.0f;
+}
+
 sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                                 const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                                 const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
                                  uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                  float* out_residual_mass, void* workspace, size_t* workspace_bytes,
                                  hipStream_t stream, int32_t argmax_draw)
@@ -419,9 +469,8 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_SAMPLE);
     if (st != SV_OK) return st;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
-    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
-    const Plan p = make_plan(shape, CALL_SAMPLE, top_k);
+    if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, CALL_SAMPLE, top_k, top_p);
     if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;
@@ -440,7 +489,7 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
 
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
     return by_dtype(shape->dtype, [&](auto dt) {
-        return run_sample<decltype(dt)::value>(shape, p, target_logits, draft_logits, draft_ids, c, top_k, seed,
+        return run_sample<decltype(dt)::value>(shape, p, target_logits, draft_logits, draft_ids, c, seed,
                                                offset, out_tokens, out_num_accepted, out_probs, out_residual_mass,
                                                workspace, stream, argmax_draw);
     });
@@ -451,23 +500,23 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
 extern "C" {
 
 sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
                                uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                float* out_residual_mass, void* workspace, size_t* workspace_bytes,
                                hipStream_t stream)
 {
-    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, seed, offset,
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
                                 out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
                                 workspace_bytes, stream, 0);
 }
 
 sv_status_t spec_verify_argmax(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                               const int32_t* draft_ids, float temperature, int32_t top_k, uint64_t seed,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
                                uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                float* out_residual_mass, void* workspace, size_t* workspace_bytes,
                                hipStream_t stream)
 {
-    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, seed, offset,
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
                                 out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
                                 workspace_bytes, stream, 1);
 }
@@ -500,15 +549,14 @@ sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logit
 }
 
 sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
-                              uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
+                              float top_p, uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
                               size_t* workspace_bytes, hipStream_t stream)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_DRAFT);
     if (st != SV_OK) return st;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
-    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
-    const Plan p = make_plan(shape, CALL_DRAFT, top_k);
+    if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, CALL_DRAFT, top_k, top_p);
     if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;
@@ -524,22 +572,21 @@ sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits,
 
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
     return by_dtype(shape->dtype, [&](auto dt) {
-        return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, top_k, seed, offset, out_ids, workspace,
-                                              stream);
+        return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, seed, offset, out_ids, workspace, stream);
     });
 }
 
 sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                                  const int32_t* tokens, float temperature, int32_t top_k, float* out_terms,
+                                  const int32_t* tokens, float temperature, int32_t top_k, float top_p,
+                                  float* out_terms,
                                   float* out_beta, double* out_nll, void* workspace, size_t* workspace_bytes,
                                   hipStream_t stream)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_LIKE);
     if (st != SV_OK) return st;
-    if (!(temperature > 0.0f) || !isfinite(temperature)) return SV_ERR_INVALID_ARGUMENT;
-    if (top_k < 0 || top_k > shape->vocab) return SV_ERR_INVALID_ARGUMENT;
-    const Plan p = make_plan(shape, CALL_LIKE, top_k);
+    if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(shape, CALL_LIKE, top_k, top_p);
     if ((int64_t)p.rows * p.nchunk > INT32_MAX || (int64_t)p.rows_t * (p.nchunk2 > 0 ? p.nchunk2 : 1) > INT32_MAX)
         return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
@@ -559,8 +606,8 @@ sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_lo
 
     const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
     return by_dtype(shape->dtype, [&](auto dt) {
-        return run_likelihood<decltype(dt)::value>(shape, p, target_logits, draft_logits, tokens, c, top_k,
-                                                   out_terms, out_beta, out_nll, workspace, stream);
+        return run_likelihood<decltype(dt)::value>(shape, p, target_logits, draft_logits, tokens, c, out_terms,
+                                                   out_beta, out_nll, workspace, stream);
     });
 }
 

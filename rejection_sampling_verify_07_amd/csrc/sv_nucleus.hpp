@@ -1,0 +1,290 @@
+// Top-p (nucleus) filter, applied after temperature and top-k: the sampling
+// filter that the "CS3602_FINAL_SpeDec" report's helpers name next to top-K
+// (its module list, and its problem analysis, item 2).  The kept set shrinks
+// to every id whose logit is >= tau_p, the largest logit value t for which
+// the probability of {v : l_v >= t} reaches top_p (ties at tau_p kept whole),
+// and the distribution is renormalised over it.  The row's maximum is always
+// kept, so m and fl32(m c) do not change; the kernel rewrites the row
+// descriptor (tau, S, kept count) and the kept list.
+//
+// One workgroup per row:
+//  - a row with a kept list (<= 1024 ids) is done by wave 0 in registers: a
+//    bitwise radix search on the select key, one wave-wide fp64 sum of the
+//    fp32 weights per bit (fixed order), then an order-keeping compaction;
+//  - a full row (no top-k, or a kept set that outgrew its list) takes a
+//    radix select over the whole row weighted by mass: per 8-bit digit, a
+//    256-bucket histogram of the weights in 2^-43 fixed point (integer LDS
+//    atomics, so the sums are exact and the result deterministic), then one
+//    last pass that sums the kept weights and writes the kept list when it
+//    fits.
+#pragma once
+
+#include "sv_common.hpp"
+#include "sv_select.hpp"
+#include "sv_topk.hpp"
+
+namespace sv {
+
+struct NucArgs {
+    RowSet rs;
+    int32_t vocab;
+    int32_t rows;
+    float c;
+    float top_p;
+    const PartialFull* partials;  // full rows: the streaming pass's chunk partials
+    int32_t nchunk;
+    RowDesc* descs;                // in (top-k) / out
+    KeptEntry* kept;               // in (top-k) / out, kKeepCap per row
+};
+
+constexpr double kFixScale = 8796093022208.0;  // 2^43: weights <= 1 summed over <= 2^20 ids stay below 2^63
+
+// Radix key of a logit for the full-row select: ordered like the logit, with
+// the meaningful bits on top (16 of them for the 16-bit types).
+template <int DT>
+__device__ __forceinline__ uint32_t nuc_key(float v)
+{
+    if constexpr (DT == DT_F16) return SelKey<DT_F16>::of(v) << 16;
+    else return order_key(v);
+}
+template <int DT>
+__device__ __forceinline__ float nuc_value(uint32_t k)
+{
+    if constexpr (DT == DT_F32) return key_to_float(k);
+    else return SelKey<DT>::value(k >> 16);
+}
+
+// Inclusive scan of a u64 across the wave (shuffles; once per digit).
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, o, kWave);
+        const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), o, kWave);
+        if (lane_id() >= o) v += ((uint64_t)hi << 32) | lo;
+    }
+    return v;
+}
+
+// Kept-list rows: wave 0 alone.
+template <int DT>
+__device__ void nucleus_list(const NucArgs& a, int32_t row, const RowDesc& d)
+{
+    using K = SelKey<DT>;
+    constexpr int PER = kKeepCap / kWave;
+    const int lane = lane_id();
+    KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;
+    const int32_t n = d.kept;
+    KeptEntry e[PER];
+    float w[PER];
+    uint32_t key[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int32_t i = j * kWave + lane;  // ascending i: j-major, then lane
+        e[j] = i < n ? kl[i] : KeptEntry{INT32_MAX, neg_inf()};
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool ok = e[j].idx != INT32_MAX;
+        w[j] = ok ? __builtin_amdgcn_exp2f(__builtin_fmaf(e[j].val, a.c, -d.mcc)) : 0.0f;
+        key[j] = ok ? K::of(e[j].val) : 0u;
+    }
+    const double target = (double)a.top_p * d.s;
+    // the largest key h with sum{w : key >= h} >= target
+    uint32_t h = 0;
+    for (int bit = K::kBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = h | (1u << bit);
+        double ls = 0.0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) ls += key[j] >= cand ? (double)w[j] : 0.0;
+        const double mass = readlane_f64(wave_sum_dpp(ls), 0);
+        if (mass >= target) h = cand;
+    }
+    // order-keeping compaction of the kept entries, in place (all loaded above)
+    int32_t nk = 0;
+    double ls = 0.0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool pred = e[j].idx != INT32_MAX && key[j] >= h;
+        const uint64_t m = __ballot(pred);
+        if (m != 0) {
+            if (pred) {
+                kl[nk + lanes_below(m)] = e[j];
+                ls += (double)w[j];
+            }
+            nk += (int32_t)__popcll(m);
+        }
+    }
+    ls = wave_sum_dpp(ls);
+    if (lane == 0) {
+        RowDesc o = d;
+        o.tau = K::value(h);
+        o.s = ls;
+        o.kept = nk;
+        a.descs[row] = o;
+    }
+}
+
+// Full rows (kept set = {l >= d.tau}): the whole workgroup.
+template <int DT>
+__device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, uint64_t* s_hist, uint64_t* s_u,
+                             int32_t* s_w, double* s_d)
+{
+    constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
+    const char* rowp = row_ptr(a.rs, row);
+    const float tau = d.tau, mcc = d.mcc, c = a.c;
+    auto fixw = [&](float l) {
+        return (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc)) * kFixScale + 0.5);
+    };
+    uint32_t prefix = 0, pmask = 0;
+    uint64_t need = 0;  // fixed-point mass still to reach inside the current prefix
+    for (int shift = 24; shift >= LOW; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
+        __syncthreads();
+        for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+#pragma unroll
+            for (int e = 0; e < Dt<DT>::kVec; ++e) {
+                const uint32_t k = nuc_key<DT>(f[e]);
+                if (ok[e] && f[e] >= tau && (k & pmask) == prefix)
+                    atomicAdd((unsigned long long*)&s_hist[(k >> shift) & 255u], (unsigned long long)fixw(f[e]));
+            }
+        });
+        __syncthreads();
+        if (wave_id() == 0) {
+            // lane L holds digits 255-4L .. 252-4L (descending)
+            const int l = lane_id();
+            uint64_t h4[4], lsum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h4[q] = s_hist[255 - 4 * l - q];
+                lsum += h4[q];
+            }
+            const uint64_t incl = wave_incl_scan_u64(lsum);
+            const uint64_t total = (uint64_t)__shfl((long long)incl, kWave - 1, kWave);
+            if (shift == 24) {
+                // the whole kept mass is in the first histogram: the fixed-point target
+                need = (uint64_t)((double)a.top_p * (double)total);
+                if (need == 0) need = 1;  // at least the maximum is kept
+            }
+            const uint64_t excl = incl - lsum;
+            int found = -1;
+            uint64_t above = 0;
+            if (excl < need && incl >= need) {
+                uint64_t cum = excl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (found < 0 && cum + h4[q] >= need) {
+                        found = 255 - 4 * l - q;
+                        above = cum;
+                    }
+                    cum += h4[q];
+                }
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            if (bal != 0) {
+                const int src = __builtin_ctzll(bal);
+                found = __shfl(found, src, kWave);
+                above = (uint64_t)__shfl((long long)above, src, kWave);
+            } else {
+                found = 0;  // rounding only: keep everything under this prefix
+                above = 0;
+            }
+            if (l == 0) {
+                s_u[0] = (uint64_t)found;
+                s_u[1] = need - above;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)s_u[0] << shift;
+        pmask |= 0xffu << shift;
+        need = s_u[1];
+        __syncthreads();
+    }
+    // the threshold value: the largest logit whose key has this prefix
+    if constexpr (LOW > 0) prefix |= 0xffffu;
+    const float tau_p = fmaxf(nuc_value<DT>(prefix), tau);
+
+    // kept sum, count and (if it fits) the ordered kept list
+    KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;
+    int32_t base = 0;
+    double ls = 0.0;
+    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) cnt += (ok[e] && f[e] >= tau_p);
+        int tot;
+        int pos = base + block_excl_scan_int(cnt, s_w, &tot);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) {
+            if (ok[e] && f[e] >= tau_p) {
+                if (pos < kKeepCap) kl[pos] = KeptEntry{r0 + e, f[e]};
+                ++pos;
+                s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+            }
+        }
+        ls += (double)s;
+        base += tot;
+    });
+    const double sum = block_sum_double(ls, s_d);
+    if (threadIdx.x == 0) {
+        RowDesc o = d;
+        o.tau = tau_p;
+        o.s = sum;
+        o.kept = base <= kKeepCap ? base : -1;
+        a.descs[row] = o;
+    }
+}
+
+template <int DT, bool FROM_DESC>
+__global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
+{
+    __shared__ uint64_t s_hist[256];
+    __shared__ uint64_t s_u[2];
+    __shared__ int32_t s_w[kWaves];
+    __shared__ double s_d[kWaves];
+    __shared__ RowDesc s_desc;
+    const int32_t row = blockIdx.x;
+    if constexpr (FROM_DESC) {
+        if (threadIdx.x == 0) s_desc = a.descs[row];
+    } else {
+        // full rows: the row's statistics from the streaming pass's partials
+        if (wave_id() == 0) {
+            const PartialFull* pp = a.partials + (int64_t)row * a.nchunk;
+            float m = neg_inf();
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
+            m = wave_max_dpp(m);
+            const float mcc = m * a.c;
+            double s = 0.0;
+            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
+                const PartialFull q = pp[ch];
+                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
+            }
+            s = wave_sum_dpp(s);
+            if (lane_id() == 0) {
+                RowDesc d;
+                d.tau = neg_inf();
+                d.m = m;
+                d.mcc = mcc;
+                d.kept = -1;
+                d.s = s;
+                d.flags = 0;
+                d.pad = 0;
+                s_desc = d;
+            }
+        }
+    }
+    __syncthreads();
+    const RowDesc d = s_desc;
+    if (!(d.s > 0.0)) {  // no finite kept logit: the consumers report the row
+        if (threadIdx.x == 0) a.descs[row] = d;
+        return;
+    }
+    if (d.kept >= 0) {
+        if (wave_id() == 0) nucleus_list<DT>(a, row, d);
+    } else {
+        nucleus_full<DT>(a, row, d, s_hist, s_u, s_w, s_d);
+    }
+}
+
+}  // namespace sv

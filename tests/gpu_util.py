@@ -10,6 +10,9 @@ import oracle
 import rejection_sampling_verify_07_amd as sv
 
 EPS_BOUNDARY = 1e-6  # a draw whose uniform lies this close to a threshold is a boundary draw
+# a top-p cut whose cumulative probability lies this close to top_p may fall either way on the GPU
+# (fp32 weights with c = fl32(log2 e / T): the cumulative mass carries errors near 1e-7)
+TOPP_EPS = 1e-6
 RTOL = {"f32": 1e-5, "bf16": 2e-3, "f16": 2e-3}  # probability tolerance by input dtype
 TORCH_16 = {"bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -33,6 +36,7 @@ def to_device(w, dev="cuda:0"):
 
 def gpu_sample(w, tensors=None, **kw):
     tgt, drf, ids, cu = tensors or to_device(w)
+    kw.setdefault("top_p", w.top_p)
     out = sv.verify_sample(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
                            offset=w.offset, max_draft=w.k_max if cu is not None else None, **kw)
     torch.cuda.synchronize()
@@ -56,11 +60,12 @@ class Report:
     boundary_final: int = 0
     max_rel_p: float = 0.0
     max_rel_z: float = 0.0
+    boundary_topp: int = 0
 
     def __str__(self):
         return (f"{self.sequences} sequences: {self.exact} compared bit-exactly, boundary draws: "
-                f"{self.boundary_accept} accept / {self.boundary_final} final; max rel err p,q {self.max_rel_p:.2e}, "
-                f"Z {self.max_rel_z:.2e}")
+                f"{self.boundary_accept} accept / {self.boundary_final} final / {self.boundary_topp} top-p cut; "
+                f"max rel err p,q {self.max_rel_p:.2e}, Z {self.max_rel_z:.2e}")
 
 
 def compare_sample(w, g, o, seqs=None, rtol=None, final_ok=None):
@@ -84,6 +89,12 @@ def compare_sample(w, g, o, seqs=None, rtol=None, final_ok=None):
         ids = w.draft_ids[d0:d0 + K]
         rep.sequences += 1
         assert n_o >= 0, f"oracle rejected sequence {b}"
+        if o.get("p_margin") is not None and o["p_margin"][b] < TOPP_EPS:
+            # a row's top-p cut is within rounding of top_p: only the form is checked
+            rep.boundary_topp += 1
+            assert 0 <= n_g <= K and np.array_equal(tok_g[:n_g], ids[:n_g]), f"seq {b}: malformed"
+            assert 0 <= tok_g[n_g] < w.vocab and np.all(tok_g[n_g + 1:] == -1), f"seq {b}: malformed"
+            continue
         # probabilities of every guess
         if "probs" in g and K > 0:
             pg = g["probs"][d0:d0 + K].astype(np.float64)
@@ -146,6 +157,7 @@ def gpu_draft(w, tensors=None, cu_override=None, **kw):
     kw.setdefault("top_k", w.top_k)
     kw.setdefault("seed", w.seed)
     kw.setdefault("offset", w.offset)
+    kw.setdefault("top_p", w.top_p)
     out = sv.draft_sample(drf, cu_draft=cu, batch=None if cu is not None else w.batch,
                           max_draft=w.k_max if cu is not None else None, **kw)
     torch.cuda.synchronize()
@@ -159,6 +171,9 @@ def compare_draft(ids_gpu, ref):
     ids_ref = ref["ids"]
     assert ids_gpu.shape == ids_ref.shape
     assert np.all(ref["flags"] & 4 == 0), "oracle flagged a bad row"
+    cut = ref["p_margin"] < TOPP_EPS   # top-p cut within rounding: only a valid id is required
+    assert np.all((ids_gpu[cut] >= 0) & (ids_gpu[cut] < 1 << 20))
+    ids_gpu = np.where(cut, ids_ref, ids_gpu)
     boundary = ref["dist"] < EPS_BOUNDARY
     exact = ~boundary
     bad = np.flatnonzero(exact & (ids_gpu != ids_ref))
@@ -174,6 +189,7 @@ GAP_BOUNDARY = 1e-4  # an argmax whose margin over the runner-up is below this (
 
 def gpu_argmax(w, tensors=None, **kw):
     tgt, drf, ids, cu = tensors or to_device(w)
+    kw.setdefault("top_p", w.top_p)
     out = sv.verify_argmax(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
                            offset=w.offset, max_draft=w.k_max if cu is not None else None, **kw)
     torch.cuda.synchronize()
@@ -208,6 +224,7 @@ def lik_to_device(w, rows=None, dev="cuda:0"):
 
 def gpu_likelihood(w, tensors=None, **kw):
     tgt, drf, tok, cu = tensors or lik_to_device(w)
+    kw.setdefault("top_p", w.top_p)
     out = sv.token_likelihood(tgt, drf, tok, cu_draft=cu, batch=None if cu is not None else w.batch,
                               temperature=w.temperature, top_k=w.top_k,
                               max_draft=w.k_max if cu is not None else None, **kw)
@@ -224,6 +241,21 @@ def compare_likelihood(w, g, o):
     rtol = RTOL[w.dtype]
     R = int(w.cu_draft[-1])
     rep = dict(positions=R)
+    # positions whose top-p cut is within rounding of top_p are left out, with their sequences' NLL
+    cut = o["p_margin"] < TOPP_EPS
+    seq_cut = np.array([cut[w.cu_draft[b]:w.cu_draft[b + 1]].any() for b in range(w.batch)], bool)
+    rep["topp_cut"] = int(cut.sum())
+    o = dict(o)
+    g = dict(g)
+    for key in ("accept", "reject", "p", "beta"):
+        o[key] = np.where(cut, 0.0, o[key])
+    if "terms" in g:
+        g["terms"] = np.where(cut[:, None], 0.0, g["terms"])
+    if "beta" in g:
+        g["beta"] = np.where(cut, 0.0, g["beta"])
+    if "nll" in g:
+        o["nll"] = np.where(seq_cut, 0.0, o["nll"])
+        g["nll"] = np.where(seq_cut, 0.0, g["nll"])
     if "terms" in g:
         a, r = g["terms"][:, 0].astype(np.float64), g["terms"][:, 1].astype(np.float64)
         ao, ro, po = o["accept"], o["reject"], o["p"]

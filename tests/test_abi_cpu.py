@@ -70,12 +70,12 @@ def _shape(B, **kw):
     return B.ShapeT(**d)
 
 
-def _query(lib, sh, T=1.0, top_k=0, greedy=False):
+def _query(lib, sh, T=1.0, top_k=0, greedy=False, top_p=1.0):
     need = C.c_size_t(0)
     if greedy:
         st = lib.spec_verify_greedy(C.byref(sh), None, None, None, None, None, C.byref(need), None)
     else:
-        st = lib.spec_verify_sample(C.byref(sh), None, None, None, T, top_k, 0, 0, None, None, None, None, None,
+        st = lib.spec_verify_sample(C.byref(sh), None, None, None, T, top_k, top_p, 0, 0, None, None, None, None, None,
                                     C.byref(need), None)
     return st, need.value
 
@@ -127,7 +127,7 @@ def test_null_and_misaligned_pointers_and_small_workspace(lib, B):
     have = C.c_size_t(need)
 
     def call(tgt=fake, drf=fake, ids=fake, tok=fake, nacc=fake, ws=fake, have_=have):
-        return lib.spec_verify_sample(C.byref(sh), tgt, drf, ids, 1.0, 0, 0, 0, tok, nacc, None, None, ws,
+        return lib.spec_verify_sample(C.byref(sh), tgt, drf, ids, 1.0, 0, 1.0, 0, 0, tok, nacc, None, None, ws,
                                       C.byref(have_), None)
 
     assert call(tgt=None) == B.SV_ERR_INVALID_ARGUMENT
@@ -139,9 +139,9 @@ def test_null_and_misaligned_pointers_and_small_workspace(lib, B):
     assert call(ids=fake + 2) == B.SV_ERR_INVALID_ARGUMENT   # int32 needs 4-byte alignment
     assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT   # workspace 256-byte aligned
     assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
-    assert lib.spec_verify_sample(C.byref(sh), fake, fake, fake, 1.0, 0, 0, 0, fake, fake, None, None, fake, None,
+    assert lib.spec_verify_sample(C.byref(sh), fake, fake, fake, 1.0, 0, 1.0, 0, 0, fake, fake, None, None, fake, None,
                                   None) == B.SV_ERR_INVALID_ARGUMENT
-    assert lib.spec_verify_sample(None, fake, fake, fake, 1.0, 0, 0, 0, fake, fake, None, None, None,
+    assert lib.spec_verify_sample(None, fake, fake, fake, 1.0, 0, 1.0, 0, 0, fake, fake, None, None, None,
                                   C.byref(have), None) == B.SV_ERR_INVALID_ARGUMENT
     # greedy
     st, needg = _query(lib, sh, greedy=True)
@@ -172,9 +172,9 @@ def test_binding_fails_loudly_without_library(tmp_path, B):
         B.load_library(str(tmp_path / "missing.so"))
 
 
-def _draft_query(lib, sh, T=1.0, top_k=0):
+def _draft_query(lib, sh, T=1.0, top_k=0, top_p=1.0):
     need = C.c_size_t(0)
-    st = lib.spec_draft_sample(C.byref(sh), None, T, top_k, 0, 0, None, None, C.byref(need), None)
+    st = lib.spec_draft_sample(C.byref(sh), None, T, top_k, top_p, 0, 0, None, None, C.byref(need), None)
     return st, need.value
 
 
@@ -195,7 +195,7 @@ def test_draft_sample_arguments(lib, B):
     have = C.c_size_t(need)
 
     def call(drf=fake, ids=fake, ws=fake, have_=have):
-        return lib.spec_draft_sample(C.byref(sh), drf, 1.0, 0, 0, 0, ids, ws, C.byref(have_), None)
+        return lib.spec_draft_sample(C.byref(sh), drf, 1.0, 0, 1.0, 0, 0, ids, ws, C.byref(have_), None)
 
     assert call(drf=None) == B.SV_ERR_INVALID_ARGUMENT
     assert call(ids=None) == B.SV_ERR_INVALID_ARGUMENT
@@ -203,20 +203,22 @@ def test_draft_sample_arguments(lib, B):
     assert call(ids=fake + 2) == B.SV_ERR_INVALID_ARGUMENT
     assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT
     assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
-    assert lib.spec_draft_sample(C.byref(sh), fake, 1.0, 0, 0, 0, fake, fake, None, None) == B.SV_ERR_INVALID_ARGUMENT
-    assert lib.spec_draft_sample(None, fake, 1.0, 0, 0, 0, fake, fake, C.byref(have), None) == \
+    assert lib.spec_draft_sample(C.byref(sh), fake, 1.0, 0, 1.0, 0, 0, fake, fake, None, None) == \
+        B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_draft_sample(None, fake, 1.0, 0, 1.0, 0, 0, fake, fake, C.byref(have), None) == \
         B.SV_ERR_INVALID_ARGUMENT
     # no draft rows: a valid call that launches nothing
     sh0 = _shape(B, max_draft=0, total_draft=0)
     st, need0 = _draft_query(lib, sh0)
     assert st == B.SV_OK
-    assert lib.spec_draft_sample(C.byref(sh0), None, 1.0, 0, 0, 0, None, fake,
+    assert lib.spec_draft_sample(C.byref(sh0), None, 1.0, 0, 1.0, 0, 0, None, fake,
                                  C.byref(C.c_size_t(need0)), None) == B.SV_OK
 
 
-def _lik_query(lib, sh, T=1.0, top_k=0):
+def _lik_query(lib, sh, T=1.0, top_k=0, top_p=1.0):
     need = C.c_size_t(0)
-    st = lib.spec_token_likelihood(C.byref(sh), None, None, None, T, top_k, None, None, None, None, C.byref(need),
+    st = lib.spec_token_likelihood(C.byref(sh), None, None, None, T, top_k, top_p, None, None, None, None,
+                                   C.byref(need),
                                    None)
     return st, need.value
 
@@ -241,7 +243,7 @@ def test_token_likelihood_arguments(lib, B):
     have = C.c_size_t(need)
 
     def call(tgt=fake, drf=fake, tok=fake, terms=fake, beta=fake, nll=fake, ws=fake, have_=have):
-        return lib.spec_token_likelihood(C.byref(sh), tgt, drf, tok, 1.0, 0, terms, beta, nll, ws, C.byref(have_),
+        return lib.spec_token_likelihood(C.byref(sh), tgt, drf, tok, 1.0, 0, 1.0, terms, beta, nll, ws, C.byref(have_),
                                          None)
 
     assert call(terms=None, beta=None, nll=None) == B.SV_ERR_INVALID_ARGUMENT
@@ -254,5 +256,19 @@ def test_token_likelihood_arguments(lib, B):
     assert call(beta=fake + 2) == B.SV_ERR_INVALID_ARGUMENT
     assert call(ws=fake + 64) == B.SV_ERR_INVALID_ARGUMENT
     assert call(have_=C.c_size_t(need - 1)) == B.SV_ERR_WORKSPACE_TOO_SMALL
-    assert lib.spec_token_likelihood(None, fake, fake, fake, 1.0, 0, fake, fake, fake, fake, C.byref(have),
+    assert lib.spec_token_likelihood(None, fake, fake, fake, 1.0, 0, 1.0, fake, fake, fake, fake, C.byref(have),
                                      None) == B.SV_ERR_INVALID_ARGUMENT
+
+
+def test_top_p_arguments(lib, B):
+    sh = _shape(B)
+    for q in (_query, _draft_query, _lik_query):
+        for bad in (0.0, -0.5, 1.0001, float("nan"), float("inf")):
+            assert q(lib, sh, top_p=bad)[0] == B.SV_ERR_INVALID_ARGUMENT, (q.__name__, bad)
+        st1, n1 = q(lib, sh, top_p=1.0)
+        st2, n2 = q(lib, sh, top_p=0.9)
+        assert st1 == st2 == B.SV_OK
+        # over full rows the nucleus pass adds row descriptors and kept lists
+        assert n2 > n1, q.__name__
+        st3, n3 = q(lib, sh, top_k=50, top_p=0.9)
+        assert st3 == B.SV_OK and n3 > 0

@@ -1,0 +1,130 @@
+"""Top-p (nucleus) filtering on the GPU against the oracle, through every
+call that samples: spec_verify_sample, spec_verify_argmax,
+spec_draft_sample and spec_token_likelihood (greedy ignores it: the argmax
+is always in the nucleus).  The filter follows temperature and top-k; the
+kept set is every id whose logit is >= tau_p, the largest logit value at
+which the cumulative probability from the top reaches top_p.
+
+Policy: as without top-p, except that a row whose cut lies within 1e-6 of
+top_p in cumulative probability (the oracle reports that margin) may fall
+either way on the GPU; such sequences (positions, draft rows) are counted
+and only their form is checked.
+"""
+import dataclasses
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import (compare_argmax, compare_draft, compare_greedy, compare_likelihood, compare_sample,
+                      gpu_argmax, gpu_draft, gpu_greedy, gpu_likelihood, gpu_sample, note)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_07_amd as sv
+
+    sv.load_library()
+
+
+def _with_guesses_from_q(w):
+    """Guesses drawn from q after both filters (the oracle's draft sampler, another seed)."""
+    d = oracle.draft_sample(w.draft, w.cu_draft, w.vocab, w.dtype, w.temperature, w.top_k, w.seed + 99, 0,
+                            threads=16, top_p=w.top_p)
+    return dataclasses.replace(w, draft_ids=d["ids"].astype(np.int32))
+
+
+def _all_calls(w, label):
+    o = oracle.verify_workload(w, "sample", threads=16)
+    rep = compare_sample(w, gpu_sample(w), o)
+    note(f"{label} sample: {rep}")
+    rep = compare_argmax(w, gpu_argmax(w), oracle.verify_workload(w, "argmax", threads=16))
+    note(f"{label} argmax: {rep}")
+    rows, nb = compare_draft(gpu_draft(w), oracle.verify_workload(w, "draft", threads=16))
+    note(f"{label} draft: {rows} rows, {nb} boundary draws")
+    rep = compare_likelihood(w, gpu_likelihood(w), oracle.verify_workload(w, "likelihood", threads=16))
+    note(f"{label} likelihood: {rep}")
+    return o
+
+
+@pytest.mark.parametrize("cfg,top_p", [(3, 0.9), (4, 0.9), (5, 0.9), (2, 0.93)])
+def test_workloads_with_top_p(cfg, top_p):
+    spec = dict(W.CONFIGS[cfg], top_p=top_p)
+    w = _with_guesses_from_q(W.make_workload(spec, gen_seed=cfg))
+    note(f"top-p {top_p} on workload {cfg} {w.name}: rows_t={w.rows_target} V={w.vocab} top_k={w.top_k}")
+    o = _all_calls(w, f"workload {cfg}")
+    # a sequence's margin is the smallest over its 2K+1 rows; most still compare exactly
+    assert np.mean(o["p_margin"] < 1e-6) < 0.2
+
+
+def _spec(**kw):
+    d = dict(name="topp_edge", batch=6, k=3, vocab=3001, dtype="bf16", temperature=1.0, top_k=0, kind="iid",
+             target_sigma=2.0, draft_sigma=1.0, ragged=False, modes=("sample",), top_p=0.9)
+    d.update(kw)
+    return d
+
+
+def _with_rows(w, f):
+    tf, df = f(w.target_f32().copy()), f(w.draft_f32().copy())
+    enc = {"f32": lambda x: x.astype(np.float32), "bf16": W.f32_to_bf16_bits, "f16": W.f32_to_f16_bits}[w.dtype]
+    return dataclasses.replace(w, target=enc(tf), draft=enc(df))
+
+
+EDGE = {
+    # full rows, large nuclei (past the kept-list capacity) and small ones
+    "iid_full_rows_bf16": (_spec(), None),
+    "iid_full_rows_f32": (_spec(dtype="f32"), None),           # 32-bit keys: four digit passes
+    "iid_full_rows_f16": (_spec(dtype="f16"), None),
+    "peaks_small_nucleus_f32": (_spec(kind="peaks", target_sigma=3.0, draft_sigma=1.5, dtype="f32", vocab=20000,
+                                      temperature=0.5), None),
+    "misaligned_rows_v1001": (_spec(vocab=1001), None),
+    "vocab1": (_spec(vocab=1, batch=3), None),
+    "top_p_tiny_keeps_the_maxima": (_spec(top_p=1e-6, temperature=0.5), None),
+    "top_p_0.999": (_spec(top_p=0.999), None),
+    "top_p_0.3_sharp": (_spec(top_p=0.3, temperature=0.3), None),
+    "top_k_50_then_top_p": (_spec(top_k=50, vocab=20000, kind="zipf"), None),
+    "top_k_300_exact_then_top_p": (_spec(top_k=300, vocab=20000, top_p=0.8), None),
+    "top_k_1_then_top_p": (_spec(top_k=1, top_p=0.5), None),
+    "ties_full_rows": (_spec(vocab=6000), lambda x: np.round(x * 2) / 2),
+    "ties_top50": (_spec(vocab=6000, top_k=50), lambda x: np.round(x * 2) / 2),
+    "constant_rows": (_spec(kind="flat", vocab=5000, top_p=0.5), None),
+    "neg_inf_masks": (_spec(vocab=6000), lambda x: np.where(np.arange(x.shape[1]) % 5 == 0, -np.inf, x)),
+    "zipf_ragged_T0.7": (_spec(kind="zipf", vocab=60000, batch=12, k=8, ragged=True, temperature=0.7,
+                               top_p=0.95), None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_top_p_edge_cases(name):
+    spec, f = EDGE[name]
+    w = W.make_workload(spec, gen_seed=zlib.crc32(name.encode()) % 1000)
+    if f is not None:
+        w = _with_rows(w, f)
+    w = _with_guesses_from_q(w)
+    note(f"top-p edge {name}: B={w.batch} V={w.vocab} {w.dtype} T={w.temperature} top_k={w.top_k} "
+         f"top_p={w.top_p}")
+    _all_calls(w, name)
+    compare_greedy(w, gpu_greedy(w), oracle.verify_workload(w, "greedy", threads=16))
+
+
+def test_top_p_one_matches_no_filter():
+    w = W.make_config(3)
+    a = gpu_sample(w)
+    b = gpu_sample(w, top_p=1.0)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+
+
+def test_top_p_determinism():
+    w = _with_guesses_from_q(W.make_workload(dict(W.CONFIGS[4], top_p=0.9), gen_seed=4, batch=64))
+    a = gpu_sample(w)
+    b = gpu_sample(w)
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key

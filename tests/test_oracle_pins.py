@@ -674,7 +674,8 @@ def test_top_p_is_the_smallest_high_logit_set(orc, top_k, top_p, T):
     assert base[kept & (l > lo)].sum() < top_p + 1e-12                 # minimal
     np.testing.assert_allclose(prob[kept], base[kept] / base[kept].sum(), rtol=1e-12)
     assert st["tau_p"] == lo
-    m = min(base[kept].sum() - top_p, top_p - base[kept & (l > lo)].sum())
+    above = kept & (l > lo)
+    m = min(base[kept].sum() - top_p, top_p - base[above].sum() if above.any() else np.inf)
     assert abs(st["margin"] - m) < 1e-12
     bigger, _ = orc.row_probs(l, "f32", T, top_k, top_p=min(1.0, top_p + 0.05))
     assert np.all(bigger[kept] > 0)
