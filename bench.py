@@ -20,6 +20,7 @@ Prints one JSON line:
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -71,7 +72,8 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
     """
     import csv
 
-    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else (mode + ("_topk" if "top" in workload else ""))]
+    topk = re.search(r"_top\d", workload) is not None
+    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else (mode + ("_topk" if topk else ""))]
 
     def per_dispatch(path, counter):
         vals = {}
@@ -147,6 +149,8 @@ def main():
                     help="sample / greedy / argmax: spec_verify_*; draft: spec_draft_sample over the draft rows")
     ap.add_argument("--dtype", choices=["bf16", "f16"], default=None,
                     help="store a 16-bit workload's logits in this type instead (same values before rounding)")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="nucleus filter after temperature and top-k (1 = off), for every call but greedy")
     ap.add_argument("--rotate-mb", type=float, default=512.0, help="total size of the rotated input copies")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -193,6 +197,10 @@ def main():
         w = W.make_workload(spec, args.config)
     else:
         w = W.make_config(args.config)
+    if args.top_p < 1.0:
+        import dataclasses
+
+        w = dataclasses.replace(w, top_p=args.top_p, name=f"{w.name}_topp{args.top_p:g}")
     mode = args.mode
     if mode not in ("draft", "argmax", "likelihood") and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
@@ -218,15 +226,18 @@ def main():
         drf = drf0 if (i == 0 or mode == "greedy") else drf0.clone()
         if mode == "likelihood":
             p = sv.LikelihoodPlan(tgt, drf, ids, cu_draft=cu, batch=None if cu is not None else w.batch,
-                                  temperature=w.temperature, top_k=w.top_k, max_draft=kmax, workspace=ws)
+                                  temperature=w.temperature, top_k=w.top_k, max_draft=kmax, workspace=ws,
+                                  top_p=w.top_p)
         elif mode == "draft":
             p = sv.DraftPlan(drf, cu_draft=cu, batch=None if cu is not None else w.batch, temperature=w.temperature,
-                             top_k=w.top_k, seed=w.seed, offset=w.offset, max_draft=kmax, workspace=ws)
+                             top_k=w.top_k, seed=w.seed, offset=w.offset, max_draft=kmax, workspace=ws,
+                             top_p=w.top_p)
         elif mode == "greedy":
             p = sv.GreedyPlan(tgt, ids, cu_draft=cu, max_draft=kmax, workspace=ws)
         else:
             p = sv.SamplePlan(tgt, drf, ids, cu_draft=cu, temperature=w.temperature, top_k=w.top_k, seed=w.seed,
-                              offset=w.offset, max_draft=kmax, workspace=ws, argmax=mode == "argmax")
+                              offset=w.offset, max_draft=kmax, workspace=ws, argmax=mode == "argmax",
+                              top_p=w.top_p)
         ws = p.workspace
         plans.append(p)
     torch.cuda.synchronize()
@@ -300,7 +311,7 @@ def main():
         "config": {
             "workload": w.name, "mode": mode, "batch": w.batch, "positions_per_step": w.positions(),
             "draft_tokens_per_step": w.rows_draft, "vocab": w.vocab, "input_dtype": w.dtype,
-            "temperature": w.temperature, "top_k": w.top_k, "bytes_per_step": bytes_step,
+            "temperature": w.temperature, "top_k": w.top_k, "top_p": w.top_p, "bytes_per_step": bytes_step,
             "rotated_copies": copies, "hbm_gbs_whole_step": round(bytes_step / (ms_step * 1e-3) / 1e9, 1),
             "wall_s": round(wall, 4),
         },
