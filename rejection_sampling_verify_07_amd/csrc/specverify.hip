@@ -324,6 +324,7 @@ sv::VerifyArgs base_args(const sv_shape_t* sh, const Plan& p, const sv::RowSet& 
     va.seed = seed;
     va.offset = offset;
     va.nchunk = p.nchunk;
+    va.chunk_blocks = sv::kThreads * p.loads;
     return va;
 }
 

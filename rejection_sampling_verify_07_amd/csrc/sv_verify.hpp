@@ -51,6 +51,7 @@ struct VerifyArgs {
     // statistics source: chunk partials (no top-k) or row descriptors (top-k)
     const PartialFull* partials;
     int32_t nchunk;
+    int32_t chunk_blocks;  // aligned 16-byte blocks per chunk of the streaming pass
     const RowDesc* descs;
     const KeptEntry* kept;
     // outputs
@@ -387,7 +388,181 @@ __device__ void argmax_full(const char* ra, const char* rb, int32_t vocab, const
     *total = z;
 }
 
-// The new token of a sequence (all threads call it; all get the result):
+// Inverse CDF of p over a full row that starts at the chunk holding the
+// crossing instead of walking the row: the streaming pass's chunk sums,
+// rescaled to the row maximum and normalised like the weights
+// (W_c = S_c 2^(mcc_c - mcc) fl32(1/S), fp64, ascending chunks), locate the
+// first chunk whose running mass exceeds u times their total; only its ids
+// are read (one block per thread or two), their fp32 weights scanned in fp64
+// from the mass before the chunk.  If rounding leaves the crossing past the
+// chunk, the walk moves on to the next one; past the last chunk the full
+// walk decides.  All threads call it; all get the token.
+template <int DT, int NT>
+__device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32_t nchunk, int32_t chunk_blocks,
+                                   int32_t vocab, const BonusW& wfn, double u, DrawLds<NT>& L, int32_t* token,
+                                   double* total)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int ES = Dt<DT>::kSize;
+    constexpr int NW = NT / kWave;
+    auto chunk_mass = [&](int32_t ch) {
+        double w = 0.0;
+        if (ch < nchunk) {
+            const PartialFull q = pp[ch];
+            if (q.s > 0.0) w = q.s * exp2((double)q.mcc - (double)wfn.mcc_t) * (double)wfn.inv_t;
+        }
+        return w;
+    };
+    // the first chunk whose running mass exceeds u * total (wave 0), and the mass before it
+    if (wave_id() == 0) {
+        double tot = 0.0;
+        for (int32_t c0 = 0; c0 < nchunk; c0 += kWave) tot += chunk_mass(c0 + lane_id());
+        tot = wave_sum_dpp(tot);
+        const double t = u * tot;
+        double carry = 0.0;
+        int32_t found = -1;
+        double before = 0.0;
+        for (int32_t c0 = 0; c0 < nchunk && found < 0; c0 += kWave) {
+            const int32_t ch = c0 + lane_id();
+            const double w = chunk_mass(ch);
+            const double incl = carry + wave_incl_scan_dpp(w);
+            const uint64_t m = __ballot(ch < nchunk && incl > t);
+            if (m != 0) {
+                const int src = __builtin_ctzll(m);
+                found = c0 + src;
+                before = readlane_f64(incl - w, src);
+            }
+            carry = readlane_f64(incl, kWave - 1);
+        }
+        if (lane_id() == 0) {
+            L.i[0] = found;
+            L.dd[0] = before;
+            L.dd[1] = tot;
+        }
+    }
+    __syncthreads();
+    int32_t ch = L.i[0];
+    double before = L.dd[0];
+    const double tot = L.dd[1];
+    const double t = u * tot;
+    __syncthreads();
+    const uintptr_t addr = (uintptr_t)row;
+    const int32_t mis = (int32_t)((addr & 15u) / ES);
+    const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
+    const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
+    const int32_t bpt = (chunk_blocks + NT - 1) / NT;  // blocks per thread
+    if (bpt > 2) {  // chunks longer than two blocks per thread: walk the row
+        inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, token, total);
+        return;
+    }
+    int32_t tok = -1;
+    for (; ch >= 0 && ch < nchunk; ++ch) {
+        // this thread's blocks of the chunk, ascending with the thread index
+        const int32_t j0 = ch * chunk_blocks + (int32_t)threadIdx.x * bpt;
+        float w[2 * VEC];
+        double ls = 0.0;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int32_t j = j0 + q;
+            const bool in = q < bpt && j < nblk && j < (ch + 1) * chunk_blocks;
+            const u32x4 raw = in ? load16<false>(base + j) : u32x4{0u, 0u, 0u, 0u};
+            float f[VEC];
+            unpack<DT>(raw, f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int32_t r = j * VEC - mis + e;
+                w[q * VEC + e] = (in && r >= 0 && r < vocab) ? wfn(f[e], 0.0f) : 0.0f;
+                ls += (double)w[q * VEC + e];
+            }
+        }
+        // exclusive scan of the thread sums in thread order (fp64)
+        const double incl = wave_incl_scan_dpp(ls);
+        if (lane_id() == kWave - 1) L.wd[wave_id()] = incl;
+        if (threadIdx.x == 0) L.i[1] = INT32_MAX;
+        __syncthreads();
+        double off = before;
+        double chunk_sum = 0.0;
+#pragma unroll
+        for (int wv = 0; wv < NW; ++wv) {
+            if (wv < wave_id()) off += L.wd[wv];
+            chunk_sum += L.wd[wv];
+        }
+        double cum = off + wave_prev_dpp(incl);
+        int32_t hit = INT32_MAX;
+#pragma unroll
+        for (int k = 0; k < 2 * VEC; ++k) {
+            cum += (double)w[k];
+            const int32_t r = (j0 + k / VEC) * VEC - mis + (k % VEC);
+            if (hit == INT32_MAX && w[k] > 0.0f && cum > t) hit = r;
+        }
+        if (hit != INT32_MAX) atomicMin(&L.i[1], hit);
+        __syncthreads();
+        tok = L.i[1];
+        __syncthreads();
+        if (tok != INT32_MAX) break;
+        before += chunk_sum;
+        tok = -1;
+    }
+    if (tok < 0 || tok == INT32_MAX) {
+        inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, token, total);
+        return;
+    }
+    *token = tok;
+    *total = tot;
+}
+
+// The argmax of p over a full row: the lowest index of the row maximum, found
+// in the first chunk whose partial maximum equals it (logits compare exactly,
+// and p is increasing in the logit).  All threads call it.
+template <int DT, int NT>
+__device__ int32_t argmax_chunks(const char* row, const PartialFull* pp, int32_t nchunk, int32_t chunk_blocks,
+                                 int32_t vocab, DrawLds<NT>& L)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int ES = Dt<DT>::kSize;
+    if (wave_id() == 0) {
+        float m = neg_inf();
+        for (int32_t c0 = lane_id(); c0 < nchunk; c0 += kWave) m = fmaxf(m, pp[c0].m);
+        m = wave_max_dpp(m);
+        int32_t first = INT32_MAX;
+        for (int32_t c0 = lane_id(); c0 < nchunk; c0 += kWave)
+            if (pp[c0].m == m) first = min(first, c0);
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o, kWave));
+        if (lane_id() == 0) {
+            L.i[0] = first;
+            L.bv[0] = m;
+            L.i[1] = INT32_MAX;
+        }
+    }
+    __syncthreads();
+    const int32_t ch = L.i[0];
+    const float m = L.bv[0];
+    if (ch != INT32_MAX) {
+        const uintptr_t addr = (uintptr_t)row;
+        const int32_t mis = (int32_t)((addr & 15u) / ES);
+        const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
+        const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
+        for (int32_t j = ch * chunk_blocks + (int32_t)threadIdx.x; j < min(nblk, (ch + 1) * chunk_blocks); j += NT) {
+            float f[VEC];
+            unpack<DT>(load16<false>(base + j), f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int32_t r = j * VEC - mis + e;
+                if (r >= 0 && r < vocab && f[e] == m) {
+                    atomicMin(&L.i[1], r);
+                    break;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int32_t tok = L.i[1];
+    __syncthreads();
+    return tok == INT32_MAX ? -1 : tok;
+}
+
+// The new token of a sequence (all threads call it; all get the result):// The new token of a sequence (all threads call it; all get the result):
 // at the first rejection n < kb the residual max(0, p_n - q_n), else p_kb --
 // drawn by the inverse CDF with u (U(b, n, 1), or U(b, kb, 2)), or, with
 // a.argmax_draw, its argmax.  rt / rd: statistics of target row n and draft
@@ -416,6 +591,10 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
             }
             __syncthreads();
             *tok = L.i[2];
+        } else if (!FROM_DESC) {
+            const PartialFull* pp = a.partials + kept_row_n * a.nchunk;
+            if (a.argmax_draw) *tok = argmax_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, L);
+            else inverse_cdf_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, bw, u, L, tok, &zz);
         } else if (a.argmax_draw) {
             argmax_full<DT, false, NT>(trow, nullptr, a.vocab, bw, L, tok, &zz);
         } else {
@@ -639,6 +818,10 @@ __global__ __launch_bounds__(NT) void draft_draw_kernel(VerifyArgs a)
         }
         __syncthreads();
         token = s_tok;
+    } else if (!FROM_DESC) {
+        const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+        inverse_cdf_chunks<DT, NT>(row_ptr(a.rs, row), a.partials + (int64_t)row * a.nchunk, a.nchunk,
+                                   a.chunk_blocks, a.vocab, bw, u, s_draw, &token, &z);
     } else {
         const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
         inverse_cdf_full<DT, false, NT>(row_ptr(a.rs, row), nullptr, a.vocab, bw, u, s_draw.seg, s_draw.wd, s_draw.i,
