@@ -11,12 +11,13 @@
 //  - a row with a kept list (<= 1024 ids) is done by wave 0 in registers: a
 //    bitwise radix search on the select key, one wave-wide fp64 sum of the
 //    fp32 weights per bit (fixed order), then an order-keeping compaction;
-//  - a full row (no top-k, or a kept set that outgrew its list) takes a
-//    radix select over the whole row weighted by mass: per 8-bit digit, a
-//    256-bucket histogram of the weights in 2^-43 fixed point (integer LDS
-//    atomics, so the sums are exact and the result deterministic), then one
-//    last pass that sums the kept weights and writes the kept list when it
-//    fits.
+//  - a full row (no top-k, or a kept set that outgrew its list) takes three
+//    reads of the row: a histogram of its weights over log-weight buckets,
+//    which finds the bucket where the mass from the top reaches top_p; the
+//    entries of that bucket staged in LDS and resolved by a mass-weighted
+//    radix select; a last pass that sums the kept weights and writes the kept
+//    list when it fits.  Weights are summed in 2^-43 fixed point with integer
+//    LDS atomics, so the sums are exact and the result deterministic.
 #pragma once
 
 #include "sv_common.hpp"
@@ -125,29 +126,19 @@ __device__ void nucleus_list(const NucArgs& a, int32_t row, const RowDesc& d)
     }
 }
 
-// Full rows (kept set = {l >= d.tau}): the whole workgroup.
-template <int DT>
-__device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, uint64_t* s_hist, uint64_t* s_u,
-                             int32_t* s_w, double* s_d)
+// Mass-weighted radix select: the largest radix key h with
+// sum{w : key >= h} >= need over the (key, fixed-point weight) pairs that
+// visit(fn) presents, 8-bit digits from the top down to `low`.  All threads
+// call it; integer sums make it exact and independent of visiting order.
+template <class Visit>
+__device__ uint32_t mass_radix(Visit&& visit, uint64_t need, int low, uint64_t* s_hist, uint64_t* s_u)
 {
-    constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
-    const char* rowp = row_ptr(a.rs, row);
-    const float tau = d.tau, mcc = d.mcc, c = a.c;
-    auto fixw = [&](float l) {
-        return (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc)) * kFixScale + 0.5);
-    };
     uint32_t prefix = 0, pmask = 0;
-    uint64_t need = 0;  // fixed-point mass still to reach inside the current prefix
-    for (int shift = 24; shift >= LOW; shift -= 8) {
+    for (int shift = 24; shift >= low; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
         __syncthreads();
-        for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
-#pragma unroll
-            for (int e = 0; e < Dt<DT>::kVec; ++e) {
-                const uint32_t k = nuc_key<DT>(f[e]);
-                if (ok[e] && f[e] >= tau && (k & pmask) == prefix)
-                    atomicAdd((unsigned long long*)&s_hist[(k >> shift) & 255u], (unsigned long long)fixw(f[e]));
-            }
+        visit([&](uint32_t k, uint64_t w) {
+            if ((k & pmask) == prefix) atomicAdd((unsigned long long*)&s_hist[(k >> shift) & 255u], (unsigned long long)w);
         });
         __syncthreads();
         if (wave_id() == 0) {
@@ -160,12 +151,6 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, ui
                 lsum += h4[q];
             }
             const uint64_t incl = wave_incl_scan_u64(lsum);
-            const uint64_t total = (uint64_t)__shfl((long long)incl, kWave - 1, kWave);
-            if (shift == 24) {
-                // the whole kept mass is in the first histogram: the fixed-point target
-                need = (uint64_t)((double)a.top_p * (double)total);
-                if (need == 0) need = 1;  // at least the maximum is kept
-            }
             const uint64_t excl = incl - lsum;
             int found = -1;
             uint64_t above = 0;
@@ -186,7 +171,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, ui
                 found = __shfl(found, src, kWave);
                 above = (uint64_t)__shfl((long long)above, src, kWave);
             } else {
-                found = 0;  // rounding only: keep everything under this prefix
+                found = 0;  // not reached (need <= the visited mass)
                 above = 0;
             }
             if (l == 0) {
@@ -200,7 +185,149 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, ui
         need = s_u[1];
         __syncthreads();
     }
-    // the threshold value: the largest logit whose key has this prefix
+    return prefix;
+}
+
+constexpr int kNucBuckets = 256;   // log-weight buckets of 1/8 bit below the row maximum
+constexpr int kNucCap = 2048;      // entries of the crossing bucket staged in LDS
+
+struct NucLds {
+    uint64_t hist[256];
+    uint64_t u[4];
+    int32_t w[kWaves];
+    double d[kWaves];
+    uint32_t ck[kNucCap];
+    uint64_t cw[kNucCap];
+    int32_t n;
+};
+
+// The crossing bucket's radix select straight from the row, for a bucket
+// too large to stage in LDS (kept out of line: it is rare and register-hungry).
+template <int DT>
+__device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* rowp, int32_t vocab, float tau,
+                                                                    float mcc, float c, uint32_t bstar,
+                                                                    uint64_t need, uint64_t* s_hist, uint64_t* s_u)
+{
+    constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
+    return mass_radix(
+        [&](auto&& fn) {
+            for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+#pragma unroll
+                for (int e = 0; e < Dt<DT>::kVec; ++e) {
+                    const float x = -__builtin_fmaf(f[e], c, -mcc) * 8.0f;
+                    const uint32_t b = (uint32_t)fminf(fmaxf(x, 0.0f), (float)(kNucBuckets - 1));
+                    if (ok[e] && f[e] >= tau && b == bstar)
+                        fn(nuc_key<DT>(f[e]),
+                           (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc)) * kFixScale +
+                                      0.5));
+                }
+            });
+        },
+        need, LOW, s_hist, s_u);
+}
+
+// Full rows (kept set = {l >= d.tau}): the whole workgroup.  First a
+// histogram of the fixed-point weights over log-weight buckets (bucket =
+// floor(8 (m - l) c), the last one open-ended): it spreads a row over many
+// buckets, so the integer LDS atomics rarely collide, and it finds the
+// bucket where the mass from the top reaches top_p.  The bucket is
+// monotone in the logit, so every higher bucket is kept whole and every lower
+// one dropped.  Its own entries (a small share of the row) are staged in LDS
+// by a second read and resolved by a mass-weighted radix select there; if
+// they do not fit, the radix select reads the row instead.
+template <int DT>
+__device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, NucLds& S)
+{
+    constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
+    const char* rowp = row_ptr(a.rs, row);
+    const float tau = d.tau, mcc = d.mcc, c = a.c;
+    auto fixw = [&](float l) {
+        return (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc)) * kFixScale + 0.5);
+    };
+    auto bucket = [&](float l) {
+        const float e = -__builtin_fmaf(l, c, -mcc) * 8.0f;  // 8 (m - l) c >= 0 up to rounding
+        return (uint32_t)fminf(fmaxf(e, 0.0f), (float)(kNucBuckets - 1));
+    };
+    // 1. log-weight histogram
+    for (int i = threadIdx.x; i < kNucBuckets; i += kThreads) S.hist[i] = 0;
+    if (threadIdx.x == 0) S.n = 0;
+    __syncthreads();
+    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e)
+            if (ok[e] && f[e] >= tau)
+                atomicAdd((unsigned long long*)&S.hist[bucket(f[e])], (unsigned long long)fixw(f[e]));
+    });
+    __syncthreads();
+    if (wave_id() == 0) {
+        // ascending buckets = descending weights; lane L holds buckets 4L .. 4L+3
+        const int l = lane_id();
+        uint64_t h4[4], lsum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h4[q] = S.hist[4 * l + q];
+            lsum += h4[q];
+        }
+        const uint64_t incl = wave_incl_scan_u64(lsum);
+        const uint64_t total = (uint64_t)__shfl((long long)incl, kWave - 1, kWave);
+        uint64_t need = (uint64_t)((double)a.top_p * (double)total);
+        if (need == 0) need = 1;  // at least the maximum is kept
+        const uint64_t excl = incl - lsum;
+        int found = -1;
+        uint64_t above = 0;
+        if (excl < need && incl >= need) {
+            uint64_t cum = excl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (found < 0 && cum + h4[q] >= need) {
+                    found = 4 * l + q;
+                    above = cum;
+                }
+                cum += h4[q];
+            }
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        const int src = bal != 0 ? __builtin_ctzll(bal) : 0;
+        found = bal != 0 ? __shfl(found, src, kWave) : kNucBuckets - 1;
+        above = bal != 0 ? (uint64_t)__shfl((long long)above, src, kWave) : 0;
+        if (l == 0) {
+            S.u[0] = (uint64_t)found;
+            S.u[1] = need - above;
+        }
+    }
+    __syncthreads();
+    const uint32_t bstar = (uint32_t)S.u[0];
+    const uint64_t need_b = S.u[1];
+    __syncthreads();
+
+    // 2. the crossing bucket's entries into LDS
+    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) {
+            if (ok[e] && f[e] >= tau && bucket(f[e]) == bstar) {
+                const int32_t slot = atomicAdd(&S.n, 1);
+                if (slot < kNucCap) {
+                    S.ck[slot] = nuc_key<DT>(f[e]);
+                    S.cw[slot] = fixw(f[e]);
+                }
+            }
+        }
+    });
+    __syncthreads();
+    const int32_t nb = S.n;
+    uint32_t prefix;
+    if (nb <= kNucCap) {
+        prefix = mass_radix(
+            [&](auto&& fn) {
+                for (int32_t i = threadIdx.x; i < nb; i += kThreads) fn(S.ck[i], S.cw[i]);
+            },
+            need_b, LOW, S.hist, S.u);
+    } else {
+        prefix = nucleus_bucket_radix<DT>(rowp, a.vocab, tau, mcc, c, bstar, need_b, S.hist, S.u);
+    }
+    int32_t* s_w = S.w;
+    double* s_d = S.d;
+    // the threshold value: the logit whose key has this prefix
     if constexpr (LOW > 0) prefix |= 0xffffu;
     const float tau_p = fmaxf(nuc_value<DT>(prefix), tau);
 
@@ -239,10 +366,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, ui
 template <int DT, bool FROM_DESC>
 __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
 {
-    __shared__ uint64_t s_hist[256];
-    __shared__ uint64_t s_u[2];
-    __shared__ int32_t s_w[kWaves];
-    __shared__ double s_d[kWaves];
+    __shared__ NucLds s_nuc;
     __shared__ RowDesc s_desc;
     const int32_t row = blockIdx.x;
     if constexpr (FROM_DESC) {
@@ -283,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
     if (d.kept >= 0) {
         if (wave_id() == 0) nucleus_list<DT>(a, row, d);
     } else {
-        nucleus_full<DT>(a, row, d, s_hist, s_u, s_w, s_d);
+        nucleus_full<DT>(a, row, d, s_nuc);
     }
 }
 
