@@ -164,9 +164,9 @@ def main():
     if args.record_traffic:
         import workloads as W
 
-        name = W.CONFIGS[args.config]["name"]
+        name = W.WORKLOADS[args.config]["name"]
         if args.dtype is not None:
-            name = name.replace(W.CONFIGS[args.config]["dtype"], args.dtype)
+            name = name.replace(W.WORKLOADS[args.config]["dtype"], args.dtype)
         rec = record_traffic(name, args.mode, args.record_traffic[0], args.record_traffic[1],
                              args.copy_calibration_mb or 256.0)
         print(json.dumps(rec))
@@ -174,7 +174,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU; the verify step shards by sequence with no exchange "
+        print("bench.py measures one GPU; the verify step shards by sequence with no exchange "
               "across GPUs, so a single-GPU figure is the measured one and no multi-GPU figure is produced", file=sys.stderr)
         sys.exit(2)
 
@@ -188,12 +188,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
-    if args.dtype is not None and W.CONFIGS[args.config]["dtype"] != args.dtype:
-        if W.CONFIGS[args.config]["dtype"] == "f32":
+    if args.dtype is not None and W.WORKLOADS[args.config]["dtype"] != args.dtype:
+        if W.WORKLOADS[args.config]["dtype"] == "f32":
             print("--dtype applies to the 16-bit workloads (3, 4, 5)", file=sys.stderr)
             sys.exit(2)
-        spec = dict(W.CONFIGS[args.config], dtype=args.dtype)
-        spec["name"] = spec["name"].replace(W.CONFIGS[args.config]["dtype"], args.dtype)
+        spec = dict(W.WORKLOADS[args.config], dtype=args.dtype)
+        spec["name"] = spec["name"].replace(W.WORKLOADS[args.config]["dtype"], args.dtype)
         w = W.make_workload(spec, args.config)
     else:
         w = W.make_config(args.config)

@@ -36,7 +36,7 @@ def _oracle(w, mode="sample"):
 
 
 def _f16_config(n):
-    spec = dict(W.CONFIGS[n])
+    spec = dict(W.WORKLOADS[n])
     spec["dtype"] = "f16"
     spec["name"] = spec["name"].replace("bf16", "f16")
     return W.make_workload(spec, gen_seed=n)

@@ -56,7 +56,7 @@ def _all_calls(w, label):
 
 @pytest.mark.parametrize("cfg,top_p", [(3, 0.9), (4, 0.9), (5, 0.9), (2, 0.93)])
 def test_workloads_with_top_p(cfg, top_p):
-    spec = dict(W.CONFIGS[cfg], top_p=top_p)
+    spec = dict(W.WORKLOADS[cfg], top_p=top_p)
     w = _with_guesses_from_q(W.make_workload(spec, gen_seed=cfg))
     note(f"top-p {top_p} on workload {cfg} {w.name}: rows_t={w.rows_target} V={w.vocab} top_k={w.top_k}")
     o = _all_calls(w, f"workload {cfg}")
@@ -123,7 +123,7 @@ def test_top_p_one_matches_no_filter():
 
 
 def test_top_p_determinism():
-    w = _with_guesses_from_q(W.make_workload(dict(W.CONFIGS[4], top_p=0.9), gen_seed=4, batch=64))
+    w = _with_guesses_from_q(W.make_workload(dict(W.WORKLOADS[4], top_p=0.9), gen_seed=4, batch=64))
     a = gpu_sample(w)
     b = gpu_sample(w)
     for key in a:

@@ -466,7 +466,7 @@ def test_argmax_variant_residual_and_extra_token_vs_numpy(orc):
     """At a rejection the token is numpy's argmax of max(0, p_n - q_n) with p
     and q from scipy's softmax; when every guess passes it is numpy's argmax
     of p_K.  Acceptance counts equal the sampling variant's (same uniforms)."""
-    w = W.make_workload(dict(W.CONFIGS[2], name="argmax_pin"), gen_seed=3, batch=24)
+    w = W.make_workload(dict(W.WORKLOADS[2], name="argmax_pin"), gen_seed=3, batch=24)
     a = orc.verify_workload(w, "argmax", threads=8)
     s = orc.verify_workload(w, "sample", threads=8)
     assert np.array_equal(a["num_accepted"], s["num_accepted"])
@@ -489,7 +489,7 @@ def test_argmax_variant_residual_and_extra_token_vs_numpy(orc):
 
 
 def test_argmax_variant_draft_equals_target(orc):
-    w = W.make_workload(dict(W.CONFIGS[1], name="argmax_eq", batch=6), gen_seed=4)
+    w = W.make_workload(dict(W.WORKLOADS[1], name="argmax_eq", batch=6), gen_seed=4)
     a = orc.verify_argmax(w.target, w.target[np.concatenate([np.arange(w.cu_draft[b] + b, w.cu_draft[b + 1] + b)
                                                             for b in range(w.batch)])],
                           w.draft_ids, w.cu_draft, w.vocab, w.dtype, w.temperature, 0, 0, 0)

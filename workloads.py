@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "Workload",
-    "CONFIGS",
+    "WORKLOADS",
     "make_config",
     "make_workload",
     "f32_to_bf16_bits",
@@ -156,7 +156,7 @@ class Workload:
 # --------------------------------------------------------------------------
 # The five named workloads
 # --------------------------------------------------------------------------
-CONFIGS = {
+WORKLOADS = {
     1: dict(
         name="tiny_b1_k4_v1000_f32",
         batch=1, k=4, vocab=1000, dtype="f32", temperature=1.0, top_k=0,
@@ -266,7 +266,7 @@ def make_workload(
     draft_lens: Optional[Sequence[int]] = None,
     threads: Optional[int] = None,
 ) -> Workload:
-    """Build a workload from a spec dict (see CONFIGS for the keys).
+    """Build a workload from a spec dict (see WORKLOADS for the keys).
 
     batch overrides spec["batch"] (the first `batch` sequences are the same
     as in the full batch).  draft_lens, when given, fixes K_b per sequence.
@@ -336,4 +336,4 @@ def make_workload(
 
 def make_config(n: int, batch: Optional[int] = None, gen_seed: Optional[int] = None, **kw) -> Workload:
     """Workload n (1..5); the generator seed defaults to n."""
-    return make_workload(CONFIGS[n], gen_seed if gen_seed is not None else n, batch=batch, **kw)
+    return make_workload(WORKLOADS[n], gen_seed if gen_seed is not None else n, batch=batch, **kw)
