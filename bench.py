@@ -129,6 +129,15 @@ def cpu_baseline(w, mode, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    # the same oracle on one host core (at least one full batch, about half the time above)
+    t1 = time.perf_counter()
+    reps1 = 0
+    while True:
+        oracle.verify_workload(w, mode, threads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t1
+        if el1 >= seconds / 2:
+            break
     return {
         "value": reps * units / el,
         "unit": unit,
@@ -136,6 +145,8 @@ def cpu_baseline(w, mode, seconds):
         "kind": "oracle",
         "sample": f"the full batch of the same workload ({w.batch} sequences, {units} {unit[:-2]}), "
                   f"{reps} repetitions in {el:.1f} s, sequences split over {threads} host threads",
+        "single_core": {"value": reps1 * units / el1, "cores": 1,
+                        "sample": f"the same batch, {reps1} repetitions in {el1:.1f} s on one thread"},
     }
 
 
