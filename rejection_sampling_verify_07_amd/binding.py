@@ -108,10 +108,14 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _rows(t: torch.Tensor, name: str):
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2:
         raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU")
+    if t.numel() == 0:
+        return t.shape[1]  # no element is read; an empty tensor may report stride 0
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
     return t.stride(0)
 
 
