@@ -133,6 +133,19 @@ __device__ __forceinline__ float key_to_float(uint32_t k)
     return __uint_as_float(b);
 }
 
+// fp32 maximum of three with no NaN canonicalisation of the inputs.  The
+// instruction ignores a quiet NaN operand and, in IEEE mode, turns a
+// signalling one into a quiet NaN result; callers pass only finite values,
+// -inf and quiet NaN fill patterns, so the result is the plain maximum of
+// the non-NaN operands.  (fmaxf quiets every operand first: one extra
+// instruction per input.)
+__device__ __forceinline__ float max3_quiet(float a, float b, float c)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // ---------------------------------------------------------------------------
 // Wave primitives (64 lanes).  Reductions run a fixed butterfly, so the
 // result is the same on every run; consumers take lane 0's copy.
@@ -230,6 +243,24 @@ __device__ __forceinline__ float wave_max_dpp(float v)
     v = fmaxf(v, __int_as_float(dpp_mov<kDppBcast15, 0xa>(ninf, __float_as_int(v))));
     v = fmaxf(v, __int_as_float(dpp_mov<kDppBcast31, 0xc>(ninf, __float_as_int(v))));
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
+// Wave-wide unsigned max and min, both returned wave-uniform (lane 63).
+__device__ __forceinline__ void wave_umax_umin_dpp(uint32_t& mx, uint32_t& mn)
+{
+    int a = (int)mx, b = (int)mn;
+#define SV_UMM_STEP(CTRL, RM)                                               \
+    a = (int)max((uint32_t)a, (uint32_t)dpp_mov<CTRL, RM>(0, a));           \
+    b = (int)min((uint32_t)b, (uint32_t)dpp_mov<CTRL, RM>(-1, b));
+    SV_UMM_STEP(kDppQuad1032, 0xf)
+    SV_UMM_STEP(kDppQuad2301, 0xf)
+    SV_UMM_STEP(kDppHalfMirror, 0xf)
+    SV_UMM_STEP(kDppMirror, 0xf)
+    SV_UMM_STEP(kDppBcast15, 0xa)
+    SV_UMM_STEP(kDppBcast31, 0xc)
+#undef SV_UMM_STEP
+    mx = (uint32_t)__builtin_amdgcn_readlane(a, kWave - 1);
+    mn = (uint32_t)__builtin_amdgcn_readlane(b, kWave - 1);
 }
 
 template <int CTRL, int ROW_MASK = 0xf>

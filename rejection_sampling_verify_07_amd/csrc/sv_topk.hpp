@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
         // Edge tiles (a block reaching outside the row) first overwrite the
         // out-of-row slots of their raw words with a NaN pattern: NaN is never
-        // selected and fmaxf ignores it, so one body serves every tile.
+        // selected and the maximum ignores it, so one body serves every tile.
         const bool interior = t.cb0 * VEC >= t.mis && (t.cb0 + kThreads * LOADS) * VEC <= t.mis + vocab;
         u32x4* rw = raw;
         if (!interior) {
@@ -239,11 +239,13 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t w = raw[i][q];
                     if constexpr (BF) {
-                        tm = fmaxf(tm, fmaxf(__uint_as_float(w << 16), __uint_as_float(w)));
+                        // both elements exactly: the raw word would be a
+                        // signalling NaN for a -inf high element
+                        tm = max3_quiet(tm, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
                     } else if constexpr (H16) {
-                        tm = fmaxf(tm, fmaxf(lo16<DT>(w), hi16<DT>(w)));
-                    } else {
-                        tm = fmaxf(tm, __uint_as_float(w));
+                        tm = max3_quiet(tm, lo16<DT>(w), hi16<DT>(w));
+                    } else if (q & 1) {
+                        tm = max3_quiet(tm, __uint_as_float(raw[i][q - 1]), __uint_as_float(w));
                     }
                 }
             }
@@ -267,14 +269,10 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             // are common to all 256 keys: start the select below them
             uint32_t kmax = max(max(k4[0], k4[1]), max(k4[2], k4[3]));
             uint32_t kmin = min(min(k4[0], k4[1]), min(k4[2], k4[3]));
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, kWave));
-                kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, kWave));
-            }
-            const uint32_t diff = __builtin_amdgcn_readfirstlane(kmax ^ kmin);
+            wave_umax_umin_dpp(kmax, kmin);
+            const uint32_t diff = kmax ^ kmin;
             const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
-            uint32_t h = __builtin_amdgcn_readfirstlane(kmax) & ~((2u << top) - 1u);  // the common prefix
+            uint32_t h = kmax & ~((2u << top) - 1u);  // the common prefix
             for (int bit = top; bit >= 0; --bit) {
                 const uint32_t cand = h | (1u << bit);
                 int cnt = 0;
