@@ -221,12 +221,15 @@ __device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int
     select_tail<DT>(row, top_k, c, descs, kept, L, e, nj);
 }
 
-// Speculative path for rows of at most kSpecChunks chunks whose chunks hold at
-// most kSpecSlots * 64 candidates each: the counts, the chunk bounds and the
-// first kSpecSlots * 64 slots of every chunk are loaded at once.  Every chunk
-// bound is a lower bound of the row's tau, so only candidates >= their
-// maximum can be kept; those few are compacted (in LDS) before the select.
-// Returns false, having written nothing, when the row does not qualify.
+// Speculative path.  Every chunk bound is a lower bound of the row's tau, so
+// only candidates >= their maximum can be kept; those few are compacted (in
+// LDS, in chunk order) before the select.  The counts and bounds are read
+// first (one lane per chunk, 64 chunks per round); the candidate slots then
+// follow in batches of kSpecChunks chunks, the first kSpecSlots * 64 slots
+// of each chunk loaded at once (a row of at most kSpecChunks chunks whose
+// counts fit those slots takes a single batch), and the rare slots past them
+// one load round at a time.  Returns false, having written nothing, when a
+// chunk overflowed or the survivors do not fit the kept list.
 constexpr int kSpecChunks = 16;
 constexpr int kSpecSlots = 2;
 
@@ -253,8 +256,9 @@ __device__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int
 {
     const int lane = lane_id();
     const int64_t t0 = (int64_t)row * nchunk;
-    const int32_t cnt_l = lane < nchunk ? counts[t0 + lane] : 0;
-    const float bnd_l = lane < nchunk ? bounds[t0 + lane] : neg_inf();
+    int32_t cnt_l = lane < nchunk ? counts[t0 + lane] : 0;  // chunk `lane` of the first 64
+    float bnd_l = lane < nchunk ? bounds[t0 + lane] : neg_inf();
+    // the first batch of candidate slots in flight with the counts and bounds
     KeptEntry e[kSpecChunks][kSpecSlots];
 #pragma unroll
     for (int ch = 0; ch < kSpecChunks; ++ch) {
@@ -263,26 +267,55 @@ __device__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int
             e[ch][q] = ch < nchunk ? cands[(t0 + ch) * cap + q * kWave + lane] : KeptEntry{INT32_MAX, neg_inf()};
         }
     }
-    if (__ballot(cnt_l > kSpecSlots * kWave) != 0) return false;
+    bool over = cnt_l > cap;
+    for (int32_t g = kWave; g < nchunk; g += kWave) {
+        const int32_t ch = g + lane;
+        if (ch < nchunk) {
+            over |= counts[t0 + ch] > cap;
+            bnd_l = fmaxf(bnd_l, bounds[t0 + ch]);
+        }
+    }
+    if (__ballot(over) != 0) return false;
     const float bmax = wave_max_dpp(bnd_l);
 
     // survivors (candidate >= the largest chunk bound), compacted in chunk order
     int32_t ns = 0;
+    auto keep = [&](const KeptEntry& x, bool valid) {
+        const bool pred = valid && x.val >= bmax;
+        const uint64_t m = __ballot(pred);
+        if (m != 0) {
+            const int32_t pos = ns + lanes_below(m);
+            if (pred && pos < kKeepCapList) {
+                L.kidx[pos] = x.idx;
+                L.kval[pos] = x.val;
+            }
+            ns += (int32_t)__popcll(m);
+        }
+    };
+    int32_t cnt_b = cnt_l;  // lane ch: the count of chunk c0 + ch
+    for (int32_t c0 = 0; c0 < nchunk; c0 += kSpecChunks) {
+        if (c0 > 0) {
 #pragma unroll
-    for (int ch = 0; ch < kSpecChunks; ++ch) {
-        if (ch < nchunk) {
-            const int32_t cnt = __builtin_amdgcn_readlane(cnt_l, ch);
+            for (int ch = 0; ch < kSpecChunks; ++ch) {
 #pragma unroll
-            for (int q = 0; q < kSpecSlots; ++q) {
-                const bool pred = q * kWave + lane < cnt && e[ch][q].val >= bmax;
-                const uint64_t m = __ballot(pred);
-                if (m != 0) {
-                    const int32_t pos = ns + lanes_below(m);
-                    if (pred && pos < kKeepCapList) {
-                        L.kidx[pos] = e[ch][q].idx;
-                        L.kval[pos] = e[ch][q].val;
-                    }
-                    ns += (int32_t)__popcll(m);
+                for (int q = 0; q < kSpecSlots; ++q) {
+                    e[ch][q] = c0 + ch < nchunk ? cands[(t0 + c0 + ch) * cap + q * kWave + lane]
+                                                : KeptEntry{INT32_MAX, neg_inf()};
+                }
+            }
+            cnt_b = lane < kSpecChunks && c0 + lane < nchunk ? counts[t0 + c0 + lane] : 0;
+        }
+#pragma unroll
+        for (int ch = 0; ch < kSpecChunks; ++ch) {
+            if (c0 + ch < nchunk) {
+                const int32_t cnt = __builtin_amdgcn_readlane(cnt_b, ch);
+#pragma unroll
+                for (int q = 0; q < kSpecSlots; ++q) keep(e[ch][q], q * kWave + lane < cnt);
+                // slots past the first batch (at most cap), one round of loads each
+                for (int32_t q = kSpecSlots; q * kWave < cnt; ++q) {
+                    const int32_t i = q * kWave + lane;
+                    const KeptEntry x = i < cnt ? cands[(t0 + c0 + ch) * cap + i] : KeptEntry{INT32_MAX, neg_inf()};
+                    keep(x, i < cnt);
                 }
             }
         }
@@ -462,8 +495,7 @@ __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int3
     __shared__ WaveSelLds L;
     __shared__ int32_t s_choff[kMaxChunks + 1];
     const int32_t row = blockIdx.x;
-    if (use_cands != 0 && nchunk <= kSpecChunks &&
-        wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L))
+    if (use_cands != 0 && wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L))
         return;
     if (use_cands != 0) {
         int32_t base = 0, bad = 0;

@@ -6,8 +6,13 @@
   the extra token of target row 0);
 - two calls in flight on two streams with their own workspaces give the
   same bits as the same calls one after the other (the library keeps no
-  state).
+  state);
+- top-k over rows of more than 16 streaming chunks (fp32 at V = 151936,
+  bf16 at V = 300000, fp32 at V = 2^20 with 128 chunks), with ties that put
+  more than 128 candidates in a chunk, and top_k = 256.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -101,3 +106,36 @@ def test_two_streams_match_sequential_calls():
         for r, o in ((ref[0], oa), (ref[1], ob)):
             for k in r:
                 assert np.array_equal(r[k].view(np.uint8), o[k].cpu().numpy().view(np.uint8)), k
+
+
+def _ties(w):
+    """Logits rounded to multiples of 0.5: long runs of equal values."""
+    t = np.round(w.target_f32() * 2) / 2
+    d = np.round(w.draft_f32() * 2) / 2
+    if w.dtype == "f32":
+        return dataclasses.replace(w, target=t.astype(np.float32), draft=d.astype(np.float32))
+    return dataclasses.replace(w, target=W.f32_to_bf16_bits(t), draft=W.f32_to_bf16_bits(d))
+
+
+MANY_CHUNKS = {
+    "f32_v151936_top50": (dict(W.WORKLOADS[5], dtype="f32", batch=8), False),
+    "bf16_v300000_top50": (dict(W.WORKLOADS[5], vocab=300000, batch=8), False),
+    "bf16_v300000_top50_ties": (dict(W.WORKLOADS[5], vocab=300000, batch=6, kind="iid"), True),
+    "bf16_v300000_top256": (dict(W.WORKLOADS[5], vocab=300000, batch=6, top_k=256), False),
+    "f32_v2p20_top64": (_spec(dtype="f32", top_k=64), False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY_CHUNKS))
+def test_topk_rows_of_many_chunks(name):
+    spec, ties = MANY_CHUNKS[name]
+    w = W.make_workload(dict(spec, name=name), gen_seed=73)
+    if ties:
+        w = _ties(w)  # the guesses stay those drawn before rounding: still valid ids
+    note(f"top-k over many chunks {name}: rows_t={w.rows_target} V={w.vocab} top_k={w.top_k}")
+    rep = compare_sample(w, gpu_sample(w), oracle.verify_workload(w, "sample", threads=16))
+    note(f"{name} sample: {rep}")
+    rows, nb = compare_draft(gpu_draft(w), oracle.verify_workload(w, "draft", threads=16))
+    note(f"{name} draft: {rows} rows, {nb} boundary draws")
+    rep = compare_likelihood(w, gpu_likelihood(w), oracle.verify_workload(w, "likelihood", threads=16))
+    note(f"{name} likelihood: {rep}")
