@@ -562,7 +562,7 @@ __device__ int32_t argmax_chunks(const char* row, const PartialFull* pp, int32_t
     return tok == INT32_MAX ? -1 : tok;
 }
 
-// The new token of a sequence (all threads call it; all get the result):// The new token of a sequence (all threads call it; all get the result):
+// The new token of a sequence (all threads call it; all get the result):
 // at the first rejection n < kb the residual max(0, p_n - q_n), else p_kb --
 // drawn by the inverse CDF with u (U(b, n, 1), or U(b, kb, 2)), or, with
 // a.argmax_draw, its argmax.  rt / rd: statistics of target row n and draft
