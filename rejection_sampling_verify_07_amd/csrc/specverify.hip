@@ -30,7 +30,7 @@ namespace {
 #define SV_STREAM_LOADS 4
 #endif
 #ifndef SV_CAND_LOADS
-#define SV_CAND_LOADS 8
+#define SV_CAND_LOADS 6
 #endif
 #ifndef SV_STREAM_NT
 #define SV_STREAM_NT 1
@@ -186,7 +186,9 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
     }
     // Streaming tiles: measured on MI355X, 8 loads per thread beat 4 once the
     // grid holds many times more tiles than the chip keeps resident, and lose
-    // below that (fewer, longer tiles leave the last wave of tiles thin).
+    // below that (fewer, longer tiles leave the last wave of tiles thin).  The
+    // top-k candidate pass measured best at 6 (20.5 us against 21.0-21.4 us at
+    // 8, and 21.0-21.2 at 7, on 314 rows of 151936 bf16 logits).
     if (p.mode == PLAN_TOPK_FAST) {
         p.loads = kCandLoads;
     } else {
