@@ -7,9 +7,9 @@
 - two calls in flight on two streams with their own workspaces give the
   same bits as the same calls one after the other (the library keeps no
   state);
-- top-k over rows of more than 16 streaming chunks (fp32 at V = 151936,
-  bf16 at V = 300000, fp32 at V = 2^20 with 128 chunks), with ties that put
-  more than 128 candidates in a chunk, and top_k = 256.
+- top-k over rows of more than 16 streaming chunks (25 for fp32 at
+  V = 151936 and for bf16 at V = 300000, 171 for fp32 at V = 2^20), with
+  ties that put more than 128 candidates in a chunk, and top_k = 256.
 """
 import dataclasses
 
