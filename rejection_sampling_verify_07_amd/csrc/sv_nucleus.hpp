@@ -11,13 +11,15 @@
 //  - a row with a kept list (<= 1024 ids) is done by wave 0 in registers: a
 //    bitwise radix search on the select key, one wave-wide fp64 sum of the
 //    fp32 weights per bit (fixed order), then an order-keeping compaction;
-//  - a full row (no top-k, or a kept set that outgrew its list) takes three
+//  - a full row (no top-k, or a kept set that outgrew its list) takes two
 //    reads of the row: a histogram of its weights over log-weight buckets,
-//    which finds the bucket where the mass from the top reaches top_p; the
-//    entries of that bucket staged in LDS and resolved by a mass-weighted
-//    radix select; a last pass that sums the kept weights and writes the kept
-//    list when it fits.  Weights are summed in 2^-43 fixed point with integer
-//    LDS atomics, so the sums are exact and the result deterministic.
+//    which finds the bucket where the mass from the top reaches top_p; then
+//    the entries of that bucket staged in LDS (and the ids above it counted)
+//    and resolved by a mass-weighted radix select.  The kept count and mass
+//    follow from those; only a kept set that fits the list takes a third
+//    read, which writes the list in id order and sums the kept weights.
+//    Weights are summed in 2^-43 fixed point with integer LDS atomics, so the
+//    sums are exact and the result deterministic.
 #pragma once
 
 #include "sv_common.hpp"
@@ -39,6 +41,14 @@ struct NucArgs {
 };
 
 constexpr double kFixScale = 8796093022208.0;  // 2^43: weights <= 1 summed over <= 2^20 ids stay below 2^63
+
+// round(w 2^43) for a weight w in [0, 1] (ties to even): w 2^43 + 2^52 in one
+// fp64 fma leaves that integer in the low mantissa bits, since w 2^43 < 2^52.
+__device__ __forceinline__ uint64_t fix43(float w)
+{
+    const double x = __builtin_fma((double)w, kFixScale, 4503599627370496.0);
+    return (uint64_t)__double_as_longlong(x) - 0x4330000000000000ull;
+}
 
 // Radix key of a logit for the full-row select: ordered like the logit, with
 // the meaningful bits on top (16 of them for the 16-bit types).
@@ -63,6 +73,18 @@ __device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
         const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, o, kWave);
         const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), o, kWave);
         if (lane_id() >= o) v += ((uint64_t)hi << 32) | lo;
+    }
+    return v;
+}
+
+// Sum of a u64 across the wave (butterfly; every lane gets it, exactly).
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, kWave);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
+        v += ((uint64_t)hi << 32) | lo;
     }
     return v;
 }
@@ -217,9 +239,7 @@ __device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* r
                     const float x = -__builtin_fmaf(f[e], c, -mcc) * 8.0f;
                     const uint32_t b = (uint32_t)fminf(fmaxf(x, 0.0f), (float)(kNucBuckets - 1));
                     if (ok[e] && f[e] >= tau && b == bstar)
-                        fn(nuc_key<DT>(f[e]),
-                           (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc)) * kFixScale +
-                                      0.5));
+                        fn(nuc_key<DT>(f[e]), fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc))));
                 }
             });
         },
@@ -241,9 +261,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
     const char* rowp = row_ptr(a.rs, row);
     const float tau = d.tau, mcc = d.mcc, c = a.c;
-    auto fixw = [&](float l) {
-        return (uint64_t)((double)__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc)) * kFixScale + 0.5);
-    };
+    auto fixw = [&](float l) { return fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc))); };
     auto bucket = [&](float l) {
         const float e = -__builtin_fmaf(l, c, -mcc) * 8.0f;  // 8 (m - l) c >= 0 up to rounding
         return (uint32_t)fminf(fmaxf(e, 0.0f), (float)(kNucBuckets - 1));
@@ -293,27 +311,39 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
         if (l == 0) {
             S.u[0] = (uint64_t)found;
             S.u[1] = need - above;
+            S.u[2] = above;
         }
     }
     __syncthreads();
     const uint32_t bstar = (uint32_t)S.u[0];
     const uint64_t need_b = S.u[1];
+    const uint64_t mass_hi = S.u[2];  // exact mass of the buckets above the crossing one
     __syncthreads();
 
-    // 2. the crossing bucket's entries into LDS
+    // 2. the crossing bucket's entries into LDS, and the count of the ids above it
+    int32_t n_hi = 0;
     for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
         for (int e = 0; e < Dt<DT>::kVec; ++e) {
-            if (ok[e] && f[e] >= tau && bucket(f[e]) == bstar) {
-                const int32_t slot = atomicAdd(&S.n, 1);
-                if (slot < kNucCap) {
-                    S.ck[slot] = nuc_key<DT>(f[e]);
-                    S.cw[slot] = fixw(f[e]);
+            if (ok[e] && f[e] >= tau) {
+                const uint32_t b = bucket(f[e]);
+                n_hi += b < bstar;
+                if (b == bstar) {
+                    const int32_t slot = atomicAdd(&S.n, 1);
+                    if (slot < kNucCap) {
+                        S.ck[slot] = nuc_key<DT>(f[e]);
+                        S.cw[slot] = fixw(f[e]);
+                    }
                 }
             }
         }
     });
+    n_hi = wave_sum_int(n_hi);
+    if (lane_id() == 0) S.w[wave_id()] = n_hi;
     __syncthreads();
+    n_hi = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) n_hi += S.w[w];
     const int32_t nb = S.n;
     uint32_t prefix;
     if (nb <= kNucCap) {
@@ -330,6 +360,47 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     // the threshold value: the logit whose key has this prefix
     if constexpr (LOW > 0) prefix |= 0xffffu;
     const float tau_p = fmaxf(nuc_value<DT>(prefix), tau);
+
+    // With the bucket staged, the kept count and mass follow without another
+    // read: the ids above the crossing bucket, plus its staged entries >= tau_p
+    // (exact fixed-point mass).  A kept set larger than the list needs nothing
+    // more; the descriptor's S is that mass.
+    if (nb <= kNucCap) {
+        int32_t nk = 0;
+        uint64_t mk = 0;
+        for (int32_t i = threadIdx.x; i < nb; i += kThreads) {
+            if (nuc_value<DT>(S.ck[i]) >= tau_p) {
+                ++nk;
+                mk += S.cw[i];
+            }
+        }
+        nk = wave_sum_int(nk);
+        mk = wave_sum_u64(mk);
+        __syncthreads();  // every thread has read S.w and the staged entries
+        if (lane_id() == 0) {
+            S.w[wave_id()] = nk;
+            S.hist[wave_id()] = mk;
+        }
+        __syncthreads();
+        int32_t kept_n = n_hi;
+        uint64_t kept_m = mass_hi;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            kept_n += S.w[w];
+            kept_m += S.hist[w];
+        }
+        if (kept_n > kKeepCap) {
+            if (threadIdx.x == 0) {
+                RowDesc o = d;
+                o.tau = tau_p;
+                o.s = (double)kept_m / kFixScale;
+                o.kept = -1;
+                a.descs[row] = o;
+            }
+            return;
+        }
+        __syncthreads();  // S.w is the scan scratch below
+    }
 
     // kept sum, count and (if it fits) the ordered kept list
     KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;

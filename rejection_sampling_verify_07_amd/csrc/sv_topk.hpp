@@ -66,11 +66,10 @@ __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, 
             float f[VEC];
             bool ok[VEC];
             unpack<DT>(raw[u], f);
+            // one unsigned compare per element: r < 0 wraps past vocab, and a
+            // block past the row (j >= nblk) starts at or beyond vocab
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const int32_t r = j * VEC - mis + e;
-                ok[e] = j < nblk && r >= 0 && r < vocab;
-            }
+            for (int e = 0; e < VEC; ++e) ok[e] = (uint32_t)(j * VEC - mis + e) < (uint32_t)vocab;
             fn(step, j * VEC - mis, f, ok);
         }
     }
