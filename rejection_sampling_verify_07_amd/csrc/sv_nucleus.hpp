@@ -213,6 +213,28 @@ __device__ uint32_t mass_radix(Visit&& visit, uint64_t need, int low, uint64_t* 
 constexpr int kNucBuckets = 256;   // log-weight buckets of 1/8 bit below the row maximum
 constexpr int kNucCap = 2048;      // entries of the crossing bucket staged in LDS
 
+// The log-weight bucket of a logit, floor(8 (m - l) c) clamped to the
+// buckets (the last one open-ended).  Every step is monotone, so the bucket
+// never increases with the logit.
+__device__ __forceinline__ uint32_t nuc_bucket(float l, float c, float mcc)
+{
+    const float e = -__builtin_fmaf(l, c, -mcc) * 8.0f;
+    return (uint32_t)__builtin_amdgcn_fmed3f(e, 0.0f, (float)(kNucBuckets - 1));
+}
+
+// The smallest logit whose bucket is at most t (a binary search over the
+// order keys from -inf to +inf; the bucket of +inf is 0).
+__device__ __forceinline__ float nuc_lowest_at_most(uint32_t t, float c, float mcc)
+{
+    uint32_t lo = order_key(neg_inf()), hi = order_key(__int_as_float(0x7f800000));
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (nuc_bucket(key_to_float(mid), c, mcc) <= t) hi = mid;
+        else lo = mid + 1;
+    }
+    return key_to_float(lo);
+}
+
 struct NucLds {
     uint64_t hist[256];
     uint64_t u[4];
@@ -236,9 +258,7 @@ __device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* r
             for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
                 for (int e = 0; e < Dt<DT>::kVec; ++e) {
-                    const float x = -__builtin_fmaf(f[e], c, -mcc) * 8.0f;
-                    const uint32_t b = (uint32_t)fminf(fmaxf(x, 0.0f), (float)(kNucBuckets - 1));
-                    if (ok[e] && f[e] >= tau && b == bstar)
+                    if (ok[e] && f[e] >= tau && nuc_bucket(f[e], c, mcc) == bstar)
                         fn(nuc_key<DT>(f[e]), fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc))));
                 }
             });
@@ -262,10 +282,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     const char* rowp = row_ptr(a.rs, row);
     const float tau = d.tau, mcc = d.mcc, c = a.c;
     auto fixw = [&](float l) { return fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc))); };
-    auto bucket = [&](float l) {
-        const float e = -__builtin_fmaf(l, c, -mcc) * 8.0f;  // 8 (m - l) c >= 0 up to rounding
-        return (uint32_t)fminf(fmaxf(e, 0.0f), (float)(kNucBuckets - 1));
-    };
+    auto bucket = [&](float l) { return nuc_bucket(l, c, mcc); };
     // 1. log-weight histogram
     for (int i = threadIdx.x; i < kNucBuckets; i += kThreads) S.hist[i] = 0;
     if (threadIdx.x == 0) S.n = 0;
@@ -320,15 +337,19 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     const uint64_t mass_hi = S.u[2];  // exact mass of the buckets above the crossing one
     __syncthreads();
 
-    // 2. the crossing bucket's entries into LDS, and the count of the ids above it
+    // 2. the crossing bucket's entries into LDS, and the count of the ids above
+    // it, by the logit bounds of the bucket: l >= l_in is in or above it,
+    // l >= l_above above it
+    const float l_in = fmaxf(nuc_lowest_at_most(bstar, c, mcc), tau);
+    const float l_above = bstar > 0 ? fmaxf(nuc_lowest_at_most(bstar - 1, c, mcc), tau) : __int_as_float(0x7f800000);
     int32_t n_hi = 0;
     for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
         for (int e = 0; e < Dt<DT>::kVec; ++e) {
-            if (ok[e] && f[e] >= tau) {
-                const uint32_t b = bucket(f[e]);
-                n_hi += b < bstar;
-                if (b == bstar) {
+            if (ok[e] && f[e] >= l_in) {
+                const bool above = f[e] >= l_above;
+                n_hi += above;
+                if (!above) {
                     const int32_t slot = atomicAdd(&S.n, 1);
                     if (slot < kNucCap) {
                         S.ck[slot] = nuc_key<DT>(f[e]);
