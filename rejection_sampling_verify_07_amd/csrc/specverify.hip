@@ -47,6 +47,7 @@ constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instea
 constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
 static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads past a chunk's candidate slots");
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
+constexpr int32_t kDraftSmallRowsMin = 512;  // draft rows from which full-row draft draws use smaller workgroups
 constexpr size_t kAlign = 256;
 
 enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
@@ -374,8 +375,16 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
     if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
     const dim3 grid((uint32_t)sh->batch, (uint32_t)sh->max_draft);  // max_draft <= SV_MAX_DRAFT fits grid y
     if (!p.desc) {
-        hipLaunchKernelGGL((sv::draft_draw_kernel<DT, false, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads), 0,
-                           stream, va);
+        // one chunk per row is walked: with many rows, smaller workgroups,
+        // two per CU (measured: 150 -> 130 us on 2048 rows of 128256; slower
+        // on 256 rows of 50304, which do not fill the chip either way)
+        if (sh->total_draft >= kDraftSmallRowsMin) {
+            hipLaunchKernelGGL((sv::draft_draw_kernel<DT, false, sv::kDraftChunkThreads>), grid,
+                               dim3(sv::kDraftChunkThreads), 0, stream, va);
+        } else {
+            hipLaunchKernelGGL((sv::draft_draw_kernel<DT, false, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads),
+                               0, stream, va);
+        }
     } else if (p.mode == PLAN_FULL) {
         hipLaunchKernelGGL((sv::draft_draw_kernel<DT, true, kVerifyFullThreads>), grid, dim3(kVerifyFullThreads), 0,
                            stream, va);

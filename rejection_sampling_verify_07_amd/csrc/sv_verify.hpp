@@ -393,10 +393,17 @@ __device__ void argmax_full(const char* ra, const char* rb, int32_t vocab, const
 // rescaled to the row maximum and normalised like the weights
 // (W_c = S_c 2^(mcc_c - mcc) fl32(1/S), fp64, ascending chunks), locate the
 // first chunk whose running mass exceeds u times their total; only its ids
-// are read (one block per thread or two), their fp32 weights scanned in fp64
+// are read (up to BPT consecutive blocks per thread), their fp32 weights scanned in fp64
 // from the mass before the chunk.  If rounding leaves the crossing past the
 // chunk, the walk moves on to the next one; past the last chunk the full
-// walk decides.  All threads call it; all get the token.
+// walk decides.  All threads call it; all get the token.  Each thread takes
+// up to BPT consecutive blocks of the chunk (enough for the longest chunk,
+// kMaxChunkBlocks, at NT threads).
+constexpr int kMaxChunkBlocks = 8 * kThreads;  // 8 loads per thread per streaming tile
+// Draft-side draws over full rows walk one chunk each.  With many rows they
+// run 512-thread workgroups (four blocks per thread), two per CU, instead of
+// one 1024-thread workgroup per CU.
+constexpr int kDraftChunkThreads = 512;
 template <int DT, int NT>
 __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32_t nchunk, int32_t chunk_blocks,
                                    int32_t vocab, const BonusW& wfn, double u, DrawLds<NT>& L, int32_t* token,
@@ -405,6 +412,7 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
     constexpr int VEC = Dt<DT>::kVec;
     constexpr int ES = Dt<DT>::kSize;
     constexpr int NW = NT / kWave;
+    constexpr int BPT = (kMaxChunkBlocks + NT - 1) / NT;
     auto chunk_mass = [&](int32_t ch) {
         double w = 0.0;
         if (ch < nchunk) {
@@ -451,29 +459,53 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
     const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
     const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
     const int32_t bpt = (chunk_blocks + NT - 1) / NT;  // blocks per thread
-    if (bpt > 2) {  // chunks longer than two blocks per thread: walk the row
+    if (bpt > BPT) {  // chunks longer than BPT blocks per thread: walk the row
         inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, token, total);
         return;
     }
     int32_t tok = -1;
     for (; ch >= 0 && ch < nchunk; ++ch) {
-        // this thread's blocks of the chunk, ascending with the thread index
+        // this thread's blocks of the chunk, ascending with the thread index.
+        // With at most two blocks per thread the weights are held; with more,
+        // the raw words are held and the weights formed twice (sum, then walk),
+        // which keeps the register count down.
+        constexpr bool HOLD_W = BPT <= 2;
         const int32_t j0 = ch * chunk_blocks + (int32_t)threadIdx.x * bpt;
-        float w[2 * VEC];
-        double ls = 0.0;
+        u32x4 raw[BPT];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < BPT; ++q) {
             const int32_t j = j0 + q;
             const bool in = q < bpt && j < nblk && j < (ch + 1) * chunk_blocks;
-            const u32x4 raw = in ? load16<false>(base + j) : u32x4{0u, 0u, 0u, 0u};
+            raw[q] = in ? load16<false>(base + j) : u32x4{0u, 0u, 0u, 0u};
+        }
+        auto weights = [&](int q, float* w) {
+            const int32_t j = j0 + q;
+            const bool in = q < bpt && j < nblk && j < (ch + 1) * chunk_blocks;
             float f[VEC];
-            unpack<DT>(raw, f);
+            unpack<DT>(raw[q], f);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 const int32_t r = j * VEC - mis + e;
-                w[q * VEC + e] = (in && r >= 0 && r < vocab) ? wfn(f[e], 0.0f) : 0.0f;
-                ls += (double)w[q * VEC + e];
+                w[e] = (in && r >= 0 && r < vocab) ? wfn(f[e], 0.0f) : 0.0f;
             }
+        };
+        float held[HOLD_W ? BPT * VEC : 1];
+        double ls = 0.0;
+#pragma unroll
+        for (int q = 0; q < BPT; ++q) {
+            float w[VEC];
+            weights(q, w);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                ls += (double)w[e];
+                if constexpr (HOLD_W) held[q * VEC + e] = w[e];
+            }
+        }
+        if constexpr (!HOLD_W) {
+            // (an empty asm that claims to update the raw words keeps the
+            // compiler from holding the weights across the scan; no instruction)
+#pragma unroll
+            for (int q = 0; q < BPT; ++q) asm volatile("" : "+v"(raw[q]));
         }
         // exclusive scan of the thread sums in thread order (fp64)
         const double incl = wave_incl_scan_dpp(ls);
@@ -490,10 +522,20 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
         double cum = off + wave_prev_dpp(incl);
         int32_t hit = INT32_MAX;
 #pragma unroll
-        for (int k = 0; k < 2 * VEC; ++k) {
-            cum += (double)w[k];
-            const int32_t r = (j0 + k / VEC) * VEC - mis + (k % VEC);
-            if (hit == INT32_MAX && w[k] > 0.0f && cum > t) hit = r;
+        for (int q = 0; q < BPT; ++q) {
+            float w[VEC];
+            if constexpr (HOLD_W) {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) w[e] = held[q * VEC + e];
+            } else {
+                weights(q, w);
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                cum += (double)w[e];
+                const int32_t r = (j0 + q) * VEC - mis + e;
+                if (hit == INT32_MAX && w[e] > 0.0f && cum > t) hit = r;
+            }
         }
         if (hit != INT32_MAX) atomicMin(&L.i[1], hit);
         __syncthreads();
@@ -761,7 +803,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
 // row (16 waves keep its re-read in flight) otherwise.
 // ---------------------------------------------------------------------------
 template <int DT, bool FROM_DESC, int NT>
-__global__ __launch_bounds__(NT) void draft_draw_kernel(VerifyArgs a)
+__global__ __launch_bounds__(NT, NT == kDraftChunkThreads ? 4 : 1) void draft_draw_kernel(VerifyArgs a)
 {
     __shared__ DrawLds<NT> s_draw;
     __shared__ RowLds s_r;
