@@ -61,6 +61,7 @@ struct Plan {
     int32_t nchunk;
     int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
     int32_t nchunk2;  // tiles per row pair of the likelihood's pair pass (full rows)
+    int32_t pair_loads;  // 16-byte loads per thread per row in that pass
     int32_t top_k;
     float top_p;
     bool topp;  // top_p < 1: the nucleus pass runs after the statistics
@@ -207,7 +208,10 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
         p.off_partials = off;
         off = align_up(off + slots * sizeof(sv::PartialFull));
         if (kind == CALL_LIKE && !p.topp) {
-            p.nchunk2 = chunks_for(sh->vocab, vec_of(sh->dtype), sv::kPairLoads);
+            const bool big2 =
+                (int64_t)p.rows_t * chunks_for(sh->vocab, vec_of(sh->dtype), sv::kPairLoads) > kBigGridTiles;
+            p.pair_loads = big2 ? sv::kPairLoadsBig : sv::kPairLoads;
+            p.nchunk2 = chunks_for(sh->vocab, vec_of(sh->dtype), p.pair_loads);
             p.off_pair = off;
             off = align_up(off + (size_t)p.rows_t * (size_t)p.nchunk2 * sizeof(double));
         }
@@ -430,8 +434,13 @@ sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt,
             double* pair = ws_at<double>(ws, p.off_pair);
             const sv::PairArgs pa{rs, sh->vocab, sh->total_draft, va.partials, p.nchunk, p.nchunk2, c, pair};
             const uint32_t grid = (uint32_t)((int64_t)sh->total_draft * p.nchunk2);
-            hipLaunchKernelGGL((sv::pair_min_kernel<DT, sv::kPairLoads>), dim3(grid), dim3(sv::kThreads), 0, stream,
-                               pa);
+            if (p.pair_loads == sv::kPairLoadsBig) {
+                hipLaunchKernelGGL((sv::pair_min_kernel<DT, sv::kPairLoadsBig>), dim3(grid), dim3(sv::kThreads), 0,
+                                   stream, pa);
+            } else {
+                hipLaunchKernelGGL((sv::pair_min_kernel<DT, sv::kPairLoads>), dim3(grid), dim3(sv::kThreads), 0,
+                                   stream, pa);
+            }
             if (launch_status() != SV_OK) return SV_ERR_HIP;
             la.pair = pair;
         }

@@ -27,6 +27,9 @@
 namespace sv {
 
 constexpr int kPairLoads = 4;  // 16-byte loads per thread per row in the pair pass
+constexpr int kPairLoadsBig = 8;  // the same over grids many times larger than the chip (measured: 334 against
+                                  // 342-346 us for the step on 2048 positions of 128256 bf16 logits; slower on
+                                  // small grids, 34.3 against 32.7 us on 256 positions of 50304)
 
 // min(p(v), q(v)) in probability units (fp32), each side masked by its
 // top-k threshold.
