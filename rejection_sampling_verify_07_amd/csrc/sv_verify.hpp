@@ -79,6 +79,17 @@ struct ResidualW {
         return fmaxf(et * inv_t - ed * inv_d, 0.0f);
     }
 };
+// The same weights for rows with no top-k threshold (tau = -inf): a -inf
+// logit already gives exp2(-inf) = 0, so the threshold test is dropped.
+struct ResidualWFull {
+    float tau_t, mcc_t, inv_t, tau_d, mcc_d, inv_d, c;
+    __device__ __forceinline__ float operator()(float lt, float ld) const
+    {
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t));
+        const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d));
+        return fmaxf(et * inv_t - ed * inv_d, 0.0f);
+    }
+};
 struct BonusW {
     float tau_t, mcc_t, inv_t, c;
     __device__ __forceinline__ float operator()(float lt, float) const
@@ -144,10 +155,11 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
         for (int uu = 0; uu < kSegUnroll; ++uu) {
             const int32_t s = s0 + uu * (NT / kWave);
             if (s < nseg) {
-                double ls = 0.0;
+                // a lane's kSegElems weights are summed in fp32, then carried in fp64
+                float fs = 0.0f;
 #pragma unroll
-                for (int e = 0; e < kSegElems; ++e) ls += (double)w[uu][e];
-                const double incl = wave_incl_scan_dpp(ls);
+                for (int e = 0; e < kSegElems; ++e) fs += w[uu][e];
+                const double incl = wave_incl_scan_dpp((double)fs);
                 if (lane == kWave - 1) s_seg[s] = incl;
             }
         }
@@ -190,17 +202,20 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
         for (; s >= 0 && tok < 0; --s) {
             float w[kSegElems];
             seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w);
-            double ls = 0.0;
+            float fs = 0.0f;
 #pragma unroll
-            for (int e = 0; e < kSegElems; ++e) ls += (double)w[e];
-            const double incl = wave_incl_scan_dpp(ls);
+            for (int e = 0; e < kSegElems; ++e) fs += w[e];
+            const double incl = wave_incl_scan_dpp((double)fs);
             const double excl = wave_prev_dpp(incl);
-            double cum = (s > 0 ? s_seg[s - 1] : 0.0) + excl;
+            const double start = (s > 0 ? s_seg[s - 1] : 0.0) + excl;
+            // the running mass inside the lane in the same fp32 order as pass 1,
+            // so that a lane ends exactly where the next one starts
+            float run = 0.0f;
             int hit = -1, lastpos = -1;
 #pragma unroll
             for (int e = 0; e < kSegElems; ++e) {
-                cum += (double)w[e];
-                if (hit < 0 && cum > t) hit = e;
+                run += w[e];
+                if (hit < 0 && start + (double)run > t) hit = e;
                 if (w[e] > 0.0f) lastpos = e;
             }
             const uint64_t bh = __ballot(hit >= 0);
@@ -663,6 +678,9 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
             z = L.dd[1];
         } else if (a.argmax_draw) {
             argmax_full<DT, true, NT>(trow, drow, a.vocab, wfn, L, &token, &z);
+        } else if constexpr (!FROM_DESC) {
+            const ResidualWFull wf{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
+            inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wf, u, L.seg, L.wd, L.i, L.dd, &token, &z);
         } else {
             inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wfn, u, L.seg, L.wd, L.i, L.dd, &token, &z);
         }
