@@ -97,6 +97,14 @@ struct BonusW {
         return lt >= tau_t ? __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) * inv_t : 0.0f;
     }
 };
+// BonusW for rows with no top-k threshold (tau = -inf; see ResidualWFull).
+struct BonusWFull {
+    float tau_t, mcc_t, inv_t, c;
+    __device__ __forceinline__ float operator()(float lt, float) const
+    {
+        return __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) * inv_t;
+    }
+};
 
 // Weights of one lane's kSegElems ids of segment s (0 outside the row).
 template <int DT, bool TWO, class W>
@@ -419,9 +427,9 @@ constexpr int kMaxChunkBlocks = 8 * kThreads;  // 8 loads per thread per streami
 // run 512-thread workgroups (four blocks per thread), two per CU, instead of
 // one 1024-thread workgroup per CU.
 constexpr int kDraftChunkThreads = 512;
-template <int DT, int NT>
+template <int DT, int NT, class W>
 __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32_t nchunk, int32_t chunk_blocks,
-                                   int32_t vocab, const BonusW& wfn, double u, DrawLds<NT>& L, int32_t* token,
+                                   int32_t vocab, const W& wfn, double u, DrawLds<NT>& L, int32_t* token,
                                    double* total)
 {
     constexpr int VEC = Dt<DT>::kVec;
@@ -504,17 +512,20 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
                 w[e] = (in && r >= 0 && r < vocab) ? wfn(f[e], 0.0f) : 0.0f;
             }
         };
+        // a block's weights are summed in fp32, the blocks carried in fp64
         float held[HOLD_W ? BPT * VEC : 1];
         double ls = 0.0;
 #pragma unroll
         for (int q = 0; q < BPT; ++q) {
             float w[VEC];
             weights(q, w);
+            float bs = 0.0f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                ls += (double)w[e];
+                bs += w[e];
                 if constexpr (HOLD_W) held[q * VEC + e] = w[e];
             }
+            ls += (double)bs;
         }
         if constexpr (!HOLD_W) {
             // (an empty asm that claims to update the raw words keeps the
@@ -545,12 +556,15 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
             } else {
                 weights(q, w);
             }
+            // the running mass in the same fp32 order as the block sums above
+            float run = 0.0f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                cum += (double)w[e];
+                run += w[e];
                 const int32_t r = (j0 + q) * VEC - mis + e;
-                if (hit == INT32_MAX && w[e] > 0.0f && cum > t) hit = r;
+                if (hit == INT32_MAX && w[e] > 0.0f && cum + (double)run > t) hit = r;
             }
+            cum += (double)run;
         }
         if (hit != INT32_MAX) atomicMin(&L.i[1], hit);
         __syncthreads();
@@ -650,8 +664,9 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
             *tok = L.i[2];
         } else if (!FROM_DESC) {
             const PartialFull* pp = a.partials + kept_row_n * a.nchunk;
+            const BonusWFull bwf{rt.tau, rt.mcc, rt.inv_s, a.c};
             if (a.argmax_draw) *tok = argmax_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, L);
-            else inverse_cdf_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, bw, u, L, tok, &zz);
+            else inverse_cdf_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, bwf, u, L, tok, &zz);
         } else if (a.argmax_draw) {
             argmax_full<DT, false, NT>(trow, nullptr, a.vocab, bw, L, tok, &zz);
         } else {
@@ -879,7 +894,7 @@ __global__ __launch_bounds__(NT, NT == kDraftChunkThreads ? 4 : 1) void draft_dr
         __syncthreads();
         token = s_tok;
     } else if (!FROM_DESC) {
-        const BonusW bw{rt.tau, rt.mcc, rt.inv_s, a.c};
+        const BonusWFull bw{rt.tau, rt.mcc, rt.inv_s, a.c};
         inverse_cdf_chunks<DT, NT>(row_ptr(a.rs, row), a.partials + (int64_t)row * a.nchunk, a.nchunk,
                                    a.chunk_blocks, a.vocab, bw, u, s_draw, &token, &z);
     } else {
