@@ -22,6 +22,7 @@
 #pragma once
 
 #include "sv_common.hpp"
+#include "sv_stats.hpp"
 #include "sv_verify.hpp"
 
 namespace sv {
@@ -39,6 +40,18 @@ struct MinW {
     {
         const float et = lt >= tau_t ? __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) * inv_t : 0.0f;
         const float ed = ld >= tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d)) * inv_d : 0.0f;
+        return fminf(et, ed);
+    }
+};
+
+// MinW for rows with no top-k threshold: a -inf logit (a mask, or an
+// out-of-row slot filled with -inf) already weighs exp2(-inf) = 0.
+struct MinWFull {
+    float mcc_t, inv_t, mcc_d, inv_d, c;
+    __device__ __forceinline__ float operator()(float lt, float ld) const
+    {
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) * inv_t;
+        const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d)) * inv_d;
         return fminf(et, ed);
     }
 };
@@ -118,18 +131,24 @@ __global__ __launch_bounds__(kThreads) void pair_min_kernel(PairArgs a)
 
     float acc = 0.0f;
     if (same) {
+        // tiles that reach outside the row fill their out-of-row slots with
+        // -inf (weight 0), so the element loop needs no threshold or bounds test
+        Tile tl;
+        tl.index = tile;
+        tl.row = r;
+        tl.cb0 = ch * (kThreads * LOADS);
+        tl.mis = mis_t;
+        tl.nblk = nblk;
+        sanitize_edge<DT, LOADS>(tl, a.vocab, rt);
+        sanitize_edge<DT, LOADS>(tl, a.vocab, rd);
+        const MinWFull wf{s_st[0], s_st[1], s_st[2], s_st[3], a.c};
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int32_t j = b0 + i * kThreads;
             float ft[VEC], fd[VEC];
             unpack<DT>(rt[i], ft);
             unpack<DT>(rd[i], fd);
-            const int32_t v0 = j * VEC - mis_t;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float w = wfn(ft[e], fd[e]);
-                acc += ((j < nblk) & ((uint32_t)(v0 + e) < (uint32_t)a.vocab)) ? w : 0.0f;
-            }
+            for (int e = 0; e < VEC; ++e) acc += wf(ft[e], fd[e]);
         }
     } else {
         // rows on different 16-byte phases: element loads on the target's block grid
