@@ -377,16 +377,24 @@ __device__ void argmax_full(const char* ra, const char* rb, int32_t vocab, const
             const int32_t s = s0 + uu * NW;
             if (s < nseg) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
         }
+        // a lane meets its ids in ascending order, so a strict > keeps the
+        // lowest id among equal weights (and best starting at 0 drops zeros);
+        // a lane's kSegElems weights are summed in fp32, then carried in fp64
 #pragma unroll
         for (int uu = 0; uu < kSegUnroll; ++uu) {
             const int32_t s = s0 + uu * NW;
             if (s < nseg) {
                 const int32_t v0 = s * kSeg + lane_id() * kSegElems;
+                float fs = 0.0f;
 #pragma unroll
                 for (int e = 0; e < kSegElems; ++e) {
-                    ls += (double)w[uu][e];
-                    if (w[uu][e] > 0.0f) argmax_merge(best, bid, w[uu][e], v0 + e);
+                    fs += w[uu][e];
+                    if (w[uu][e] > best) {
+                        best = w[uu][e];
+                        bid = v0 + e;
+                    }
                 }
+                ls += (double)fs;
             }
         }
     }
@@ -692,7 +700,12 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
             token = L.i[2];
             z = L.dd[1];
         } else if (a.argmax_draw) {
-            argmax_full<DT, true, NT>(trow, drow, a.vocab, wfn, L, &token, &z);
+            if constexpr (!FROM_DESC) {
+                const ResidualWFull wf{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
+                argmax_full<DT, true, NT>(trow, drow, a.vocab, wf, L, &token, &z);
+            } else {
+                argmax_full<DT, true, NT>(trow, drow, a.vocab, wfn, L, &token, &z);
+            }
         } else if constexpr (!FROM_DESC) {
             const ResidualWFull wf{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
             inverse_cdf_full<DT, true, NT>(trow, drow, a.vocab, wf, u, L.seg, L.wd, L.i, L.dd, &token, &z);
