@@ -99,7 +99,7 @@ __device__ __forceinline__ int block_excl_scan_int(int v, int* s_w, int* total)
 // (bf16: keys are determined by their top 16 bits).  Returns the key and
 // the number of keys equal to it; *greater gets the number above it.
 template <class Visit>
-__device__ uint32_t block_radix_select(Visit&& visit, int32_t k, int low_shift, uint32_t* s_hist,
+__device__ __forceinline__ uint32_t block_radix_select(Visit&& visit, int32_t k, int low_shift, uint32_t* s_hist,
                                        int32_t* s_misc, int32_t* greater, int32_t* equal)
 {
     uint32_t prefix = 0, pmask = 0;
