@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
     constexpr bool BF = DT == DT_BF16;
     constexpr bool H16 = DT == DT_F16;
-    __shared__ float s_val[kChunkLds];
+    __shared__ __align__(16) float s_val[kChunkLds];
     __shared__ int32_t s_ix[kChunkLds];
     __shared__ uint32_t s_lk[kThreads];
     __shared__ int32_t s_wc[kWaves];
@@ -231,23 +231,30 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
         const int wbase = wave_id() * kWaveLds;
         float bound;  // the tile's lower bound of the row's tau
         {
-            float tm = neg_inf();
+            // the maximum of each 16-byte block, and the lane's maximum
+            float bm[LOADS];
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
+                float b = neg_inf();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const uint32_t w = raw[i][q];
                     if constexpr (BF) {
                         // both elements exactly: the raw word would be a
                         // signalling NaN for a -inf high element
-                        tm = max3_quiet(tm, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+                        b = max3_quiet(b, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
                     } else if constexpr (H16) {
-                        tm = max3_quiet(tm, lo16<DT>(w), hi16<DT>(w));
+                        b = max3_quiet(b, lo16<DT>(w), hi16<DT>(w));
                     } else if (q & 1) {
-                        tm = max3_quiet(tm, __uint_as_float(raw[i][q - 1]), __uint_as_float(w));
+                        b = max3_quiet(b, __uint_as_float(raw[i][q - 1]), __uint_as_float(w));
                     }
                 }
+                bm[i] = b;
             }
+            float tm = bm[0];
+#pragma unroll
+            for (int i = 1; i < LOADS; i += 2)
+                tm = (i + 1 < LOADS) ? max3_quiet(tm, bm[i], bm[i + 1]) : max3_quiet(tm, bm[i], bm[i]);
 
             // Recompute the widened values in the compaction pass instead of
             // keeping all of them live across the barrier (an empty asm that
@@ -282,31 +289,97 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             // smallest float whose key has these top bits; the -inf bucket maps to -inf
             bound = (h <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(h << 16);
 
-            // candidates into this wave's LDS region, in (load, element, lane)
-            // order; the exact value and the row index are formed only on the
-            // rare taken branch.  Slots past the region are clamped (the tile is
-            // then reported as overflowed and its staging is not used).
+            // Candidates into this wave's LDS region.  Only blocks whose maximum
+            // reaches the bound can hold one (about 14 of the wave's 64 * LOADS
+            // blocks on logits of a language model), so those blocks are first
+            // staged in the same region (at most kStage of them), read back one
+            // per lane, and only they take the per-element ballots.  The compare
+            // of each element is the one of the full walk below, so both give
+            // the same candidates.  The exact value and the row index are formed
+            // only on the rare taken branch.  Slots past the region are clamped
+            // (the tile is then reported as overflowed and its staging is not
+            // used).
+            auto element_cmp = [&](uint32_t w, int e) -> float {
+                return BF    ? __uint_as_float((e & 1) ? w : (w << 16))
+                       : H16 ? ((e & 1) ? hi16<DT>(w) : lo16<DT>(w))
+                             : __uint_as_float(w);
+            };
+            auto element_bits = [&](uint32_t w, int e, float cmp) -> uint32_t {
+                return BF ? ((e & 1) ? (w & 0xffff0000u) : (w << 16)) : H16 ? __float_as_uint(cmp) : w;
+            };
+            constexpr int kStage = kWaveLds / 4;  // 16-byte blocks in the wave's part of s_val
+            u32x4* stage = reinterpret_cast<u32x4*>(s_val + wbase);
+            int32_t* stage_blk = s_ix + wbase;
+            int32_t nb = 0;  // wave-uniform count of blocks that reach the bound
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
+                const bool hb = bm[i] >= bound;
+                const uint64_t m = __ballot(hb);
+                if (hb) {
+                    const int32_t pos = nb + lanes_below(m);
+                    if (pos < kStage) {
+                        stage[pos] = raw[i];
+                        stage_blk[pos] = i * kThreads + (int32_t)threadIdx.x;  // block - t.cb0
+                    }
+                }
+                nb += (int32_t)__popcll(m);
+            }
+            __builtin_amdgcn_wave_barrier();
+            if (nb <= 2 * kWave) {
+                // read every staged block back before the candidates overwrite
+                // them (a wave's LDS operations complete in issue order)
+                u32x4 sb[2];
+                int32_t so[2];
+                bool sv[2];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const int q = Dt<DT>::kSize == 2 ? e / 2 : e;
-                    const uint32_t w = raw[i][q];
-                    const float cmp = BF    ? __uint_as_float((e & 1) ? w : (w << 16))
-                                      : H16 ? ((e & 1) ? hi16<DT>(w) : lo16<DT>(w))
-                                            : __uint_as_float(w);
-                    const bool pred = cmp >= bound;
-                    const uint64_t m = __ballot(pred);
-                    if (m != 0) {
-                        if (pred) {
-                            const int pos = min(wcount + lanes_below(m), kWaveLds - 1);
-                            const uint32_t bits = BF    ? ((e & 1) ? (w & 0xffff0000u) : (w << 16))
-                                                  : H16 ? __float_as_uint(cmp)
-                                                        : w;
-                            s_val[wbase + pos] = __uint_as_float(bits);
-                            s_ix[wbase + pos] = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
+                for (int r = 0; r < 2; ++r) {
+                    const int32_t sidx = r * kWave + lane_id();
+                    sv[r] = sidx < nb;
+                    const int32_t sc = min(sidx, kStage - 1);
+                    sb[r] = stage[sc];
+                    so[r] = stage_blk[sc];
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int r = 0; r < 2; ++r) {
+                    if (r * kWave >= nb) break;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const int q = Dt<DT>::kSize == 2 ? e / 2 : e;
+                        const uint32_t w = sb[r][q];
+                        const float cmp = element_cmp(w, e);
+                        const bool pred = sv[r] && cmp >= bound;
+                        const uint64_t m = __ballot(pred);
+                        if (m != 0) {
+                            if (pred) {
+                                const int pos = min(wcount + lanes_below(m), kWaveLds - 1);
+                                s_val[wbase + pos] = __uint_as_float(element_bits(w, e, cmp));
+                                s_ix[wbase + pos] = (t.cb0 + so[r]) * VEC - t.mis + e;
+                            }
+                            wcount += (int)__popcll(m);
                         }
-                        wcount += (int)__popcll(m);
+                    }
+                }
+            } else {
+                // many blocks reach the bound (ties, flat rows): every element
+                // of the tile, in (load, element, lane) order
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        const int q = Dt<DT>::kSize == 2 ? e / 2 : e;
+                        const uint32_t w = raw[i][q];
+                        const float cmp = element_cmp(w, e);
+                        const bool pred = cmp >= bound;
+                        const uint64_t m = __ballot(pred);
+                        if (m != 0) {
+                            if (pred) {
+                                const int pos = min(wcount + lanes_below(m), kWaveLds - 1);
+                                s_val[wbase + pos] = __uint_as_float(element_bits(w, e, cmp));
+                                s_ix[wbase + pos] = (tile_b0(t) + i * kThreads) * VEC - t.mis + e;
+                            }
+                            wcount += (int)__popcll(m);
+                        }
                     }
                 }
             }
