@@ -69,6 +69,20 @@ struct RowLds {
     double s;
 };
 
+// The residual weight max(0, p - q) of one id from its two unnormalised
+// terms and the rows' fl32(1 / S): both probabilities are rounded to fp32
+// before the difference.  Fusing one product into the subtraction would leave
+// its rounding error where the two probabilities are equal, and a residual
+// that has no mass (p = q on the whole support) would then be drawn from that
+// noise instead of being recognised as empty.
+__device__ __forceinline__ float resid_weight(float et, float inv_t, float ed, float inv_d)
+{
+#pragma clang fp contract(off)
+    const float pt = et * inv_t;
+    const float pd = ed * inv_d;
+    return fmaxf(pt - pd, 0.0f);
+}
+
 // Weights of the inverse-CDF draw, in probability units (fp32).
 struct ResidualW {
     float tau_t, mcc_t, inv_t, tau_d, mcc_d, inv_d, c;
@@ -76,7 +90,7 @@ struct ResidualW {
     {
         const float et = lt >= tau_t ? __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t)) : 0.0f;
         const float ed = ld >= tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d)) : 0.0f;
-        return fmaxf(et * inv_t - ed * inv_d, 0.0f);
+        return resid_weight(et, inv_t, ed, inv_d);
     }
 };
 // The same weights for rows with no top-k threshold (tau = -inf): a -inf
@@ -87,7 +101,7 @@ struct ResidualWFull {
     {
         const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(lt, c, -mcc_t));
         const float ed = __builtin_amdgcn_exp2f(__builtin_fmaf(ld, c, -mcc_d));
-        return fmaxf(et * inv_t - ed * inv_d, 0.0f);
+        return resid_weight(et, inv_t, ed, inv_d);
     }
 };
 struct BonusW {
@@ -271,14 +285,13 @@ __device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, con
         if (i < hi) {
             const KeptEntry e = entry(i);
             ix[q] = e.idx;
-            const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
+            const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t));
             if constexpr (RESID) {
                 const float ld = draft(i, e.idx);
-                const float ed =
-                    ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
-                w[q] = fmaxf(et - ed, 0.0f);
+                const float ed = ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) : 0.0f;
+                w[q] = resid_weight(et, rw.inv_t, ed, rw.inv_d);
             } else {
-                w[q] = et;
+                w[q] = et * rw.inv_t;
             }
             ls += (double)w[q];
         }
@@ -342,13 +355,12 @@ __device__ void argmax_list_of(Entry&& entry, int32_t n, Draft&& draft, const Re
     double ls = 0.0;
     for (int32_t i = lo; i < hi; ++i) {
         const KeptEntry e = entry(i);
-        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t)) * rw.inv_t;
-        float w = et;
+        const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t));
+        float w = et * rw.inv_t;
         if constexpr (RESID) {
             const float ld = draft(i, e.idx);
-            const float ed =
-                ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) * rw.inv_d : 0.0f;
-            w = fmaxf(et - ed, 0.0f);
+            const float ed = ld >= rw.tau_d ? __builtin_amdgcn_exp2f(__builtin_fmaf(ld, rw.c, -rw.mcc_d)) : 0.0f;
+            w = resid_weight(et, rw.inv_t, ed, rw.inv_d);
         }
         ls += (double)w;
         if (w > 0.0f) argmax_merge(best, bid, w, e.idx);
@@ -666,10 +678,10 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
                 int32_t t1;
                 if (a.argmax_draw) argmax_list_of<false>(entry, rt.kept, none, pw, &t1, &zz);
                 else inverse_cdf_list_of<false>(entry, rt.kept, none, pw, u, &t1, &zz);
-                if (lane_id() == 0) L.i[2] = t1;
+                if (lane_id() == 0) L.i[3] = t1;  // not i[2]: it may still be read for the residual's token
             }
             __syncthreads();
-            *tok = L.i[2];
+            *tok = L.i[3];
         } else if (!FROM_DESC) {
             const PartialFull* pp = a.partials + kept_row_n * a.nchunk;
             const BonusWFull bwf{rt.tau, rt.mcc, rt.inv_s, a.c};

@@ -75,6 +75,39 @@ def _masked(x):
     return x
 
 
+def _wave0_peaks(vec):
+    """100 peaks in the first tile of every row, one element in each of the
+    blocks (load 0 or 1, thread 0..49), all other logits near -5.  The peaks
+    take four levels 5 + k/32 (exact in bf16), and thread 0 has both of its
+    peaks at the lowest one, which is then the tile bound: all 100 peak blocks,
+    every one in wave 0, reach it, so the staged candidate compaction takes its
+    second round, and the kept set has ties at tau.  vec: logits per 16-byte
+    block."""
+
+    def f(x):
+        y = x * np.float32(0.2) - np.float32(5.0)
+        rows = np.arange(y.shape[0])[:, None]
+        tid = np.arange(50)
+        for i in (0, 1):
+            cols = (i * 256 + tid) * vec + (tid * 3 + i) % vec
+            level = np.where(tid > 0, (rows * 7 + tid * 3 + i * 5) % 4, 0)
+            y[:, cols] = np.float32(5.0) + np.float32(1.0 / 32.0) * level
+        return y
+
+    return f
+
+
+def _wave0_blocks_at_bound(x, vec, top_k, loads=6):
+    """Blocks of wave 0 in the first tile of row x whose maximum reaches the
+    tile bound (the top_k-th largest lane maximum, cut to its top 16 key bits;
+    the values here are positive)."""
+    bmax = x[: 256 * loads * vec].reshape(loads, 256, vec).max(axis=2)
+    b = np.float32(np.sort(bmax.max(axis=0))[::-1][top_k - 1])
+    bound = (np.array([b]).view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)[0]
+    assert bound > 0
+    return int((bmax[:, :64] >= bound).sum())
+
+
 def _few_finite(x):
     # 10 finite logits per row: fewer than top_k, so tau = -inf
     y = np.full_like(x, -np.inf)
@@ -102,6 +135,8 @@ CASES = {
     "bf16_neg_inf_masks": (_spec(vocab=6000), _masked),
     "f16_neg_inf_masks": (_spec(vocab=6000, dtype="f16"), _masked),
     "bf16_fewer_finite_than_top_k": (_spec(vocab=4000), _few_finite),
+    "bf16_wave0_peaks_two_rounds": (_spec(vocab=20000), _wave0_peaks(8)),
+    "f32_wave0_peaks_two_rounds": (_spec(vocab=20000, dtype="f32"), _wave0_peaks(4)),
 }
 
 
@@ -112,6 +147,9 @@ def test_topk_many_rows(name):
     if f is not None:
         w = _with_rows(w, f)
     assert w.rows_draft >= 256 and w.rows_target + w.rows_draft >= 256
+    if "wave0_peaks" in name:
+        nb = _wave0_blocks_at_bound(w.target_f32()[0], 4 if w.dtype == "f32" else 8, w.top_k)
+        assert 64 < nb <= 128, nb
     note(f"top-k rows {name}: B={w.batch} rows_t={w.rows_target} rows_d={w.rows_draft} V={w.vocab} "
          f"{w.dtype} top_k={w.top_k}")
     rep = compare_sample(w, gpu_sample(w), oracle.verify_workload(w, "sample", threads=16))
