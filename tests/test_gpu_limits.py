@@ -9,7 +9,9 @@
   state);
 - top-k over rows of more than 16 streaming chunks (25 for fp32 at
   V = 151936 and for bf16 at V = 300000, 171 for fp32 at V = 2^20), with
-  ties that put more than 128 candidates in a chunk, and top_k = 256.
+  ties that put more than 128 candidates in a chunk, and top_k = 256;
+- a residual with no mass: draft rows equal to their target rows and every
+  guess on an id masked in both, so the new token comes from p_n.
 """
 import dataclasses
 
@@ -139,3 +141,30 @@ def test_topk_rows_of_many_chunks(name):
     note(f"{name} draft: {rows} rows, {nb} boundary draws")
     rep = compare_likelihood(w, gpu_likelihood(w), oracle.verify_workload(w, "likelihood", threads=16))
     note(f"{name} likelihood: {rep}")
+
+
+@pytest.mark.parametrize("dtype,top_k", [("bf16", 0), ("f32", 0), ("bf16", 50)])
+def test_zero_residual_mass_draws_from_p(dtype, top_k):
+    """Draft rows equal to their target rows, every fifth id masked to -inf in
+    both, and every guess on a masked id: p(x) = q(x) = 0 rejects each first
+    guess, and p = q everywhere else leaves the residual with no mass, so the
+    new token is drawn from p_n with the residual's uniform (the argmax of p_n
+    in the argmax variant), as the oracle does."""
+    w = W.make_workload(_spec(vocab=20000, batch=8, k=4, top_k=top_k, dtype=dtype, kind="iid", ragged=False),
+                        gen_seed=74)
+    t = w.target_f32().copy()
+    t[:, ::5] = -np.inf
+    d = np.empty((w.rows_draft, w.vocab), np.float32)
+    k0 = 0
+    for b, kb in enumerate(w.draft_lens.tolist()):
+        d[k0:k0 + kb] = t[k0 + b:k0 + b + kb]  # draft row (b, k) = target row (b, k)
+        k0 += kb
+    ids = ((np.arange(w.rows_draft) * 7919) % (w.vocab // 5) * 5).astype(np.int32)  # masked ids
+    enc = (lambda x: x.astype(np.float32)) if dtype == "f32" else W.f32_to_bf16_bits
+    w = dataclasses.replace(w, target=enc(t), draft=enc(d), draft_ids=ids)
+    note(f"zero residual mass {dtype} top_k={top_k}")
+    o = oracle.verify_workload(w, "sample", threads=16)
+    assert np.all(o["num_accepted"] == 0)
+    assert np.all(o["flags"] & oracle.FLAG_ZERO_RESIDUAL)
+    compare_sample(w, gpu_sample(w), o)
+    compare_argmax(w, gpu_argmax(w), oracle.verify_workload(w, "argmax", threads=16))
