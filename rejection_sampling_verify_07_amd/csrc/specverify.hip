@@ -46,7 +46,15 @@ constexpr int64_t kBigGridTiles = 16384;     // 4-load tiles beyond which kLoads
 constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
 constexpr bool kNT = SV_STREAM_NT != 0;
 constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instead of one tile per workgroup
-constexpr int32_t kCandCap = 256;    // candidate slots per (row, chunk) in the top-k pass
+constexpr int32_t kCandCap = 512;    // candidate slots per (row, chunk) in the top-k pass
+// Largest top_k that takes the candidate pass.  Close to the pass's own
+// limit (one lane maximum per thread, 256) the tile bound is the smallest lane
+// maxima, the candidates of a row outgrow the select's list, and each row then
+// falls to the one-wave full-row select: on 314 rows of 151936 bf16 logits a
+// call took 80 us at top_k 240 but 550-670 us at 250-256, against 366 us for
+// the workgroup-per-row exact select that larger top_k use.
+constexpr int32_t kTopkFastPlanMax = 240;
+static_assert(kTopkFastPlanMax <= sv::kTopkFastMax, "the candidate pass needs top_k lane maxima");
 static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads past a chunk's candidate slots");
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
 constexpr int32_t kDraftSmallRowsMin = 512;  // draft rows from which full-row draft draws use smaller workgroups
@@ -186,7 +194,7 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
     } else if (!topk) {
         p.mode = PLAN_FULL;
     } else {
-        p.mode = top_k <= sv::kTopkFastMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
+        p.mode = top_k <= kTopkFastPlanMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
     }
     // Streaming tiles: measured on MI355X, 8 loads per thread beat 4 once the
     // grid holds many times more tiles than the chip keeps resident, and lose

@@ -408,6 +408,12 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 },
                 top_k, LOW, s_hist, s_misc + 2, &greater, &equal);
             written = greater + equal;
+            // The tile's own top_k-th largest value is a lower bound of the
+            // row's tau too, and a much tighter one than the lane maxima give
+            // when top_k is close to 256: reported as the tile's bound, it
+            // keeps the select's survivors (candidates >= the largest bound)
+            // within its list.
+            if (tkey > (order_key(neg_inf()) & (~0u << LOW))) bound = fmaxf(bound, key_to_float(tkey));
             if (written <= cap) {
                 if (threadIdx.x == 0) s_misc[1] = 0;
                 __syncthreads();

@@ -9,7 +9,8 @@
   state);
 - top-k over rows of more than 16 streaming chunks (25 for fp32 at
   V = 151936 and for bf16 at V = 300000, 171 for fp32 at V = 2^20), with
-  ties that put more than 128 candidates in a chunk, and top_k = 256;
+  ties that put more than 128 candidates in a chunk, and top_k = 240 (the
+  largest that takes the candidate pass);
 - a residual with no mass: draft rows equal to their target rows and every
   guess on an id masked in both, so the new token comes from p_n.
 """
@@ -123,7 +124,7 @@ MANY_CHUNKS = {
     "f32_v151936_top50": (dict(W.WORKLOADS[5], dtype="f32", batch=8), False),
     "bf16_v300000_top50": (dict(W.WORKLOADS[5], vocab=300000, batch=8), False),
     "bf16_v300000_top50_ties": (dict(W.WORKLOADS[5], vocab=300000, batch=6, kind="iid"), True),
-    "bf16_v300000_top256": (dict(W.WORKLOADS[5], vocab=300000, batch=6, top_k=256), False),
+    "bf16_v300000_top240": (dict(W.WORKLOADS[5], vocab=300000, batch=6, top_k=240), False),
     "f32_v2p20_top64": (_spec(dtype="f32", top_k=64), False),
 }
 

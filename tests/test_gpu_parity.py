@@ -90,7 +90,8 @@ EDGE = {
     "top_k_1": (_spec(top_k=1, vocab=4000, batch=6), {}),
     "top_k_v_minus_1": (_spec(top_k=1000, batch=3), {}),
     "top_k_v": (_spec(top_k=1001, batch=3), {}),
-    "top_k_256_fast_limit": (_spec(top_k=256, vocab=20000, batch=4), {}),
+    "top_k_240_fast_limit": (_spec(top_k=240, vocab=20000, batch=4), {}),
+    "top_k_256_exact_path": (_spec(top_k=256, vocab=20000, batch=4), {}),
     "top_k_300_exact_path": (_spec(top_k=300, vocab=20000, batch=4), {}),
     "temperature_0.05": (_spec(temperature=0.05, vocab=8000, batch=8), {}),
     "temperature_5": (_spec(temperature=5.0, vocab=8000, batch=8), {}),

@@ -124,8 +124,9 @@ CASES = {
     "f32_v1001_misaligned": (_spec(dtype="f32", vocab=1001), None),
     "f16_v5000_top50": (_spec(dtype="f16"), None),
     "bf16_top1": (_spec(top_k=1), None),
+    "bf16_top240": (_spec(top_k=240, vocab=20000), None),
+    "f32_top240": (_spec(top_k=240, vocab=20000, dtype="f32"), None),
     "bf16_top256": (_spec(top_k=256, vocab=20000), None),
-    "f32_top256": (_spec(top_k=256, vocab=20000, dtype="f32"), None),
     "bf16_zipf_ragged": (_spec(kind="zipf", k=8, ragged=True, vocab=60000, temperature=0.7), None),
     "bf16_ties": (_spec(vocab=9000), _ties),
     "bf16_constant_rows": (_spec(vocab=3000), _constant),
