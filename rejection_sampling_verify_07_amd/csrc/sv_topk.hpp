@@ -785,82 +785,73 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     float m;
     double s_sum = 0.0;
     int32_t kept_n;
-    if (nkept <= keep_cap) {
+    if (nkept <= keep_cap && nkept <= kKeepCapList) {
+        // the kept entries into LDS in any order (an LDS slot counter), then
+        // sorted by id (bitonic); the row's maximum is one of them
+        if (threadIdx.x == 0) s_misc[4] = 0;
+        __syncthreads();
         if (fast) {
-            // compact the candidates >= tau, then sort them by id (bitonic)
-            if (threadIdx.x == 0) s_misc[4] = 0;
-            __syncthreads();
             for (int32_t i = threadIdx.x; i < total; i += kThreads) {
                 if (s_key[i] >= tau_key) {
                     const int32_t slot = atomicAdd(&s_misc[4], 1);
-                    if (slot < 1024) {
+                    if (slot < kKeepCapList) {
                         s_kidx[slot] = s_idx[i];
                         s_kval[slot] = key_to_float(s_key[i]);
                     }
                 }
             }
-            __syncthreads();
-            int32_t npad = 1;
-            while (npad < nkept) npad <<= 1;
-            for (int32_t i = nkept + threadIdx.x; i < npad; i += kThreads) {
-                s_kidx[i] = INT32_MAX;
-                s_kval[i] = neg_inf();
-            }
-            __syncthreads();
-            for (int32_t size = 2; size <= npad; size <<= 1) {
-                for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                    for (int32_t i = threadIdx.x; i < npad; i += kThreads) {
-                        const int32_t p = i ^ stride;
-                        if (p > i) {
-                            const bool up = (i & size) == 0;
-                            const int32_t a = s_kidx[i], bb = s_kidx[p];
-                            if ((a > bb) == up) {
-                                s_kidx[i] = bb;
-                                s_kidx[p] = a;
-                                const float t = s_kval[i];
-                                s_kval[i] = s_kval[p];
-                                s_kval[p] = t;
-                            }
-                        }
-                    }
-                    __syncthreads();
-                }
-            }
-            for (int32_t i = threadIdx.x; i < nkept; i += kThreads) klist[i] = KeptEntry{s_kidx[i], s_kval[i]};
-            // max and sum over the list (fixed order)
-            float lm = neg_inf();
-            for (int32_t i = threadIdx.x; i < nkept; i += kThreads) lm = fmaxf(lm, s_kval[i]);
-            m = block_max_float(lm, s_f);
-            const float mcc = m * c;
-            double ls = 0.0;
-            for (int32_t i = threadIdx.x; i < nkept; i += kThreads)
-                ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(s_kval[i], c, -mcc));
-            s_sum = block_sum_double(ls, s_d);
         } else {
-            // ordered compaction straight from the row, after its max
-            m = block_row_max<DT>(rowp, vocab, s_f);
-            const float mcc = m * c;
-            int32_t base = 0;
-            double ls = 0.0;
+            // one walk of the row: at most a list's worth of ids pass
             for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
-                int cnt = 0;
-#pragma unroll
-                for (int e = 0; e < Dt<DT>::kVec; ++e) cnt += (ok[e] && order_key(f[e]) >= tau_key);
-                int tot;
-                int pos = base + block_excl_scan_int(cnt, s_w, &tot);
-                float s = 0.0f;
 #pragma unroll
                 for (int e = 0; e < Dt<DT>::kVec; ++e) {
                     if (ok[e] && order_key(f[e]) >= tau_key) {
-                        klist[pos++] = KeptEntry{r0 + e, f[e]};
-                        s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+                        const int32_t slot = atomicAdd(&s_misc[4], 1);
+                        if (slot < kKeepCapList) {
+                            s_kidx[slot] = r0 + e;
+                            s_kval[slot] = f[e];
+                        }
                     }
                 }
-                ls += (double)s;
-                base += tot;
             });
-            s_sum = block_sum_double(ls, s_d);
         }
+        __syncthreads();
+        int32_t npad = 1;
+        while (npad < nkept) npad <<= 1;
+        for (int32_t i = nkept + threadIdx.x; i < npad; i += kThreads) {
+            s_kidx[i] = INT32_MAX;
+            s_kval[i] = neg_inf();
+        }
+        __syncthreads();
+        for (int32_t size = 2; size <= npad; size <<= 1) {
+            for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int32_t i = threadIdx.x; i < npad; i += kThreads) {
+                    const int32_t p = i ^ stride;
+                    if (p > i) {
+                        const bool up = (i & size) == 0;
+                        const int32_t a = s_kidx[i], bb = s_kidx[p];
+                        if ((a > bb) == up) {
+                            s_kidx[i] = bb;
+                            s_kidx[p] = a;
+                            const float t = s_kval[i];
+                            s_kval[i] = s_kval[p];
+                            s_kval[p] = t;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int32_t i = threadIdx.x; i < nkept; i += kThreads) klist[i] = KeptEntry{s_kidx[i], s_kval[i]};
+        // max and sum over the list (fixed order)
+        float lm = neg_inf();
+        for (int32_t i = threadIdx.x; i < nkept; i += kThreads) lm = fmaxf(lm, s_kval[i]);
+        m = block_max_float(lm, s_f);
+        const float mcc = m * c;
+        double ls = 0.0;
+        for (int32_t i = threadIdx.x; i < nkept; i += kThreads)
+            ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(s_kval[i], c, -mcc));
+        s_sum = block_sum_double(ls, s_d);
         kept_n = nkept;
     } else {
         // too many kept ids for a list: describe the row as "full row masked by tau"
