@@ -760,8 +760,108 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
 
     // ---- exact top_k-th largest key
     int32_t greater = 0, equal = 0;
-    uint32_t tau_key;
-    if (fast) {
+    uint32_t tau_key = 0;
+    // Full rows first take two walks: (1) a histogram of the top 12 key bits
+    // (s_key as 4096 counters: few keys share a counter), which gives the
+    // bucket holding the top_k-th key, the count above it and its size;
+    // (2) the bucket's own entries staged in LDS, where the select finishes,
+    // and, when the list can hold them, the ids above the bucket straight
+    // into it.  Only a bucket too large for LDS leaves the select to the
+    // radix passes over the row below.
+    bool staged = false;  // s_kidx / s_kval already hold the kept entries
+    bool have_tau = false;
+    if (!fast) {
+        for (int i = threadIdx.x; i < kSelCap; i += kThreads) s_key[i] = 0;
+        __syncthreads();
+        for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+#pragma unroll
+            for (int e = 0; e < Dt<DT>::kVec; ++e)
+                if (ok[e]) atomicAdd(&s_key[order_key(f[e]) >> 20], 1u);
+        });
+        __syncthreads();
+        // thread t owns buckets 4095 - 16t down to 4080 - 16t
+        constexpr int kPer = kSelCap / kThreads;
+        const int32_t top = kSelCap - 1 - kPer * (int32_t)threadIdx.x;
+        int32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) mine += (int32_t)s_key[top - j];
+        int32_t tot;
+        const int32_t excl = block_excl_scan_int(mine, s_w, &tot);
+        if (threadIdx.x == 0) s_misc[5] = -1;
+        __syncthreads();
+        if (excl < top_k && excl + mine >= top_k) {
+            int32_t cum = excl;
+            for (int j = 0; j < kPer; ++j) {
+                const int32_t n = (int32_t)s_key[top - j];
+                if (cum + n >= top_k) {
+                    s_misc[5] = top - j;  // the bucket
+                    s_misc[6] = cum;      // ids above it
+                    s_misc[7] = n;        // ids in it
+                    break;
+                }
+                cum += n;
+            }
+        }
+        __syncthreads();
+        const int32_t bucket = s_misc[5], above = s_misc[6], inb = s_misc[7];
+        __syncthreads();
+        if (bucket >= 0 && inb <= kSelCap) {
+            const bool list = above + inb <= kKeepCapList && above + inb <= keep_cap;
+            if (threadIdx.x == 0) {
+                s_misc[4] = 0;  // kept ids so far
+                s_misc[3] = 0;  // staged entries of the bucket
+            }
+            __syncthreads();
+            for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
+#pragma unroll
+                for (int e = 0; e < Dt<DT>::kVec; ++e) {
+                    if (!ok[e]) continue;
+                    const uint32_t key = order_key(f[e]);
+                    const int32_t b = (int32_t)(key >> 20);
+                    if (b > bucket) {
+                        if (!list) continue;
+                        const int32_t slot = atomicAdd(&s_misc[4], 1);
+                        if (slot < kKeepCapList) {
+                            s_kidx[slot] = r0 + e;
+                            s_kval[slot] = f[e];
+                        }
+                    } else if (b == bucket) {
+                        const int32_t slot = atomicAdd(&s_misc[3], 1);
+                        if (slot < kSelCap) {
+                            s_key[slot] = key;
+                            s_idx[slot] = r0 + e;
+                        }
+                    }
+                }
+            });
+            __syncthreads();
+            const int32_t nb = min(s_misc[3], kSelCap);
+            int32_t gb, eb;
+            tau_key = block_radix_select(
+                [&](auto&& fn) {
+                    for (int32_t i = threadIdx.x; i < nb; i += kThreads) fn(s_key[i]);
+                },
+                top_k - above, LOW, s_hist, s_misc, &gb, &eb);
+            greater = above + gb;
+            equal = eb;
+            // the bucket's entries >= tau join the list
+            for (int32_t i = threadIdx.x; list && i < nb; i += kThreads) {
+                if (s_key[i] >= tau_key) {
+                    const int32_t slot = atomicAdd(&s_misc[4], 1);
+                    if (slot < kKeepCapList) {
+                        s_kidx[slot] = s_idx[i];
+                        s_kval[slot] = key_to_float(s_key[i]);
+                    }
+                }
+            }
+            __syncthreads();
+            staged = list;
+            have_tau = true;
+        }
+    }
+    if (have_tau) {
+        // done above
+    } else if (fast) {
         tau_key = block_radix_select(
             [&](auto&& fn) {
                 for (int32_t i = threadIdx.x; i < total; i += kThreads) fn(s_key[i]);
@@ -788,9 +888,11 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     if (nkept <= keep_cap && nkept <= kKeepCapList) {
         // the kept entries into LDS in any order (an LDS slot counter), then
         // sorted by id (bitonic); the row's maximum is one of them
-        if (threadIdx.x == 0) s_misc[4] = 0;
+        if (!staged && threadIdx.x == 0) s_misc[4] = 0;
         __syncthreads();
-        if (fast) {
+        if (staged) {
+            // already in s_kidx / s_kval
+        } else if (fast) {
             for (int32_t i = threadIdx.x; i < total; i += kThreads) {
                 if (s_key[i] >= tau_key) {
                     const int32_t slot = atomicAdd(&s_misc[4], 1);

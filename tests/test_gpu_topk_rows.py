@@ -127,6 +127,11 @@ CASES = {
     "bf16_top240": (_spec(top_k=240, vocab=20000), None),
     "f32_top240": (_spec(top_k=240, vocab=20000, dtype="f32"), None),
     "bf16_top256": (_spec(top_k=256, vocab=20000), None),
+    # top_k above the candidate pass: the exact select over full rows
+    "bf16_top300_ties": (_spec(top_k=300, vocab=20000), _ties),  # staged bucket, ties at tau
+    "bf16_top300_constant_rows": (_spec(top_k=300, vocab=20000), _constant),  # bucket too large for LDS
+    "f32_top1000": (_spec(top_k=1000, vocab=20000, dtype="f32"), None),  # list filled by a separate walk
+    "bf16_top2000": (_spec(top_k=2000, vocab=20000), None),  # more kept ids than a list holds
     "bf16_zipf_ragged": (_spec(kind="zipf", k=8, ragged=True, vocab=60000, temperature=0.7), None),
     "bf16_ties": (_spec(vocab=9000), _ties),
     "bf16_constant_rows": (_spec(vocab=3000), _constant),
