@@ -232,6 +232,7 @@ __device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int
 // chunk overflowed or the survivors do not fit the kept list.
 constexpr int kSpecChunks = 16;
 constexpr int kSpecSlots = 2;
+constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (512 slots: all of them)
 
 // The select over n candidates staged in L.kidx / L.kval (n <= NJ * 64).
 template <int DT, int NJ>
@@ -311,11 +312,17 @@ __device__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int
                 const int32_t cnt = __builtin_amdgcn_readlane(cnt_b, ch);
 #pragma unroll
                 for (int q = 0; q < kSpecSlots; ++q) keep(e[ch][q], q * kWave + lane < cnt);
-                // slots past the first batch (at most cap), one round of loads each
-                for (int32_t q = kSpecSlots; q * kWave < cnt; ++q) {
-                    const int32_t i = q * kWave + lane;
-                    const KeptEntry x = i < cnt ? cands[(t0 + c0 + ch) * cap + i] : KeptEntry{INT32_MAX, neg_inf()};
-                    keep(x, i < cnt);
+                // slots past the first batch (at most cap), kSpecExtra rounds of
+                // loads in flight together
+                for (int32_t q0 = kSpecSlots; q0 * kWave < cnt; q0 += kSpecExtra) {
+                    KeptEntry x[kSpecExtra];
+#pragma unroll
+                    for (int u = 0; u < kSpecExtra; ++u) {
+                        const int32_t i = (q0 + u) * kWave + lane;
+                        x[u] = i < cnt ? cands[(t0 + c0 + ch) * cap + i] : KeptEntry{INT32_MAX, neg_inf()};
+                    }
+#pragma unroll
+                    for (int u = 0; u < kSpecExtra; ++u) keep(x[u], (q0 + u) * kWave + lane < cnt);
                 }
             }
         }
