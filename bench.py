@@ -276,12 +276,11 @@ def main():
     roof = None
     if not args.no_profile_pass:
         ev = sv.HipEvents(K)
-        ev.arm()
+        pairs = [ev.pair(i) for i in range(K)]
         torch.cuda.synchronize()
         for i in range(K):
-            plans[i % copies]()
+            plans[i % copies].profiled(pairs[i])
         torch.cuda.synchronize()
-        sv.HipEvents.disarm()
         dur = np.array(ev.elapsed_ms()) * 1e-3
         ev.close()
         avg = float(dur.mean())

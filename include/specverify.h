@@ -55,11 +55,13 @@
  *   Errors.  Argument checks are synchronous and happen before any launch:
  *   SV_ERR_INVALID_ARGUMENT (null or misaligned pointer, B < 1, V < 1,
  *   K < 0, total_draft inconsistent with B*K when cu_draft is NULL, stride
- *   < V, temperature not finite and > 0, top_k < 0 or > V),
+ *   < V, temperature not finite and > 0, or so small that log2(e) / T
+ *   overflows fp32 (T below about 4.2e-39), top_k < 0 or > V),
  *   SV_ERR_UNSUPPORTED (V > SV_MAX_VOCAB, max_draft > SV_MAX_DRAFT),
  *   SV_ERR_WORKSPACE_TOO_SMALL, SV_ERR_HIP (a launch failed).  Data
  *   preconditions are the caller's: logits finite or -inf with at least one
- *   finite logit in each row's kept set; cu_draft monotone.  The kernels
+ *   finite logit in each row's kept set, and |logit| * log2(e) / T finite in
+ *   fp32; cu_draft monotone.  The kernels
  *   never read out of bounds when they are violated: a bad sequence reports
  *   num_accepted = -1.
  */
@@ -130,7 +132,8 @@ typedef struct {
  * Arguments
  *   target_logits [rows_t, stride] and draft_logits [rows_d, stride] in
  *   shape->dtype; draft_ids int32 [total_draft] in [0, V).
- *   temperature > 0 and finite.  top_k in [0, V].  top_p in (0, 1]; 1 is
+ *   temperature > 0, finite, and >= about 4.2e-39 (log2(e) / T must be a
+ *   finite fp32).  top_k in [0, V].  top_p in (0, 1]; 1 is
  *   off.  top-p over full rows costs several extra reads of each row (a
  *   mass-weighted radix select); after top-k it works on the kept lists.
  *   out_tokens int32 [total_draft + B]; out_num_accepted int32 [B];
@@ -280,16 +283,6 @@ SV_API sv_status_t spec_token_likelihood(const sv_shape_t* shape,
 
 /* A static, human-readable name for a status code. */
 SV_API const char* spec_verify_status_string(sv_status_t status);
-
-/*
- * Profiling hook (not thread-safe; for benchmarks).  When `starts` and
- * `stops` are non-NULL, the next n calls of spec_verify_sample /
- * spec_verify_greedy record starts[i] right before and stops[i] right after
- * the launch of their streaming pass (the kernel that reads every logit),
- * on the call's stream.  Call with n = 0 to switch it off.  The events are
- * owned by the caller.
- */
-SV_API sv_status_t spec_verify_set_profile_events(hipEvent_t* starts, hipEvent_t* stops, int32_t n);
 
 #ifdef __cplusplus
 }

@@ -49,13 +49,30 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out: str) -> str:
+    """The same oracle built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (every report fatal), for a CPU test run under SPECVERIFY_ORACLE_LIB; the
+    Python process needs libasan preloaded."""
+    cmd = [
+        os.environ.get("CC", "gcc"), "-O1", "-g", "-std=c11", "-Wall", "-Wextra",
+        "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+        "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+        "-o", out, _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = C.CDLL(_LIB_PATH)
+    path = os.environ.get("SPECVERIFY_ORACLE_LIB")  # another build of the same source (sanitized)
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+    lib = C.CDLL(path)
     P = C.c_void_p
     lib.orc_decode.restype = C.c_double
     lib.orc_decode.argtypes = [P, C.c_int32, C.c_int64]

@@ -796,6 +796,15 @@ int orc_verify_greedy(int32_t B, const int32_t* cu, int64_t V, int32_t dtype,
         int64_t trow0 = (int64_t)cu[b] + b;
         int64_t drow0 = cu[b];
         for (int32_t j = 0; j <= K; ++j) tokens[trow0 + j] = -1;
+        /* a guess outside [0, V) makes the sequence invalid (reported as -1),
+           wherever it stands, as in the sampling variant */
+        int bad = 0;
+        for (int32_t k = 0; k < K; ++k)
+            if (ids[drow0 + k] < 0 || (int64_t)ids[drow0 + k] >= V) bad = 1;
+        if (bad) {
+            n_acc[b] = -1;
+            continue;
+        }
         int32_t n = K;
         for (int32_t k = 0; k <= K; ++k) {
             const char* row = (const char*)target + (size_t)(trow0 + k) * (size_t)t_stride * esz;

@@ -33,6 +33,11 @@ class SpecVerifyError(RuntimeError):
         self.status = status
 
 
+class ProfileEventsT(C.Structure):
+    """sv_profile_events_t (specverify_profile.h): two raw HIP events."""
+    _fields_ = [("start", C.c_void_p), ("stop", C.c_void_p)]
+
+
 class ShapeT(C.Structure):
     _fields_ = [
         ("batch", C.c_int32),
@@ -81,8 +86,12 @@ def load_library(path: Optional[str] = None):
     ]
     lib.spec_verify_status_string.restype = C.c_char_p
     lib.spec_verify_status_string.argtypes = [C.c_int]
-    lib.spec_verify_set_profile_events.restype = C.c_int
-    lib.spec_verify_set_profile_events.argtypes = [VP, VP, C.c_int32]
+    # benchmark entry points: the same calls with a leading events argument
+    for name in ("spec_verify_sample", "spec_verify_argmax", "spec_verify_greedy", "spec_draft_sample",
+                 "spec_token_likelihood"):
+        f = getattr(lib, name + "_profiled")
+        f.restype = C.c_int
+        f.argtypes = [C.POINTER(ProfileEventsT)] + list(getattr(lib, name).argtypes)
     if path is None:
         _lib = lib
     return lib
@@ -120,10 +129,27 @@ def _rows(t: torch.Tensor, name: str):
 
 
 def make_shape(target: torch.Tensor, draft: Optional[torch.Tensor], batch: int, max_draft: int,
-               total_draft: int, cu_draft: Optional[torch.Tensor]) -> ShapeT:
+               total_draft: int, cu_draft: Optional[torch.Tensor], target_rows: int,
+               draft_rows: int = 0) -> ShapeT:
+    """The C shape of a call.  target_rows / draft_rows: the rows the call
+    reads from each tensor (the kernels index rows by the geometry, so a tensor
+    that is shorter, or of another element type or width than the other, would
+    be read past its end)."""
+    if target.dim() != 2:
+        raise ValueError("target_logits must be a 2-D tensor with unit column stride")
     vocab = target.shape[1]
+    if target.shape[0] < target_rows:
+        raise ValueError(f"target_logits has {target.shape[0]} rows; the batch needs {target_rows}")
+    other = draft is not None and draft is not target
+    if other:
+        if draft.dtype != target.dtype:
+            raise ValueError(f"draft_logits is {draft.dtype} but target_logits is {target.dtype}")
+        if draft.dim() != 2 or draft.shape[1] != vocab:
+            raise ValueError(f"draft_logits must have {vocab} columns, like target_logits")
+        if draft.shape[0] < draft_rows:
+            raise ValueError(f"draft_logits has {draft.shape[0]} rows; the batch needs {draft_rows}")
     ts = _rows(target, "target_logits")
-    ds = _rows(draft, "draft_logits") if (draft is not None and draft.numel() > 0) else vocab
+    ds = _rows(draft, "draft_logits") if (other and draft.numel() > 0) else vocab
     return ShapeT(
         batch=batch, max_draft=max_draft, total_draft=total_draft, vocab=vocab, dtype=_dtype_code(target),
         target_row_stride=ts, draft_row_stride=ds,
@@ -144,6 +170,11 @@ def _batch_geometry(target, draft_ids, cu_draft, max_draft):
     if cu_draft.dtype != torch.int32 or cu_draft.dim() != 1:
         raise ValueError("cu_draft must be a 1-D int32 tensor")
     batch = cu_draft.numel() - 1
+    if batch < 1:
+        raise ValueError("cu_draft needs B + 1 >= 2 entries")
+    if target.shape[0] < total + batch:
+        raise ValueError(f"target_logits has {target.shape[0]} rows; {batch} sequences with {total} draft ids "
+                         f"need {total + batch}")
     if max_draft is None:
         max_draft = int((cu_draft[1:] - cu_draft[:-1]).max().item()) if batch > 0 else 0
     return batch, max_draft, total
@@ -174,7 +205,7 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
     batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
     if draft_ids.dtype != torch.int32:
         raise TypeError("draft_ids must be int32")
-    shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
+    shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft, total + batch, total)
     dev = target_logits.device
     need = C.c_size_t(0)
     _check(fn(C.byref(shape), None, None, None, float(temperature), int(top_k), float(top_p), int(seed),
@@ -215,7 +246,7 @@ def verify_greedy(target_logits: torch.Tensor, draft_ids: torch.Tensor, cu_draft
     batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
     if draft_ids.dtype != torch.int32:
         raise TypeError("draft_ids must be int32")
-    shape = make_shape(target_logits, None, batch, kmax, total, cu_draft)
+    shape = make_shape(target_logits, None, batch, kmax, total, cu_draft, total + batch)
     dev = target_logits.device
     need = C.c_size_t(0)
     _check(lib.spec_verify_greedy(C.byref(shape), None, None, None, None, None, C.byref(need), None),
@@ -265,7 +296,7 @@ def draft_sample(draft_logits: torch.Tensor, cu_draft: Optional[torch.Tensor] = 
     """
     lib = load_library()
     b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
-    shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
+    shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft, total)
     dev = draft_logits.device
     need = C.c_size_t(0)
     _check(lib.spec_draft_sample(C.byref(shape), None, float(temperature), int(top_k), float(top_p), int(seed),
@@ -319,7 +350,7 @@ def token_likelihood(target_logits: torch.Tensor, draft_logits: torch.Tensor, to
     if target_logits.shape[0] != draft_logits.shape[0] or target_logits.shape[0] != tokens.numel():
         raise ValueError("target_logits, draft_logits and tokens need one row per position")
     b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
-    shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
+    shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft, total, total)
     dev = target_logits.device
     need = C.c_size_t(0)
     _check(lib.spec_token_likelihood(C.byref(shape), None, None, None, float(temperature), int(top_k), float(top_p),
@@ -342,7 +373,8 @@ def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k
                     greedy=False) -> int:
     lib = load_library()
     batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
-    shape = make_shape(target_logits, None if greedy else draft_logits, batch, kmax, total, cu_draft)
+    shape = make_shape(target_logits, None if greedy else draft_logits, batch, kmax, total, cu_draft, total + batch,
+                       0 if greedy else total)
     need = C.c_size_t(0)
     if greedy:
         st = lib.spec_verify_greedy(C.byref(shape), None, None, None, None, None, C.byref(need), None)
@@ -354,7 +386,9 @@ def workspace_bytes(target_logits, draft_logits, draft_ids, cu_draft=None, top_k
 
 
 class HipEvents:
-    """n pairs of raw HIP events (created eagerly) for the profiling hook."""
+    """n pairs of raw HIP events (created eagerly), passed one pair per call
+    to the *_profiled entry points, which record them around the streaming
+    kernel of that call."""
 
     def __init__(self, n: int):
         self._hip = C.CDLL("libamdhip64.so")
@@ -362,41 +396,56 @@ class HipEvents:
         self._hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self._hip.hipEventDestroy.argtypes = [C.c_void_p]
         self.n = n
-        self.starts = (C.c_void_p * n)()
-        self.stops = (C.c_void_p * n)()
+        self.pairs = (ProfileEventsT * n)()
         for i in range(n):
-            for arr in (self.starts, self.stops):
+            for field in ("start", "stop"):
                 h = C.c_void_p()
                 if self._hip.hipEventCreate(C.byref(h)) != 0:
                     raise RuntimeError("hipEventCreate failed")
-                arr[i] = h
+                setattr(self.pairs[i], field, h.value)
 
-    def arm(self):
-        """The next n library calls record their streaming kernel into these events."""
-        _check(load_library().spec_verify_set_profile_events(self.starts, self.stops, self.n), "profile events")
-
-    @staticmethod
-    def disarm():
-        _check(load_library().spec_verify_set_profile_events(None, None, 0), "profile events")
+    def pair(self, i: int):
+        """A pointer to pair i, the leading argument of a *_profiled call."""
+        return C.pointer(self.pairs[i])
 
     def elapsed_ms(self):
         """Per-call durations (ms) of the streaming kernel; call after a device sync."""
         out = []
         for i in range(self.n):
             ms = C.c_float(0)
-            if self._hip.hipEventElapsedTime(C.byref(ms), self.starts[i], self.stops[i]) != 0:
+            if self._hip.hipEventElapsedTime(C.byref(ms), self.pairs[i].start, self.pairs[i].stop) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
             out.append(ms.value)
         return out
 
     def close(self):
         for i in range(self.n):
-            self._hip.hipEventDestroy(self.starts[i])
-            self._hip.hipEventDestroy(self.stops[i])
+            self._hip.hipEventDestroy(self.pairs[i].start)
+            self._hip.hipEventDestroy(self.pairs[i].stop)
         self.n = 0
 
 
-class SamplePlan:
+class _Plan:
+    """A call with every argument marshalled once (for tight loops).  __call__
+    enqueues it; profiled(events) enqueues the *_profiled form with a pointer
+    from HipEvents.pair()."""
+
+    name = ""
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, self.name)
+        return self.out
+
+    def profiled(self, events):
+        st = self.fn_profiled(events, *self.args)
+        if st != SV_OK:
+            raise SpecVerifyError(st, self.name + "_profiled")
+        return self.out
+
+
+class SamplePlan(_Plan):
     """spec_verify_sample with every argument marshalled once (for tight loops).
 
     Holds references to the tensors it was built from; __call__ enqueues one
@@ -408,7 +457,7 @@ class SamplePlan:
                  top_p=1.0):
         self.lib = load_library()
         batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
-        self.shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft)
+        self.shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft, total + batch, total)
         dev = target_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_verify_sample(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
@@ -431,22 +480,20 @@ class SamplePlan:
                      C.c_void_p(self.out["residual_mass"].data_ptr() if probs else None),
                      C.c_void_p(self.workspace.data_ptr()), C.byref(self.have),
                      C.c_void_p(_stream_handle(stream)))
-        self.fn = self.lib.spec_verify_argmax if argmax else self.lib.spec_verify_sample
-
-    def __call__(self):
-        st = self.fn(*self.args)
-        if st != SV_OK:
-            raise SpecVerifyError(st, "spec_verify_sample")
+        self.name = "spec_verify_argmax" if argmax else "spec_verify_sample"
+        self.fn = getattr(self.lib, self.name)
+        self.fn_profiled = getattr(self.lib, self.name + "_profiled")
 
 
-class GreedyPlan:
+
+class GreedyPlan(_Plan):
     """spec_verify_greedy with every argument marshalled once."""
 
     def __init__(self, target_logits, draft_ids, cu_draft=None, max_draft=None, out=None, workspace=None,
                  stream=None):
         self.lib = load_library()
         batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
-        self.shape = make_shape(target_logits, None, batch, kmax, total, cu_draft)
+        self.shape = make_shape(target_logits, None, batch, kmax, total, cu_draft, total + batch)
         dev = target_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_verify_greedy(C.byref(self.shape), None, None, None, None, None, C.byref(need), None),
@@ -461,22 +508,20 @@ class GreedyPlan:
                      C.c_void_p(draft_ids.data_ptr() if draft_ids.numel() else None),
                      C.c_void_p(self.out["tokens"].data_ptr()), C.c_void_p(self.out["num_accepted"].data_ptr()),
                      C.c_void_p(self.workspace.data_ptr()), C.byref(self.have), C.c_void_p(_stream_handle(stream)))
-        self.fn = self.lib.spec_verify_greedy
-
-    def __call__(self):
-        st = self.fn(*self.args)
-        if st != SV_OK:
-            raise SpecVerifyError(st, "spec_verify_greedy")
+        self.name = "spec_verify_greedy"
+        self.fn = getattr(self.lib, self.name)
+        self.fn_profiled = getattr(self.lib, self.name + "_profiled")
 
 
-class LikelihoodPlan:
+
+class LikelihoodPlan(_Plan):
     """spec_token_likelihood with every argument marshalled once."""
 
     def __init__(self, target_logits, draft_logits, tokens, cu_draft=None, batch=None, temperature=1.0, top_k=0,
                  max_draft=None, terms=True, beta=True, nll=True, workspace=None, stream=None, top_p=1.0):
         self.lib = load_library()
         b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
-        self.shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft)
+        self.shape = make_shape(target_logits, draft_logits, b, kmax, total, cu_draft, total, total)
         dev = target_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_token_likelihood(C.byref(self.shape), None, None, None, float(temperature), int(top_k),
@@ -492,23 +537,20 @@ class LikelihoodPlan:
                      C.c_void_p(_ptr_or_none(self.out, "terms")), C.c_void_p(_ptr_or_none(self.out, "beta")),
                      C.c_void_p(_ptr_or_none(self.out, "nll")), C.c_void_p(self.workspace.data_ptr()),
                      C.byref(self.have), C.c_void_p(_stream_handle(stream)))
-        self.fn = self.lib.spec_token_likelihood
-
-    def __call__(self):
-        st = self.fn(*self.args)
-        if st != SV_OK:
-            raise SpecVerifyError(st, "spec_token_likelihood")
-        return self.out
+        self.name = "spec_token_likelihood"
+        self.fn = getattr(self.lib, self.name)
+        self.fn_profiled = getattr(self.lib, self.name + "_profiled")
 
 
-class DraftPlan:
+
+class DraftPlan(_Plan):
     """spec_draft_sample with every argument marshalled once."""
 
     def __init__(self, draft_logits, cu_draft=None, batch=None, temperature=1.0, top_k=0, seed=0, offset=0,
                  max_draft=None, out=None, workspace=None, stream=None, top_p=1.0):
         self.lib = load_library()
         b, kmax, total = _draft_geometry(draft_logits, cu_draft, batch, max_draft)
-        self.shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft)
+        self.shape = make_shape(draft_logits, draft_logits, b, kmax, total, cu_draft, total)
         dev = draft_logits.device
         need = C.c_size_t(0)
         _check(self.lib.spec_draft_sample(C.byref(self.shape), None, float(temperature), int(top_k), float(top_p),
@@ -522,9 +564,7 @@ class DraftPlan:
                      C.c_int32(top_k), C.c_float(top_p), C.c_uint64(seed), C.c_uint32(offset),
                      C.c_void_p(self.out.data_ptr()),
                      C.c_void_p(self.workspace.data_ptr()), C.byref(self.have), C.c_void_p(_stream_handle(stream)))
-        self.fn = self.lib.spec_draft_sample
+        self.name = "spec_draft_sample"
+        self.fn = getattr(self.lib, self.name)
+        self.fn_profiled = getattr(self.lib, self.name + "_profiled")
 
-    def __call__(self):
-        st = self.fn(*self.args)
-        if st != SV_OK:
-            raise SpecVerifyError(st, "spec_draft_sample")

@@ -21,13 +21,24 @@ def hipcc_path() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer for the argument
+# checks, plan and workspace layout (the device code is built as usual): each
+# -fsanitize applies to the host compilation only.
+HOST_SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-g",
+]
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), host_sanitize: bool = False) -> str:
     """Compile the HIP sources into rejection_sampling_verify_07_amd/libspecverify.so
-    (or `out`, with extra -D defines, for tuning builds)."""
+    (or `out`, with extra -D defines, for tuning builds; host_sanitize: a host
+    ASan/UBSan build for the CPU tests of the argument checks)."""
     src = os.path.join(CSRC, "specverify.hip")
     tmp = out + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-I",
-           CSRC, src, "-o", tmp]
+    extra = HOST_SANITIZE_FLAGS if host_sanitize else []
+    cmd = [hipcc_path(), *HIPCC_FLAGS, *extra, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"),
+           "-I", CSRC, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

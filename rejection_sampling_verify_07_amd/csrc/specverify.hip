@@ -1,6 +1,7 @@
 // specverify C ABI: argument checks, workspace layout and kernel launches.
 // The operation and the conventions are documented in include/specverify.h.
 #include "specverify.h"
+#include "specverify_profile.h"
 
 #include <hip/hip_ext.h>
 
@@ -35,9 +36,6 @@ namespace {
 #ifndef SV_STREAM_NT
 #define SV_STREAM_NT 1
 #endif
-#ifndef SV_STREAM_PIPE
-#define SV_STREAM_PIPE 0
-#endif
 constexpr int kLoads = SV_STREAM_LOADS;      // row statistics (sampling and greedy)
 constexpr int kLoadsBig = 8;                 // row statistics over grids much larger than the chip
 constexpr int kLoadsBigArgmax = 6;           // the greedy argmax pass over such grids (measured: 93.1 against 94.5 us
@@ -45,7 +43,6 @@ constexpr int kLoadsBigArgmax = 6;           // the greedy argmax pass over such
 constexpr int64_t kBigGridTiles = 16384;     // 4-load tiles beyond which kLoadsBig is used (8x the resident slots)
 constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
 constexpr bool kNT = SV_STREAM_NT != 0;
-constexpr bool kPipe = SV_STREAM_PIPE != 0;  // persistent pipelined grid instead of one tile per workgroup
 constexpr int32_t kCandCap = 512;    // candidate slots per (row, chunk) in the top-k pass
 // Largest top_k that takes the candidate pass.  Close to the pass's own
 // limit (one lane maximum per thread, 256) the tile bound is the smallest lane
@@ -104,54 +101,31 @@ int32_t chunks_for(int32_t vocab, int vec, int loads)
     return (int32_t)((nblk + per - 1) / per);
 }
 
-// ---- profiling hook (benchmarks only; not thread-safe)
-hipEvent_t* g_prof_start = nullptr;
-hipEvent_t* g_prof_stop = nullptr;
-int32_t g_prof_n = 0;
-int32_t g_prof_i = 0;
-
-// Workgroups of `kernel` the current device keeps resident at once: the
-// grid of the persistent streaming passes.  Cached per kernel and device.
-template <class K>
-uint32_t resident_grid(K kernel)
-{
-    struct Entry {
-        const void* fn;
-        int dev;
-        uint32_t grid;
-    };
-    static Entry cache[32];
-    static int n_cache = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    for (int i = 0; i < n_cache; ++i)
-        if (cache[i].fn == (const void*)kernel && cache[i].dev == dev) return cache[i].grid;
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, sv::kThreads, 0) != hipSuccess) return 0;
-    const uint32_t g = (uint32_t)(cus > 0 ? cus : 1) * (uint32_t)(per_cu > 0 ? per_cu : 1);
-    if (n_cache < 32) cache[n_cache++] = Entry{(const void*)kernel, dev, g};
-    return g;
-}
-
-// Launch a streaming-pass kernel over `ntiles` tiles with a resident grid;
-// while the hook is armed, the launch itself records the kernel's start and
-// end into the caller's events.
+// Launch a streaming-pass kernel, one tile per workgroup.  With `prof`
+// (the benchmark entry points), the launch itself records the caller's
+// events right before and after the kernel on the call's stream.
 template <class K, class... Args>
-void launch_stream(K kernel, uint32_t ntiles, hipStream_t s, Args... args)
+void launch_stream(const sv_profile_events_t* prof, K kernel, uint32_t ntiles, hipStream_t s, Args... args)
 {
-    uint32_t grid = kPipe ? resident_grid(kernel) : ntiles;
-    if (grid == 0 || grid > ntiles) grid = ntiles;
-    if (g_prof_start != nullptr && g_prof_i < g_prof_n) {
-        hipExtLaunchKernelGGL(kernel, dim3(grid), dim3(sv::kThreads), 0, s, g_prof_start[g_prof_i],
-                              g_prof_stop[g_prof_i], 0, args...);
-        ++g_prof_i;
+    if (prof != nullptr) {
+        hipExtLaunchKernelGGL(kernel, dim3(ntiles), dim3(sv::kThreads), 0, s, prof->start, prof->stop, 0, args...);
     } else {
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(sv::kThreads), 0, s, args...);
+        hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(sv::kThreads), 0, s, args...);
     }
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The caller's dtype field as an integer.  A C caller may store any int in
+// it; reading a value outside the enumerators through the C++ enum type is
+// undefined, so the bytes are copied out and checked first.
+static_assert(sizeof(sv_dtype_t) == sizeof(int32_t), "sv_dtype_t is an int-sized enum");
+int32_t dtype_field(const sv_shape_t* sh)
+{
+    int32_t v;
+    memcpy(&v, &sh->dtype, sizeof v);
+    return v;
+}
 
 sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
 {
@@ -159,8 +133,8 @@ sv_status_t check_shape(const sv_shape_t* sh, CallKind kind)
     if (sh == nullptr) return SV_ERR_INVALID_ARGUMENT;
     if (sh->batch < 1 || sh->vocab < 1 || sh->max_draft < 0 || sh->total_draft < 0)
         return SV_ERR_INVALID_ARGUMENT;
-    if (sh->dtype != SV_DTYPE_F32 && sh->dtype != SV_DTYPE_BF16 && sh->dtype != SV_DTYPE_F16)
-        return SV_ERR_INVALID_ARGUMENT;
+    const int32_t dt = dtype_field(sh);
+    if (dt != SV_DTYPE_F32 && dt != SV_DTYPE_BF16 && dt != SV_DTYPE_F16) return SV_ERR_INVALID_ARGUMENT;
     if (sh->cu_draft == nullptr && (int64_t)sh->total_draft != (int64_t)sh->batch * sh->max_draft)
         return SV_ERR_INVALID_ARGUMENT;
     if (sh->cu_draft != nullptr && !aligned(sh->cu_draft, 4)) return SV_ERR_INVALID_ARGUMENT;
@@ -266,17 +240,17 @@ sv_status_t launch_status()
 // fills va.partials (full rows) or va.descs / va.kept (top-k).
 template <int DT>
 sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, void* ws,
-                           hipStream_t stream, sv::VerifyArgs& va)
+                           hipStream_t stream, sv::VerifyArgs& va, const sv_profile_events_t* prof)
 {
     const int32_t top_k = p.top_k;
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows * p.nchunk);
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
         if (p.loads == kLoadsBig) {
-            launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoadsBig, kNT, kPipe, true>, grid_stream, stream, rs,
+            launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_FULL, kLoadsBig, kNT, true>, grid_stream, stream, rs,
                           sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
         } else {
-            launch_stream(sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT, kPipe>, grid_stream, stream, rs,
+            launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT>, grid_stream, stream, rs,
                           sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
         }
         va.partials = part;
@@ -291,7 +265,7 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
         counts = ws_at<int32_t>(ws, p.off_counts);
         bounds = ws_at<float>(ws, p.off_bounds);
         cands = ws_at<sv::KeptEntry>(ws, p.off_cands);
-        launch_stream(sv::topk_cand_kernel<DT, kCandLoads, kNT, kPipe>, grid_stream, stream, rs, sh->vocab, p.nchunk,
+        launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT>, grid_stream, stream, rs, sh->vocab, p.nchunk,
                       (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         // one wave per row; rows whose chunks overflowed take the exact path inside
@@ -299,8 +273,7 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
                            sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, (int32_t)1, descs, kept);
     } else {
         hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
-                           p.nchunk, top_k, kCandCap, c, counts, cands, (int32_t)0, (int32_t)sv::kKeepCap, descs,
-                           kept);
+                           top_k, c, (int32_t)sv::kKeepCap, descs, kept);
     }
     va.descs = descs;
     va.kept = kept;
@@ -312,9 +285,9 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
 // descriptors too).
 template <int DT>
 sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, void* ws,
-                      hipStream_t stream, sv::VerifyArgs& va)
+                      hipStream_t stream, sv::VerifyArgs& va, const sv_profile_events_t* prof)
 {
-    if (run_stats_topk<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (run_stats_topk<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
     if (!p.topp) return SV_OK;
     sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p, va.partials, p.nchunk,
                    ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
@@ -350,7 +323,7 @@ template <int DT>
 sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
                        const int32_t* ids, float c, uint64_t seed, uint32_t offset,
                        int32_t* out_tokens, int32_t* out_nacc, float* out_probs, float* out_z, void* ws,
-                       hipStream_t stream, int32_t argmax_draw)
+                       hipStream_t stream, int32_t argmax_draw, const sv_profile_events_t* prof)
 {
     const size_t es = esize_of(sh->dtype);
     const sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
@@ -363,7 +336,7 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     va.out_probs = out_probs;
     va.out_zmass = out_z;
     va.argmax_draw = argmax_draw;
-    if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (run_stats<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
     if (!p.desc) {
         hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
                            stream, va);
@@ -379,7 +352,7 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
 
 template <int DT>
 sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, float c, uint64_t seed, uint32_t offset,
-                      int32_t* out_ids, void* ws, hipStream_t stream)
+                      int32_t* out_ids, void* ws, hipStream_t stream, const sv_profile_events_t* prof)
 {
     const size_t es = esize_of(sh->dtype);
     // the draft rows are the streamed rows
@@ -387,7 +360,7 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
                         p.rows_t};
     sv::VerifyArgs va = base_args(sh, p, rs, c, seed, offset);
     va.out_tokens = out_ids;
-    if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+    if (run_stats<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
     const dim3 grid((uint32_t)sh->batch, (uint32_t)sh->max_draft);  // max_draft <= SV_MAX_DRAFT fits grid y
     if (!p.desc) {
         // one chunk per row is walked: with many rows, smaller workgroups,
@@ -412,7 +385,7 @@ sv_status_t run_draft(const sv_shape_t* sh, const Plan& p, const void* drf, floa
 template <int DT>
 sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt, const void* drf,
                            const int32_t* tokens, float c, float* out_terms, float* out_beta,
-                           double* out_nll, void* ws, hipStream_t stream)
+                           double* out_nll, void* ws, hipStream_t stream, const sv_profile_events_t* prof)
 {
     const size_t es = esize_of(sh->dtype);
     const sv::RowSet rs{static_cast<const char*>(tgt), static_cast<const char*>(drf),
@@ -434,7 +407,7 @@ sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt,
     la.out_nll = out_nll;
     if (sh->total_draft > 0) {
         sv::VerifyArgs va = base_args(sh, p, rs, c, 0, 0);
-        if (run_stats<DT>(sh, p, rs, c, ws, stream, va) != SV_OK) return SV_ERR_HIP;
+        if (run_stats<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
         la.partials = va.partials;
         la.descs = va.descs;
         la.kept = va.kept;
@@ -463,7 +436,8 @@ sv_status_t run_likelihood(const sv_shape_t* sh, const Plan& p, const void* tgt,
 
 template <int DT>
 sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, const int32_t* ids,
-                       int32_t* out_tokens, int32_t* out_nacc, void* ws, hipStream_t stream)
+                       int32_t* out_tokens, int32_t* out_nacc, void* ws, hipStream_t stream,
+                       const sv_profile_events_t* prof)
 {
     const size_t es = esize_of(sh->dtype);
     sv::RowSet rs{static_cast<const char*>(tgt), nullptr, (int64_t)(sh->target_row_stride * (int64_t)es), 0,
@@ -471,10 +445,10 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     sv::PartialArg* part = ws_at<sv::PartialArg>(ws, p.off_partials);
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows_t * p.nchunk);
     if (p.loads == kLoadsBigArgmax) {
-        launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoadsBigArgmax, kNT, kPipe>, grid_stream, stream, rs,
+        launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoadsBigArgmax, kNT>, grid_stream, stream, rs,
                       sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
     } else {
-        launch_stream(sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT, kPipe>, grid_stream, stream, rs,
+        launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT>, grid_stream, stream, rs,
                       sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
     }
     if (launch_status() != SV_OK) return SV_ERR_HIP;
@@ -485,18 +459,23 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     return launch_status();
 }
 
-// Temperature, top-k and top-p arguments shared by the sampling calls.
+// c = fl32(log2(e) / T): the softmax's exp(l / T) is computed as exp2(l * c).
+float scale_of(float temperature) { return (float)(1.4426950408889634 / (double)temperature); }
+
+// Temperature, top-k and top-p arguments shared by the sampling calls.  A
+// temperature so small that c overflows fp32 (T below about 4.2e-39) is
+// rejected: every weight would be inf/NaN.
 bool filters_ok(const sv_shape_t* sh, float temperature, int32_t top_k, float top_p)
 {
-    return temperature > 0.0f && isfinite(temperature) && top_k >= 0 && top_k <= sh->vocab && top_p > 0.0f &&
-           top_p <= 1.0f;
+    return temperature > 0.0f && isfinite(temperature) && isfinite(scale_of(temperature)) && top_k >= 0 &&
+           top_k <= sh->vocab && top_p > 0.0f && top_p <= 1.0f;
 }
 
 sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
                                  const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
                                  uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
                                  float* out_residual_mass, void* workspace, size_t* workspace_bytes,
-                                 hipStream_t stream, int32_t argmax_draw)
+                                 hipStream_t stream, int32_t argmax_draw, const sv_profile_events_t* prof)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_SAMPLE);
@@ -519,43 +498,18 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
     if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
 
-    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    const float c = scale_of(temperature);
     return by_dtype(shape->dtype, [&](auto dt) {
         return run_sample<decltype(dt)::value>(shape, p, target_logits, draft_logits, draft_ids, c, seed,
                                                offset, out_tokens, out_num_accepted, out_probs, out_residual_mass,
-                                               workspace, stream, argmax_draw);
+                                               workspace, stream, argmax_draw, prof);
     });
 }
 
-}  // namespace
-
-extern "C" {
-
-sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
-                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
-                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
-                               hipStream_t stream)
-{
-    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
-                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
-                                workspace_bytes, stream, 0);
-}
-
-sv_status_t spec_verify_argmax(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
-                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
-                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
-                               hipStream_t stream)
-{
-    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
-                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
-                                workspace_bytes, stream, 1);
-}
-
-sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,
+sv_status_t verify_greedy_common(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,
                                int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
-                               size_t* workspace_bytes, hipStream_t stream)
+                               size_t* workspace_bytes, hipStream_t stream,
+                                 const sv_profile_events_t* prof)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_GREEDY);
@@ -576,13 +530,14 @@ sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logit
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
     return by_dtype(shape->dtype, [&](auto dt) {
         return run_greedy<decltype(dt)::value>(shape, p, target_logits, draft_ids, out_tokens, out_num_accepted,
-                                               workspace, stream);
+                                               workspace, stream, prof);
     });
 }
 
-sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
+sv_status_t draft_sample_common(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
                               float top_p, uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
-                              size_t* workspace_bytes, hipStream_t stream)
+                              size_t* workspace_bytes, hipStream_t stream,
+                                const sv_profile_events_t* prof)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_DRAFT);
@@ -602,17 +557,18 @@ sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits,
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
     if (shape->total_draft == 0 || shape->max_draft == 0) return SV_OK;  // no draft rows: nothing to draw
 
-    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    const float c = scale_of(temperature);
     return by_dtype(shape->dtype, [&](auto dt) {
-        return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, seed, offset, out_ids, workspace, stream);
+        return run_draft<decltype(dt)::value>(shape, p, draft_logits, c, seed, offset, out_ids, workspace, stream,
+                                              prof);
     });
 }
 
-sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+sv_status_t token_likelihood_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
                                   const int32_t* tokens, float temperature, int32_t top_k, float top_p,
                                   float* out_terms,
                                   float* out_beta, double* out_nll, void* workspace, size_t* workspace_bytes,
-                                  hipStream_t stream)
+                                  hipStream_t stream, const sv_profile_events_t* prof)
 {
     if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_LIKE);
@@ -636,11 +592,62 @@ sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_lo
     if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
     if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
 
-    const float c = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+    const float c = scale_of(temperature);
     return by_dtype(shape->dtype, [&](auto dt) {
         return run_likelihood<decltype(dt)::value>(shape, p, target_logits, draft_logits, tokens, c, out_terms,
-                                                   out_beta, out_nll, workspace, stream);
+                                                   out_beta, out_nll, workspace, stream, prof);
     });
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
+                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream)
+{
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 0, nullptr);
+}
+
+sv_status_t spec_verify_argmax(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                               const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
+                               uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                               float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                               hipStream_t stream)
+{
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 1, nullptr);
+}
+
+sv_status_t spec_verify_greedy(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,
+                               int32_t* out_tokens, int32_t* out_num_accepted, void* workspace,
+                               size_t* workspace_bytes, hipStream_t stream)
+{
+    return verify_greedy_common(shape, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
+                                workspace_bytes, stream, nullptr);
+}
+
+sv_status_t spec_draft_sample(const sv_shape_t* shape, const void* draft_logits, float temperature, int32_t top_k,
+                              float top_p, uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
+                              size_t* workspace_bytes, hipStream_t stream)
+{
+    return draft_sample_common(shape, draft_logits, temperature, top_k, top_p, seed, offset, out_ids, workspace,
+                               workspace_bytes, stream, nullptr);
+}
+
+sv_status_t spec_token_likelihood(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                                  const int32_t* tokens, float temperature, int32_t top_k, float top_p,
+                                  float* out_terms, float* out_beta, double* out_nll, void* workspace,
+                                  size_t* workspace_bytes, hipStream_t stream)
+{
+    return token_likelihood_common(shape, target_logits, draft_logits, tokens, temperature, top_k, top_p, out_terms,
+                                   out_beta, out_nll, workspace, workspace_bytes, stream, nullptr);
 }
 
 const char* spec_verify_status_string(sv_status_t status)
@@ -655,14 +662,59 @@ const char* spec_verify_status_string(sv_status_t status)
     return "SV_ERR_UNKNOWN";
 }
 
-sv_status_t spec_verify_set_profile_events(hipEvent_t* starts, hipEvent_t* stops, int32_t n)
+// ---- benchmark entry points (specverify_profile.h): the same calls with
+// the caller's events recorded around the streaming pass
+
+sv_status_t spec_verify_sample_profiled(const sv_profile_events_t* events, const sv_shape_t* shape,
+                                        const void* target_logits, const void* draft_logits, const int32_t* draft_ids,
+                                        float temperature, int32_t top_k, float top_p, uint64_t seed, uint32_t offset,
+                                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                        float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                                        hipStream_t stream)
 {
-    if (n < 0 || (n > 0 && (starts == nullptr || stops == nullptr))) return SV_ERR_INVALID_ARGUMENT;
-    g_prof_start = n > 0 ? starts : nullptr;
-    g_prof_stop = n > 0 ? stops : nullptr;
-    g_prof_n = n;
-    g_prof_i = 0;
-    return SV_OK;
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 0, events);
+}
+
+sv_status_t spec_verify_argmax_profiled(const sv_profile_events_t* events, const sv_shape_t* shape,
+                                        const void* target_logits, const void* draft_logits, const int32_t* draft_ids,
+                                        float temperature, int32_t top_k, float top_p, uint64_t seed, uint32_t offset,
+                                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                        float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                                        hipStream_t stream)
+{
+    return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
+                                out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
+                                workspace_bytes, stream, 1, events);
+}
+
+sv_status_t spec_verify_greedy_profiled(const sv_profile_events_t* events, const sv_shape_t* shape,
+                                        const void* target_logits, const int32_t* draft_ids, int32_t* out_tokens,
+                                        int32_t* out_num_accepted, void* workspace, size_t* workspace_bytes,
+                                        hipStream_t stream)
+{
+    return verify_greedy_common(shape, target_logits, draft_ids, out_tokens, out_num_accepted, workspace,
+                                workspace_bytes, stream, events);
+}
+
+sv_status_t spec_draft_sample_profiled(const sv_profile_events_t* events, const sv_shape_t* shape,
+                                       const void* draft_logits, float temperature, int32_t top_k, float top_p,
+                                       uint64_t seed, uint32_t offset, int32_t* out_ids, void* workspace,
+                                       size_t* workspace_bytes, hipStream_t stream)
+{
+    return draft_sample_common(shape, draft_logits, temperature, top_k, top_p, seed, offset, out_ids, workspace,
+                               workspace_bytes, stream, events);
+}
+
+sv_status_t spec_token_likelihood_profiled(const sv_profile_events_t* events, const sv_shape_t* shape,
+                                           const void* target_logits, const void* draft_logits, const int32_t* tokens,
+                                           float temperature, int32_t top_k, float top_p, float* out_terms,
+                                           float* out_beta, double* out_nll, void* workspace, size_t* workspace_bytes,
+                                           hipStream_t stream)
+{
+    return token_likelihood_common(shape, target_logits, draft_logits, tokens, temperature, top_k, top_p, out_terms,
+                                   out_beta, out_nll, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

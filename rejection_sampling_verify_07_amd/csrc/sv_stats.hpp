@@ -114,7 +114,7 @@ __device__ __forceinline__ void full_masked(const Tile& t, const u32x4* raw, int
     }
 }
 
-template <int DT, int MODE, int LOADS, bool NT, bool PIPE, bool MASKED = false>
+template <int DT, int MODE, int LOADS, bool NT, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                              int32_t ntiles, float c, void* __restrict__ partials)
 {
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t 
     __shared__ int32_t s_i[kWaves];
     __shared__ double s_s[kWaves];
 
-    walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
+    walk_tiles<DT, LOADS, NT>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
         if constexpr (MODE == MODE_FULL && MASKED) {
             full_masked<DT, LOADS>(t, raw, vocab, c, partials, s_m, s_s);
             return;
@@ -174,7 +174,6 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t 
                 out->m = m;
                 out->idx = ix;
             }
-            if constexpr (PIPE) __syncthreads();  // s_m / s_i are rewritten by the next tile of a persistent grid
         } else {
             const float mcc = m * c;
             double acc = 0.0;

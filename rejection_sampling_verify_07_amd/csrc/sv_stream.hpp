@@ -1,13 +1,10 @@
-// Persistent, software-pipelined walk over the (row, chunk) tiles of the
-// streaming passes.
+// Walk over the (row, chunk) tiles of the streaming passes.
 //
 // A chunk is kThreads * LOADS aligned 16-byte blocks of one row; tile c is
-// chunk (c mod nchunk) of row (c / nchunk).  The grid holds as many
-// workgroups as the chip keeps resident; workgroup g handles tiles g,
-// g + G, g + 2G, ... and issues the loads of its next tile before it works
-// on the current one, so the reduction, barrier and compaction work of a
-// tile overlaps the HBM latency of the next.  Two register sets alternate
-// (the walk is unrolled by two) so no copies are needed.
+// chunk (c mod nchunk) of row (c / nchunk), and workgroup c takes tile c
+// (one tile per workgroup: the hardware refills a finished workgroup's slot
+// with the next tile, which overlapped the loads better than a persistent
+// grid with the next tile's loads in flight, measured on MI355X).
 #pragma once
 
 #include "sv_common.hpp"
@@ -54,45 +51,19 @@ __device__ __forceinline__ void issue_tile(const Tile& t, const u32x4* base, u32
     }
 }
 
-// body(tile, raw) is called once per tile (raw: the thread's LOADS words,
-// which the body may overwrite), by every thread of the workgroup (it may contain barriers; it must end with the workgroup's LDS
-// free for the next tile).  PIPELINE = false: one tile per workgroup
-// (grid = ntiles), no prefetch register set.
-template <int DT, int LOADS, bool NT, bool PIPELINE, class Body>
+// body(tile, raw) is called once, by every thread of the workgroup, with the
+// thread's LOADS raw words (which the body may overwrite).
+template <int DT, int LOADS, bool NT, class Body>
 __device__ __forceinline__ void walk_tiles(const RowSet& rs, int32_t vocab, int32_t nchunk, int32_t ntiles,
                                            Body&& body)
 {
-    int32_t c = (int32_t)blockIdx.x;
+    const int32_t c = (int32_t)blockIdx.x;
     if (c >= ntiles) return;
     const u32x4* base;
-    u32x4 ra[LOADS];
-    Tile ta = make_tile<DT>(rs, vocab, nchunk, c, LOADS, &base);
-    issue_tile<DT, LOADS, NT>(ta, base, ra);
-    if constexpr (!PIPELINE) {
-        body(ta, ra);
-    } else {
-        const int32_t stride = (int32_t)gridDim.x;
-        u32x4 rb[LOADS];
-        while (true) {
-            // tile in ra is in flight; start the next one into rb
-            const int32_t cb = c + stride;
-            Tile tb;
-            if (cb < ntiles) {
-                tb = make_tile<DT>(rs, vocab, nchunk, cb, LOADS, &base);
-                issue_tile<DT, LOADS, NT>(tb, base, rb);
-            }
-            body(ta, ra);
-            if (cb >= ntiles) break;
-            const int32_t ca = cb + stride;
-            if (ca < ntiles) {
-                ta = make_tile<DT>(rs, vocab, nchunk, ca, LOADS, &base);
-                issue_tile<DT, LOADS, NT>(ta, base, ra);
-            }
-            body(tb, rb);
-            if (ca >= ntiles) break;
-            c = ca;
-        }
-    }
+    u32x4 raw[LOADS];
+    const Tile t = make_tile<DT>(rs, vocab, nchunk, c, LOADS, &base);
+    issue_tile<DT, LOADS, NT>(t, base, raw);
+    body(t, raw);
 }
 
 // Widen block i of a tile to fp32 and replace elements outside the row by

@@ -188,7 +188,7 @@ constexpr int kChunkLds = kWaves * kWaveLds;
 // smallest fp32 of some bf16 order class, so `word >= t` and `element >= t`
 // agree.  The low element needs a shift.  The lane maxima that set the bound
 // are taken over all elements.  fp16 elements are widened (exactly) instead.
-template <int DT, int LOADS, bool NT, bool PIPE>
+template <int DT, int LOADS, bool NT>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
     int32_t* __restrict__ counts, float* __restrict__ bounds, KeptEntry* __restrict__ cands)
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     __shared__ uint32_t s_hist[256];
     __shared__ int32_t s_misc[8];
 
-    walk_tiles<DT, LOADS, NT, PIPE>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
+    walk_tiles<DT, LOADS, NT>(rs, vocab, nchunk, ntiles, [&](const Tile& t, u32x4* raw) {
         // Edge tiles (a block reaching outside the row) first overwrite the
         // out-of-row slots of their raw words with a NaN pattern: NaN is never
         // selected and the maximum ignores it, so one body serves every tile.
@@ -434,10 +434,6 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             counts[t.index] = written;  // > cap marks an overflow
             bounds[t.index] = bound;
         }
-        // LDS is reused by the next tile of a persistent grid.  With one tile
-        // per workgroup there is none, and a barrier here would only keep the
-        // waves resident until their candidate stores are acknowledged.
-        if constexpr (PIPE) __syncthreads();
     });
 }
 
@@ -478,200 +474,12 @@ __device__ float block_row_max(const char* rowp, int32_t vocab, float* s_f)
     return block_max_float(lm, s_f);
 }
 
-// ---------------------------------------------------------------------------
-// Fast select of one row by a single wave (no workgroup barriers): used when
-// no chunk overflowed and the row's candidates fit a kept list.  Candidates
-// go to LDS in one round of loads, an LDS-histogram radix select finds the
-// top_k-th largest key, the kept ids are compacted with ballots and sorted
-// by id (in registers when at most 64 are kept), and the max and the exp2
-// sum are wave reductions in a fixed order.
-// s_choff must hold nchunk + 1 ints; s_key / s_idx kKeepCap entries;
-// s_kidx / s_kval kKeepCap entries.
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ void select_row_wave(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
-                                const int32_t* __restrict__ counts, const KeptEntry* __restrict__ cands,
-                                int32_t total, int32_t keep_cap, RowDesc* __restrict__ descs,
-                                KeptEntry* __restrict__ kept, int32_t* s_choff, uint32_t* s_key, int32_t* s_idx,
-                                uint32_t* s_hist, int32_t* s_kidx, float* s_kval)
-{
-    constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
-    constexpr int PER = kKeepCapList / kWave;
-    const int lane = lane_id();
-
-    // candidates of every chunk into LDS (entry i lives in the chunk whose
-    // offset range holds it), all loads issued before any store
-    KeptEntry e[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int32_t i = lane + j * kWave;
-        if (i < total) {
-            int32_t lo = 0, hi = nchunk;
-            while (hi - lo > 1) {
-                const int32_t mid = (lo + hi) >> 1;
-                if (s_choff[mid] <= i) lo = mid; else hi = mid;
-            }
-            e[j] = cands[((int64_t)row * nchunk + lo) * cap + (i - s_choff[lo])];
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int32_t i = lane + j * kWave;
-        if (i < total) {
-            s_key[i] = order_key(e[j].val);
-            s_idx[i] = e[j].idx;
-        }
-    }
-
-    // radix select of the top_k-th largest key (8-bit digits from the top)
-    uint32_t prefix = 0, pmask = 0;
-    int32_t kk = top_k, eq = 0;
-    for (int shift = 24; shift >= LOW; shift -= 8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) s_hist[lane * 4 + q] = 0;
-        __builtin_amdgcn_wave_barrier();
-        for (int32_t i = lane; i < total; i += kWave) {
-            const uint32_t key = s_key[i];
-            if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-        }
-        __builtin_amdgcn_wave_barrier();
-        int c4[4], lsum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            c4[q] = (int)s_hist[255 - 4 * lane - q];
-            lsum += c4[q];
-        }
-        const int incl = wave_incl_scan_int(lsum);
-        const int excl = incl - lsum;
-        int found = -1, above = 0, cnt = 0;
-        if (excl < kk && incl >= kk) {
-            int cc = excl;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (found < 0 && cc + c4[q] >= kk) {
-                    found = 255 - 4 * lane - q;
-                    above = cc;
-                    cnt = c4[q];
-                }
-                cc += c4[q];
-            }
-        }
-        const uint64_t bal = __ballot(found >= 0);
-        const int src = bal ? __builtin_ctzll(bal) : 0;
-        found = __shfl(found, src, kWave);
-        above = __shfl(above, src, kWave);
-        cnt = __shfl(cnt, src, kWave);
-        if (bal == 0) {
-            found = 0;
-            cnt = 0;
-        }
-        prefix |= (uint32_t)found << shift;
-        pmask |= 0xffu << shift;
-        kk -= above;
-        eq = cnt;
-        __builtin_amdgcn_wave_barrier();
-    }
-    if (LOW > 0) prefix |= (prefix & 0x80000000u) ? 0u : ((1u << LOW) - 1u);
-    const uint32_t tau_key = prefix;
-    (void)eq;
-
-    // kept ids (key >= tau_key), compacted in candidate order
-    int32_t nk = 0;
-    for (int32_t b = 0; b < total; b += kWave) {
-        const int32_t i = b + lane;
-        const bool pred = i < total && s_key[i] >= tau_key;
-        const uint64_t m = __ballot(pred);
-        if (pred) {
-            const int32_t pos = nk + lanes_below(m);
-            s_kidx[pos] = s_idx[i];
-            s_kval[pos] = key_to_float(s_key[i]);
-        }
-        nk += (int32_t)__popcll(m);
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // sort by id
-    KeptEntry* klist = kept + (int64_t)row * keep_cap;
-    float lm = neg_inf();
-    double ls = 0.0;
-    if (nk <= kWave) {
-        int32_t ix = lane < nk ? s_kidx[lane] : INT32_MAX;
-        float v = lane < nk ? s_kval[lane] : neg_inf();
-#pragma unroll
-        for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-            for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                const int32_t pix = __shfl_xor(ix, stride, kWave);
-                const float pv = __shfl_xor(v, stride, kWave);
-                const bool up = (lane & size) == 0;
-                const bool lower = (lane & stride) == 0;
-                const bool take = (lower == up) ? (pix < ix) : (pix > ix);
-                if (take) {
-                    ix = pix;
-                    v = pv;
-                }
-            }
-        }
-        if (lane < nk) klist[lane] = KeptEntry{ix, v};
-        lm = wave_max(v);
-        lm = __shfl(lm, 0, kWave);
-        const float mcc = lm * c;
-        ls = lane < nk ? (double)__builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mcc)) : 0.0;
-    } else {
-        int32_t npad = kWave;
-        while (npad < nk) npad <<= 1;
-        for (int32_t i = nk + lane; i < npad; i += kWave) {
-            s_kidx[i] = INT32_MAX;
-            s_kval[i] = neg_inf();
-        }
-        __builtin_amdgcn_wave_barrier();
-        for (int32_t size = 2; size <= npad; size <<= 1) {
-            for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int32_t i = lane; i < npad; i += kWave) {
-                    const int32_t p = i ^ stride;
-                    if (p > i) {
-                        const bool up = (i & size) == 0;
-                        const int32_t a = s_kidx[i], bb = s_kidx[p];
-                        if ((a > bb) == up) {
-                            s_kidx[i] = bb;
-                            s_kidx[p] = a;
-                            const float tv = s_kval[i];
-                            s_kval[i] = s_kval[p];
-                            s_kval[p] = tv;
-                        }
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
-        }
-        for (int32_t i = lane; i < nk; i += kWave) {
-            klist[i] = KeptEntry{s_kidx[i], s_kval[i]};
-            lm = fmaxf(lm, s_kval[i]);
-        }
-        lm = __shfl(wave_max(lm), 0, kWave);
-        const float mcc = lm * c;
-        for (int32_t i = lane; i < nk; i += kWave)
-            ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(s_kval[i], c, -mcc));
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) {
-        RowDesc d;
-        d.tau = key_to_float(tau_key);
-        d.m = lm;
-        d.mcc = lm * c;
-        d.kept = nk;
-        d.s = ls;
-        d.flags = 0;
-        d.pad = 0;
-        descs[row] = d;
-    }
-}
-
+// The exact select over a full row, one workgroup per row: the path of
+// top_k too large for the candidate pass.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(
-    RowSet rs, int32_t vocab, int32_t nchunk, int32_t top_k, int32_t cap, float c,
-    const int32_t* __restrict__ counts, const KeptEntry* __restrict__ cands, int32_t use_cands,
-    int32_t keep_cap, RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept)
+    RowSet rs, int32_t vocab, int32_t top_k, float c, int32_t keep_cap, RowDesc* __restrict__ descs,
+    KeptEntry* __restrict__ kept)
 {
     constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
     __shared__ uint32_t s_key[kSelCap];
@@ -687,77 +495,6 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     KeptEntry* klist = kept + (int64_t)row * keep_cap;
     __shared__ int32_t s_kidx[kKeepCapList];
     __shared__ float s_kval[kKeepCapList];
-    __shared__ int32_t s_choff[kMaxChunks + 1];
-
-    // Every wave reads the chunk counts and reaches the same decision; on the
-    // fast path waves 1..3 leave and wave 0 selects the row without barriers.
-    if (use_cands != 0) {
-        int32_t base = 0, bad = 0;
-        for (int32_t g = 0; g < nchunk; g += kWave) {
-            const int32_t ch = g + lane_id();
-            const int32_t n = ch < nchunk ? counts[(int64_t)row * nchunk + ch] : 0;
-            bad |= n > cap;
-            const int32_t nc = min(n, cap);
-            const int incl = wave_incl_scan_int(nc);
-            if (wave_id() == 0 && ch < nchunk) s_choff[ch] = base + incl - nc;
-            base += __shfl(incl, kWave - 1, kWave);
-        }
-        const bool any_bad = __ballot(bad != 0) != 0;
-        if (!any_bad && base >= top_k && base <= kKeepCapList && keep_cap >= kKeepCapList) {
-            if (wave_id() != 0) return;
-            if (lane_id() == 0) s_choff[nchunk] = base;
-            __builtin_amdgcn_wave_barrier();
-            select_row_wave<DT>(row, nchunk, top_k, cap, c, counts, cands, base, keep_cap, descs, kept, s_choff,
-                                s_key, (int32_t*)s_idx, s_hist, s_kidx, s_kval);
-            return;
-        }
-    }
-
-    // ---- gather the candidates of this row (if pass 1 ran and nothing overflowed)
-    int32_t total = 0;
-    bool fast = use_cands != 0;
-    if (fast) {
-        // per-chunk counts read in parallel; exclusive offsets by a block scan
-        const int32_t per = (nchunk + kThreads - 1) / kThreads;
-        const int32_t lo = min(nchunk, (int32_t)threadIdx.x * per), hi = min(nchunk, lo + per);
-        int mine = 0, bad = 0;
-        for (int32_t ch = lo; ch < hi; ++ch) {
-            const int32_t n = counts[(int64_t)row * nchunk + ch];
-            bad |= n > cap;
-            s_choff[ch] = min(n, cap);
-            mine += min(n, cap);
-        }
-        int tot;
-        int off = block_excl_scan_int(mine, s_w, &tot);
-        for (int32_t ch = lo; ch < hi; ++ch) {
-            const int32_t n = s_choff[ch];
-            s_choff[ch] = off;
-            off += n;
-        }
-        if (threadIdx.x == 0) s_misc[1] = 0;
-        __syncthreads();
-        if (bad) atomicOr(&s_misc[1], 1);
-        if (threadIdx.x == 0) s_choff[nchunk] = tot;
-        __syncthreads();
-        total = tot;
-        fast = s_misc[1] == 0 && total <= kSelCap && total >= top_k;
-        __syncthreads();
-    }
-    if (fast) {
-        for (int32_t ch = wave_id(); ch < nchunk; ch += kWaves) {
-            const int64_t g = (int64_t)row * nchunk + ch;
-            const int32_t off = s_choff[ch];
-            const int32_t n = s_choff[ch + 1] - off;
-            const KeptEntry* src = cands + g * cap;
-            for (int32_t t = lane_id(); t < n; t += kWave) {
-                const KeptEntry e = src[t];
-                s_key[off + t] = order_key(e.val);
-                s_idx[off + t] = e.idx;
-            }
-        }
-        __syncthreads();
-    }
-
     // ---- exact top_k-th largest key
     int32_t greater = 0, equal = 0;
     uint32_t tau_key = 0;
@@ -770,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
     // radix passes over the row below.
     bool staged = false;  // s_kidx / s_kval already hold the kept entries
     bool have_tau = false;
-    if (!fast) {
+    {
         for (int i = threadIdx.x; i < kSelCap; i += kThreads) s_key[i] = 0;
         __syncthreads();
         for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
@@ -859,15 +596,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
             have_tau = true;
         }
     }
-    if (have_tau) {
-        // done above
-    } else if (fast) {
-        tau_key = block_radix_select(
-            [&](auto&& fn) {
-                for (int32_t i = threadIdx.x; i < total; i += kThreads) fn(s_key[i]);
-            },
-            top_k, LOW, s_hist, s_misc, &greater, &equal);
-    } else {
+    if (!have_tau) {
         tau_key = block_radix_select(
             [&](auto&& fn) {
                 for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
@@ -890,19 +619,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
         // sorted by id (bitonic); the row's maximum is one of them
         if (!staged && threadIdx.x == 0) s_misc[4] = 0;
         __syncthreads();
-        if (staged) {
-            // already in s_kidx / s_kval
-        } else if (fast) {
-            for (int32_t i = threadIdx.x; i < total; i += kThreads) {
-                if (s_key[i] >= tau_key) {
-                    const int32_t slot = atomicAdd(&s_misc[4], 1);
-                    if (slot < kKeepCapList) {
-                        s_kidx[slot] = s_idx[i];
-                        s_kval[slot] = key_to_float(s_key[i]);
-                    }
-                }
-            }
-        } else {
+        if (!staged) {
             // one walk of the row: at most a list's worth of ids pass
             for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
 #pragma unroll
@@ -977,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(
         d.mcc = m * c;
         d.kept = kept_n;
         d.s = s_sum;
-        d.flags = fast ? 0 : 1;
+        d.flags = 1;
         d.pad = 0;
         descs[row] = d;
     }

@@ -965,8 +965,18 @@ __global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs a)
         kb = a.kmax;
     }
     const int32_t trow0 = k0 + b;
+    // every guess id is checked first, also those past the first mismatch, as
+    // the sampling verify does: a sequence with any id outside [0, V) reports -1
+    bool bad_id = false;
+    for (int32_t k = lane_id(); k < kb; k += kWave) {
+        const int32_t x = a.ids[k0 + k];
+        bad_id |= x < 0 || x >= a.vocab;
+    }
+    if (__ballot(bad_id) != 0) {
+        if (lane_id() == 0) a.out_nacc[b] = -1;
+        return;
+    }
     int32_t n = kb, an = -1;
-    bool bad = false;
     for (int32_t k = 0; k <= kb; ++k) {
         const PartialArg* pp = a.partials + (int64_t)(trow0 + k) * a.nchunk;
         float v = neg_inf();
@@ -979,19 +989,11 @@ __global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs a)
             break;
         }
         const int32_t x = a.ids[k0 + k];
-        if (x < 0 || x >= a.vocab) {
-            bad = true;
-            break;
-        }
         if (x != ix) {
             n = k;
             an = ix;
             break;
         }
-    }
-    if (bad) {
-        if (lane_id() == 0) a.out_nacc[b] = -1;
-        return;
     }
     for (int32_t j = lane_id(); j <= kb; j += kWave) {
         a.out_tokens[trow0 + j] = j < n ? a.ids[k0 + j] : (j == n ? an : -1);

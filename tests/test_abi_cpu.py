@@ -10,6 +10,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "specverify.h")
+PROFILE_HEADER = os.path.join(ROOT, "include", "specverify_profile.h")
 
 
 @pytest.fixture(scope="module")
@@ -30,8 +31,8 @@ def B():
     return binding
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(headers=(HEADER, PROFILE_HEADER)):
+    text = "".join(open(h).read() for h in headers)
     return sorted(set(re.findall(r"SV_API\s+[\w\s\*]+?\b(spec_\w+)\s*\(", text)))
 
 
@@ -41,6 +42,10 @@ def test_header_declares_the_boundary():
     assert "spec_draft_sample" in names and "spec_verify_argmax" in names
     assert "spec_token_likelihood" in names
     assert "spec_verify_status_string" in names
+    # every call has a benchmark form with per-call events, and nothing else
+    plain = declared_functions((HEADER,))
+    prof = declared_functions((PROFILE_HEADER,))
+    assert sorted(prof) == sorted(n + "_profiled" for n in plain if n != "spec_verify_status_string")
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -55,8 +60,9 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_header_compiles_as_c():
-    # the header is plain C: compile a translation unit that includes it
-    src = '#include "specverify.h"\nint main(void){ sv_shape_t s; (void)s; return SV_OK; }\n'
+    # the headers are plain C: compile a translation unit that includes them
+    src = ('#include "specverify.h"\n#include "specverify_profile.h"\n'
+           'int main(void){ sv_shape_t s; sv_profile_events_t e; (void)s; (void)e; return SV_OK; }\n')
     r = subprocess.run(["gcc", "-x", "c", "-std=c11", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
                         "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", "-"],
                        input=src, capture_output=True, text=True)
@@ -115,9 +121,16 @@ def test_invalid_shapes(lib, B, kw, code):
 
 
 @pytest.mark.parametrize("T,top_k,code", [(0.0, 0, 1), (-1.0, 0, 1), (float("inf"), 0, 1), (float("nan"), 0, 1),
-                                          (1.0, -1, 1), (1.0, 1001, 1), (0.05, 1, 0), (5.0, 1000, 0)])
+                                          (1.0, -1, 1), (1.0, 1001, 1), (0.05, 1, 0), (5.0, 1000, 0),
+                                          # log2(e) / T overflows fp32 below about 4.24e-39
+                                          (1e-39, 0, 1), (4.3e-39, 0, 0), (1e-45, 50, 1)])
 def test_temperature_and_top_k(lib, B, T, top_k, code):
     assert _query(lib, _shape(B), T=T, top_k=top_k)[0] == code
+    need = C.c_size_t(0)
+    assert lib.spec_draft_sample(C.byref(_shape(B)), None, T, top_k, 1.0, 0, 0, None, None, C.byref(need),
+                                 None) == code
+    assert lib.spec_token_likelihood(C.byref(_shape(B)), None, None, None, T, top_k, 1.0, None, None, None, None,
+                                     C.byref(need), None) == code
 
 
 def test_null_and_misaligned_pointers_and_small_workspace(lib, B):
@@ -161,10 +174,33 @@ def test_ragged_shape_needs_consistent_totals(lib, B):
     assert _query(lib, sh)[0] == B.SV_ERR_INVALID_ARGUMENT
 
 
-def test_profile_hook_arguments(lib, B):
-    assert lib.spec_verify_set_profile_events(None, None, 3) == B.SV_ERR_INVALID_ARGUMENT
-    assert lib.spec_verify_set_profile_events(None, None, -1) == B.SV_ERR_INVALID_ARGUMENT
-    assert lib.spec_verify_set_profile_events(None, None, 0) == B.SV_OK
+def test_profiled_calls_check_arguments_like_the_plain_ones(lib, B):
+    """The benchmark forms take per-call events (nothing is armed or kept in
+    the library) and answer queries and reject arguments exactly as the plain
+    calls do; events are never touched by a call that launches nothing."""
+    ev = B.ProfileEventsT(1 << 40, (1 << 40) + 64)  # never used: nothing below launches
+    sh = _shape(B)
+    for T, top_k in ((1.0, 0), (1.0, 50), (0.0, 0), (1.0, -1)):
+        for prof in (None, C.pointer(ev)):
+            need = C.c_size_t(0)
+            st = lib.spec_verify_sample_profiled(prof, C.byref(sh), None, None, None, T, top_k, 1.0, 0, 0, None,
+                                                 None, None, None, None, C.byref(need), None)
+            assert (st, need.value) == _query(lib, sh, T=T, top_k=top_k)
+    need = C.c_size_t(0)
+    assert lib.spec_verify_greedy_profiled(C.pointer(ev), C.byref(sh), None, None, None, None, None, C.byref(need),
+                                           None) == B.SV_OK
+    assert need.value == _query(lib, sh, greedy=True)[1]
+    fake = 1 << 40
+    have = C.c_size_t(need.value - 1)
+    assert lib.spec_verify_greedy_profiled(C.pointer(ev), C.byref(sh), fake, fake, fake, fake, fake, C.byref(have),
+                                           None) == B.SV_ERR_WORKSPACE_TOO_SMALL
+    assert lib.spec_draft_sample_profiled(C.pointer(ev), C.byref(sh), None, 1.0, 0, 1.0, 0, 0, None, None,
+                                          C.byref(need), None) == B.SV_OK
+    assert lib.spec_token_likelihood_profiled(C.pointer(ev), C.byref(sh), None, None, None, 1.0, 0, 1.0, None, None,
+                                              None, None, C.byref(need), None) == B.SV_OK
+    assert lib.spec_verify_argmax_profiled(C.pointer(ev), C.byref(_shape(B, batch=0)), None, None, None, 1.0, 0, 1.0,
+                                           0, 0, None, None, None, None, None, C.byref(need),
+                                           None) == B.SV_ERR_INVALID_ARGUMENT
 
 
 def test_binding_fails_loudly_without_library(tmp_path, B):
@@ -272,3 +308,93 @@ def test_top_p_arguments(lib, B):
         assert n2 > n1, q.__name__
         st3, n3 = q(lib, sh, top_k=50, top_p=0.9)
         assert st3 == B.SV_OK and n3 > 0
+
+
+# --------------------------------------------------------------------------
+# the Python binding rejects tensors that disagree with each other or with the
+# batch geometry before any call into the library (the kernels index rows by
+# the geometry and read both tensors with one element type and width)
+# --------------------------------------------------------------------------
+def _tensors(torch, rows_t=10, rows_d=8, V=64, dt_t=None, dt_d=None):
+    dt_t = dt_t or torch.bfloat16
+    dt_d = dt_d or dt_t
+    return torch.zeros(rows_t, V, dtype=dt_t), torch.zeros(rows_d, V, dtype=dt_d)
+
+
+@pytest.mark.parametrize("case", ["dtype", "columns", "short_draft", "short_target_ragged", "short_target_uniform"])
+def test_binding_rejects_mismatched_tensors(B, case):
+    import torch
+
+    ids = torch.zeros(8, dtype=torch.int32)
+    cu = None
+    tgt, drf = _tensors(torch)
+    if case == "dtype":
+        tgt, drf = _tensors(torch, dt_t=torch.float32, dt_d=torch.bfloat16)
+    elif case == "columns":
+        drf = torch.zeros(8, 32, dtype=torch.bfloat16)
+    elif case == "short_draft":
+        drf = drf[:7]
+    elif case == "short_target_ragged":
+        cu = torch.tensor([0, 3, 8], dtype=torch.int32)
+        tgt = tgt[:9]
+    elif case == "short_target_uniform":
+        tgt = tgt[:9]   # 9 rows for 8 ids: no uniform K fits
+    with pytest.raises(ValueError):
+        B.verify_sample(tgt, drf, ids, cu_draft=cu)
+    if case in ("dtype", "columns", "short_draft"):
+        with pytest.raises(ValueError):
+            B.SamplePlan(tgt, drf, ids, cu_draft=cu)
+        with pytest.raises(ValueError):
+            B.token_likelihood(tgt[:8], drf, ids, batch=2)
+    if case.startswith("short_target"):
+        with pytest.raises(ValueError):
+            B.verify_greedy(tgt, ids, cu_draft=cu)
+
+
+def test_binding_checks_come_before_the_device_check(B):
+    """Well-formed CPU tensors get past the agreement checks and stop at the
+    device check: the checks above are the ones that raised."""
+    import torch
+
+    tgt, drf = _tensors(torch)
+    with pytest.raises(ValueError, match="GPU"):
+        B.verify_sample(tgt, drf, torch.zeros(8, dtype=torch.int32))
+
+
+def test_workspace_queries_over_many_shapes(lib, B):
+    """Plans for every call over a grid of shapes, filters and dtypes (the host
+    code the sanitized build checks): sizes are positive, 256-byte multiples,
+    and do not shrink when the batch grows."""
+    need = C.c_size_t(0)
+
+    def sizes(sh, top_k, top_p):
+        out = {}
+        for name, call in (
+                ("sample", lambda: lib.spec_verify_sample(C.byref(sh), None, None, None, 0.7, top_k, top_p, 0, 0, None,
+                                                          None, None, None, None, C.byref(need), None)),
+                ("greedy", lambda: lib.spec_verify_greedy(C.byref(sh), None, None, None, None, None, C.byref(need),
+                                                          None)),
+                ("draft", lambda: lib.spec_draft_sample(C.byref(sh), None, 0.7, top_k, top_p, 0, 0, None, None,
+                                                        C.byref(need), None)),
+                ("likelihood", lambda: lib.spec_token_likelihood(C.byref(sh), None, None, None, 0.7, top_k, top_p,
+                                                                 None, None, None, None, C.byref(need), None))):
+            st = call()
+            assert st == B.SV_OK, (name, st)
+            assert need.value > 0 and need.value % 256 == 0, (name, need.value)
+            out[name] = need.value
+        return out
+
+    for dt in (B.SV_DTYPE_F32, B.SV_DTYPE_BF16, B.SV_DTYPE_F16):
+        for V in (1, 7, 1000, 50304, 151936, 1 << 20):
+            for top_k in sorted({0, 1, 50, 240, 241, max(V - 1, 0), V}):
+                if top_k > V:
+                    continue
+                for top_p in (1.0, 0.9):
+                    prev = None
+                    for batch, K in ((1, 0), (1, 4), (32, 8), (256, 8)):
+                        sh = _shape(B, batch=batch, max_draft=K, total_draft=batch * K, vocab=V, dtype=dt,
+                                    target_row_stride=V, draft_row_stride=V)
+                        cur = sizes(sh, top_k, top_p)
+                        if prev is not None and K == 8:
+                            assert all(cur[k] >= prev[k] for k in cur), (dt, V, top_k, top_p, batch)
+                        prev = cur

@@ -245,7 +245,13 @@ def test_out_of_range_ids_and_bad_offsets_are_reported():
     o = _oracle(w)
     compare_sample(w2, g, o, seqs=[0, 2])
     gg = gpu_greedy(w2)
-    assert gg["num_accepted"][3] == -1
+    # sequence 1's bad id sits at position 1, past a possible first mismatch:
+    # every id is checked, as in the sampling verify
+    assert gg["num_accepted"][1] == -1 and gg["num_accepted"][3] == -1
+    og = oracle.verify_greedy(w2.target, w2.draft_ids, w2.cu_draft, w2.vocab, w2.dtype)
+    assert og["num_accepted"][1] == -1 and og["num_accepted"][3] == -1
+    for b in (0, 2):
+        assert gg["num_accepted"][b] == og["num_accepted"][b]
     # a prefix array that points past the draft rows
     tgt, drf, idt, cu = to_device(w)
     cu_bad = cu.clone()

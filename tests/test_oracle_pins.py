@@ -488,6 +488,72 @@ def test_argmax_variant_residual_and_extra_token_vs_numpy(orc):
     assert seen_reject > 0
 
 
+def _best_and_runner_up(wt):
+    """numpy reference for the argmax draw: the lowest id of the largest
+    positive weight; the runner-up is the lowest id of the largest positive
+    weight among the other ids (-1 when there is none); gap = (best -
+    runner-up) / best, 1 with no runner-up."""
+    pos = np.flatnonzero(wt > 0)
+    if pos.size == 0:
+        return -1, -1, 0.0
+    order = pos[np.lexsort((pos, -wt[pos]))]  # descending weight, ascending id among equals
+    best = int(order[0])
+    if order.size == 1:
+        return best, -1, 1.0
+    sec = int(order[1])
+    return best, sec, float((wt[best] - wt[sec]) / wt[best])
+
+
+def test_argmax_variant_gap_and_runner_up_vs_numpy(orc):
+    """The argmax variant also reports, per sequence, the runner-up id of its
+    final argmax and the relative gap to it (the GPU test accepts either id
+    when the gap is small).  Against numpy on max(0, p_n - q_n) (or p_K) from
+    scipy's softmax: the runner-up is the best other id, the gap its margin."""
+    w = W.make_workload(dict(W.WORKLOADS[2], name="argmax_gap_pin"), gen_seed=3, batch=24)
+    a = orc.verify_workload(w, "argmax", threads=8)
+    tf, df = w.target_f32(), w.draft_f32()
+    for b in range(w.batch):
+        k0, k1 = w.cu_draft[b], w.cu_draft[b + 1]
+        n = a["num_accepted"][b]
+        p = _softmax(tf[k0 + b + n], w.temperature, w.top_k)
+        wt = np.maximum(p - _softmax(df[k0 + n], w.temperature, w.top_k), 0.0) if n < k1 - k0 else p
+        best, sec, gap = _best_and_runner_up(wt)
+        assert a["tokens"][k0 + b + n] == best
+        assert a["second"][b] == sec
+        assert abs(a["gap"][b] - gap) <= 1e-9 * max(1.0, gap)
+
+
+# Hand-built rows (V = 4, T = 1, fp32): (target row 0, target row 1, draft row
+# 0, guess) -> (token, runner-up, gap).  A draft equal to target row 0 accepts
+# its guess (p = q), so the token is the argmax of p_1; a point-mass draft
+# (q = 1 at the guess, where p is about e^-33) rejects it, and the residual is
+# p_0 on the other ids.
+_NEG = -np.inf
+ARGMAX_CASES = {
+    "extra_tie_at_max": ([0, 0, 0, 0], [0, 3, 3, 1], None, 0, (1, 2, 0.0)),
+    "extra_tie_at_runner_up": ([0, 0, 0, 0], [5, 1, 3, 3], None, 0, (0, 2, 1 - np.exp(-2.0))),
+    "extra_max_after_runner_up": ([0, 0, 0, 0], [1, 3, 5, 0], None, 0, (2, 1, 1 - np.exp(-2.0))),
+    "extra_single_positive": ([0, 0, 0, 0], [0, _NEG, _NEG, _NEG], None, 0, (0, -1, 1.0)),
+    "residual_tie_at_max": ([3, 3, 1, -30], [0, 0, 0, 0], [_NEG, _NEG, _NEG, 0], 3, (0, 1, 0.0)),
+    "residual_runner_up_after_max": ([1, 4, 2, -30], [0, 0, 0, 0], [_NEG, _NEG, _NEG, 0], 3,
+                                     (1, 2, 1 - np.exp(-2.0))),
+    "residual_single_positive": ([2, _NEG, _NEG, -30], [0, 0, 0, 0], [_NEG, _NEG, _NEG, 0], 3, (0, -1, 1.0)),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ARGMAX_CASES))
+def test_argmax_variant_gap_and_runner_up_hand_cases(orc, name):
+    t0, t1, d0, x, (tok, sec, gap) = ARGMAX_CASES[name]
+    tgt = np.array([t0, t1], np.float32)
+    drf = np.array([d0 if d0 is not None else t0], np.float32)
+    a = orc.verify_argmax(tgt, drf, np.array([x], np.int32), np.array([0, 1], np.int32), 4, "f32", 1.0, 0, 0, 0)
+    n = 1 if d0 is None else 0
+    assert a["num_accepted"][0] == n
+    assert a["tokens"][n] == tok
+    assert a["second"][0] == sec
+    assert a["gap"][0] == pytest.approx(gap, rel=1e-12, abs=1e-15)
+
+
 def test_argmax_variant_draft_equals_target(orc):
     w = W.make_workload(dict(W.WORKLOADS[1], name="argmax_eq", batch=6), gen_seed=4)
     a = orc.verify_argmax(w.target, w.target[np.concatenate([np.arange(w.cu_draft[b] + b, w.cu_draft[b + 1] + b)
