@@ -149,7 +149,10 @@ def make_shape(target: torch.Tensor, draft: Optional[torch.Tensor], batch: int, 
         if draft.shape[0] < draft_rows:
             raise ValueError(f"draft_logits has {draft.shape[0]} rows; the batch needs {draft_rows}")
     ts = _rows(target, "target_logits")
-    ds = _rows(draft, "draft_logits") if (other and draft.numel() > 0) else vocab
+    if draft is target:  # draft-side sampling: the draft rows are the one tensor
+        ds = ts
+    else:
+        ds = _rows(draft, "draft_logits") if (other and draft.numel() > 0) else vocab
     return ShapeT(
         batch=batch, max_draft=max_draft, total_draft=total_draft, vocab=vocab, dtype=_dtype_code(target),
         target_row_stride=ts, draft_row_stride=ds,
