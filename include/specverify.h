@@ -159,6 +159,39 @@ SV_API sv_status_t spec_verify_sample(const sv_shape_t* shape,
                                hipStream_t stream);
 
 /*
+ * spec_verify_sample for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, results and errors, with no workspace
+ * argument.  Its scratch is one file-scope device array of
+ * SV_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends; its address is taken once per device, on the first call
+ * made with that device current.  The call allocates nothing.
+ *   A shape and mode whose workspace (the size spec_verify_sample's query
+ *   reports) exceeds SV_NOALLOC_SCRATCH_BYTES is rejected with
+ *   SV_ERR_WORKSPACE_TOO_SMALL before anything is launched.
+ *   Every call on one GPU shares that GPU's array and leaves the last call's
+ *   contents in it (no call relies on them: every call writes what it
+ *   reads).  Calls that overlap in time on one GPU race, on any streams:
+ *   serialise them, or use spec_verify_sample with separate workspaces.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+SV_API sv_status_t spec_verify_sample_noalloc(const sv_shape_t* shape,
+                               const void* target_logits,
+                               const void* draft_logits,
+                               const int32_t* draft_ids,
+                               float temperature,
+                               int32_t top_k,
+                               float top_p,
+                               uint64_t seed,
+                               uint32_t offset,
+                               int32_t* out_tokens,
+                               int32_t* out_num_accepted,
+                               float* out_probs,
+                               float* out_residual_mass,
+                               hipStream_t stream);
+
+/*
  * Verify with argmax draws, the variant the OpenVINO page implements
  * ("Text Generation via Speculative Sampling, KV Caching, and OpenVINO",
  * "Prepare speculative sampling", steps 3 and 4): the same probabilistic

@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     verify_argmax,
     verify_greedy,
     verify_sample,
+    verify_sample_noalloc,
     workspace_bytes,
 )

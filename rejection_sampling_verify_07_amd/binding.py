@@ -72,6 +72,10 @@ def load_library(path: Optional[str] = None):
     ]
     lib.spec_verify_argmax.restype = C.c_int
     lib.spec_verify_argmax.argtypes = lib.spec_verify_sample.argtypes
+    lib.spec_verify_sample_noalloc.restype = C.c_int
+    lib.spec_verify_sample_noalloc.argtypes = [
+        C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_float, C.c_uint64, C.c_uint32, VP, VP, VP, VP, VP,
+    ]
     lib.spec_verify_greedy.restype = C.c_int
     lib.spec_verify_greedy.argtypes = [C.POINTER(ShapeT), VP, VP, VP, VP, VP, C.POINTER(C.c_size_t), VP]
     lib.spec_draft_sample.restype = C.c_int
@@ -233,6 +237,36 @@ def verify_sample(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft
         out["residual_mass"].data_ptr() if out.get("residual_mass") is not None else None,
         workspace.data_ptr(), C.byref(have), C.c_void_p(_stream_handle(stream)))
     _check(st, name)
+    return out
+
+
+def verify_sample_noalloc(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_ids: torch.Tensor,
+                          cu_draft: Optional[torch.Tensor] = None, temperature: float = 1.0, top_k: int = 0,
+                          seed: int = 0, offset: int = 0, max_draft: Optional[int] = None, out: Optional[dict] = None,
+                          stream=None, top_p: float = 1.0) -> dict:
+    """spec_verify_sample_noalloc: verify_sample with the library's own
+    per-device scratch instead of a workspace (the library allocates nothing;
+    calls that overlap on one GPU race).  `out` (tokens, num_accepted, probs,
+    residual_mass) may be preallocated; otherwise it is allocated here."""
+    lib = load_library()
+    batch, kmax, total = _batch_geometry(target_logits, draft_ids, cu_draft, max_draft)
+    if draft_ids.dtype != torch.int32:
+        raise TypeError("draft_ids must be int32")
+    shape = make_shape(target_logits, draft_logits, batch, kmax, total, cu_draft, total + batch, total)
+    dev = target_logits.device
+    if out is None:
+        out = dict(tokens=torch.empty(total + batch, dtype=torch.int32, device=dev),
+                   num_accepted=torch.empty(batch, dtype=torch.int32, device=dev),
+                   probs=torch.empty((max(total, 1), 2), dtype=torch.float32, device=dev)[:total],
+                   residual_mass=torch.empty(batch, dtype=torch.float32, device=dev))
+    st = lib.spec_verify_sample_noalloc(
+        C.byref(shape), target_logits.data_ptr(), draft_logits.data_ptr() if draft_logits.numel() else None,
+        draft_ids.data_ptr() if draft_ids.numel() else None, float(temperature), int(top_k), float(top_p), int(seed),
+        int(offset), out["tokens"].data_ptr(), out["num_accepted"].data_ptr(),
+        out["probs"].data_ptr() if out.get("probs") is not None and total > 0 else None,
+        out["residual_mass"].data_ptr() if out.get("residual_mass") is not None else None,
+        C.c_void_p(_stream_handle(stream)))
+    _check(st, "spec_verify_sample_noalloc")
     return out
 
 

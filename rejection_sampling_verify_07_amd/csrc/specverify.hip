@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "sv_common.hpp"
@@ -471,22 +472,22 @@ bool filters_ok(const sv_shape_t* sh, float temperature, int32_t top_k, float to
            top_k <= sh->vocab && top_p > 0.0f && top_p <= 1.0f;
 }
 
-sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
-                                 const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
-                                 uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
-                                 float* out_residual_mass, void* workspace, size_t* workspace_bytes,
-                                 hipStream_t stream, int32_t argmax_draw, const sv_profile_events_t* prof)
+// Shape, filters and plan of a sampling verify (no pointer is looked at).
+sv_status_t sample_plan(const sv_shape_t* shape, float temperature, int32_t top_k, float top_p, Plan* p)
 {
-    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
     sv_status_t st = check_shape(shape, CALL_SAMPLE);
     if (st != SV_OK) return st;
     if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
-    const Plan p = make_plan(shape, CALL_SAMPLE, top_k, top_p);
-    if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
-    if (workspace == nullptr) {
-        *workspace_bytes = p.bytes;
-        return SV_OK;
-    }
+    *p = make_plan(shape, CALL_SAMPLE, top_k, top_p);
+    if ((int64_t)p->rows * p->nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    return SV_OK;
+}
+
+// The data pointers of a sampling verify: present where the shape needs them, aligned.
+sv_status_t sample_pointers(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                            const int32_t* draft_ids, const int32_t* out_tokens, const int32_t* out_num_accepted,
+                            const float* out_probs, const float* out_residual_mass)
+{
     const size_t es = esize_of(shape->dtype);
     if (target_logits == nullptr || out_tokens == nullptr || out_num_accepted == nullptr) return SV_ERR_INVALID_ARGUMENT;
     if (shape->total_draft > 0 && (draft_logits == nullptr || draft_ids == nullptr)) return SV_ERR_INVALID_ARGUMENT;
@@ -495,15 +496,43 @@ sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_log
     if (!aligned(out_tokens, 4) || !aligned(out_num_accepted, 4) || (draft_ids && !aligned(draft_ids, 4)) ||
         (out_probs && !aligned(out_probs, 4)) || (out_residual_mass && !aligned(out_residual_mass, 4)))
         return SV_ERR_INVALID_ARGUMENT;
-    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
-    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+    return SV_OK;
+}
 
+sv_status_t launch_sample(const sv_shape_t* shape, const Plan& p, const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_ids, float temperature, uint64_t seed, uint32_t offset,
+                          int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs, float* out_residual_mass,
+                          void* workspace, hipStream_t stream, int32_t argmax_draw, const sv_profile_events_t* prof)
+{
     const float c = scale_of(temperature);
     return by_dtype(shape->dtype, [&](auto dt) {
         return run_sample<decltype(dt)::value>(shape, p, target_logits, draft_logits, draft_ids, c, seed,
                                                offset, out_tokens, out_num_accepted, out_probs, out_residual_mass,
                                                workspace, stream, argmax_draw, prof);
     });
+}
+
+sv_status_t verify_sample_common(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                                 const int32_t* draft_ids, float temperature, int32_t top_k, float top_p, uint64_t seed,
+                                 uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted, float* out_probs,
+                                 float* out_residual_mass, void* workspace, size_t* workspace_bytes,
+                                 hipStream_t stream, int32_t argmax_draw, const sv_profile_events_t* prof)
+{
+    if (workspace_bytes == nullptr) return SV_ERR_INVALID_ARGUMENT;
+    Plan p;
+    sv_status_t st = sample_plan(shape, temperature, top_k, top_p, &p);
+    if (st != SV_OK) return st;
+    if (workspace == nullptr) {
+        *workspace_bytes = p.bytes;
+        return SV_OK;
+    }
+    st = sample_pointers(shape, target_logits, draft_logits, draft_ids, out_tokens, out_num_accepted, out_probs,
+                         out_residual_mass);
+    if (st != SV_OK) return st;
+    if (!aligned(workspace, kAlign)) return SV_ERR_INVALID_ARGUMENT;
+    if (*workspace_bytes < p.bytes) return SV_ERR_WORKSPACE_TOO_SMALL;
+    return launch_sample(shape, p, target_logits, draft_logits, draft_ids, temperature, seed, offset, out_tokens,
+                         out_num_accepted, out_probs, out_residual_mass, workspace, stream, argmax_draw, prof);
 }
 
 sv_status_t verify_greedy_common(const sv_shape_t* shape, const void* target_logits, const int32_t* draft_ids,
@@ -599,6 +628,36 @@ sv_status_t token_likelihood_common(const sv_shape_t* shape, const void* target_
     });
 }
 
+// ---- scratch of the allocation-free entry point
+//
+// One device array per GPU, held until the process ends.  Host code never
+// passes `scratch` itself to a kernel (in host code the name is a host-side
+// stand-in, not a device address): the device address is taken once per
+// device with hipGetSymbolAddress, with that device current, and kept here.
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// The current device's address of `scratch` (nullptr on a HIP error).
+void* scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -612,6 +671,25 @@ sv_status_t spec_verify_sample(const sv_shape_t* shape, const void* target_logit
     return verify_sample_common(shape, target_logits, draft_logits, draft_ids, temperature, top_k, top_p, seed, offset,
                                 out_tokens, out_num_accepted, out_probs, out_residual_mass, workspace,
                                 workspace_bytes, stream, 0, nullptr);
+}
+
+sv_status_t spec_verify_sample_noalloc(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,
+                                       const int32_t* draft_ids, float temperature, int32_t top_k, float top_p,
+                                       uint64_t seed, uint32_t offset, int32_t* out_tokens, int32_t* out_num_accepted,
+                                       float* out_probs, float* out_residual_mass, hipStream_t stream)
+{
+    // every argument check, then the plan's size: nothing touches the device before they pass
+    Plan p;
+    sv_status_t st = sample_plan(shape, temperature, top_k, top_p, &p);
+    if (st != SV_OK) return st;
+    st = sample_pointers(shape, target_logits, draft_logits, draft_ids, out_tokens, out_num_accepted, out_probs,
+                         out_residual_mass);
+    if (st != SV_OK) return st;
+    if (p.bytes > SV_NOALLOC_SCRATCH_BYTES) return SV_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = scratch_for_current_device();
+    if (ws == nullptr) return SV_ERR_HIP;
+    return launch_sample(shape, p, target_logits, draft_logits, draft_ids, temperature, seed, offset, out_tokens,
+                         out_num_accepted, out_probs, out_residual_mass, ws, stream, 0, nullptr);
 }
 
 sv_status_t spec_verify_argmax(const sv_shape_t* shape, const void* target_logits, const void* draft_logits,

@@ -45,7 +45,9 @@ def test_header_declares_the_boundary():
     # every call has a benchmark form with per-call events, and nothing else
     plain = declared_functions((HEADER,))
     prof = declared_functions((PROFILE_HEADER,))
-    assert sorted(prof) == sorted(n + "_profiled" for n in plain if n != "spec_verify_status_string")
+    assert "spec_verify_sample_noalloc" in plain
+    assert sorted(prof) == sorted(n + "_profiled" for n in plain
+                                  if n not in ("spec_verify_status_string", "spec_verify_sample_noalloc"))
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -398,3 +400,27 @@ def test_workspace_queries_over_many_shapes(lib, B):
                         if prev is not None and K == 8:
                             assert all(cur[k] >= prev[k] for k in cur), (dt, V, top_k, top_p, batch)
                         prev = cur
+
+
+def test_noalloc_checks_arguments_and_rejects_plans_past_its_scratch(lib, B):
+    """spec_verify_sample_noalloc checks its arguments as spec_verify_sample
+    does and rejects a plan larger than its fixed scratch, before touching
+    the device (no GPU is needed for any of these)."""
+    fake = 1 << 40
+
+    def call(sh, tgt=fake, T=1.0, top_k=0):
+        return lib.spec_verify_sample_noalloc(C.byref(sh), tgt, fake, fake, T, top_k, 1.0, 0, 0, fake, fake, None, None,
+                                              None)
+
+    assert call(_shape(B, batch=0)) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(_shape(B), T=0.0) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(_shape(B), tgt=None) == B.SV_ERR_INVALID_ARGUMENT
+    assert call(_shape(B), tgt=fake + 1) == B.SV_ERR_INVALID_ARGUMENT
+    assert lib.spec_verify_sample_noalloc(None, fake, fake, fake, 1.0, 0, 1.0, 0, 0, fake, fake, None, None,
+                                          None) == B.SV_ERR_INVALID_ARGUMENT
+    # a plan past the scratch: 128 sequences of 8 guesses over 151936 logits with top-k 50
+    big = _shape(B, batch=128, max_draft=8, total_draft=1024, vocab=151936, target_row_stride=151936,
+                 draft_row_stride=151936)
+    st, need = _query(lib, big, top_k=50)
+    assert st == B.SV_OK and need > (64 << 20)
+    assert call(big, top_k=50) == B.SV_ERR_WORKSPACE_TOO_SMALL
