@@ -57,6 +57,11 @@ static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads 
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
 constexpr int32_t kDraftSmallRowsMin = 512;  // draft rows from which full-row draft draws use smaller workgroups
 constexpr size_t kAlign = 256;
+// XCDs of an MI355X: workgroups are dealt to them in turn, workgroup g to XCD g mod 8
+#ifndef SV_XCDS
+#define SV_XCDS 8
+#endif
+constexpr int32_t kXcds = SV_XCDS;
 
 enum PlanMode { PLAN_FULL = 0, PLAN_TOPK_FAST = 1, PLAN_TOPK_EXACT = 2, PLAN_GREEDY = 3 };
 enum CallKind { CALL_SAMPLE = 0, CALL_GREEDY = 1, CALL_DRAFT = 2, CALL_LIKE = 3 };
@@ -266,12 +271,16 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
         counts = ws_at<int32_t>(ws, p.off_counts);
         bounds = ws_at<float>(ws, p.off_bounds);
         cands = ws_at<sv::KeptEntry>(ws, p.off_cands);
-        launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT>, grid_stream, stream, rs, sh->vocab, p.nchunk,
-                      (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands);
+        // tiles grouped by XCD so that each row's candidates are in the L2 of
+        // the XCD that runs the row's select (workgroup `row` of the next kernel)
+        const uint32_t xrows = (uint32_t)((p.rows + kXcds - 1) / kXcds * kXcds);
+        launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT>, xrows * (uint32_t)p.nchunk, stream, rs,
+                      sh->vocab, p.nchunk, (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands,
+                      (int32_t)kXcds);
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         // one wave per row; rows whose chunks overflowed take the exact path inside
         hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,
-                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, (int32_t)1, descs, kept);
+                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, descs, kept);
     } else {
         hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
                            top_k, c, (int32_t)sv::kKeepCap, descs, kept);
@@ -479,7 +488,7 @@ sv_status_t sample_plan(const sv_shape_t* shape, float temperature, int32_t top_
     if (st != SV_OK) return st;
     if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
     *p = make_plan(shape, CALL_SAMPLE, top_k, top_p);
-    if ((int64_t)p->rows * p->nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    if (((int64_t)p->rows + kXcds) * p->nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     return SV_OK;
 }
 
@@ -573,7 +582,7 @@ sv_status_t draft_sample_common(const sv_shape_t* shape, const void* draft_logit
     if (st != SV_OK) return st;
     if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
     const Plan p = make_plan(shape, CALL_DRAFT, top_k, top_p);
-    if ((int64_t)p.rows * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    if (((int64_t)p.rows + kXcds) * p.nchunk > INT32_MAX) return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;
         return SV_OK;
@@ -604,7 +613,7 @@ sv_status_t token_likelihood_common(const sv_shape_t* shape, const void* target_
     if (st != SV_OK) return st;
     if (!filters_ok(shape, temperature, top_k, top_p)) return SV_ERR_INVALID_ARGUMENT;
     const Plan p = make_plan(shape, CALL_LIKE, top_k, top_p);
-    if ((int64_t)p.rows * p.nchunk > INT32_MAX || (int64_t)p.rows_t * (p.nchunk2 > 0 ? p.nchunk2 : 1) > INT32_MAX)
+    if (((int64_t)p.rows + kXcds) * p.nchunk > INT32_MAX || (int64_t)p.rows_t * (p.nchunk2 > 0 ? p.nchunk2 : 1) > INT32_MAX)
         return SV_ERR_UNSUPPORTED;
     if (workspace == nullptr) {
         *workspace_bytes = p.bytes;

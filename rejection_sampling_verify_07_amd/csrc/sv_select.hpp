@@ -489,40 +489,49 @@ __device__ void wave_select_exact(int32_t row, const char* rowp, int32_t vocab, 
     }
 }
 
-// One wave per row.  use_cands = 0: every row takes the exact path.
+// The select of one row by one wave: the speculative path, else the
+// chunk-list path, else the exact path over the full row.
+template <int DT>
+__device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, int32_t vocab, int32_t nchunk, int32_t top_k,
+                                int32_t cap, float c, const int32_t* __restrict__ counts,
+                                const float* __restrict__ bounds, const KeptEntry* __restrict__ cands,
+                                RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
+                                int32_t* s_choff)
+{
+    if (wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L)) return;
+    int32_t base = 0, bad = 0;
+    for (int32_t g = 0; g < nchunk; g += kWave) {
+        const int32_t ch = g + lane_id();
+        const int32_t n = ch < nchunk ? counts[(int64_t)row * nchunk + ch] : 0;
+        bad |= n > cap;
+        const int32_t nc = min(n, cap);
+        const int incl = wave_incl_scan_int(nc);
+        if (ch < nchunk) s_choff[ch] = base + incl - nc;
+        base += __shfl(incl, kWave - 1, kWave);
+    }
+    if (lane_id() == 0) s_choff[nchunk] = base;
+    __builtin_amdgcn_wave_barrier();
+    if (__ballot(bad != 0) == 0 && base >= top_k && base <= kKeepCapList) {
+        wave_select_fast<DT>(row, nchunk, top_k, cap, c, cands, descs, kept, L, s_choff, base);
+        return;
+    }
+    wave_select_exact<DT>(row, row_ptr(rs, row), vocab, top_k, c, descs, kept, L);
+}
+
+// One wave per row, over the candidates of the top-k streaming pass.
 template <int DT>
 __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                                  int32_t top_k, int32_t cap, float c,
                                                                  const int32_t* __restrict__ counts,
                                                                  const float* __restrict__ bounds,
                                                                  const KeptEntry* __restrict__ cands,
-                                                                 int32_t use_cands, RowDesc* __restrict__ descs,
+                                                                 RowDesc* __restrict__ descs,
                                                                  KeptEntry* __restrict__ kept)
 {
     __shared__ WaveSelLds L;
     __shared__ int32_t s_choff[kMaxChunks + 1];
-    const int32_t row = blockIdx.x;
-    if (use_cands != 0 && wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L))
-        return;
-    if (use_cands != 0) {
-        int32_t base = 0, bad = 0;
-        for (int32_t g = 0; g < nchunk; g += kWave) {
-            const int32_t ch = g + lane_id();
-            const int32_t n = ch < nchunk ? counts[(int64_t)row * nchunk + ch] : 0;
-            bad |= n > cap;
-            const int32_t nc = min(n, cap);
-            const int incl = wave_incl_scan_int(nc);
-            if (ch < nchunk) s_choff[ch] = base + incl - nc;
-            base += __shfl(incl, kWave - 1, kWave);
-        }
-        if (lane_id() == 0) s_choff[nchunk] = base;
-        __builtin_amdgcn_wave_barrier();
-        if (__ballot(bad != 0) == 0 && base >= top_k && base <= kKeepCapList) {
-            wave_select_fast<DT>(row, nchunk, top_k, cap, c, cands, descs, kept, L, s_choff, base);
-            return;
-        }
-    }
-    wave_select_exact<DT>(row, row_ptr(rs, row), vocab, top_k, c, descs, kept, L);
+    select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L,
+                        s_choff);
 }
 
 }  // namespace sv

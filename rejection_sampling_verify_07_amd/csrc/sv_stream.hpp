@@ -51,14 +51,29 @@ __device__ __forceinline__ void issue_tile(const Tile& t, const u32x4* base, u32
     }
 }
 
+// The tile of workgroup g.  With xcd > 1 the tiles of row r go to the
+// workgroups g = r (mod xcd): the dispatcher deals workgroups to the XCDs in
+// turn (MI355X: 8 XCDs), so all of a row's tiles run on one XCD, the one that
+// also runs workgroup r of a per-row kernel launched next, which then finds
+// the row's partial results in that XCD's L2.  The grid holds xcd *
+// ceil(rows / xcd) * nchunk workgroups; -1 marks a padding workgroup.
+__device__ __forceinline__ int32_t tile_of(int32_t g, int32_t ntiles, int32_t nchunk, int32_t xcd)
+{
+    if (xcd <= 1) return g < ntiles ? g : -1;
+    const int32_t x = g % xcd, local = g / xcd;
+    const int32_t row = (local / nchunk) * xcd + x;
+    const int32_t c = row * nchunk + local % nchunk;
+    return c < ntiles ? c : -1;
+}
+
 // body(tile, raw) is called once, by every thread of the workgroup, with the
 // thread's LOADS raw words (which the body may overwrite).
 template <int DT, int LOADS, bool NT, class Body>
 __device__ __forceinline__ void walk_tiles(const RowSet& rs, int32_t vocab, int32_t nchunk, int32_t ntiles,
-                                           Body&& body)
+                                           Body&& body, int32_t xcd = 1)
 {
-    const int32_t c = (int32_t)blockIdx.x;
-    if (c >= ntiles) return;
+    const int32_t c = tile_of((int32_t)blockIdx.x, ntiles, nchunk, xcd);
+    if (c < 0) return;
     const u32x4* base;
     u32x4 raw[LOADS];
     const Tile t = make_tile<DT>(rs, vocab, nchunk, c, LOADS, &base);

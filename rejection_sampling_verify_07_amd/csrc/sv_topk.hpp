@@ -191,7 +191,7 @@ constexpr int kChunkLds = kWaves * kWaveLds;
 template <int DT, int LOADS, bool NT>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
-    int32_t* __restrict__ counts, float* __restrict__ bounds, KeptEntry* __restrict__ cands)
+    int32_t* __restrict__ counts, float* __restrict__ bounds, KeptEntry* __restrict__ cands, int32_t xcd)
 {
     constexpr int VEC = Dt<DT>::kVec;
     constexpr int LOW = (DT == DT_BF16) ? 16 : 0;
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
             counts[t.index] = written;  // > cap marks an overflow
             bounds[t.index] = bound;
         }
-    });
+    }, xcd);
 }
 
 // Block-wide max / sum (fixed order); every thread gets the result.

@@ -348,12 +348,16 @@ template <bool RESID, class Entry, class Draft>
 __device__ void argmax_list_of(Entry&& entry, int32_t n, Draft&& draft, const ResidualW& rw, int32_t* token,
                                double* total)
 {
+    constexpr int PER = kKeepCap / kWave;  // entries per lane
     const int32_t per = (n + kWave - 1) / kWave;
     const int32_t lo = min(n, lane_id() * per), hi = min(n, lo + per);
     float best = 0.0f;
     int32_t bid = INT32_MAX;
     double ls = 0.0;
-    for (int32_t i = lo; i < hi; ++i) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int32_t i = lo + q;
+        if (i >= hi) continue;
         const KeptEntry e = entry(i);
         const float et = __builtin_amdgcn_exp2f(__builtin_fmaf(e.val, rw.c, -rw.mcc_t));
         float w = et * rw.inv_t;
@@ -733,28 +737,35 @@ __device__ __forceinline__ void draw_token(const VerifyArgs& a, int32_t n, int32
     *z_out = z;
 }
 
-template <int DT, bool FROM_DESC, int NT>
-__global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
-{
-    __shared__ RowLds s_row[2 * kMaxDraft + 1];
-    __shared__ DrawLds<NT> s_draw;
-    __shared__ double s_udraw[kMaxDraft + 1];
-    __shared__ int32_t s_n, s_bad;
+// LDS of one sequence's verify.
+template <int NT>
+struct VerifyLds {
+    RowLds row[2 * kMaxDraft + 1];
+    DrawLds<NT> draw;
+    double udraw[kMaxDraft + 1];
+    int32_t n, bad;
+};
 
-    const int32_t b = blockIdx.x;
-    int32_t k0, kb;
+// The sequence's draft offset k0 and length kb from cu (or the uniform K);
+// false when its cu entries are out of range.
+__device__ __forceinline__ bool seq_range(const VerifyArgs& a, int32_t b, int32_t* k0, int32_t* kb)
+{
     if (a.cu != nullptr) {
-        k0 = a.cu[b];
+        *k0 = a.cu[b];
         const int32_t k1 = a.cu[b + 1];
-        kb = k1 - k0;
-        if (k0 < 0 || kb < 0 || kb > a.kmax || k1 > a.total_draft) {
-            if (threadIdx.x == 0) a.out_nacc[b] = -1;
-            return;
-        }
-    } else {
-        k0 = b * a.kmax;
-        kb = a.kmax;
+        *kb = k1 - *k0;
+        return !(*k0 < 0 || *kb < 0 || *kb > a.kmax || k1 > a.total_draft);
     }
+    *k0 = b * a.kmax;
+    *kb = a.kmax;
+    return true;
+}
+
+// Verify of sequence b (draft rows k0 .. k0+kb-1, target rows k0+b .. k0+b+kb),
+// by all NT threads of the workgroup.
+template <int DT, bool FROM_DESC, int NT>
+__device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb, VerifyLds<NT>& S)
+{
     const int32_t trow0 = k0 + b;  // first target row of the sequence
     const int32_t drow0 = k0;      // first draft row
     const int32_t nrows = 2 * kb + 1;
@@ -764,21 +775,22 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
     };
 
     if (threadIdx.x == 0) {
-        s_n = kb;
-        s_bad = 0;
+        S.n = kb;
+        S.bad = 0;
     }
     // every uniform the step can use, computed while the first loads are in
-    // flight: thread k holds U(b, k, 0); s_udraw[k] = U(b, k, 1), s_udraw[kb] = U(b, kb, 2)
-    static_assert(NT > kMaxDraft, "one thread per draft position");
+    // flight: thread k holds U(b, k, 0) (positions past NT compute their own);
+    // S.udraw[k] = U(b, k, 1), S.udraw[kb] = U(b, kb, 2)
     const int32_t tk = threadIdx.x;
     const double u_acc = uniform24(a.seed, (uint32_t)b, (uint32_t)tk, 0u, a.offset);
-    if (tk <= kb) s_udraw[tk] = uniform24(a.seed, (uint32_t)b, (uint32_t)tk, tk < kb ? 1u : 2u, a.offset);
+    for (int32_t t = tk; t <= kb; t += NT)
+        S.udraw[t] = uniform24(a.seed, (uint32_t)b, (uint32_t)t, t < kb ? 1u : 2u, a.offset);
 
     // ---- A: row statistics
     if constexpr (FROM_DESC) {
         for (int32_t r = threadIdx.x; r < nrows; r += NT) {
             const RowDesc d = a.descs[grow(r)];
-            s_row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
+            S.row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
         }
     } else {
         for (int32_t r = wave_id(); r < nrows; r += (NT / kWave)) {
@@ -793,7 +805,7 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
                 if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
             }
             s = wave_sum_dpp(s);
-            if (lane_id() == 0) s_row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+            if (lane_id() == 0) S.row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
         }
     }
     __syncthreads();
@@ -804,13 +816,13 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
     for (int32_t k = threadIdx.x; k < kb; k += NT) {
         const int32_t x = a.ids[drow0 + k];
         if (x < 0 || x >= a.vocab) {
-            atomicOr(&s_bad, 1);
+            atomicOr(&S.bad, 1);
             continue;
         }
         const float lt = load_one<DT>(tbase + (int64_t)(trow0 + k) * a.rs.t_stride_bytes, x);
         const float ld = load_one<DT>(dbase + (int64_t)(drow0 + k) * a.rs.d_stride_bytes, x);
-        const RowLds& rt = s_row[k];
-        const RowLds& rd = s_row[kb + 1 + k];
+        const RowLds& rt = S.row[k];
+        const RowLds& rd = S.row[kb + 1 + k];
         const double cd = (double)a.c;
         const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
         const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
@@ -819,24 +831,26 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
             a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
         }
         const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        if (!(u_acc < ratio)) atomicMin(&s_n, k);
+        const double u = k == tk ? u_acc : uniform24(a.seed, (uint32_t)b, (uint32_t)k, 0u, a.offset);
+        if (!(u < ratio)) atomicMin(&S.n, k);
     }
     __syncthreads();
-    if (s_bad != 0) {
+    if (S.bad != 0) {
         if (threadIdx.x == 0) a.out_nacc[b] = -1;
         return;
     }
-    const int32_t n = s_n;
+    const int32_t n = S.n;
 
     // ---- C: residual or extra-token draw
     int32_t token;
     double z;
     {
-        const RowLds rt = s_row[n];
-        const RowLds rd = s_row[n < kb ? kb + 1 + n : n];
+        const RowLds rt = S.row[n];
+        const RowLds rd = S.row[n < kb ? kb + 1 + n : n];
         const char* trow = tbase + (int64_t)(trow0 + n) * a.rs.t_stride_bytes;
         const char* drow = n < kb ? dbase + (int64_t)(drow0 + n) * a.rs.d_stride_bytes : nullptr;
-        draw_token<DT, FROM_DESC, NT>(a, n, kb, s_udraw[n], rt, rd, trow, drow, (int64_t)grow(n), s_draw, &token, &z);
+        draw_token<DT, FROM_DESC, NT>(a, n, kb, S.udraw[n], rt, rd, trow, drow, (int64_t)grow(n), S.draw, &token,
+                                      &z);
     }
 
     // ---- D: outputs
@@ -847,6 +861,21 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
         a.out_nacc[b] = n;
         if (a.out_zmass != nullptr) a.out_zmass[b] = (float)z;
     }
+}
+
+// One workgroup per sequence, after the streaming pass (and the top-k select
+// or top-p pass) has finished.
+template <int DT, bool FROM_DESC, int NT>
+__global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
+{
+    __shared__ VerifyLds<NT> S;
+    const int32_t b = blockIdx.x;
+    int32_t k0, kb;
+    if (!seq_range(a, b, &k0, &kb)) {
+        if (threadIdx.x == 0) a.out_nacc[b] = -1;
+        return;
+    }
+    verify_seq<DT, FROM_DESC, NT>(a, b, k0, kb, S);
 }
 
 // ---------------------------------------------------------------------------
