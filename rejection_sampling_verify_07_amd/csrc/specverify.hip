@@ -55,6 +55,20 @@ constexpr int32_t kTopkFastPlanMax = 240;
 static_assert(kTopkFastPlanMax <= sv::kTopkFastMax, "the candidate pass needs top_k lane maxima");
 static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads past a chunk's candidate slots");
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
+constexpr int kSplitThreads = 512;        // workgroups of the split verify over full rows
+// Workgroups per sequence of the full-row verify: enough to spread a batch's
+// residual walks over about 512 workgroups (a batch of 256 sequences or more
+// keeps one 1024-thread workgroup per sequence), with at least 4 segments of
+// 512 ids each.
+int32_t split_groups(int32_t batch, int32_t vocab)
+{
+    if (batch >= 256) return 1;
+    const int32_t nseg = (vocab + sv::kSeg - 1) / sv::kSeg;
+    int32_t g = 512 / batch;
+    if (g > 16) g = 16;
+    if (g > nseg / 4) g = nseg / 4;
+    return g < 2 ? 1 : g;
+}
 constexpr int32_t kDraftSmallRowsMin = 512;  // draft rows from which full-row draft draws use smaller workgroups
 constexpr size_t kAlign = 256;
 // XCDs of an MI355X: workgroups are dealt to them in turn, workgroup g to XCD g mod 8
@@ -72,12 +86,14 @@ struct Plan {
     int32_t nchunk;
     int32_t loads;  // 16-byte loads per thread per tile of the streaming pass
     int32_t nchunk2;  // tiles per row pair of the likelihood's pair pass (full rows)
+    int32_t groups;   // workgroups per sequence of the split verify over full rows (1: one workgroup)
     int32_t pair_loads;  // 16-byte loads per thread per row in that pass
     int32_t top_k;
     float top_p;
     bool topp;  // top_p < 1: the nucleus pass runs after the statistics
     bool desc;  // the consumers read row descriptors (top-k and/or top-p), not chunk partials
-    size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, off_pair, bytes;
+    size_t off_partials, off_counts, off_bounds, off_cands, off_descs, off_kept, off_pair, off_segsum, off_tickets,
+        bytes;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -195,6 +211,14 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
     if (p.mode == PLAN_FULL) {
         p.off_partials = off;
         off = align_up(off + slots * sizeof(sv::PartialFull));
+        p.groups = (kind == CALL_SAMPLE && !p.topp) ? split_groups(sh->batch, sh->vocab) : 1;
+        if (p.groups > 1) {
+            const size_t nseg = (size_t)(sh->vocab + sv::kSeg - 1) / sv::kSeg;
+            p.off_segsum = off;
+            off = align_up(off + (size_t)sh->batch * nseg * sizeof(double));
+            p.off_tickets = off;
+            off = align_up(off + (size_t)sh->batch * sv::kTicketStride * sizeof(int32_t));
+        }
         if (kind == CALL_LIKE && !p.topp) {
             const bool big2 =
                 (int64_t)p.rows_t * chunks_for(sh->vocab, vec_of(sh->dtype), sv::kPairLoads) > kBigGridTiles;
@@ -252,12 +276,14 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows * p.nchunk);
     if (p.mode == PLAN_FULL) {
         sv::PartialFull* part = ws_at<sv::PartialFull>(ws, p.off_partials);
+        int32_t* tickets = p.groups > 1 ? ws_at<int32_t>(ws, p.off_tickets) : nullptr;
+        const int32_t nzero = p.groups > 1 ? sh->batch * sv::kTicketStride : 0;
         if (p.loads == kLoadsBig) {
             launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_FULL, kLoadsBig, kNT, true>, grid_stream, stream, rs,
-                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part, tickets, nzero);
         } else {
             launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_FULL, kLoads, kNT>, grid_stream, stream, rs,
-                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part);
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, c, (void*)part, tickets, nzero);
         }
         va.partials = part;
         return launch_status();
@@ -347,7 +373,11 @@ sv_status_t run_sample(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     va.out_zmass = out_z;
     va.argmax_draw = argmax_draw;
     if (run_stats<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
-    if (!p.desc) {
+    if (!p.desc && p.groups > 1 && argmax_draw == 0) {
+        const sv::SplitArgs sa{va, ws_at<double>(ws, p.off_segsum), ws_at<int32_t>(ws, p.off_tickets)};
+        hipLaunchKernelGGL((sv::verify_split_kernel<DT, kSplitThreads>), dim3(sh->batch, p.groups),
+                           dim3(kSplitThreads), 0, stream, sa);
+    } else if (!p.desc) {
         hipLaunchKernelGGL((sv::verify_kernel<DT, false, kVerifyFullThreads>), dim3(sh->batch), dim3(kVerifyFullThreads), 0,
                            stream, va);
     } else if (p.mode == PLAN_FULL) {  // top-p over full rows: a nucleus may still be a masked full row
@@ -456,10 +486,10 @@ sv_status_t run_greedy(const sv_shape_t* sh, const Plan& p, const void* tgt, con
     const uint32_t grid_stream = (uint32_t)((int64_t)p.rows_t * p.nchunk);
     if (p.loads == kLoadsBigArgmax) {
         launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoadsBigArgmax, kNT>, grid_stream, stream, rs,
-                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
+                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part, (int32_t*)nullptr, (int32_t)0);
     } else {
         launch_stream(prof, sv::row_stats_kernel<DT, sv::MODE_ARGMAX, kLoads, kNT>, grid_stream, stream, rs,
-                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part);
+                      sh->vocab, p.nchunk, (int32_t)grid_stream, 0.0f, (void*)part, (int32_t*)nullptr, (int32_t)0);
     }
     if (launch_status() != SV_OK) return SV_ERR_HIP;
     sv::GreedyArgs ga{sh->cu_draft, sh->batch, sh->max_draft, sh->total_draft, sh->vocab, ids, part, p.nchunk,

@@ -411,4 +411,45 @@ struct KeptEntry {
     float val;
 };
 
+// ---------------------------------------------------------------------------
+// Hand-off between the workgroups of one kernel.  The L2 of each XCD is not
+// coherent with the others', so data that one workgroup publishes for
+// another travels in relaxed agent-scope atomic stores and loads (global
+// store / load with sc1: written through to, and read from, the agent's
+// point of coherence) rather than in plain stores, which a release fence
+// would have to write back from L2 (buffer_wbl2) in every publishing
+// workgroup.  Each publishing wave waits for its stores to complete
+// (wait_stores) before the workgroup takes a ticket with an agent-scope
+// atomic; the workgroup that takes the last ticket reads with agent loads
+// only after its atomic has returned.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent_f64(double* p, double v)
+{
+    __hip_atomic_store((SV_GLOBAL uint64_t*)p, (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_agent_f64(const double* p)
+{
+    return __longlong_as_double(
+        (long long)__hip_atomic_load((const SV_GLOBAL uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// An agent-scope atomic add that returns the previous value: a ticket.
+__device__ __forceinline__ int32_t ticket_agent(int32_t* p)
+{
+    return __hip_atomic_fetch_add((SV_GLOBAL int32_t*)p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every memory operation this wave has issued is complete (stores written to
+// their level of coherence); the compiler keeps memory operations on their
+// side of it.
+__device__ __forceinline__ void wait_stores()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Tickets sit 256 bytes apart, one cache line each, so that the atomics of
+// different sequences do not contend for a line (measured: 32 tickets in
+// one line cost 1.5 us per step at 10 arrivals each).
+constexpr int kTicketStride = 64;
+
 }  // namespace sv

@@ -114,10 +114,15 @@ __device__ __forceinline__ void full_masked(const Tile& t, const u32x4* raw, int
     }
 }
 
+// zero[0 .. nzero): cleared (grid-stride) for a kernel that runs after this
+// one (the per-sequence tickets of the split verify).
 template <int DT, int MODE, int LOADS, bool NT, bool MASKED = false>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
-                                                             int32_t ntiles, float c, void* __restrict__ partials)
+                                                             int32_t ntiles, float c, void* __restrict__ partials,
+                                                             int32_t* __restrict__ zero, int32_t nzero)
 {
+    for (int32_t i = (int32_t)(blockIdx.x * kThreads + threadIdx.x); i < nzero; i += (int32_t)(gridDim.x * kThreads))
+        zero[i] = 0;
     constexpr int VEC = Dt<DT>::kVec;
     __shared__ float s_m[kWaves];
     __shared__ int32_t s_i[kWaves];

@@ -154,40 +154,47 @@ __device__ __forceinline__ void seg_weights(const char* ra, const char* rb, int3
     }
 }
 
-// Inverse CDF over a full row (or row pair).  All threads call it; all get
-// the token and the total.
-template <int DT, bool TWO, int NT, class W>
-__device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, const W& wfn, double u,
-                                 double* s_seg, double* s_wd, int32_t* s_i, double* s_dd,
-                                 int32_t* token, double* total)
+// Pass 1 of the inverse CDF over a full row (or row pair): the sums of the
+// weights of segments [s_begin, s_end), each handed to put(s, sum).  A lane
+// sums its kSegElems weights in fp32, then a wave scan carries them in fp64;
+// the order is fixed, so a segment's sum is the same whichever workgroup
+// computes it.
+template <int DT, bool TWO, int NT, class W, class Put>
+__device__ __forceinline__ void cdf_segment_sums(const char* ra, const char* rb, int32_t vocab, bool vec,
+                                                 const W& wfn, int32_t s_begin, int32_t s_end, Put&& put)
 {
-    const int32_t nseg = (vocab + kSeg - 1) / kSeg;
-    const bool vec = ((uintptr_t)ra & 15u) == 0 && (!TWO || ((uintptr_t)rb & 15u) == 0);
     const int lane = lane_id();
-
-    // pass 1: per-segment sums (lane sums in fp64, then a wave inclusive scan)
-    for (int32_t s0 = wave_id(); s0 < nseg; s0 += (NT / kWave) * kSegUnroll) {
+    for (int32_t s0 = s_begin + wave_id(); s0 < s_end; s0 += (NT / kWave) * kSegUnroll) {
         float w[kSegUnroll][kSegElems];
 #pragma unroll
         for (int uu = 0; uu < kSegUnroll; ++uu) {
             const int32_t s = s0 + uu * (NT / kWave);
-            if (s < nseg) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
+            if (s < s_end) seg_weights<DT, TWO>(ra, rb, vocab, vec, s, wfn, w[uu]);
         }
 #pragma unroll
         for (int uu = 0; uu < kSegUnroll; ++uu) {
             const int32_t s = s0 + uu * (NT / kWave);
-            if (s < nseg) {
-                // a lane's kSegElems weights are summed in fp32, then carried in fp64
+            if (s < s_end) {
                 float fs = 0.0f;
 #pragma unroll
                 for (int e = 0; e < kSegElems; ++e) fs += w[uu][e];
                 const double incl = wave_incl_scan_dpp((double)fs);
-                if (lane == kWave - 1) s_seg[s] = incl;
+                if (lane == kWave - 1) put(s, incl);
             }
         }
     }
-    __syncthreads();
+}
 
+// The rest of the inverse CDF, with every segment sum in s_seg[0 .. nseg):
+// a workgroup scan of them (in place), the first segment whose running mass
+// exceeds u times the total, and a re-walk of that segment by wave 0.  All
+// threads call it; all get the token and the total.
+template <int DT, bool TWO, int NT, class W>
+__device__ void cdf_finish(const char* ra, const char* rb, int32_t vocab, bool vec, const W& wfn, double u,
+                           int32_t nseg, double* s_seg, double* s_wd, int32_t* s_i, double* s_dd, int32_t* token,
+                           double* total)
+{
+    const int lane = lane_id();
     // workgroup inclusive scan of the segment sums, in place
     const int32_t per = (nseg + NT - 1) / NT;
     const int32_t lo = min(nseg, (int32_t)threadIdx.x * per), hi = min(nseg, lo + per);
@@ -262,6 +269,20 @@ __device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, 
     *token = s_i[1];
     *total = s_dd[0];
     __syncthreads();
+}
+
+// Inverse CDF over a full row (or row pair) by one workgroup.  All threads
+// call it; all get the token and the total.
+template <int DT, bool TWO, int NT, class W>
+__device__ void inverse_cdf_full(const char* ra, const char* rb, int32_t vocab, const W& wfn, double u,
+                                 double* s_seg, double* s_wd, int32_t* s_i, double* s_dd,
+                                 int32_t* token, double* total)
+{
+    const int32_t nseg = (vocab + kSeg - 1) / kSeg;
+    const bool vec = ((uintptr_t)ra & 15u) == 0 && (!TWO || ((uintptr_t)rb & 15u) == 0);
+    cdf_segment_sums<DT, TWO, NT>(ra, rb, vocab, vec, wfn, 0, nseg, [&](int32_t s, double v) { s_seg[s] = v; });
+    __syncthreads();
+    cdf_finish<DT, TWO, NT>(ra, rb, vocab, vec, wfn, u, nseg, s_seg, s_wd, s_i, s_dd, token, total);
 }
 
 // Inverse CDF over a kept list (ascending ids), one wave.  entry(i) yields the
@@ -743,7 +764,7 @@ struct VerifyLds {
     RowLds row[2 * kMaxDraft + 1];
     DrawLds<NT> draw;
     double udraw[kMaxDraft + 1];
-    int32_t n, bad;
+    int32_t n, bad, ticket;
 };
 
 // The sequence's draft offset k0 and length kb from cu (or the uniform K);
@@ -761,18 +782,25 @@ __device__ __forceinline__ bool seq_range(const VerifyArgs& a, int32_t b, int32_
     return true;
 }
 
-// Verify of sequence b (draft rows k0 .. k0+kb-1, target rows k0+b .. k0+b+kb),
-// by all NT threads of the workgroup.
+// Sequence row r -> global row (target rows k0+b .. k0+b+kb first, then the
+// draft rows k0 .. k0+kb-1 after all rows_t target rows).
+__device__ __forceinline__ int32_t seq_row(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb, int32_t r)
+{
+    return r <= kb ? k0 + b + r : a.rs.rows_t + k0 + (r - kb - 1);
+}
+
+// Phases A and B of sequence b's verify, by all NT threads of the workgroup:
+// row statistics into S.row, every uniform into S.udraw, and the accept test
+// at every guess.  Returns n, the first rejected position (or kb), or -1
+// when a guess id is out of range.  p(x), q(x) go to out_probs when
+// write_probs.
 template <int DT, bool FROM_DESC, int NT>
-__device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb, VerifyLds<NT>& S)
+__device__ __forceinline__ int32_t verify_accept(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb,
+                                                 VerifyLds<NT>& S, bool write_probs)
 {
     const int32_t trow0 = k0 + b;  // first target row of the sequence
     const int32_t drow0 = k0;      // first draft row
     const int32_t nrows = 2 * kb + 1;
-    const int32_t rows_t = a.rs.rows_t;
-    auto grow = [&](int32_t r) {  // sequence row r -> global row (target rows first)
-        return r <= kb ? trow0 + r : rows_t + drow0 + (r - kb - 1);
-    };
 
     if (threadIdx.x == 0) {
         S.n = kb;
@@ -789,12 +817,12 @@ __device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32
     // ---- A: row statistics
     if constexpr (FROM_DESC) {
         for (int32_t r = threadIdx.x; r < nrows; r += NT) {
-            const RowDesc d = a.descs[grow(r)];
+            const RowDesc d = a.descs[seq_row(a, b, k0, kb, r)];
             S.row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
         }
     } else {
         for (int32_t r = wave_id(); r < nrows; r += (NT / kWave)) {
-            const PartialFull* pp = a.partials + (int64_t)grow(r) * a.nchunk;
+            const PartialFull* pp = a.partials + (int64_t)seq_row(a, b, k0, kb, r) * a.nchunk;
             float m = neg_inf();
             for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
             m = wave_max_dpp(m);
@@ -826,7 +854,7 @@ __device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32
         const double cd = (double)a.c;
         const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
         const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
-        if (a.out_probs != nullptr) {
+        if (write_probs && a.out_probs != nullptr) {
             a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
             a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
         }
@@ -835,32 +863,45 @@ __device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32
         if (!(u < ratio)) atomicMin(&S.n, k);
     }
     __syncthreads();
-    if (S.bad != 0) {
+    return S.bad != 0 ? -1 : S.n;
+}
+
+// Phase D: tokens x_0 .. x_{n-1}, the new token, then -1; n; the residual mass.
+template <int NT>
+__device__ __forceinline__ void verify_outputs(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb, int32_t n,
+                                               int32_t token, double z)
+{
+    const int32_t trow0 = k0 + b;
+    for (int32_t j = threadIdx.x; j <= kb; j += NT) {
+        a.out_tokens[trow0 + j] = j < n ? a.ids[k0 + j] : (j == n ? token : -1);
+    }
+    if (threadIdx.x == 0) {
+        a.out_nacc[b] = n;
+        if (a.out_zmass != nullptr) a.out_zmass[b] = (float)z;
+    }
+}
+
+// Verify of sequence b by all NT threads of the workgroup.
+template <int DT, bool FROM_DESC, int NT>
+__device__ __forceinline__ void verify_seq(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb, VerifyLds<NT>& S)
+{
+    const int32_t n = verify_accept<DT, FROM_DESC, NT>(a, b, k0, kb, S, true);
+    if (n < 0) {
         if (threadIdx.x == 0) a.out_nacc[b] = -1;
         return;
     }
-    const int32_t n = S.n;
-
     // ---- C: residual or extra-token draw
     int32_t token;
     double z;
     {
         const RowLds rt = S.row[n];
         const RowLds rd = S.row[n < kb ? kb + 1 + n : n];
-        const char* trow = tbase + (int64_t)(trow0 + n) * a.rs.t_stride_bytes;
-        const char* drow = n < kb ? dbase + (int64_t)(drow0 + n) * a.rs.d_stride_bytes : nullptr;
-        draw_token<DT, FROM_DESC, NT>(a, n, kb, S.udraw[n], rt, rd, trow, drow, (int64_t)grow(n), S.draw, &token,
-                                      &z);
+        const char* trow = a.rs.tgt + (int64_t)(k0 + b + n) * a.rs.t_stride_bytes;
+        const char* drow = n < kb ? a.rs.drf + (int64_t)(k0 + n) * a.rs.d_stride_bytes : nullptr;
+        draw_token<DT, FROM_DESC, NT>(a, n, kb, S.udraw[n], rt, rd, trow, drow, (int64_t)seq_row(a, b, k0, kb, n),
+                                      S.draw, &token, &z);
     }
-
-    // ---- D: outputs
-    for (int32_t j = threadIdx.x; j <= kb; j += NT) {
-        a.out_tokens[trow0 + j] = j < n ? a.ids[drow0 + j] : (j == n ? token : -1);
-    }
-    if (threadIdx.x == 0) {
-        a.out_nacc[b] = n;
-        if (a.out_zmass != nullptr) a.out_zmass[b] = (float)z;
-    }
+    verify_outputs<NT>(a, b, k0, kb, n, token, z);
 }
 
 // One workgroup per sequence, after the streaming pass (and the top-k select
@@ -876,6 +917,78 @@ __global__ __launch_bounds__(NT) void verify_kernel(VerifyArgs a)
         return;
     }
     verify_seq<DT, FROM_DESC, NT>(a, b, k0, kb, S);
+}
+
+// Verify over full rows with the residual draw spread over the G = gridDim.y
+// workgroups of a sequence.  Each one repeats phases A and B (small), then
+// computes the segment sums of its G-th of the two rows' residual weights
+// max(0, p_n - q_n) and publishes them (agent-scope stores); the workgroup
+// that takes the sequence's last ticket scans all of them and re-walks the
+// one segment that holds the crossing.  The draw is the one-workgroup
+// draw's, segment for segment.  Sequences that accept every guess draw the
+// extra token from the streaming pass's chunk sums in workgroup 0 alone.
+struct SplitArgs {
+    VerifyArgs va;
+    double* segsum;    // [B][nseg] residual segment sums
+    int32_t* tickets;  // [B * kTicketStride], zero at launch (the streaming pass clears them)
+};
+
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void verify_split_kernel(SplitArgs sa)
+{
+    __shared__ VerifyLds<NT> S;
+    const VerifyArgs& a = sa.va;
+    const int32_t b = blockIdx.x;
+    const int32_t g = blockIdx.y;
+    const int32_t G = gridDim.y;
+    int32_t k0, kb;
+    if (!seq_range(a, b, &k0, &kb)) {
+        if (g == 0 && threadIdx.x == 0) a.out_nacc[b] = -1;
+        return;
+    }
+    const int32_t n = verify_accept<DT, false, NT>(a, b, k0, kb, S, g == 0);
+    if (n < 0) {
+        if (g == 0 && threadIdx.x == 0) a.out_nacc[b] = -1;
+        return;
+    }
+    const RowLds rt = S.row[n];
+    const char* trow = a.rs.tgt + (int64_t)(k0 + b + n) * a.rs.t_stride_bytes;
+    const PartialFull* pp = a.partials + (int64_t)seq_row(a, b, k0, kb, n) * a.nchunk;
+    const BonusWFull bwf{rt.tau, rt.mcc, rt.inv_s, a.c};
+    int32_t token = -1;
+    double z = 0.0;
+    if (n == kb) {  // every guess accepted: the extra token from p_kb
+        if (g != 0) return;
+        inverse_cdf_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, bwf, S.udraw[n], S.draw, &token, &z);
+        verify_outputs<NT>(a, b, k0, kb, n, token, 0.0);
+        return;
+    }
+    const RowLds rd = S.row[kb + 1 + n];
+    const char* drow = a.rs.drf + (int64_t)(k0 + n) * a.rs.d_stride_bytes;
+    const ResidualWFull wf{rt.tau, rt.mcc, rt.inv_s, rd.tau, rd.mcc, rd.inv_s, a.c};
+    const int32_t nseg = (a.vocab + kSeg - 1) / kSeg;
+    const bool vec = ((uintptr_t)trow & 15u) == 0 && ((uintptr_t)drow & 15u) == 0;
+    double* ss = sa.segsum + (int64_t)b * nseg;
+    const int32_t s_lo = (int32_t)((int64_t)nseg * g / G), s_hi = (int32_t)((int64_t)nseg * (g + 1) / G);
+    cdf_segment_sums<DT, true, NT>(trow, drow, a.vocab, vec, wf, s_lo, s_hi,
+                                   [&](int32_t s, double v) { st_agent_f64(ss + s, v); });
+    // publish, then take the sequence's ticket
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) S.ticket = ticket_agent(sa.tickets + (int64_t)b * kTicketStride);
+    __syncthreads();
+    if (S.ticket != G - 1) return;
+    // the last workgroup: every segment sum, then the scan and the re-walk
+    for (int32_t s = threadIdx.x; s < nseg; s += NT) S.draw.seg[s] = ld_agent_f64(ss + s);
+    __syncthreads();
+    cdf_finish<DT, true, NT>(trow, drow, a.vocab, vec, wf, S.udraw[n], nseg, S.draw.seg, S.draw.wd, S.draw.i,
+                             S.draw.dd, &token, &z);
+    // no positive residual mass (rounding only): p_n with the same uniform
+    if (token < 0) {
+        double zz;
+        inverse_cdf_chunks<DT, NT>(trow, pp, a.nchunk, a.chunk_blocks, a.vocab, bwf, S.udraw[n], S.draw, &token, &zz);
+    }
+    verify_outputs<NT>(a, b, k0, kb, n, token, z);
 }
 
 // ---------------------------------------------------------------------------
