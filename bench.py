@@ -114,13 +114,74 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
     return rec
 
 
+EPS_BOUNDARY = 1e-6  # a draw whose uniform lies this close to its threshold or CDF edge is a boundary draw
+
+
+def draws_vs_oracle(w, mode, gpu, ref):
+    """Outcome of the measured call against the oracle on the same inputs.
+
+    For the sampling calls: the realized acceptance rate (accepted guesses /
+    guesses) and beta at the first rejection (1 - the residual mass), and the
+    oracle's boundary draws -- accept draws (|u - min(1, p/q)| < 1e-6 at an
+    evaluated position), final draws (u within 1e-6 of the chosen token's CDF
+    interval edge), top-p cuts within 1e-6 of top_p -- with the number of
+    sequences whose accepted count or tokens differ from the oracle's outside
+    them.  Greedy and draft-side sampling: compared entries and mismatches.
+    """
+    import numpy as np
+
+    if mode == "greedy":
+        bad = int(np.sum(gpu["num_accepted"] != ref["num_accepted"]) + np.sum(gpu["tokens"] != ref["tokens"]))
+        return {"compared_sequences": int(w.batch), "mismatches": bad}
+    if mode == "draft":
+        ids_g, ids_o = gpu["ids"], ref["ids"]
+        boundary = (ref["dist"] < EPS_BOUNDARY) | (ref["p_margin"] < EPS_BOUNDARY)
+        return {"compared_rows": int(ids_o.size), "boundary_final": int(boundary.sum()),
+                "mismatches": int(np.sum((ids_g != ids_o) & ~boundary))}
+    if mode == "likelihood":
+        return None
+    cu, lens = w.cu_draft, w.draft_lens
+    nacc = gpu["num_accepted"].astype(np.int64)
+    rej = nacc < lens
+    out = {"acceptance_rate": round(float(nacc.sum() / max(int(lens.sum()), 1)), 4),
+           "beta_at_rejection_mean": round(float(np.mean(1.0 - gpu["residual_mass"][rej])), 4) if rej.any() else None,
+           "rejecting_sequences": int(rej.sum()), "compared_sequences": int(w.batch)}
+    b_acc = b_fin = b_topp = mism = 0
+    for b in range(w.batch):
+        K, t0, d0 = int(lens[b]), int(cu[b]) + b, int(cu[b])
+        n_o = int(ref["num_accepted"][b])
+        if ref.get("p_margin") is not None and ref["p_margin"][b] < EPS_BOUNDARY:
+            b_topp += 1
+            continue
+        if any(ref["d_acc"][d0 + k] < EPS_BOUNDARY for k in range(min(n_o + 1, K))):
+            b_acc += 1
+            continue
+        if mode == "sample" and ref["d_fin"][b] < EPS_BOUNDARY:
+            b_fin += 1
+            mism += int(gpu["num_accepted"][b] != n_o)
+            continue
+        if mode == "argmax" and ref["gap"][b] < 1e-4:
+            b_fin += 1
+            mism += int(gpu["num_accepted"][b] != n_o)
+            continue
+        same = gpu["num_accepted"][b] == n_o and np.array_equal(gpu["tokens"][t0:t0 + K + 1],
+                                                                ref["tokens"][t0:t0 + K + 1])
+        mism += int(not same)
+    out.update({"boundary_accept": b_acc, "boundary_final": b_fin, "boundary_topp": b_topp,
+                "mismatches_outside_boundary": mism})
+    return out
+
+
 def cpu_baseline(w, mode, seconds):
     import oracle
 
     units = w.rows_draft if mode in ("draft", "likelihood") else w.positions()
     unit = "draft tokens/s" if mode == "draft" else "positions/s"
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    oracle.verify_workload(w, mode, threads=threads)  # warm (page in, build)
+    visible = len(os.sched_getaffinity(0))
+    # the host's CPU share of one GPU is 16 cores on the machines this runs on:
+    # the oracle's thread pool is sized to that share, not to every visible core
+    threads = max(1, min(16, visible))
+    ref = oracle.verify_workload(w, mode, threads=threads)  # also warms (page in, build)
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -138,13 +199,15 @@ def cpu_baseline(w, mode, seconds):
         el1 = time.perf_counter() - t1
         if el1 >= seconds / 2:
             break
-    return {
+    return ref, {
         "value": reps * units / el,
         "unit": unit,
         "cores": threads,
+        "cores_visible": visible,
         "kind": "oracle",
         "sample": f"the full batch of the same workload ({w.batch} sequences, {units} {unit[:-2]}), "
-                  f"{reps} repetitions in {el:.1f} s, sequences split over {threads} host threads",
+                  f"{reps} repetitions in {el:.1f} s, sequences split over {threads} host threads "
+                  f"(the CPU share of one GPU; {visible} cores visible to the process)",
         "single_core": {"value": reps1 * units / el1, "cores": 1,
                         "sample": f"the same batch, {reps1} repetitions in {el1:.1f} s on one thread"},
     }
@@ -166,6 +229,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile-pass", action="store_true")
+    ap.add_argument("--batches", type=int, default=5,
+                    help="after the K timed steps, this many further batches of >= --batch-ms each (spread)")
+    ap.add_argument("--batch-ms", type=float, default=200.0)
     ap.add_argument("--copy-calibration-mb", type=float, default=0.0,
                     help="also run a plain device copy of this size (for counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -272,6 +338,22 @@ def main():
     positions = w.rows_draft if mode in ("draft", "likelihood") else w.positions()  # units per step
     value = positions / (ms_step * 1e-3)
 
+    # ---- spread: further batches of at least --batch-ms each (the value above is the K-step region)
+    spread = None
+    if args.batches > 0:
+        n_b = max(K, int(np.ceil(args.batch_ms / max(ms_step, 1e-6))))
+        per = []
+        for _ in range(args.batches):
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(n_b):
+                plans[i % copies]()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / n_b * 1e3)
+        spread = {"batches": args.batches, "steps_per_batch": n_b, "median_us": round(float(np.median(per)), 3),
+                  "min_us": round(min(per), 3), "max_us": round(max(per), 3)}
+
     # ---- profiled pass: HIP events around each streaming-kernel launch
     roof = None
     if not args.no_profile_pass:
@@ -292,6 +374,27 @@ def main():
             "kernel": STREAM_KERNEL[kind], "bytes_per_launch": bytes_step,
             "avg_us": round(avg * 1e6, 3), "median_us": round(float(np.median(dur)) * 1e6, 3),
         }
+        # practical roof: a plain read of the same bytes with the same loads and
+        # tiles, over as many rotated buffers, timed the same way
+        nbytes = bytes_step // 16 * 16
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        reads = [sv.StreamReadPlan(b) for b in bufs]
+        evr = sv.HipEvents(K)
+        pairs_r = [evr.pair(i) for i in range(K)]
+        for i in range(min(K, 20)):
+            reads[i % copies].profiled(pairs_r[i])
+        torch.cuda.synchronize()
+        for i in range(K):
+            reads[i % copies].profiled(pairs_r[i])
+        torch.cuda.synchronize()
+        dr = np.array(evr.elapsed_ms()) * 1e-3
+        evr.close()
+        del bufs, reads
+        practical = nbytes / float(dr.mean()) / 1e9
+        roof.update({"practical_roof": round(practical, 1), "frac_of_practical": round(achieved / practical, 4),
+                     "practical_roof_kernel": "spec_profile_stream_read: plain read, 6 nontemporal 16-byte loads "
+                                              "per thread, 256 threads, one tile per workgroup",
+                     "practical_avg_us": round(float(dr.mean()) * 1e6, 3)})
 
     if args.copy_calibration_mb > 0:
         n = int(args.copy_calibration_mb * 1e6) // 4
@@ -302,8 +405,19 @@ def main():
         torch.cuda.synchronize()
 
     cpu = None
+    draws = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, mode, args.cpu_seconds)
+        ref, cpu = cpu_baseline(w, mode, args.cpu_seconds)
+        p0 = plans[0]
+        p0()
+        torch.cuda.synchronize()
+        if mode == "draft":
+            gpu = {"ids": p0.out.cpu().numpy()}
+        elif mode == "likelihood":
+            gpu = None
+        else:
+            gpu = {k: v.cpu().numpy() for k, v in p0.out.items()}
+        draws = draws_vs_oracle(w, mode, gpu, ref) if gpu is not None else None
 
     line = {
         "metric": {"draft": METRIC_DRAFT, "likelihood": METRIC_LIK}.get(mode, METRIC),
@@ -327,6 +441,8 @@ def main():
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "timing_spread": spread,
+        "draws": draws,
     }
     print(json.dumps(line), flush=True)
 

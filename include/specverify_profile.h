@@ -1,8 +1,8 @@
 /*
  * specverify profiling entry points -- for benchmarks, not for serving.
  *
- * Each call below is the call of the same name in specverify.h with one more
- * leading argument, `events`.  When `events` is non-NULL, the call records
+ * Each *_profiled call below is the call of the same name in specverify.h
+ * with one more leading argument, `events`.  When `events` is non-NULL, the call records
  * events->start on its stream right before the launch of its streaming pass
  * (the kernel that reads every logit row once) and events->stop right after
  * it, so that hipEventElapsedTime(start, stop) is that kernel's duration.
@@ -61,6 +61,21 @@ SV_API sv_status_t spec_token_likelihood_profiled(const sv_profile_events_t* eve
                                                   const int32_t* tokens, float temperature, int32_t top_k,
                                                   float top_p, float* out_terms, float* out_beta, double* out_nll,
                                                   void* workspace, size_t* workspace_bytes, hipStream_t stream);
+
+/*
+ * A plain streaming read, the practical roof the streaming passes are
+ * measured against: every 16-byte block of [data, data + bytes) is loaded
+ * once, with the nontemporal 16-byte loads and the tile shape of the top-k
+ * candidate pass (256 threads per workgroup, 6 loads per thread, one tile per
+ * workgroup), and nothing is computed from it.  data: device memory, 16-byte
+ * aligned; bytes: a positive multiple of 16.  sink: device memory of 4 bytes,
+ * written only when the xor of a thread's words equals 0x9E3779B9 (this keeps
+ * the loads; its content has no meaning).  events as above, recorded around
+ * the read.  SV_ERR_INVALID_ARGUMENT for a null or misaligned pointer or a
+ * bad size.
+ */
+SV_API sv_status_t spec_profile_stream_read(const sv_profile_events_t* events, const void* data, size_t bytes,
+                                            uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

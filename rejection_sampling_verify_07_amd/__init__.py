@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     GreedyPlan,
     LikelihoodPlan,
     SamplePlan,
+    StreamReadPlan,
     HipEvents,
     SpecVerifyError,
     load_library,

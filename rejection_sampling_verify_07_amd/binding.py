@@ -88,6 +88,8 @@ def load_library(path: Optional[str] = None):
         C.POINTER(ShapeT), VP, VP, VP, C.c_float, C.c_int32, C.c_float, VP, VP, VP, VP, C.POINTER(C.c_size_t),
         VP,
     ]
+    lib.spec_profile_stream_read.restype = C.c_int
+    lib.spec_profile_stream_read.argtypes = [C.POINTER(ProfileEventsT), VP, C.c_size_t, VP, VP]
     lib.spec_verify_status_string.restype = C.c_char_p
     lib.spec_verify_status_string.argtypes = [C.c_int]
     # benchmark entry points: the same calls with a leading events argument
@@ -460,6 +462,22 @@ class HipEvents:
             self._hip.hipEventDestroy(self.pairs[i].start)
             self._hip.hipEventDestroy(self.pairs[i].stop)
         self.n = 0
+
+
+class StreamReadPlan:
+    """spec_profile_stream_read over one device buffer (benchmark only): a
+    plain read of its bytes with the streaming passes' loads and tiles."""
+
+    def __init__(self, buf: torch.Tensor, stream=None):
+        self.lib = load_library()
+        self.buf = buf
+        self.nbytes = buf.numel() * buf.element_size() // 16 * 16
+        self.sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+        self.args = (C.c_void_p(buf.data_ptr()), C.c_size_t(self.nbytes), C.c_void_p(self.sink.data_ptr()),
+                     C.c_void_p(_stream_handle(stream)))
+
+    def profiled(self, events):
+        _check(self.lib.spec_profile_stream_read(events, *self.args), "spec_profile_stream_read")
 
 
 class _Plan:

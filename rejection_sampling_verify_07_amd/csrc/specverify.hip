@@ -834,4 +834,18 @@ sv_status_t spec_token_likelihood_profiled(const sv_profile_events_t* events, co
                                    out_beta, out_nll, workspace, workspace_bytes, stream, events);
 }
 
+sv_status_t spec_profile_stream_read(const sv_profile_events_t* events, const void* data, size_t bytes, uint32_t* sink,
+                                     hipStream_t stream)
+{
+    if (data == nullptr || sink == nullptr || !aligned(data, 16) || !aligned(sink, 4) || bytes == 0 || bytes % 16 != 0)
+        return SV_ERR_INVALID_ARGUMENT;
+    const int64_t nblk = (int64_t)(bytes / 16);
+    const int64_t per = (int64_t)sv::kThreads * kCandLoads;
+    const int64_t grid = (nblk + per - 1) / per;
+    if (grid > INT32_MAX) return SV_ERR_UNSUPPORTED;
+    launch_stream(events, sv::stream_read_kernel<kCandLoads>, (uint32_t)grid, stream,
+                  static_cast<const sv::u32x4*>(data), nblk, (uint32_t)0x9E3779B9u, sink);
+    return launch_status();
+}
+
 }  // extern "C"

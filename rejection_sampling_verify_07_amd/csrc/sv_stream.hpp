@@ -81,6 +81,27 @@ __device__ __forceinline__ void walk_tiles(const RowSet& rs, int32_t vocab, int3
     body(t, raw);
 }
 
+// A plain read of nblk 16-byte blocks with the loads and tile shape of the
+// streaming passes (LOADS loads per thread, one tile per workgroup): the
+// practical roof they are measured against.  A thread writes `sink` only
+// when the xor of its words equals `never`, which keeps the loads.
+template <int LOADS>
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ p, int64_t nblk,
+                                                               uint32_t never, uint32_t* __restrict__ sink)
+{
+    const int64_t b0 = (int64_t)blockIdx.x * (kThreads * LOADS) + threadIdx.x;
+    u32x4 raw[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int64_t j = b0 + (int64_t)i * kThreads;
+        raw[i] = j < nblk ? load16<true>(p + j) : u32x4{0u, 0u, 0u, 0u};
+    }
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) x ^= raw[i].x ^ raw[i].y ^ raw[i].z ^ raw[i].w;
+    if (x == never) *sink = x;
+}
+
 // Widen block i of a tile to fp32 and replace elements outside the row by
 // `fill`.  The checks are branch-free selects (measured faster here than a
 // per-block branch around them).
