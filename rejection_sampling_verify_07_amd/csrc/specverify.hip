@@ -45,14 +45,20 @@ constexpr int64_t kBigGridTiles = 16384;     // 4-load tiles beyond which kLoads
 constexpr int kCandLoads = SV_CAND_LOADS;   // top-k candidate pass
 constexpr bool kNT = SV_STREAM_NT != 0;
 constexpr int32_t kCandCap = 512;    // candidate slots per (row, chunk) in the top-k pass
-// Largest top_k that takes the candidate pass.  Close to the pass's own
-// limit (one lane maximum per thread, 256) the tile bound is the smallest lane
-// maxima, the candidates of a row outgrow the select's list, and each row then
-// falls to the one-wave full-row select: on 314 rows of 151936 bf16 logits a
-// call took 80 us at top_k 240 but 550-670 us at 250-256, against 366 us for
-// the workgroup-per-row exact select that larger top_k use.
-constexpr int32_t kTopkFastPlanMax = 240;
+// Largest top_k whose candidate pass takes its tile bound from one key per
+// lane (the lane maximum).  Near the pass's own limit (256 lane maxima) that
+// bound sinks to the smallest lane maxima and the candidates grow; two keys
+// per lane (the lane's two largest block maxima) keep it tighter.  Measured
+// on 314 rows of 151936 bf16 logits (us per call, one key / two keys):
+// top_k 128: 46.6 / 46.4; 160: 48.6 / 49.1; 200: 57.9 / 50.6; 240: 68.8 / 52.5.
+constexpr int32_t kTopkFastPlanMax = 160;
 static_assert(kTopkFastPlanMax <= sv::kTopkFastMax, "the candidate pass needs top_k lane maxima");
+// Largest top_k that takes the candidate pass with two keys per lane (about
+// 400 candidates per tile at top_k 300; tiles past their 512 slots cut to
+// their own top_k); above it the exact workgroup-per-row select.  top_k 300:
+// 70 us per call, 400: 79 us, against 163 and 166 us for the exact select.
+constexpr int32_t kTopkFast2PlanMax = 400;
+static_assert(kTopkFast2PlanMax <= sv::kTopkFastMax2, "the candidate pass needs top_k keys");
 static_assert(sv::kSpecSlots * sv::kWave <= kCandCap, "speculative select reads past a chunk's candidate slots");
 constexpr int kVerifyFullThreads = 1024;  // verify over full rows: 16 waves keep the residual re-read in flight
 constexpr int kSplitThreads = 512;        // workgroups of the split verify over full rows
@@ -89,6 +95,7 @@ struct Plan {
     int32_t groups;   // workgroups per sequence of the split verify over full rows (1: one workgroup)
     int32_t pair_loads;  // 16-byte loads per thread per row in that pass
     int32_t top_k;
+    int32_t keys;  // keys per lane of the top-k candidate pass's tile bound (1 or 2)
     float top_p;
     bool topp;  // top_p < 1: the nucleus pass runs after the statistics
     bool desc;  // the consumers read row descriptors (top-k and/or top-p), not chunk partials
@@ -190,7 +197,8 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
     } else if (!topk) {
         p.mode = PLAN_FULL;
     } else {
-        p.mode = top_k <= kTopkFastPlanMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
+        p.mode = top_k <= kTopkFast2PlanMax ? PLAN_TOPK_FAST : PLAN_TOPK_EXACT;
+        p.keys = top_k <= kTopkFastPlanMax ? 1 : 2;
     }
     // Streaming tiles: measured on MI355X, 8 loads per thread beat 4 once the
     // grid holds many times more tiles than the chip keeps resident, and lose
@@ -300,9 +308,15 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
         // tiles grouped by XCD so that each row's candidates are in the L2 of
         // the XCD that runs the row's select (workgroup `row` of the next kernel)
         const uint32_t xrows = (uint32_t)((p.rows + kXcds - 1) / kXcds * kXcds);
-        launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT>, xrows * (uint32_t)p.nchunk, stream, rs,
-                      sh->vocab, p.nchunk, (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands,
-                      (int32_t)kXcds);
+        if (p.keys == 1) {
+            launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT, 1>, xrows * (uint32_t)p.nchunk, stream, rs,
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands,
+                          (int32_t)kXcds);
+        } else {
+            launch_stream(prof, sv::topk_cand_kernel<DT, kCandLoads, kNT, 2>, xrows * (uint32_t)p.nchunk, stream, rs,
+                          sh->vocab, p.nchunk, (int32_t)grid_stream, top_k, kCandCap, counts, bounds, cands,
+                          (int32_t)kXcds);
+        }
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         // one wave per row; rows whose chunks overflowed take the exact path inside
         hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,

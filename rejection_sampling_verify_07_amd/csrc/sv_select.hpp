@@ -62,6 +62,83 @@ struct alignas(16) WaveSelLds {
     uint32_t hist[256];
 };
 
+// Bitonic sort of 64 * P (id, value) entries by ascending id, in the wave's
+// registers: entry i = lane * P + r is slot r of lane `lane`.  Compare-and-
+// exchange partners closer than P are in the same lane; farther ones are
+// fetched from lane ^ (stride / P) with shuffles.  Ids are distinct except
+// padding (INT32_MAX).
+template <int P>
+__device__ __forceinline__ void wave_bitonic_sort(int32_t (&id)[P], float (&val)[P])
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int size = 2; size <= kWave * P; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= P) {
+                const int ls = stride / P;  // partner lane distance
+                const bool lower = (lane & ls) == 0;
+#pragma unroll
+                for (int r = 0; r < P; ++r) {
+                    const int32_t i = lane * P + r;
+                    const bool up = (i & size) == 0;
+                    const int32_t oid = __shfl_xor(id[r], ls, kWave);
+                    const float ov = __shfl_xor(val[r], ls, kWave);
+                    const bool take = (lower == up) ? (oid < id[r]) : (oid > id[r]);
+                    if (take) {
+                        id[r] = oid;
+                        val[r] = ov;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < P; ++r) {
+                    const int r2 = r ^ stride;
+                    if (r2 > r) {
+                        const bool up = ((lane * P + r) & size) == 0;
+                        if ((id[r] > id[r2]) == up) {
+                            const int32_t ti = id[r];
+                            id[r] = id[r2];
+                            id[r2] = ti;
+                            const float tv = val[r];
+                            val[r] = val[r2];
+                            val[r2] = tv;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The nk kept entries staged in L.kidx / L.kval (nk <= 64 * P), sorted by id
+// in registers and written to klist; returns the lane's fp64 sum of their
+// exp2 weights.
+template <int P>
+__device__ __forceinline__ double sort_write_kept(WaveSelLds& L, int32_t nk, KeptEntry* klist, float c, float mcc)
+{
+    const int lane = lane_id();
+    int32_t id[P];
+    float val[P];
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        const int32_t i = lane * P + r;
+        id[r] = i < nk ? L.kidx[i] : INT32_MAX;
+        val[r] = i < nk ? L.kval[i] : neg_inf();
+    }
+    wave_bitonic_sort<P>(id, val);
+    double ls = 0.0;
+#pragma unroll
+    for (int r = 0; r < P; ++r) {
+        const int32_t i = lane * P + r;
+        if (i < nk) {
+            klist[i] = KeptEntry{id[r], val[r]};
+            ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(val[r], c, -mcc));
+        }
+    }
+    return ls;
+}
+
 // The select proper, from NJ candidate slots per lane in registers (idx
 // INT32_MAX marks an empty slot): tau by a ballot radix select, the kept
 // entries compacted and sorted by id, their max and sum, the descriptor.
@@ -130,37 +207,12 @@ __device__ void select_tail_n(int32_t row, int32_t top_k, float c, RowDesc* __re
             ls = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mcc));
         }
     } else {
+        // more than one per lane: a register bitonic sort of the next power of two
         __builtin_amdgcn_wave_barrier();
-        int32_t npad = kWave;
-        while (npad < nk) npad <<= 1;
-        for (int32_t i = nk + lane; i < npad; i += kWave) {
-            L.kidx[i] = INT32_MAX;
-            L.kval[i] = neg_inf();
-        }
-        __builtin_amdgcn_wave_barrier();
-        for (int32_t size = 2; size <= npad; size <<= 1) {
-            for (int32_t stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int32_t i = lane; i < npad; i += kWave) {
-                    const int32_t p = i ^ stride;
-                    if (p > i) {
-                        const bool up = (i & size) == 0;
-                        const int32_t a = L.kidx[i], bb = L.kidx[p];
-                        if ((a > bb) == up) {
-                            L.kidx[i] = bb;
-                            L.kidx[p] = a;
-                            const float tv = L.kval[i];
-                            L.kval[i] = L.kval[p];
-                            L.kval[p] = tv;
-                        }
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
-            }
-        }
-        for (int32_t i = lane; i < nk; i += kWave) {
-            klist[i] = KeptEntry{L.kidx[i], L.kval[i]};
-            ls += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(L.kval[i], c, -mcc));
-        }
+        if (nk <= 2 * kWave) ls = sort_write_kept<2>(L, nk, klist, c, mcc);
+        else if (nk <= 4 * kWave) ls = sort_write_kept<4>(L, nk, klist, c, mcc);
+        else if (nk <= 8 * kWave) ls = sort_write_kept<8>(L, nk, klist, c, mcc);
+        else ls = sort_write_kept<16>(L, nk, klist, c, mcc);
     }
     ls = wave_sum_dpp(ls);
     if (lane == 0) {

@@ -27,6 +27,7 @@ namespace sv {
 
 constexpr int kSelCap = 4096;  // candidates a row can hold in LDS
 constexpr int kTopkFastMax = kThreads;   // largest top_k pass 1 supports (one lane maximum each)
+constexpr int kTopkFastMax2 = 2 * kThreads;  // with two keys per lane
 constexpr int kMaxChunks = 512;          // chunks per row the select pass can index
 constexpr int kKeepCapList = 1024;       // kept-list capacity per row (ids kept by top-k)
 
@@ -188,7 +189,11 @@ constexpr int kChunkLds = kWaves * kWaveLds;
 // smallest fp32 of some bf16 order class, so `word >= t` and `element >= t`
 // agree.  The low element needs a shift.  The lane maxima that set the bound
 // are taken over all elements.  fp16 elements are widened (exactly) instead.
-template <int DT, int LOADS, bool NT>
+//
+// KEYS = 2 (larger top_k): the bound comes from 512 keys, each lane's largest
+// and second-largest 16-byte block maximum (distinct elements of the tile, so
+// top_k of them reaching a value means top_k elements do).
+template <int DT, int LOADS, bool NT, int KEYS>
 __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     RowSet rs, int32_t vocab, int32_t nchunk, int32_t ntiles, int32_t top_k, int32_t cap,
     int32_t* __restrict__ counts, float* __restrict__ bounds, KeptEntry* __restrict__ cands, int32_t xcd)
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     constexpr bool H16 = DT == DT_F16;
     __shared__ __align__(16) float s_val[kChunkLds];
     __shared__ int32_t s_ix[kChunkLds];
-    __shared__ uint32_t s_lk[kThreads];
+    __shared__ uint32_t s_lk[kThreads * KEYS];
     __shared__ int32_t s_wc[kWaves];
     __shared__ uint32_t s_hist[256];
     __shared__ int32_t s_misc[8];
@@ -263,18 +268,34 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) asm volatile("" : "+v"(rw[i]));
 
-            // the top_k-th largest of the workgroup's 256 lane maxima (on the top
-            // 16 key bits): every wave runs the same ballot radix select over all
-            // of them, four per lane
+            // the top_k-th largest of the workgroup's 256 * KEYS keys (lane maxima,
+            // and with KEYS = 2 the lanes' second-largest block maxima too; on the
+            // top 16 key bits): every wave runs the same ballot radix select over
+            // all of them, 4 * KEYS per lane
+            constexpr int KPL = 4 * KEYS;  // keys per lane
             s_lk[threadIdx.x] = order_key(tm) >> 16;
-            __syncthreads();
-            uint32_t k4[4];
+            if constexpr (KEYS == 2) {
+                // the second largest of the lane's block maxima (never NaN: -inf or finite)
+                float t1 = bm[0], t2 = neg_inf();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) k4[q] = s_lk[lane_id() + q * kWave];
+                for (int i = 1; i < LOADS; ++i) {
+                    t2 = __builtin_amdgcn_fmed3f(t1, t2, bm[i]);
+                    t1 = fmaxf(t1, bm[i]);
+                }
+                s_lk[kThreads + threadIdx.x] = order_key(t2) >> 16;
+            }
+            __syncthreads();
+            uint32_t kk[KPL];
+#pragma unroll
+            for (int q = 0; q < KPL; ++q) kk[q] = s_lk[lane_id() + q * kWave];
             // bits above the highest one where the largest and smallest key differ
-            // are common to all 256 keys: start the select below them
-            uint32_t kmax = max(max(k4[0], k4[1]), max(k4[2], k4[3]));
-            uint32_t kmin = min(min(k4[0], k4[1]), min(k4[2], k4[3]));
+            // are common to all keys: start the select below them
+            uint32_t kmax = kk[0], kmin = kk[0];
+#pragma unroll
+            for (int q = 1; q < KPL; ++q) {
+                kmax = max(kmax, kk[q]);
+                kmin = min(kmin, kk[q]);
+            }
             wave_umax_umin_dpp(kmax, kmin);
             const uint32_t diff = kmax ^ kmin;
             const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
@@ -283,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 const uint32_t cand = h | (1u << bit);
                 int cnt = 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) cnt += (int)__popcll(__ballot(k4[q] >= cand));
+                for (int q = 0; q < KPL; ++q) cnt += (int)__popcll(__ballot(kk[q] >= cand));
                 if (cnt >= top_k) h = cand;
             }
             // smallest float whose key has these top bits; the -inf bucket maps to -inf

@@ -35,7 +35,8 @@ EDGE = {
     "vocab7_f32": _spec(vocab=7, dtype="f32"),
     "misaligned_rows": _spec(),
     "top_k_1": _spec(top_k=1, vocab=4000),
-    "top_k_300_exact_path": _spec(top_k=300, vocab=20000, batch=4),
+    "top_k_300_two_keys": _spec(top_k=300, vocab=20000, batch=4),
+    "top_k_600_exact_path": _spec(top_k=600, vocab=20000, batch=4),
     "zipf_top50_ragged": _spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
     "peaks_f32_wide": _spec(kind="peaks", target_sigma=3.0, draft_sigma=1.5, vocab=70001, dtype="f32", batch=3),
     "draft_close_to_target": _spec(draft_sigma=0.05, vocab=5000, batch=16, k=4),

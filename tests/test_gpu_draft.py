@@ -45,7 +45,8 @@ EDGE = {
     "misaligned_rows_bf16": _spec(),
     "top_k_1": _spec(top_k=1, vocab=4000),
     "top_k_v": _spec(top_k=1001),
-    "top_k_300_exact_path": _spec(top_k=300, vocab=20000),
+    "top_k_300_two_keys": _spec(top_k=300, vocab=20000),
+    "top_k_600_exact_path": _spec(top_k=600, vocab=20000),
     "zipf_top50_ragged": _spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
     "peaks_f32_wide": _spec(kind="peaks", target_sigma=3.0, draft_sigma=1.5, vocab=70001, dtype="f32", batch=3),
     "k128": _spec(k=128, batch=2, vocab=300, dtype="f32"),

@@ -90,9 +90,11 @@ EDGE = {
     "vocab1001_misaligned_rows": (_spec(), None, {}),
     "ragged_with_zero_lengths": (_spec(batch=6, k=8, vocab=5000), None, dict(draft_lens=[0, 3, 0, 1, 8, 2])),
     "top_k_1": (_spec(top_k=1, vocab=4000, batch=6), None, {}),
-    "top_k_240_fast_limit": (_spec(top_k=240, vocab=20000), None, {}),
-    "top_k_256_exact_path": (_spec(top_k=256, vocab=20000), None, {}),
-    "top_k_300_exact_path": (_spec(top_k=300, vocab=20000), None, {}),
+    "top_k_160_one_key_limit": (_spec(top_k=160, vocab=20000), None, {}),
+    "top_k_240_two_keys": (_spec(top_k=240, vocab=20000), None, {}),
+    "top_k_256_two_keys": (_spec(top_k=256, vocab=20000), None, {}),
+    "top_k_300_two_keys": (_spec(top_k=300, vocab=20000), None, {}),
+    "top_k_600_exact_path": (_spec(top_k=600, vocab=20000), None, {}),
     "zipf_top50_ragged": (_spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
                           None, {}),
     "ties_top50": (_spec(vocab=9000, batch=8, k=4, top_k=50), lambda x: np.round(x * 2) / 2, {}),

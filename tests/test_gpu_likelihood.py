@@ -71,7 +71,8 @@ EDGE = {
     "ragged_with_zero_lengths": (_spec(batch=6, k=8, vocab=5000), None, dict(draft_lens=[0, 3, 0, 1, 8, 2])),
     "long_sequences_k300": (_spec(batch=3, k=300, vocab=2000, dtype="f32"), None, {}),
     "top_k_1": (_spec(top_k=1, vocab=4000, batch=6), None, {}),
-    "top_k_300_exact_path": (_spec(top_k=300, vocab=20000), None, {}),
+    "top_k_300_two_keys": (_spec(top_k=300, vocab=20000), None, {}),
+    "top_k_600_exact_path": (_spec(top_k=600, vocab=20000), None, {}),
     "top_k_v": (_spec(top_k=1001), None, {}),
     "zipf_top50_ragged": (_spec(kind="zipf", top_k=50, vocab=60000, batch=12, k=8, ragged=True, temperature=0.7),
                           None, {}),

@@ -90,9 +90,13 @@ EDGE = {
     "top_k_1": (_spec(top_k=1, vocab=4000, batch=6), {}),
     "top_k_v_minus_1": (_spec(top_k=1000, batch=3), {}),
     "top_k_v": (_spec(top_k=1001, batch=3), {}),
-    "top_k_240_fast_limit": (_spec(top_k=240, vocab=20000, batch=4), {}),
-    "top_k_256_exact_path": (_spec(top_k=256, vocab=20000, batch=4), {}),
-    "top_k_300_exact_path": (_spec(top_k=300, vocab=20000, batch=4), {}),
+    "top_k_160_one_key_limit": (_spec(top_k=160, vocab=20000, batch=4), {}),
+    "top_k_161_two_keys": (_spec(top_k=161, vocab=20000, batch=4), {}),
+    "top_k_240_two_keys": (_spec(top_k=240, vocab=20000, batch=4), {}),
+    "top_k_256_two_keys": (_spec(top_k=256, vocab=20000, batch=4), {}),
+    "top_k_300_two_keys": (_spec(top_k=300, vocab=20000, batch=4), {}),
+    "top_k_400_two_keys_limit": (_spec(top_k=400, vocab=20000, batch=4), {}),
+    "top_k_600_exact_path": (_spec(top_k=600, vocab=20000, batch=4), {}),
     "temperature_0.05": (_spec(temperature=0.05, vocab=8000, batch=8), {}),
     "temperature_5": (_spec(temperature=5.0, vocab=8000, batch=8), {}),
     "k128": (_spec(k=128, batch=2, vocab=300, dtype="f32"), {}),

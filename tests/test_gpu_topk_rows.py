@@ -127,6 +127,8 @@ CASES = {
     "bf16_top240": (_spec(top_k=240, vocab=20000), None),
     "f32_top240": (_spec(top_k=240, vocab=20000, dtype="f32"), None),
     "bf16_top256": (_spec(top_k=256, vocab=20000), None),
+    "bf16_top400": (_spec(top_k=400, vocab=20000), None),  # the two-key pass's limit: tiles cut to their top_k
+    "bf16_top600_ties": (_spec(top_k=600, vocab=20000), _ties),  # exact path: staged bucket, ties at tau
     # top_k above the candidate pass: the exact select over full rows
     "bf16_top300_ties": (_spec(top_k=300, vocab=20000), _ties),  # staged bucket, ties at tau
     "bf16_top300_constant_rows": (_spec(top_k=300, vocab=20000), _constant),  # bucket too large for LDS

@@ -90,7 +90,8 @@ EDGE = {
     "top_p_0.999": (_spec(top_p=0.999), None),
     "top_p_0.3_sharp": (_spec(top_p=0.3, temperature=0.3), None),
     "top_k_50_then_top_p": (_spec(top_k=50, vocab=20000, kind="zipf"), None),
-    "top_k_300_exact_then_top_p": (_spec(top_k=300, vocab=20000, top_p=0.8), None),
+    "top_k_300_two_keys_then_top_p": (_spec(top_k=300, vocab=20000, top_p=0.8), None),
+    "top_k_600_exact_then_top_p": (_spec(top_k=600, vocab=20000, top_p=0.8), None),
     "top_k_1_then_top_p": (_spec(top_k=1, top_p=0.5), None),
     "ties_full_rows": (_spec(vocab=6000), lambda x: np.round(x * 2) / 2),
     "ties_top50": (_spec(vocab=6000, top_k=50), lambda x: np.round(x * 2) / 2),
