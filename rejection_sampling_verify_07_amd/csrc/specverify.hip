@@ -23,6 +23,8 @@
 static_assert(SV_MAX_DRAFT == sv::kMaxDraft, "draft limit mismatch");
 static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
 static_assert(sv::kKeepCap == sv::kKeepCapList, "kept-list capacity mismatch");
+// the per-row top-p kernel groups a row's 16-byte blocks by at most 64 (adjacent lanes)
+static_assert((int64_t)sv::kNucGroups * 64 >= SV_MAX_VOCAB / 4 + 2, "top-p block groups too small for the largest row");
 
 namespace {
 
@@ -134,13 +136,20 @@ int32_t chunks_for(int32_t vocab, int vec, int loads)
 // (the benchmark entry points), the launch itself records the caller's
 // events right before and after the kernel on the call's stream.
 template <class K, class... Args>
-void launch_stream(const sv_profile_events_t* prof, K kernel, uint32_t ntiles, hipStream_t s, Args... args)
+void launch_stream_nt(const sv_profile_events_t* prof, K kernel, uint32_t ntiles, uint32_t nt, hipStream_t s,
+                      Args... args)
 {
     if (prof != nullptr) {
-        hipExtLaunchKernelGGL(kernel, dim3(ntiles), dim3(sv::kThreads), 0, s, prof->start, prof->stop, 0, args...);
+        hipExtLaunchKernelGGL(kernel, dim3(ntiles), dim3(nt), 0, s, prof->start, prof->stop, 0, args...);
     } else {
-        hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(sv::kThreads), 0, s, args...);
+        hipLaunchKernelGGL(kernel, dim3(ntiles), dim3(nt), 0, s, args...);
     }
+}
+
+template <class K, class... Args>
+void launch_stream(const sv_profile_events_t* prof, K kernel, uint32_t ntiles, hipStream_t s, Args... args)
+{
+    launch_stream_nt(prof, kernel, ntiles, sv::kThreads, s, args...);
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -217,8 +226,10 @@ Plan make_plan(const sv_shape_t* sh, CallKind kind, int32_t top_k, float top_p =
     size_t off = 0;
     const size_t slots = (size_t)p.rows * (size_t)p.nchunk;
     if (p.mode == PLAN_FULL) {
-        p.off_partials = off;
-        off = align_up(off + slots * sizeof(sv::PartialFull));
+        if (!p.topp) {  // with top-p, one kernel per row writes row descriptors instead of chunk partials
+            p.off_partials = off;
+            off = align_up(off + slots * sizeof(sv::PartialFull));
+        }
         p.groups = (kind == CALL_SAMPLE && !p.topp) ? split_groups(sh->batch, sh->vocab) : 1;
         if (p.groups > 1) {
             const size_t nseg = (size_t)(sh->vocab + sv::kSeg - 1) / sv::kSeg;
@@ -337,15 +348,23 @@ template <int DT>
 sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs, float c, void* ws,
                       hipStream_t stream, sv::VerifyArgs& va, const sv_profile_events_t* prof)
 {
+    if (p.mode == PLAN_FULL && p.topp) {
+        // full rows with top-p: statistics and cut in one kernel per row (it
+        // reads every row, so it is the timed streaming pass)
+        const sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p,
+                             ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
+        launch_stream_nt(prof, sv::nucleus_row_kernel<DT, sv::kNucRowThreads>, (uint32_t)p.rows,
+                         (uint32_t)sv::kNucRowThreads, stream, na);
+        va.descs = na.descs;
+        va.kept = na.kept;
+        return launch_status();
+    }
     if (run_stats_topk<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
     if (!p.topp) return SV_OK;
-    sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p, va.partials, p.nchunk,
-                   ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
-    if (p.mode == PLAN_FULL) {
-        hipLaunchKernelGGL((sv::nucleus_kernel<DT, false>), dim3(p.rows), dim3(sv::kThreads), 0, stream, na);
-    } else {
-        hipLaunchKernelGGL((sv::nucleus_kernel<DT, true>), dim3(p.rows), dim3(sv::kThreads), 0, stream, na);
-    }
+    // a top-k row's kept list (or a kept set that outgrew it) narrowed by top-p
+    const sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p,
+                         ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
+    hipLaunchKernelGGL((sv::nucleus_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, na);
     va.descs = na.descs;
     va.kept = na.kept;
     return launch_status();

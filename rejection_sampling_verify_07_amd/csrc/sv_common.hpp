@@ -314,6 +314,34 @@ __device__ __forceinline__ double wave_incl_scan_dpp(double v)
     return s;
 }
 
+// The same inclusive prefix sum for exact u64 sums (fixed-point masses).
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t b)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, ROW_MASK, BANK_MASK, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, ROW_MASK, BANK_MASK, true);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64_dpp(uint64_t v)
+{
+    uint64_t s = v + dpp_u64<kDppRowShr1, 0xf, 0xf>(v);
+    s = s + dpp_u64<kDppRowShr2, 0xf, 0xf>(v);
+    s = s + dpp_u64<kDppRowShr3, 0xf, 0xf>(v);
+    s = s + dpp_u64<kDppRowShr4, 0xf, 0xe>(s);
+    s = s + dpp_u64<kDppRowShr8, 0xf, 0xc>(s);
+    s = s + dpp_u64<kDppBcast15, 0xa, 0xf>(s);
+    s = s + dpp_u64<kDppBcast31, 0xc, 0xf>(s);
+    return s;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // The previous lane's value (0 in lane 0).
 __device__ __forceinline__ double wave_prev_dpp(double v) { return dpp_f64<kDppWaveShr1, 0xf, 0xf>(v); }
 

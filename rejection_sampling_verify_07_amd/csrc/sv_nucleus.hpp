@@ -11,15 +11,23 @@
 //  - a row with a kept list (<= 1024 ids) is done by wave 0 in registers: a
 //    bitwise radix search on the select key, one wave-wide fp64 sum of the
 //    fp32 weights per bit (fixed order), then an order-keeping compaction;
-//  - a full row (no top-k, or a kept set that outgrew its list) takes two
-//    reads of the row: a histogram of its weights over log-weight buckets,
+//  - a full row with no top-k (nucleus_row_kernel) takes its statistics and
+//    its cut in one kernel: one read of the row for its maximum and sum,
+//    then a 1/16 subsample whose tail mass predicts a logit l_low safely
+//    below the cut, then a second walk (mostly served by the caches) that
+//    stages every logit >= l_low in LDS, where a mass-weighted radix select
+//    finds the cut exactly.  If the staged mass falls short of top_p or the
+//    stage overflows, the row takes the exact path below; the result does not
+//    depend on the prediction either way;
+//  - the exact path (nucleus_full; also a top-k row whose kept set outgrew
+//    its list): a histogram of the row's weights over log-weight buckets,
 //    which finds the bucket where the mass from the top reaches top_p; then
 //    the entries of that bucket staged in LDS (and the ids above it counted)
-//    and resolved by a mass-weighted radix select.  The kept count and mass
-//    follow from those; only a kept set that fits the list takes a third
-//    read, which writes the list in id order and sums the kept weights.
-//    Weights are summed in 2^-43 fixed point with integer LDS atomics, so the
-//    sums are exact and the result deterministic.
+//    and resolved by a mass-weighted radix select.
+//  The kept count and mass follow from those; only a kept set that fits the
+//  list takes one more read, which writes the list in id order and sums the
+//  kept weights.  Weights are summed in 2^-43 fixed point with integer
+//  atomics, so the sums are exact and the result deterministic.
 #pragma once
 
 #include "sv_common.hpp"
@@ -34,10 +42,8 @@ struct NucArgs {
     int32_t rows;
     float c;
     float top_p;
-    const PartialFull* partials;  // full rows: the streaming pass's chunk partials
-    int32_t nchunk;
-    RowDesc* descs;                // in (top-k) / out
-    KeptEntry* kept;               // in (top-k) / out, kKeepCap per row
+    RowDesc* descs;    // in (top-k) / out
+    KeptEntry* kept;   // in (top-k) / out, kKeepCap per row
 };
 
 constexpr double kFixScale = 8796093022208.0;  // 2^43: weights <= 1 summed over <= 2^20 ids stay below 2^63
@@ -63,18 +69,6 @@ __device__ __forceinline__ float nuc_value(uint32_t k)
 {
     if constexpr (DT == DT_F32) return key_to_float(k);
     else return SelKey<DT>::value(k >> 16);
-}
-
-// Inclusive scan of a u64 across the wave (shuffles; once per digit).
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, o, kWave);
-        const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), o, kWave);
-        if (lane_id() >= o) v += ((uint64_t)hi << 32) | lo;
-    }
-    return v;
 }
 
 // Sum of a u64 across the wave (butterfly; every lane gets it, exactly).
@@ -152,12 +146,12 @@ __device__ void nucleus_list(const NucArgs& a, int32_t row, const RowDesc& d)
 // sum{w : key >= h} >= need over the (key, fixed-point weight) pairs that
 // visit(fn) presents, 8-bit digits from the top down to `low`.  All threads
 // call it; integer sums make it exact and independent of visiting order.
-template <class Visit>
+template <int NT = kThreads, class Visit>
 __device__ uint32_t mass_radix(Visit&& visit, uint64_t need, int low, uint64_t* s_hist, uint64_t* s_u)
 {
     uint32_t prefix = 0, pmask = 0;
     for (int shift = 24; shift >= low; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += kThreads) s_hist[i] = 0;
+        for (int i = threadIdx.x; i < 256; i += NT) s_hist[i] = 0;
         __syncthreads();
         visit([&](uint32_t k, uint64_t w) {
             if ((k & pmask) == prefix) atomicAdd((unsigned long long*)&s_hist[(k >> shift) & 255u], (unsigned long long)w);
@@ -172,7 +166,7 @@ __device__ uint32_t mass_radix(Visit&& visit, uint64_t need, int low, uint64_t* 
                 h4[q] = s_hist[255 - 4 * l - q];
                 lsum += h4[q];
             }
-            const uint64_t incl = wave_incl_scan_u64(lsum);
+            const uint64_t incl = wave_incl_scan_u64_dpp(lsum);
             const uint64_t excl = incl - lsum;
             int found = -1;
             uint64_t above = 0;
@@ -210,6 +204,61 @@ __device__ uint32_t mass_radix(Visit&& visit, uint64_t need, int low, uint64_t* 
     return prefix;
 }
 
+// mass_radix by one wave alone (its lanes run in lockstep and its LDS
+// operations complete in order, so no workgroup barrier is needed): the
+// other waves of the workgroup may be elsewhere.
+template <class Visit>
+__device__ uint32_t mass_radix_wave(Visit&& visit, uint64_t need, int low, uint64_t* s_hist)
+{
+    const int l = lane_id();
+    uint32_t prefix = 0, pmask = 0;
+    for (int shift = 24; shift >= low; shift -= 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_hist[4 * l + q] = 0;
+        __builtin_amdgcn_wave_barrier();
+        visit([&](uint32_t k, uint64_t w) {
+            if ((k & pmask) == prefix) atomicAdd((unsigned long long*)&s_hist[(k >> shift) & 255u], (unsigned long long)w);
+        });
+        __builtin_amdgcn_wave_barrier();
+        // lane L holds digits 255-4L .. 252-4L (descending)
+        uint64_t h4[4], lsum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h4[q] = s_hist[255 - 4 * l - q];
+            lsum += h4[q];
+        }
+        const uint64_t incl = wave_incl_scan_u64_dpp(lsum);
+        const uint64_t excl = incl - lsum;
+        int found = -1;
+        uint64_t above = 0;
+        if (excl < need && incl >= need) {
+            uint64_t cum = excl;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (found < 0 && cum + h4[q] >= need) {
+                    found = 255 - 4 * l - q;
+                    above = cum;
+                }
+                cum += h4[q];
+            }
+        }
+        const uint64_t bal = __ballot(found >= 0);
+        if (bal != 0) {
+            const int src = __builtin_ctzll(bal);
+            found = __shfl(found, src, kWave);
+            above = (uint64_t)__shfl((long long)above, src, kWave);
+        } else {
+            found = 0;  // not reached (need <= the visited mass)
+            above = 0;
+        }
+        __builtin_amdgcn_wave_barrier();  // every lane has read the histogram
+        prefix |= (uint32_t)found << shift;
+        pmask |= 0xffu << shift;
+        need -= above;
+    }
+    return prefix;
+}
+
 constexpr int kNucBuckets = 256;   // log-weight buckets of 1/8 bit below the row maximum
 constexpr int kNucCap = 2048;      // entries of the crossing bucket staged in LDS
 
@@ -235,11 +284,12 @@ __device__ __forceinline__ float nuc_lowest_at_most(uint32_t t, float c, float m
     return key_to_float(lo);
 }
 
+template <int NT>
 struct NucLds {
     uint64_t hist[256];
     uint64_t u[4];
-    int32_t w[kWaves];
-    double d[kWaves];
+    int32_t w[NT / kWave];
+    double d[NT / kWave];
     uint32_t ck[kNucCap];
     uint64_t cw[kNucCap];
     int32_t n;
@@ -247,15 +297,15 @@ struct NucLds {
 
 // The crossing bucket's radix select straight from the row, for a bucket
 // too large to stage in LDS (kept out of line: it is rare and register-hungry).
-template <int DT>
+template <int DT, int NT, int U>
 __device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* rowp, int32_t vocab, float tau,
                                                                     float mcc, float c, uint32_t bstar,
                                                                     uint64_t need, uint64_t* s_hist, uint64_t* s_u)
 {
     constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
-    return mass_radix(
+    return mass_radix<NT>(
         [&](auto&& fn) {
-            for_row_blocks<DT>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+            for_row_blocks<DT, NT, U>(rowp, vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
                 for (int e = 0; e < Dt<DT>::kVec; ++e) {
                     if (ok[e] && f[e] >= tau && nuc_bucket(f[e], c, mcc) == bstar)
@@ -264,6 +314,46 @@ __device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* r
             });
         },
         need, LOW, s_hist, s_u);
+}
+
+// The kept set {l >= tau_p} of a full row, one walk: its count, its sum of
+// weights (fp32 per block, fp64 across), and, when it fits, the kept list in
+// id order; then the row's descriptor.
+template <int DT, int NT, int U>
+__device__ void nucleus_write_list(const NucArgs& a, int32_t row, const RowDesc& d, float tau_p, int32_t* s_w,
+                                   double* s_d)
+{
+    const char* rowp = row_ptr(a.rs, row);
+    const float c = a.c, mcc = d.mcc;
+    KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;
+    int32_t base = 0;
+    double ls = 0.0;
+    for_row_blocks<DT, NT, U>(rowp, a.vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) cnt += (ok[e] && f[e] >= tau_p);
+        int tot;
+        int pos = base + block_excl_scan_int<NT>(cnt, s_w, &tot);
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < Dt<DT>::kVec; ++e) {
+            if (ok[e] && f[e] >= tau_p) {
+                if (pos < kKeepCap) kl[pos] = KeptEntry{r0 + e, f[e]};
+                ++pos;
+                s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+            }
+        }
+        ls += (double)s;
+        base += tot;
+    });
+    const double sum = block_sum_double<NT>(ls, s_d);
+    if (threadIdx.x == 0) {
+        RowDesc o = d;
+        o.tau = tau_p;
+        o.s = sum;
+        o.kept = base <= kKeepCap ? base : -1;
+        a.descs[row] = o;
+    }
 }
 
 // Full rows (kept set = {l >= d.tau}): the whole workgroup.  First a
@@ -275,8 +365,8 @@ __device__ __attribute__((noinline)) uint32_t nucleus_bucket_radix(const char* r
 // one dropped.  Its own entries (a small share of the row) are staged in LDS
 // by a second read and resolved by a mass-weighted radix select there; if
 // they do not fit, the radix select reads the row instead.
-template <int DT>
-__device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, NucLds& S)
+template <int DT, int NT, int U>
+__device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, NucLds<NT>& S)
 {
     constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
     const char* rowp = row_ptr(a.rs, row);
@@ -284,10 +374,10 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     auto fixw = [&](float l) { return fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(l, c, -mcc))); };
     auto bucket = [&](float l) { return nuc_bucket(l, c, mcc); };
     // 1. log-weight histogram
-    for (int i = threadIdx.x; i < kNucBuckets; i += kThreads) S.hist[i] = 0;
+    for (int i = threadIdx.x; i < kNucBuckets; i += NT) S.hist[i] = 0;
     if (threadIdx.x == 0) S.n = 0;
     __syncthreads();
-    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+    for_row_blocks<DT, NT, U>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
         for (int e = 0; e < Dt<DT>::kVec; ++e)
             if (ok[e] && f[e] >= tau)
@@ -303,7 +393,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
             h4[q] = S.hist[4 * l + q];
             lsum += h4[q];
         }
-        const uint64_t incl = wave_incl_scan_u64(lsum);
+        const uint64_t incl = wave_incl_scan_u64_dpp(lsum);
         const uint64_t total = (uint64_t)__shfl((long long)incl, kWave - 1, kWave);
         uint64_t need = (uint64_t)((double)a.top_p * (double)total);
         if (need == 0) need = 1;  // at least the maximum is kept
@@ -343,7 +433,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     const float l_in = fmaxf(nuc_lowest_at_most(bstar, c, mcc), tau);
     const float l_above = bstar > 0 ? fmaxf(nuc_lowest_at_most(bstar - 1, c, mcc), tau) : __int_as_float(0x7f800000);
     int32_t n_hi = 0;
-    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
+    for_row_blocks<DT, NT, U>(rowp, a.vocab, [&](int32_t, int32_t, const float* f, const bool* ok) {
 #pragma unroll
         for (int e = 0; e < Dt<DT>::kVec; ++e) {
             if (ok[e] && f[e] >= l_in) {
@@ -364,20 +454,18 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     __syncthreads();
     n_hi = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) n_hi += S.w[w];
+    for (int w = 0; w < NT / kWave; ++w) n_hi += S.w[w];
     const int32_t nb = S.n;
     uint32_t prefix;
     if (nb <= kNucCap) {
-        prefix = mass_radix(
+        prefix = mass_radix<NT>(
             [&](auto&& fn) {
-                for (int32_t i = threadIdx.x; i < nb; i += kThreads) fn(S.ck[i], S.cw[i]);
+                for (int32_t i = threadIdx.x; i < nb; i += NT) fn(S.ck[i], S.cw[i]);
             },
             need_b, LOW, S.hist, S.u);
     } else {
-        prefix = nucleus_bucket_radix<DT>(rowp, a.vocab, tau, mcc, c, bstar, need_b, S.hist, S.u);
+        prefix = nucleus_bucket_radix<DT, NT, U>(rowp, a.vocab, tau, mcc, c, bstar, need_b, S.hist, S.u);
     }
-    int32_t* s_w = S.w;
-    double* s_d = S.d;
     // the threshold value: the logit whose key has this prefix
     if constexpr (LOW > 0) prefix |= 0xffffu;
     const float tau_p = fmaxf(nuc_value<DT>(prefix), tau);
@@ -389,7 +477,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     if (nb <= kNucCap) {
         int32_t nk = 0;
         uint64_t mk = 0;
-        for (int32_t i = threadIdx.x; i < nb; i += kThreads) {
+        for (int32_t i = threadIdx.x; i < nb; i += NT) {
             if (nuc_value<DT>(S.ck[i]) >= tau_p) {
                 ++nk;
                 mk += S.cw[i];
@@ -406,7 +494,7 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
         int32_t kept_n = n_hi;
         uint64_t kept_m = mass_hi;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NT / kWave; ++w) {
             kept_n += S.w[w];
             kept_m += S.hist[w];
         }
@@ -423,73 +511,18 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
         __syncthreads();  // S.w is the scan scratch below
     }
 
-    // kept sum, count and (if it fits) the ordered kept list
-    KeptEntry* kl = a.kept + (int64_t)row * kKeepCap;
-    int32_t base = 0;
-    double ls = 0.0;
-    for_row_blocks<DT>(rowp, a.vocab, [&](int32_t, int32_t r0, const float* f, const bool* ok) {
-        int cnt = 0;
-#pragma unroll
-        for (int e = 0; e < Dt<DT>::kVec; ++e) cnt += (ok[e] && f[e] >= tau_p);
-        int tot;
-        int pos = base + block_excl_scan_int(cnt, s_w, &tot);
-        float s = 0.0f;
-#pragma unroll
-        for (int e = 0; e < Dt<DT>::kVec; ++e) {
-            if (ok[e] && f[e] >= tau_p) {
-                if (pos < kKeepCap) kl[pos] = KeptEntry{r0 + e, f[e]};
-                ++pos;
-                s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
-            }
-        }
-        ls += (double)s;
-        base += tot;
-    });
-    const double sum = block_sum_double(ls, s_d);
-    if (threadIdx.x == 0) {
-        RowDesc o = d;
-        o.tau = tau_p;
-        o.s = sum;
-        o.kept = base <= kKeepCap ? base : -1;
-        a.descs[row] = o;
-    }
+    nucleus_write_list<DT, NT, U>(a, row, d, tau_p, S.w, S.d);
 }
 
-template <int DT, bool FROM_DESC>
+// Top-k rows narrowed by top-p: the select's descriptor and kept list in,
+// the nucleus's out.
+template <int DT>
 __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
 {
-    __shared__ NucLds s_nuc;
+    __shared__ NucLds<kThreads> s_nuc;
     __shared__ RowDesc s_desc;
     const int32_t row = blockIdx.x;
-    if constexpr (FROM_DESC) {
-        if (threadIdx.x == 0) s_desc = a.descs[row];
-    } else {
-        // full rows: the row's statistics from the streaming pass's partials
-        if (wave_id() == 0) {
-            const PartialFull* pp = a.partials + (int64_t)row * a.nchunk;
-            float m = neg_inf();
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
-            m = wave_max_dpp(m);
-            const float mcc = m * a.c;
-            double s = 0.0;
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
-                const PartialFull q = pp[ch];
-                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
-            }
-            s = wave_sum_dpp(s);
-            if (lane_id() == 0) {
-                RowDesc d;
-                d.tau = neg_inf();
-                d.m = m;
-                d.mcc = mcc;
-                d.kept = -1;
-                d.s = s;
-                d.flags = 0;
-                d.pad = 0;
-                s_desc = d;
-            }
-        }
-    }
+    if (threadIdx.x == 0) s_desc = a.descs[row];
     __syncthreads();
     const RowDesc d = s_desc;
     if (!(d.s > 0.0)) {  // no finite kept logit: the consumers report the row
@@ -499,8 +532,621 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
     if (d.kept >= 0) {
         if (wave_id() == 0) nucleus_list<DT>(a, row, d);
     } else {
-        nucleus_full<DT>(a, row, d, s_nuc);
+        nucleus_full<DT, kThreads, kRowUnroll>(a, row, d, s_nuc);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Full rows with no top-k: statistics and cut in one kernel, one row per
+// workgroup of kNucRowThreads threads (two per CU).
+//
+//  1. One read of the row (from HBM): the maximum m and S = sum of
+//     exp2(fma(l, c, -fl32(m c))), the maximum of every group of G 16-byte
+//     blocks into LDS (16-bit order keys), and a subsample (every
+//     stride-th block, at most kNucSubMax blocks) into LDS.
+//  2. From the subsample: its weights over the log-weight buckets estimate
+//     the tail mass below each bucket; l_low is the lowest logit of the first
+//     bucket whose estimated tail below it is at most kNucTailKeep (1 - top_p) S.
+//  3. The groups whose maximum reaches l_low (a minority: the cut lies in the
+//     upper tail) are read again, mostly from the caches, and every logit
+//     >= l_low is staged in LDS, each wave into its own slice.
+//  4. On the staged logits alone: the log-weight histogram of their
+//     fixed-point weights gives the crossing bucket (if their mass reaches
+//     top_p at all: then the cut lies among them, since every logit above
+//     l_low is staged), that bucket's entries are compacted and resolved by
+//     the mass-weighted radix select.
+//  A row whose staged mass falls short of top_p, or whose stage overflows,
+//  takes the exact path (nucleus_full) instead.  The result does not depend
+//  on the prediction.
+// ---------------------------------------------------------------------------
+constexpr int kNucRowThreads = 512;
+constexpr int kNucRowUnroll = 4;        // 16-byte loads per thread per round of the first read (two in flight)
+constexpr int kNucHitUnroll = 8;        // ... in the re-read of the groups that reach l_low
+constexpr int kNucListUnroll = 4;       // ... in the exact path and the kept-list walk
+constexpr int kNucGroups = 16384;       // group-maximum slots (16-bit keys)
+constexpr int kNucStageBytes = 32768;   // staged keys: 16 bits (16-bit types) or 32 bits (fp32)
+constexpr int kNucSubMax = 1024;        // subsample blocks kept in LDS
+constexpr int kNucSubStrideMin = 16;    // the subsample takes at most every 16th block
+// The predicted cut leaves this share of the estimated tail mass (1 - top_p)
+// below it unstaged, and the prediction is used only if the subsample puts at
+// most kNucStageFill of a wave's stage slice above it (on average).
+constexpr double kNucTailKeep = 0.75;
+constexpr double kNucStageFill = 0.7;
+
+template <int DT>
+struct NucStage {
+    using T = typename std::conditional<Dt<DT>::kSize == 2, uint16_t, uint32_t>::type;
+    static constexpr int kCap = kNucStageBytes / (int)sizeof(T);
+    // a logit is staged as its raw bits: element e of a 16-byte block
+    __device__ __forceinline__ static T raw(const u32x4& w, int e)
+    {
+        if constexpr (Dt<DT>::kSize == 2) return (T)(w[e >> 1] >> (16 * (e & 1)));
+        else return w[e];
+    }
+    __device__ __forceinline__ static float value(T s)
+    {
+        if constexpr (DT == DT_BF16) return __uint_as_float((uint32_t)s << 16);
+        else if constexpr (DT == DT_F16) return half_bits_to_float(s);
+        else return __uint_as_float(s);
+    }
+    // its radix key (nuc_key of its value)
+    __device__ __forceinline__ static uint32_t key(T s)
+    {
+        if constexpr (DT == DT_F16) return (uint32_t)((s & 0x8000u) ? (~s & 0xffffu) : (s | 0x8000u)) << 16;
+        else return order_key(value(s));
+    }
+};
+
+// 16-bit order key of a logit, monotone (non-decreasing) in it.
+template <int DT>
+__device__ __forceinline__ uint32_t key16(float v)
+{
+    if constexpr (DT == DT_F16) return SelKey<DT_F16>::of(v);
+    else return order_key(v) >> 16;
+}
+
+template <int DT, int NT>
+struct NucRowLds {
+    union {
+        uint16_t gmax[kNucGroups];  // walks 1-3: group maxima, then each wave's hit list
+        struct {
+            uint32_t ck[kNucCap];   // step 4: the crossing bucket's entries
+            uint64_t cw[kNucCap];
+        } x;
+        NucLds<NT> full;            // the exact path
+    } a;
+    union {
+        u32x4 sub[kNucSubMax];                                  // walks 1-2: the subsample
+        typename NucStage<DT>::T stage[NucStage<DT>::kCap];    // walk 3 on: the staged keys
+    } b;
+    uint64_t hist[256];
+    uint64_t hstage[256];  // the staged logits' fixed-point weights per log-weight bucket
+    uint64_t q[4];
+    uint64_t red[NT / kWave];
+    float f[NT / kWave];
+    double d[NT / kWave];
+    int32_t w[NT / kWave];
+    int32_t nw[NT / kWave];   // staged entries per wave (> slice: overflow)
+    int32_t go;
+    int32_t jl;     // the last bucket staged whole
+    float l_low;
+};
+
+// The 16-byte blocks that cover a row (its start may be misaligned).
+template <int DT>
+struct RowBlocks {
+    const u32x4* base;
+    int32_t mis;   // elements of the first block before the row
+    int32_t nblk;
+    __device__ __forceinline__ RowBlocks(const char* rowp, int32_t vocab)
+    {
+        const uintptr_t addr = (uintptr_t)rowp;
+        mis = (int32_t)((addr & 15u) / Dt<DT>::kSize);
+        base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
+        nblk = (mis + vocab + Dt<DT>::kVec - 1) / Dt<DT>::kVec;
+    }
+};
+
+// The out-of-row elements of a raw block whose first element is row index
+// r0 become -inf: no maximum rises and no weight appears for them.
+template <int DT>
+__device__ __forceinline__ void fill_edge(u32x4& w, int32_t r0, int32_t vocab)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t x = w[q];
+        if constexpr (Dt<DT>::kSize == 2) {
+            if ((uint32_t)(r0 + 2 * q) >= (uint32_t)vocab) x = (x & 0xffff0000u) | Dt<DT>::kNegInf;
+            if ((uint32_t)(r0 + 2 * q + 1) >= (uint32_t)vocab) x = (x & 0x0000ffffu) | (Dt<DT>::kNegInf << 16);
+        } else {
+            if ((uint32_t)(r0 + q) >= (uint32_t)vocab) x = 0xff800000u;
+        }
+        w[q] = x;
+    }
+}
+
+// Walk 1.  Per thread: the running maximum lm of its blocks and the sum, in
+// fp64, of exp2(fma(l, c, -fl32(lm c))) over them (fp32 terms per round of
+// U blocks, rescaled in fp64 when the maximum grows); per group of
+// G = 2^lg_g blocks (G <= 64: adjacent lanes) its maximum's 16-bit key into
+// gmax; every 2^lg_s-th block into sub.  Block j of round r is
+// (r U + u) NT + tid.  Two rounds of loads are in flight: round r + 1 is
+// loading while round r is reduced, and the registers of round r then take
+// round r + 2.  A round that reaches past either end of the row first fills
+// its out-of-row elements with -inf.
+template <int DT, int NT, int U>
+struct Walk1 {
+    static constexpr int VEC = Dt<DT>::kVec;
+    const RowBlocks<DT>& rb;
+    int32_t vocab;
+    float c;
+    int lg_g, lg_s;
+    uint16_t* gmax;
+    u32x4* sub;
+    float lm = neg_inf(), lmcc = neg_inf();
+    double ls = 0.0;
+
+    // unconditional loads (a block past the row reloads the last one, and
+    // the edge fill then masks it): loads issued under a branch would make
+    // the compiler wait for every load in flight before the next reduction
+    __device__ __forceinline__ void load(u32x4* raw, int32_t r) const
+    {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = (r * U + u) * NT + (int32_t)threadIdx.x;
+            raw[u] = load16<false>(rb.base + min(j, rb.nblk - 1));
+        }
+    }
+
+    __device__ __forceinline__ void reduce(u32x4* raw, int32_t r)
+    {
+        const int32_t G = 1 << lg_g;
+        const int32_t jlo = r * U * NT, jhi = (r + 1) * U * NT;  // the round's blocks [jlo, jhi)
+        if (jlo * VEC < rb.mis || jhi * VEC > rb.mis + vocab) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                fill_edge<DT>(raw[u], ((r * U + u) * NT + (int32_t)threadIdx.x) * VEC - rb.mis, vocab);
+        }
+        float rm = neg_inf();
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = (r * U + u) * NT + (int32_t)threadIdx.x;
+            float f[VEC];
+            unpack<DT>(raw[u], f);
+            float bm = f[0];
+#pragma unroll
+            for (int e = 1; e < VEC; ++e) bm = fmaxf(bm, f[e]);
+            rm = fmaxf(rm, bm);
+            uint32_t k = key16<DT>(bm);
+            for (int o = 1; o < G; o <<= 1) k = max(k, (uint32_t)__shfl_xor((int)k, o, kWave));
+            if (j < rb.nblk) {
+                if ((j & (G - 1)) == 0) gmax[j >> lg_g] = (uint16_t)k;
+                if ((j & ((1 << lg_s) - 1)) == 0) sub[j >> lg_s] = raw[u];
+            }
+        }
+        if (rm > lm) {
+            const float mcc = rm * c;
+            ls = lm == neg_inf() ? 0.0 : ls * exp2((double)lmcc - (double)mcc);
+            lm = rm;
+            lmcc = mcc;
+        }
+        if (lm != neg_inf()) {
+            float t = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[VEC];
+                unpack<DT>(raw[u], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -lmcc));
+            }
+            ls += (double)t;
+        }
+    }
+
+    // every load is issued unconditionally (rounds past the row reload its
+    // last block, unused), so the wait before each reduction counts exactly
+    // the other buffer's loads as still in flight
+    __device__ __forceinline__ void run()
+    {
+        const int32_t rounds = (rb.nblk + NT * U - 1) / (NT * U);
+        u32x4 a[U], b[U];
+        load(a, 0);
+        __builtin_amdgcn_sched_barrier(0);  // a's loads first, as in the loop below
+        load(b, 1);
+        for (int32_t r = 0; r < rounds; r += 2) {
+            reduce(a, r);
+            load(a, r + 2);
+            if (r + 1 < rounds) reduce(b, r + 1);
+            load(b, r + 3);
+        }
+    }
+};
+
+template <int DT, int NT>
+__global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
+{
+    constexpr int VEC = Dt<DT>::kVec;
+    constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
+    constexpr int NW = NT / kWave;
+    constexpr int U = kNucRowUnroll;
+    constexpr int UH = kNucHitUnroll;
+    constexpr int UL = kNucListUnroll;
+    using St = NucStage<DT>;
+    constexpr int SLICE = St::kCap / NW;  // stage entries per wave
+    __shared__ NucRowLds<DT, NT> S;
+    const int32_t row = blockIdx.x;
+    const char* rowp = row_ptr(a.rs, row);
+    const RowBlocks<DT> rb(rowp, a.vocab);
+    const float c = a.c;
+    const int lane = lane_id(), wv = wave_id();
+    for (int i = threadIdx.x; i < kNucBuckets; i += NT) S.hstage[i] = 0;  // (published by walk 1's barriers)
+    // group size G = 2^lg_g: the smallest with nblk / G <= kNucGroups (G <= 64
+    // for any row the ABI takes); subsample stride 2^lg_s: the smallest
+    // >= kNucSubStrideMin with nblk / stride <= kNucSubMax
+    int lg_g = 0, lg_s = 0;
+    while (((int64_t)1 << lg_g) * kNucGroups < rb.nblk) ++lg_g;
+    while ((1 << lg_s) < kNucSubStrideMin || ((int64_t)1 << lg_s) * kNucSubMax < rb.nblk) ++lg_s;
+    const int32_t G = 1 << lg_g;
+    const int32_t ngroups = (rb.nblk + G - 1) >> lg_g;
+    const int32_t nsub = (rb.nblk + (1 << lg_s) - 1) >> lg_s;
+
+    // 1. statistics, group maxima, subsample
+    float lm;
+    double ls;
+    {
+        Walk1<DT, NT, U> w1{rb, a.vocab, c, lg_g, lg_s, S.a.gmax, S.b.sub};
+        w1.run();
+        lm = w1.lm;
+        ls = w1.ls;
+    }
+    const float m = block_max_float<NT>(lm, S.f);  // (its barriers also publish gmax and sub)
+    const float mcc = m * c;
+    const double part = lm == neg_inf() ? 0.0 : ls * exp2((double)(lm * c) - (double)mcc);
+    const double total = block_sum_double<NT>(part, S.d);
+    RowDesc d;
+    d.tau = neg_inf();
+    d.m = m;
+    d.mcc = mcc;
+    d.kept = -1;
+    d.s = total;
+    d.flags = 0;
+    d.pad = 0;
+    if (!(total > 0.0)) {  // no finite logit: the consumers report the row
+        if (threadIdx.x == 0) a.descs[row] = d;
+        return;
+    }
+    auto wfix = [&](float v) { return fix43(__builtin_amdgcn_exp2f(__builtin_fmaf(v, c, -mcc))); };
+
+    // 2. the predicted cut (rows that fit the stage twice over are staged whole)
+    if ((int64_t)a.vocab * 2 <= St::kCap) {
+        if (threadIdx.x == 0) {
+            S.go = 1;
+            S.jl = kNucBuckets - 1;
+            S.l_low = neg_inf();
+        }
+    } else {
+        for (int i = threadIdx.x; i < kNucBuckets; i += NT) S.hist[i] = 0;
+        __syncthreads();
+        // per subsample logit one atomic: its weight in 2^-31 units (below
+        // 2^44 summed over the at most 8192 of them) plus 2^48 to count it
+        constexpr uint64_t kOne = 1ull << 48;
+        for (int32_t k = threadIdx.x; k < nsub; k += NT) {
+            const int32_t j = k << lg_s;
+            float f[VEC];
+            unpack<DT>(S.b.sub[k], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if ((uint32_t)(j * VEC - rb.mis + e) < (uint32_t)a.vocab) {
+                    const uint32_t b = nuc_bucket(f[e], c, mcc);
+                    const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc)) * 2147483648.0f;
+                    atomicAdd((unsigned long long*)&S.hist[b], (unsigned long long)(kOne + (uint64_t)(uint32_t)w));
+                }
+            }
+        }
+        __syncthreads();
+        if (wv == 0) {
+            // ascending buckets = descending weights; lane L holds buckets 4L .. 4L+3
+            uint64_t h4[4], lsum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h4[q] = S.hist[4 * lane + q] & (kOne - 1);
+                lsum += h4[q];
+            }
+            const uint64_t incl = wave_incl_scan_u64_dpp(lsum);
+            const uint64_t all = readlane_u64(incl, kWave - 1);
+            const double scale = (double)rb.nblk / (double)nsub;
+            const double keep = kNucTailKeep * (1.0 - (double)a.top_p) * total * 2147483648.0;
+            // the first bucket j with scale * (mass of the buckets after j) <= keep
+            const double thr = (double)all - keep / scale;
+            int found = -1;
+            uint64_t cum = incl - lsum;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                cum += h4[q];
+                if (found < 0 && (double)cum >= thr) found = 4 * lane + q;
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            const int jl = bal != 0 ? __shfl(found, __builtin_ctzll(bal), kWave) : kNucBuckets - 1;
+            uint32_t n4 = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) n4 += 4 * lane + q <= jl ? (uint32_t)(S.hist[4 * lane + q] >> 48) : 0u;
+            const int32_t nsum = wave_sum_int((int)n4);
+            if (lane == 0) {
+                S.go = (double)nsum * scale <= kNucStageFill * (double)St::kCap;
+                S.jl = jl;
+                // a logit at or below every logit of the buckets <= jl: the
+                // bucket boundary solved in fp64, then lowered until its own
+                // bucket lies past jl (bucket never increases with the logit)
+                float lo = neg_inf();
+                if (jl < kNucBuckets - 1) {
+                    lo = (float)(((double)mcc - (double)(jl + 1) * 0.125) / (double)c);
+                    while (nuc_bucket(lo, c, mcc) <= (uint32_t)jl) lo = key_to_float(order_key(lo) - 1u);
+                }
+                S.l_low = lo;
+            }
+        }
+    }
+    __syncthreads();
+    const bool go = S.go != 0;
+    const int32_t jl = S.jl;
+    const float l_low = S.l_low;
+
+    // 3. the groups whose maximum reaches l_low: each wave compacts its own
+    // groups (g = s NT + 64 wave + lane) into its own slots of gmax, in
+    // order, then stages their logits >= l_low into its stage slice.
+    int32_t nst_w = 0;  // this wave's staged entries (wave-uniform)
+    // staged: the finite logits >= l_low (a -inf logit weighs nothing and is
+    // never kept, so the staged mass per bucket is still the row's)
+    const float l_stage = fmaxf(l_low, -__FLT_MAX__);
+    if (go) {
+        const uint32_t klow = key16<DT>(l_low);
+        int32_t nh = 0;  // this wave's hits so far (wave-uniform)
+        constexpr int LA = 8;  // steps whose keys are read before any slot is written
+        for (int32_t s0 = 0; s0 < ngroups; s0 += NT * LA) {
+            uint32_t kk[LA];
+#pragma unroll
+            for (int b = 0; b < LA; ++b) {
+                const int32_t g = s0 + b * NT + 64 * wv + lane;
+                kk[b] = g < ngroups ? (uint32_t)S.a.gmax[g] : 0u;
+            }
+            // the k-th hit goes to the wave's k-th own slot, one already read
+#pragma unroll
+            for (int b = 0; b < LA; ++b) {
+                const int32_t g = s0 + b * NT + 64 * wv + lane;
+                const bool hit = g < ngroups && kk[b] >= klow;
+                const uint64_t mask = __ballot(hit);
+                if (hit) {
+                    const int32_t k = nh + (int32_t)lanes_below(mask);
+                    S.a.gmax[(k / kWave) * NT + 64 * wv + (k % kWave)] = (uint16_t)g;
+                }
+                nh += (int32_t)__popcll(mask);
+            }
+        }
+        typename St::T* slice = S.b.stage + wv * SLICE;
+        for (int32_t k0 = 0; k0 < nh * G; k0 += kWave * UH) {
+            u32x4 raw[UH];
+            int32_t jb[UH];
+#pragma unroll
+            for (int u = 0; u < UH; ++u) {
+                const int32_t k = k0 + u * kWave + lane;  // the k-th block of the wave's hit groups
+                const int32_t h = k >> lg_g;
+                int32_t j = -1;
+                if (k < nh * G)
+                    j = ((int32_t)S.a.gmax[(h / kWave) * NT + 64 * wv + (h % kWave)] << lg_g) + (k & (G - 1));
+                jb[u] = j < rb.nblk ? j : -1;
+                // unconditional load (block 0 stands in for no block; jb < 0 masks it)
+                raw[u] = load16<false>(rb.base + (jb[u] >= 0 ? jb[u] : 0));
+            }
+#pragma unroll
+            for (int u = 0; u < UH; ++u) {
+                // a block at a row end (or no block) gets -inf in its
+                // out-of-row slots, which never reach l_stage
+                const int32_t r0 = jb[u] >= 0 ? jb[u] * VEC - rb.mis : a.vocab;
+                if (r0 < 0 || r0 + VEC > a.vocab) fill_edge<DT>(raw[u], r0, a.vocab);
+                float f[VEC];
+                unpack<DT>(raw[u], f);
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    const bool pred = f[e] >= l_stage;
+                    const uint64_t mask = __ballot(pred);
+                    if (mask != 0) {
+                        if (pred) {
+                            const int32_t pos = nst_w + (int32_t)lanes_below(mask);
+                            if (pos < SLICE) slice[pos] = St::raw(raw[u], e);
+                            atomicAdd((unsigned long long*)&S.hstage[nuc_bucket(f[e], c, mcc)],
+                                      (unsigned long long)wfix(f[e]));
+                        }
+                        nst_w += (int32_t)__popcll(mask);
+                    }
+                }
+            }
+        }
+        if (lane == 0) S.nw[wv] = nst_w;
+    }
+    __syncthreads();
+    bool fast = go;
+    if (fast) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) fast = fast && S.nw[w] <= SLICE;
+    }
+    uint64_t need = (uint64_t)((double)a.top_p * total * kFixScale);
+    if (need == 0) need = 1;  // at least the maximum is kept
+
+    // 4. on the staged logits: log-weight histogram, crossing bucket
+    // (each thread visits its own wave's slice)
+    // fn(valid, v, k) for the wave's staged entries, called by every lane of
+    // the wave the same number of times (valid: the lane holds an entry)
+    auto for_staged = [&](auto&& fn) {
+        const typename St::T* slice = S.b.stage + wv * SLICE;
+        for (int32_t i0 = 0; i0 < nst_w; i0 += kWave) {
+            const bool valid = i0 + lane < nst_w;
+            const typename St::T r = slice[valid ? i0 + lane : 0];
+            fn(valid, St::value(r), St::key(r));
+        }
+    };
+    int32_t bstar = 0;
+    uint64_t need_b = 0, mass_hi = 0;
+    if (fast) {
+        if (wv == 0) {
+            uint64_t h4[4], lsum = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h4[q] = S.hstage[4 * lane + q];
+                lsum += h4[q];
+            }
+            const uint64_t incl = wave_incl_scan_u64_dpp(lsum);
+            const uint64_t excl = incl - lsum;
+            int found = -1;
+            uint64_t above = 0;
+            if (excl < need && incl >= need) {
+                uint64_t cum = excl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (found < 0 && cum + h4[q] >= need) {
+                        found = 4 * lane + q;
+                        above = cum;
+                    }
+                    cum += h4[q];
+                }
+            }
+            const uint64_t bal = __ballot(found >= 0);
+            const int fb = __shfl(found, bal != 0 ? __builtin_ctzll(bal) : 0, kWave);
+            // the staged mass reaches top_p within the buckets staged whole
+            if (lane == 0) S.go = bal != 0 && fb <= jl;
+            if (bal != 0) {
+                const int src = __builtin_ctzll(bal);
+                found = __shfl(found, src, kWave);
+                above = (uint64_t)__shfl((long long)above, src, kWave);
+                if (lane == 0) {
+                    S.q[0] = (uint64_t)found;
+                    S.q[1] = need - above;
+                    S.q[2] = above;
+                }
+            }
+        }
+        __syncthreads();
+        fast = S.go != 0;
+        bstar = (int32_t)S.q[0];
+        need_b = S.q[1];
+        mass_hi = S.q[2];
+    }
+    if (!fast) {
+        __syncthreads();  // S.a / S.b are reused by the exact path
+        nucleus_full<DT, NT, UL>(a, row, d, S.a.full);
+        return;
+    }
+    // the crossing bucket's entries (each wave into its own region of
+    // kNucCap / NW), and the count above it
+    constexpr int CREG = kNucCap / NW;
+    int32_t n_hi = 0, nc = 0;  // nc: this wave's crossing entries (wave-uniform)
+    for_staged([&](bool valid, float v, uint32_t k) {
+        const uint32_t b = nuc_bucket(v, c, mcc);
+        n_hi += valid && b < (uint32_t)bstar;
+        const bool in = valid && b == (uint32_t)bstar;
+        const uint64_t mask = __ballot(in);
+        if (in) {
+            const int32_t slot = nc + (int32_t)lanes_below(mask);
+            if (slot < CREG) {
+                S.a.x.ck[wv * CREG + slot] = k;
+                S.a.x.cw[wv * CREG + slot] = wfix(v);
+            }
+        }
+        nc += (int32_t)__popcll(mask);
+    });
+    n_hi = wave_sum_int(n_hi);
+    if (lane == 0) {
+        S.w[wv] = n_hi;
+        S.nw[wv] = nc;
+    }
+    __syncthreads();
+    n_hi = 0;
+    bool creg_ok = true;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        n_hi += S.w[w];
+        creg_ok = creg_ok && S.nw[w] <= CREG;
+    }
+    // visits the crossing entries of every wave's region: entry t of their
+    // concatenation for t = first, first + step, ...
+    auto for_crossing = [&](int first, int step, auto&& fn) {
+        int32_t pre[NW + 1];
+        pre[0] = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) pre[w + 1] = pre[w] + S.nw[w];
+        for (int32_t t = first; t < pre[NW]; t += step) {
+            int w = 0;
+#pragma unroll
+            for (int q = 1; q < NW; ++q) w += t >= pre[q];
+            const int32_t i = w * CREG + (t - pre[w]);
+            fn(S.a.x.ck[i], S.a.x.cw[i]);
+        }
+    };
+    uint32_t prefix;
+    if (creg_ok) {
+        if (wv == 0) {
+            prefix = mass_radix_wave([&](auto&& fn) { for_crossing(lane, kWave, fn); }, need_b, LOW, S.hist);
+            if (lane == 0) S.q[0] = prefix;
+        }
+        __syncthreads();
+        prefix = (uint32_t)S.q[0];
+    } else {  // a crossing bucket too large for LDS: the radix over the staged entries in it
+        prefix = mass_radix<NT>(
+            [&](auto&& fn) {
+                for_staged([&](bool valid, float v, uint32_t k) {
+                    if (valid && nuc_bucket(v, c, mcc) == (uint32_t)bstar) fn(k, wfix(v));
+                });
+            },
+            need_b, LOW, S.hist, S.q);
+    }
+    if constexpr (LOW > 0) prefix |= 0xffffu;
+    const float tau_p = nuc_value<DT>(prefix);
+    // kept count and mass: the ids above the crossing bucket, plus its entries >= tau_p
+    int32_t nk = 0;
+    uint64_t mk = 0;
+    if (creg_ok) {
+        if (wv == 0) {
+            for_crossing(lane, kWave, [&](uint32_t k, uint64_t w) {
+                if (nuc_value<DT>(k) >= tau_p) {
+                    ++nk;
+                    mk += w;
+                }
+            });
+        }
+    } else {
+        for_staged([&](bool valid, float v, uint32_t) {
+            if (valid && v >= tau_p && nuc_bucket(v, c, mcc) == (uint32_t)bstar) {
+                ++nk;
+                mk += wfix(v);
+            }
+        });
+    }
+    nk = wave_sum_int(nk);
+    mk = wave_sum_u64(mk);
+    __syncthreads();  // every thread has read S.w
+    if (lane == 0) {
+        S.w[wv] = nk;
+        S.red[wv] = mk;
+    }
+    __syncthreads();
+    int32_t kept_n = n_hi;
+    uint64_t kept_m = mass_hi;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        kept_n += S.w[w];
+        kept_m += S.red[w];
+    }
+    if (kept_n > kKeepCap) {
+        if (threadIdx.x == 0) {
+            RowDesc o = d;
+            o.tau = tau_p;
+            o.s = (double)kept_m / kFixScale;
+            o.kept = -1;
+            a.descs[row] = o;
+        }
+        return;
+    }
+    __syncthreads();  // S.w is the scan scratch below
+    nucleus_write_list<DT, NT, UL>(a, row, d, tau_p, S.w, S.d);
 }
 
 }  // namespace sv

@@ -35,15 +35,16 @@ constexpr int kKeepCapList = 1024;       // kept-list capacity per row (ids kept
 // Pass 2 helpers
 // ---------------------------------------------------------------------------
 
-// Visit every element of a full row in ascending 16-byte blocks.  Each
-// thread keeps kRowUnroll loads in flight; fn(step, r0, f, ok) is then called
-// once per block, in the same step for all threads, where step s covers
-// blocks s*256 .. s*256+255 (so a workgroup scan per step yields ascending
-// id order); r0 is the row index of the block's first element and ok[e]
-// tells which of its elements lie inside the row.
+// Visit every element of a full row in ascending 16-byte blocks, with a
+// workgroup of NT threads.  Each thread keeps U loads in flight;
+// fn(step, r0, f, ok) is then called once per block, in the same step for
+// all threads, where step s covers blocks s*NT .. s*NT+NT-1 (so a workgroup
+// scan per step yields ascending id order); r0 is the row index of the
+// block's first element and ok[e] tells which of its elements lie inside the
+// row.
 constexpr int kRowUnroll = 8;
 
-template <int DT, class F>
+template <int DT, int NT = kThreads, int U = kRowUnroll, class F>
 __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, F&& fn)
 {
     constexpr int VEC = Dt<DT>::kVec;
@@ -52,18 +53,18 @@ __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, 
     const int32_t mis = (int32_t)((addr & 15u) / ES);
     const u32x4* base = reinterpret_cast<const u32x4*>(addr - (addr & 15u));
     const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
-    const int32_t iters = (nblk + kThreads * kRowUnroll - 1) / (kThreads * kRowUnroll);
+    const int32_t iters = (nblk + NT * U - 1) / (NT * U);
     for (int32_t it = 0; it < iters; ++it) {
-        u32x4 raw[kRowUnroll];
+        u32x4 raw[U];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int32_t j = (it * kRowUnroll + u) * kThreads + (int32_t)threadIdx.x;
+        for (int u = 0; u < U; ++u) {
+            const int32_t j = (it * U + u) * NT + (int32_t)threadIdx.x;
             raw[u] = (j < nblk) ? load16<false>(base + j) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int32_t step = it * kRowUnroll + u;
-            const int32_t j = step * kThreads + (int32_t)threadIdx.x;
+        for (int u = 0; u < U; ++u) {
+            const int32_t step = it * U + u;
+            const int32_t j = step * NT + (int32_t)threadIdx.x;
             float f[VEC];
             bool ok[VEC];
             unpack<DT>(raw[u], f);
@@ -77,6 +78,8 @@ __device__ __forceinline__ void for_row_blocks(const char* rowp, int32_t vocab, 
 }
 
 // Block-wide exclusive prefix sum of an int (fixed order); total via *total.
+// s_w holds NT / 64 ints.
+template <int NT = kThreads>
 __device__ __forceinline__ int block_excl_scan_int(int v, int* s_w, int* total)
 {
     const int incl = wave_incl_scan_int(v);
@@ -84,7 +87,7 @@ __device__ __forceinline__ int block_excl_scan_int(int v, int* s_w, int* total)
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NT / kWave; ++w) {
         if (w < wave_id()) off += s_w[w];
         tot += s_w[w];
     }
@@ -458,7 +461,9 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
     }, xcd);
 }
 
-// Block-wide max / sum (fixed order); every thread gets the result.
+// Block-wide max / sum over NT threads (fixed order); every thread gets the
+// result.  s_f / s_d hold NT / 64 values.
+template <int NT = kThreads>
 __device__ __forceinline__ float block_max_float(float v, float* s_f)
 {
     v = wave_max(v);
@@ -467,10 +472,11 @@ __device__ __forceinline__ float block_max_float(float v, float* s_f)
     __syncthreads();
     float m = s_f[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = fmaxf(m, s_f[w]);
+    for (int w = 1; w < NT / kWave; ++w) m = fmaxf(m, s_f[w]);
     return m;
 }
 
+template <int NT = kThreads>
 __device__ __forceinline__ double block_sum_double(double v, double* s_d)
 {
     v = wave_sum(v);
@@ -479,7 +485,7 @@ __device__ __forceinline__ double block_sum_double(double v, double* s_d)
     __syncthreads();
     double t = s_d[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) t += s_d[w];
+    for (int w = 1; w < NT / kWave; ++w) t += s_d[w];
     return t;
 }
 
