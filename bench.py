@@ -35,7 +35,17 @@ METRIC_LIK = "positions scored/sec (speculative likelihood: both parts, beta, NL
 STREAM_KERNEL = {"sample_topk": "topk_cand_kernel", "sample": "row_stats_kernel", "greedy": "row_stats_kernel",
                  "draft_topk": "topk_cand_kernel", "draft": "row_stats_kernel",
                  "argmax_topk": "topk_cand_kernel", "argmax": "row_stats_kernel",
-                 "likelihood_topk": "topk_cand_kernel", "likelihood": "row_stats_kernel"}
+                 "likelihood_topk": "topk_cand_kernel", "likelihood": "row_stats_kernel",
+                 # full rows with top-p: statistics and cut in one kernel per row
+                 "sample_topp": "nucleus_row_kernel", "draft_topp": "nucleus_row_kernel",
+                 "argmax_topp": "nucleus_row_kernel", "likelihood_topp": "nucleus_row_kernel"}
+
+
+def stream_kind(mode: str, top_k: bool, top_p: bool) -> str:
+    """Key of STREAM_KERNEL: the kernel that reads every logit row once."""
+    if mode == "greedy":
+        return "greedy"
+    return mode + ("_topk" if top_k else "_topp" if top_p else "")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -73,7 +83,8 @@ def record_traffic(workload: str, mode: str, fetch_csv: str, write_csv: str, cop
     import csv
 
     topk = re.search(r"_top\d", workload) is not None
-    kind_kernel = STREAM_KERNEL["greedy" if mode == "greedy" else (mode + ("_topk" if topk else ""))]
+    topp = re.search(r"_topp", workload) is not None
+    kind_kernel = STREAM_KERNEL[stream_kind(mode, topk, topp)]
 
     def per_dispatch(path, counter):
         vals = {}
@@ -244,6 +255,8 @@ def main():
         name = W.WORKLOADS[args.config]["name"]
         if args.dtype is not None:
             name = name.replace(W.WORKLOADS[args.config]["dtype"], args.dtype)
+        if args.top_p < 1.0:
+            name = f"{name}_topp{args.top_p:g}"  # as the timed run names it
         rec = record_traffic(name, args.mode, args.record_traffic[0], args.record_traffic[1],
                              args.copy_calibration_mb or 256.0)
         print(json.dumps(rec))
@@ -282,7 +295,7 @@ def main():
     if mode not in ("draft", "argmax", "likelihood") and mode not in w.modes:
         print(f"config {args.config} is not measured in {mode} mode", file=sys.stderr)
         sys.exit(2)
-    kind = "greedy" if mode == "greedy" else (mode + ("_topk" if w.top_k > 0 else ""))
+    kind = stream_kind(mode, w.top_k > 0, w.top_p < 1.0)
     bytes_step = w.algorithmic_bytes(mode)
     copies = max(1, int(np.ceil(args.rotate_mb * 1e6 / bytes_step)))
 

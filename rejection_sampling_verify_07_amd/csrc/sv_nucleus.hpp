@@ -211,8 +211,20 @@ template <class Visit>
 __device__ uint32_t mass_radix_wave(Visit&& visit, uint64_t need, int low, uint64_t* s_hist)
 {
     const int l = lane_id();
+    // leading digits on which every visited key agrees need no pass
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    visit([&](uint32_t k, uint64_t) {
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+    });
+    wave_umax_umin_dpp(kmax, kmin);
     uint32_t prefix = 0, pmask = 0;
-    for (int shift = 24; shift >= low; shift -= 8) {
+    int shift = 24;
+    for (; shift >= low && (((kmin ^ kmax) >> shift) & 0xffu) == 0; shift -= 8) {
+        prefix |= kmin & (0xffu << shift);
+        pmask |= 0xffu << shift;
+    }
+    for (; shift >= low; shift -= 8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) s_hist[4 * l + q] = 0;
         __builtin_amdgcn_wave_barrier();
@@ -707,7 +719,11 @@ struct Walk1 {
             for (int u = 0; u < U; ++u)
                 fill_edge<DT>(raw[u], ((r * U + u) * NT + (int32_t)threadIdx.x) * VEC - rb.mis, vocab);
         }
-        float rm = neg_inf();
+        // one pass over the round: block maxima and the exp2 terms against
+        // the reference the lane had before it (a term exceeds 1 when the
+        // round raises the maximum; the sum is rescaled below)
+        const float ref = lmcc;
+        float rm = neg_inf(), t = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t j = (r * U + u) * NT + (int32_t)threadIdx.x;
@@ -723,22 +739,29 @@ struct Walk1 {
                 if ((j & (G - 1)) == 0) gmax[j >> lg_g] = (uint16_t)k;
                 if ((j & ((1 << lg_s) - 1)) == 0) sub[j >> lg_s] = raw[u];
             }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -ref));
         }
         if (rm > lm) {
             const float mcc = rm * c;
-            ls = lm == neg_inf() ? 0.0 : ls * exp2((double)lmcc - (double)mcc);
+            if (!(mcc - ref <= 64.0f)) {
+                // no finite reference yet (ref = -inf), or a rise of more than
+                // 64 bits: the terms above are unusable, sum again against mcc
+                t = 0.0f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float f[VEC];
+                    unpack<DT>(raw[u], f);
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+                }
+                ls = (lm == neg_inf() ? 0.0 : ls * exp2((double)lmcc - (double)mcc)) + (double)t;
+            } else {
+                ls = (ls + (double)t) * exp2((double)ref - (double)mcc);
+            }
             lm = rm;
             lmcc = mcc;
-        }
-        if (lm != neg_inf()) {
-            float t = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float f[VEC];
-                unpack<DT>(raw[u], f);
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -lmcc));
-            }
+        } else if (lm != neg_inf()) {
             ls += (double)t;
         }
     }
@@ -901,7 +924,7 @@ __global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
     if (go) {
         const uint32_t klow = key16<DT>(l_low);
         int32_t nh = 0;  // this wave's hits so far (wave-uniform)
-        constexpr int LA = 8;  // steps whose keys are read before any slot is written
+        constexpr int LA = 16;  // steps whose keys are read before any slot is written
         for (int32_t s0 = 0; s0 < ngroups; s0 += NT * LA) {
             uint32_t kk[LA];
 #pragma unroll
@@ -950,12 +973,8 @@ __global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
                     const bool pred = f[e] >= l_stage;
                     const uint64_t mask = __ballot(pred);
                     if (mask != 0) {
-                        if (pred) {
-                            const int32_t pos = nst_w + (int32_t)lanes_below(mask);
-                            if (pos < SLICE) slice[pos] = St::raw(raw[u], e);
-                            atomicAdd((unsigned long long*)&S.hstage[nuc_bucket(f[e], c, mcc)],
-                                      (unsigned long long)wfix(f[e]));
-                        }
+                        const int32_t pos = nst_w + (int32_t)lanes_below(mask);
+                        if (pred && pos < SLICE) slice[pos] = St::raw(raw[u], e);
                         nst_w += (int32_t)__popcll(mask);
                     }
                 }
@@ -977,16 +996,30 @@ __global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
     // fn(valid, v, k) for the wave's staged entries, called by every lane of
     // the wave the same number of times (valid: the lane holds an entry)
     auto for_staged = [&](auto&& fn) {
+        constexpr int B = 4;  // entries per lane read before any is used
         const typename St::T* slice = S.b.stage + wv * SLICE;
-        for (int32_t i0 = 0; i0 < nst_w; i0 += kWave) {
-            const bool valid = i0 + lane < nst_w;
-            const typename St::T r = slice[valid ? i0 + lane : 0];
-            fn(valid, St::value(r), St::key(r));
+        for (int32_t i0 = 0; i0 < nst_w; i0 += kWave * B) {
+            typename St::T r[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const int32_t i = i0 + b * kWave + lane;
+                r[b] = slice[i < nst_w ? i : 0];
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) fn(i0 + b * kWave + lane < nst_w, St::value(r[b]), St::key(r[b]));
         }
     };
     int32_t bstar = 0;
     uint64_t need_b = 0, mass_hi = 0;
     if (fast) {
+        // the staged logits' fixed-point weights per log-weight bucket (a visit
+        // of the staged entries issues far fewer instructions than the same
+        // atomics inside the staging walk, where nearly every element position
+        // has some lane to serve)
+        for_staged([&](bool valid, float v, uint32_t) {
+            if (valid) atomicAdd((unsigned long long*)&S.hstage[nuc_bucket(v, c, mcc)], (unsigned long long)wfix(v));
+        });
+        __syncthreads();
         if (wv == 0) {
             uint64_t h4[4], lsum = 0;
 #pragma unroll
