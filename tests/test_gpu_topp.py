@@ -99,7 +99,29 @@ EDGE = {
     "neg_inf_masks": (_spec(vocab=6000), lambda x: np.where(np.arange(x.shape[1]) % 5 == 0, -np.inf, x)),
     "zipf_ragged_T0.7": (_spec(kind="zipf", vocab=60000, batch=12, k=8, ragged=True, temperature=0.7,
                                top_p=0.95), None),
+    # Rows longer than the per-row kernel stages whole (more than 8192 16-bit
+    # or 4096 fp32 logits) take its predicted cut: every 16th 16-byte block is
+    # the subsample.
+    "predicted_cut_bf16": (_spec(vocab=30000, top_p=0.95), None),
+    "predicted_cut_f16": (_spec(vocab=30000, dtype="f16"), None),
+    "predicted_cut_f32": (_spec(vocab=30000, dtype="f32", top_p=0.5), None),
+    # the subsample sees none of the tail (every subsampled block holds -30):
+    # the prediction stages too little and the row takes the exact path
+    "prediction_misses_the_tail": (_spec(vocab=40000),
+                                   lambda x: np.where((np.arange(x.shape[1]) // 8) % 16 == 0, -30.0, x)),
+    # the cut falls in a bucket of 3000 tied logits: more crossing entries
+    # than the per-wave regions hold (the radix then runs over the staged set)
+    "crossing_bucket_of_3000_ties": (_spec(vocab=30000), lambda x: _tied_crossing(x)),
 }
+
+
+def _tied_crossing(x):
+    """Ids 1000..1099 at 5, ids 1100..4099 at 0, the rest at -20 (every row):
+    at T = 1 the 100 large logits hold 83% of the mass, so top_p 0.9 cuts
+    inside the 3000 tied ones and keeps them all."""
+    ids = np.arange(x.shape[1])
+    row = np.where((ids >= 1000) & (ids < 1100), 5.0, np.where((ids >= 1100) & (ids < 4100), 0.0, -20.0))
+    return np.broadcast_to(row, x.shape).astype(x.dtype)
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
