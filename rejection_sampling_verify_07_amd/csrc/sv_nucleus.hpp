@@ -695,7 +695,9 @@ struct Walk1 {
     int lg_g, lg_s;
     uint16_t* gmax;
     u32x4* sub;
-    float lm = neg_inf(), lmcc = neg_inf();
+    // lref: an integer number of bits at or above lm c, the reference of ls,
+    // so that moving it is an exact power-of-two rescale
+    float lm = neg_inf(), lref = neg_inf();
     double ls = 0.0;
 
     // unconditional loads (a block past the row reloads the last one, and
@@ -722,7 +724,7 @@ struct Walk1 {
         // one pass over the round: block maxima and the exp2 terms against
         // the reference the lane had before it (a term exceeds 1 when the
         // round raises the maximum; the sum is rescaled below)
-        const float ref = lmcc;
+        const float ref = lref;
         float rm = neg_inf(), t = 0.0f;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -743,24 +745,25 @@ struct Walk1 {
             for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -ref));
         }
         if (rm > lm) {
-            const float mcc = rm * c;
-            if (!(mcc - ref <= 64.0f)) {
+            const float nref = ceilf(rm * c);
+            if (!(nref - ref <= 64.0f)) {
                 // no finite reference yet (ref = -inf), or a rise of more than
-                // 64 bits: the terms above are unusable, sum again against mcc
+                // 64 bits: the terms above are unusable, sum again against nref
                 t = 0.0f;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     float f[VEC];
                     unpack<DT>(raw[u], f);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -mcc));
+                    for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -nref));
                 }
-                ls = (lm == neg_inf() ? 0.0 : ls * exp2((double)lmcc - (double)mcc)) + (double)t;
+                // (a shift below -2000 leaves no double bits; the clamp keeps the cast defined)
+                ls = (lm == neg_inf() ? 0.0 : ldexp(ls, (int)fmaxf(ref - nref, -2000.0f))) + (double)t;
             } else {
-                ls = (ls + (double)t) * exp2((double)ref - (double)mcc);
+                ls = ldexp(ls + (double)t, (int)(ref - nref));
             }
             lm = rm;
-            lmcc = mcc;
+            lref = nref;
         } else if (lm != neg_inf()) {
             ls += (double)t;
         }
@@ -814,17 +817,18 @@ __global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
     const int32_t nsub = (rb.nblk + (1 << lg_s) - 1) >> lg_s;
 
     // 1. statistics, group maxima, subsample
-    float lm;
+    float lm, lref;
     double ls;
     {
         Walk1<DT, NT, U> w1{rb, a.vocab, c, lg_g, lg_s, S.a.gmax, S.b.sub};
         w1.run();
         lm = w1.lm;
+        lref = w1.lref;
         ls = w1.ls;
     }
     const float m = block_max_float<NT>(lm, S.f);  // (its barriers also publish gmax and sub)
     const float mcc = m * c;
-    const double part = lm == neg_inf() ? 0.0 : ls * exp2((double)(lm * c) - (double)mcc);
+    const double part = lm == neg_inf() ? 0.0 : ls * exp2((double)lref - (double)mcc);
     const double total = block_sum_double<NT>(part, S.d);
     RowDesc d;
     d.tau = neg_inf();
