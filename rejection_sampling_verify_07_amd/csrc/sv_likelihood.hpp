@@ -56,24 +56,6 @@ struct MinWFull {
     }
 };
 
-// Merge one row's chunk partials (m, fl32(m c), S at the chunk max) into the
-// row's fl32(m c) and S, by one wave; every lane gets the result.
-__device__ __forceinline__ void merge_row_partials(const PartialFull* pp, int32_t nchunk, float c, float* mcc_out,
-                                                   double* s_out)
-{
-    float m = neg_inf();
-    for (int32_t ch = lane_id(); ch < nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
-    m = wave_max_dpp(m);
-    const float mcc = m * c;
-    double s = 0.0;
-    for (int32_t ch = lane_id(); ch < nchunk; ch += kWave) {
-        const PartialFull q = pp[ch];
-        if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
-    }
-    *mcc_out = mcc;
-    *s_out = wave_sum_dpp(s);
-}
-
 struct PairArgs {
     RowSet rs;          // target rows [0, R), draft rows [R, 2R)
     int32_t vocab;

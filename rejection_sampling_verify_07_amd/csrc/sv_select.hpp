@@ -145,7 +145,7 @@ __device__ __forceinline__ double sort_write_kept(WaveSelLds& L, int32_t nk, Kep
 // NJ is a template argument so that every per-slot loop is unrolled without
 // branches; select_tail picks the smallest NJ that holds the candidates.
 template <int DT, int NJ>
-__device__ void select_tail_n(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+__device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
                               KeptEntry* __restrict__ kept, WaveSelLds& L, const KeptEntry* e)
 {
     using K = SelKey<DT>;
@@ -250,7 +250,7 @@ __device__ void select_tail(int32_t row, int32_t top_k, float c, RowDesc* __rest
 // each, choff their exclusive prefix sums (in LDS); candidate i is found by a
 // binary search over choff.
 template <int DT>
-__device__ void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+__device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
                                  const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
                                  KeptEntry* __restrict__ kept, WaveSelLds& L, const int32_t* choff, int32_t total)
 {
@@ -288,7 +288,7 @@ constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (51
 
 // The select over n candidates staged in L.kidx / L.kval (n <= NJ * 64).
 template <int DT, int NJ>
-__device__ void select_from_lds(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+__device__ __forceinline__ void select_from_lds(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
                                 KeptEntry* __restrict__ kept, WaveSelLds& L, int32_t n)
 {
     KeptEntry r[NJ];
@@ -302,7 +302,7 @@ __device__ void select_from_lds(int32_t row, int32_t top_k, float c, RowDesc* __
 }
 
 template <int DT>
-__device__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+__device__ __forceinline__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
                                  const int32_t* __restrict__ counts, const float* __restrict__ bounds,
                                  const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
                                  KeptEntry* __restrict__ kept, WaveSelLds& L)
@@ -434,7 +434,7 @@ __device__ __forceinline__ void wave_row_blocks(const char* rowp, int32_t vocab,
 // (one pass per digit), then the kept list by an ordered compaction (ascending
 // ids) or, past the list capacity, the masked full-row description.
 template <int DT>
-__device__ void wave_select_exact(int32_t row, const char* rowp, int32_t vocab, int32_t top_k, float c,
+__device__ __attribute__((noinline)) void wave_select_exact(int32_t row, const char* rowp, int32_t vocab, int32_t top_k, float c,
                                   RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L)
 {
     const int lane = lane_id();

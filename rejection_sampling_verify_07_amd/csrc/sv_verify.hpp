@@ -472,6 +472,24 @@ constexpr int kMaxChunkBlocks = 8 * kThreads;  // 8 loads per thread per streami
 // run 512-thread workgroups (four blocks per thread), two per CU, instead of
 // one 1024-thread workgroup per CU.
 constexpr int kDraftChunkThreads = 512;
+
+// The full-row walk as the rare fallback of the chunk walk below: out of line,
+// with the weights taken by value and the token and total returned, so that
+// no local of the caller needs an address (one would be kept in scratch memory
+// on every path).
+struct TokenTotal {
+    int32_t token;
+    double total;
+};
+template <int DT, int NT, class W>
+__device__ __attribute__((noinline)) TokenTotal cdf_full_fallback(const char* row, int32_t vocab, W wfn, double u,
+                                                                   DrawLds<NT>& L)
+{
+    TokenTotal r;
+    inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, &r.token, &r.total);
+    return r;
+}
+
 template <int DT, int NT, class W>
 __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32_t nchunk, int32_t chunk_blocks,
                                    int32_t vocab, const W& wfn, double u, DrawLds<NT>& L, int32_t* token,
@@ -528,7 +546,9 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
     const int32_t nblk = (mis + vocab + VEC - 1) / VEC;
     const int32_t bpt = (chunk_blocks + NT - 1) / NT;  // blocks per thread
     if (bpt > BPT) {  // chunks longer than BPT blocks per thread: walk the row
-        inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, token, total);
+        const TokenTotal r = cdf_full_fallback<DT, NT>(row, vocab, wfn, u, L);
+        *token = r.token;
+        *total = r.total;
         return;
     }
     int32_t tok = -1;
@@ -620,7 +640,9 @@ __device__ void inverse_cdf_chunks(const char* row, const PartialFull* pp, int32
         tok = -1;
     }
     if (tok < 0 || tok == INT32_MAX) {
-        inverse_cdf_full<DT, false, NT>(row, nullptr, vocab, wfn, u, L.seg, L.wd, L.i, L.dd, token, total);
+        const TokenTotal r = cdf_full_fallback<DT, NT>(row, vocab, wfn, u, L);
+        *token = r.token;
+        *total = r.total;
         return;
     }
     *token = tok;
@@ -794,6 +816,43 @@ __device__ __forceinline__ int32_t seq_row(const VerifyArgs& a, int32_t b, int32
 // at every guess.  Returns n, the first rejected position (or kb), or -1
 // when a guess id is out of range.  p(x), q(x) go to out_probs when
 // write_probs.
+// Merge one row's chunk partials (m, fl32(m c), S at the chunk max) into the
+// row's fl32(m c) and S, by one wave; every lane gets the result.  Rows of at
+// most one chunk per lane load their partials once (one memory round instead
+// of one for the maximum and one for the sums); the per-lane terms and the
+// reduction order are the same either way.
+__device__ __forceinline__ PartialFull lane_partial(const PartialFull* pp, int32_t nchunk)
+{
+    const int l = lane_id();
+    return l < nchunk ? pp[l] : PartialFull{neg_inf(), neg_inf(), 0.0};
+}
+__device__ __forceinline__ void reduce_lane_partials(const PartialFull& q, float c, float* mcc_out, double* s_out)
+{
+    const float mcc = wave_max_dpp(q.m) * c;
+    *mcc_out = mcc;
+    *s_out = wave_sum_dpp(q.s > 0.0 ? q.s * exp2((double)q.mcc - (double)mcc) : 0.0);
+}
+__device__ __forceinline__ void merge_row_partials(const PartialFull* pp, int32_t nchunk, float c, float* mcc_out,
+                                                   double* s_out)
+{
+    const int l = lane_id();
+    if (nchunk <= kWave) {
+        reduce_lane_partials(lane_partial(pp, nchunk), c, mcc_out, s_out);
+        return;
+    }
+    float m = neg_inf();
+    for (int32_t ch = l; ch < nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
+    m = wave_max_dpp(m);
+    const float mcc = m * c;
+    double s = 0.0;
+    for (int32_t ch = l; ch < nchunk; ch += kWave) {
+        const PartialFull q = pp[ch];
+        if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
+    }
+    *mcc_out = mcc;
+    *s_out = wave_sum_dpp(s);
+}
+
 template <int DT, bool FROM_DESC, int NT>
 __device__ __forceinline__ int32_t verify_accept(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb,
                                                  VerifyLds<NT>& S, bool write_probs)
@@ -821,19 +880,37 @@ __device__ __forceinline__ int32_t verify_accept(const VerifyArgs& a, int32_t b,
             S.row[r] = RowLds{d.tau, d.mcc, (float)(1.0 / d.s), d.kept, d.s};
         }
     } else {
-        for (int32_t r = wave_id(); r < nrows; r += (NT / kWave)) {
-            const PartialFull* pp = a.partials + (int64_t)seq_row(a, b, k0, kb, r) * a.nchunk;
-            float m = neg_inf();
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
-            m = wave_max_dpp(m);
-            const float mcc = m * a.c;
-            double s = 0.0;
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
-                const PartialFull q = pp[ch];
-                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
+        constexpr int NW = NT / kWave;
+        if (a.nchunk <= kWave) {
+            // a wave's rows (up to RPW of them) have their partials in flight together
+            constexpr int RPW = 4;
+            for (int32_t r0 = wave_id(); r0 < nrows; r0 += NW * RPW) {
+                PartialFull q[RPW];
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const int32_t r = r0 + i * NW;
+                    q[i] = r < nrows ? lane_partial(a.partials + (int64_t)seq_row(a, b, k0, kb, r) * a.nchunk, a.nchunk)
+                                     : PartialFull{neg_inf(), neg_inf(), 0.0};
+                }
+#pragma unroll
+                for (int i = 0; i < RPW; ++i) {
+                    const int32_t r = r0 + i * NW;
+                    if (r < nrows) {
+                        float mcc;
+                        double s;
+                        reduce_lane_partials(q[i], a.c, &mcc, &s);
+                        if (lane_id() == 0) S.row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+                    }
+                }
             }
-            s = wave_sum_dpp(s);
-            if (lane_id() == 0) S.row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+        } else {
+            for (int32_t r = wave_id(); r < nrows; r += NW) {
+                float mcc;
+                double s;
+                merge_row_partials(a.partials + (int64_t)seq_row(a, b, k0, kb, r) * a.nchunk, a.nchunk, a.c, &mcc,
+                                   &s);
+                if (lane_id() == 0) S.row[r] = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
+            }
         }
     }
     __syncthreads();
@@ -1031,17 +1108,9 @@ __global__ __launch_bounds__(NT, NT == kDraftChunkThreads ? 4 : 1) void draft_dr
         }
     } else {
         if (wave_id() == 0) {
-            const PartialFull* pp = a.partials + (int64_t)row * a.nchunk;
-            float m = neg_inf();
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) m = fmaxf(m, pp[ch].m);
-            m = wave_max_dpp(m);
-            const float mcc = m * a.c;
-            double s = 0.0;
-            for (int32_t ch = lane_id(); ch < a.nchunk; ch += kWave) {
-                const PartialFull q = pp[ch];
-                if (q.s > 0.0) s += q.s * exp2((double)q.mcc - (double)mcc);
-            }
-            s = wave_sum_dpp(s);
+            float mcc;
+            double s;
+            merge_row_partials(a.partials + (int64_t)row * a.nchunk, a.nchunk, a.c, &mcc, &s);
             if (lane_id() == 0) s_r = RowLds{neg_inf(), mcc, (float)(1.0 / s), -1, s};
         }
     }
