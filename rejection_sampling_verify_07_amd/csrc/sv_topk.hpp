@@ -273,8 +273,9 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
 
             // the top_k-th largest of the workgroup's 256 * KEYS keys (lane maxima,
             // and with KEYS = 2 the lanes' second-largest block maxima too; on the
-            // top 16 key bits): every wave runs the same ballot radix select over
-            // all of them, 4 * KEYS per lane
+            // top 16 key bits): wave 0 runs a ballot radix select over all of
+            // them, 4 * KEYS per lane, and hands the result to the others
+            // through LDS, so the other waves' SIMDs are free for other tiles
             constexpr int KPL = 4 * KEYS;  // keys per lane
             s_lk[threadIdx.x] = order_key(tm) >> 16;
             if constexpr (KEYS == 2) {
@@ -288,28 +289,33 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 s_lk[kThreads + threadIdx.x] = order_key(t2) >> 16;
             }
             __syncthreads();
-            uint32_t kk[KPL];
+            if (__builtin_amdgcn_readfirstlane(threadIdx.x) < kWave) {
+                uint32_t kk[KPL];
 #pragma unroll
-            for (int q = 0; q < KPL; ++q) kk[q] = s_lk[lane_id() + q * kWave];
-            // bits above the highest one where the largest and smallest key differ
-            // are common to all keys: start the select below them
-            uint32_t kmax = kk[0], kmin = kk[0];
+                for (int q = 0; q < KPL; ++q) kk[q] = s_lk[lane_id() + q * kWave];
+                // bits above the highest one where the largest and smallest key
+                // differ are common to all keys: start the select below them
+                uint32_t kmax = kk[0], kmin = kk[0];
 #pragma unroll
-            for (int q = 1; q < KPL; ++q) {
-                kmax = max(kmax, kk[q]);
-                kmin = min(kmin, kk[q]);
+                for (int q = 1; q < KPL; ++q) {
+                    kmax = max(kmax, kk[q]);
+                    kmin = min(kmin, kk[q]);
+                }
+                wave_umax_umin_dpp(kmax, kmin);
+                const uint32_t diff = kmax ^ kmin;
+                const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+                uint32_t hs = kmax & ~((2u << top) - 1u);  // the common prefix
+                for (int bit = top; bit >= 0; --bit) {
+                    const uint32_t cand = hs | (1u << bit);
+                    int cnt = 0;
+#pragma unroll
+                    for (int q = 0; q < KPL; ++q) cnt += (int)__popcll(__ballot(kk[q] >= cand));
+                    if (cnt >= top_k) hs = cand;
+                }
+                if (lane_id() == 0) s_misc[0] = (int32_t)hs;
             }
-            wave_umax_umin_dpp(kmax, kmin);
-            const uint32_t diff = kmax ^ kmin;
-            const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
-            uint32_t h = kmax & ~((2u << top) - 1u);  // the common prefix
-            for (int bit = top; bit >= 0; --bit) {
-                const uint32_t cand = h | (1u << bit);
-                int cnt = 0;
-#pragma unroll
-                for (int q = 0; q < KPL; ++q) cnt += (int)__popcll(__ballot(kk[q] >= cand));
-                if (cnt >= top_k) h = cand;
-            }
+            __syncthreads();
+            const uint32_t h = (uint32_t)s_misc[0];
             // smallest float whose key has these top bits; the -inf bucket maps to -inf
             bound = (h <= (order_key(neg_inf()) >> 16)) ? neg_inf() : key_to_float(h << 16);
 
