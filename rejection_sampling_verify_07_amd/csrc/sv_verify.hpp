@@ -298,8 +298,11 @@ __device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, con
     float w[PER];
     int32_t ix[PER];
     double ls = 0.0;
+    // slots q >= per are empty in every lane: both loops stop there (per is
+    // uniform), which leaves every sum and every pick as it was
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
+        if (q >= per) break;
         const int32_t i = lo + q;
         w[q] = 0.0f;
         ix[q] = -1;
@@ -325,6 +328,7 @@ __device__ void inverse_cdf_list_of(Entry&& entry, int32_t n, Draft&& draft, con
     int hit = -1, lastpos = -1;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
+        if (q >= per) break;
         cum += (double)w[q];
         if (hit < 0 && ix[q] >= 0 && cum > t) hit = ix[q];
         if (w[q] > 0.0f) lastpos = ix[q];
@@ -377,6 +381,7 @@ __device__ void argmax_list_of(Entry&& entry, int32_t n, Draft&& draft, const Re
     double ls = 0.0;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
+        if (q >= per) break;  // uniform: empty in every lane from here on
         const int32_t i = lo + q;
         if (i >= hi) continue;
         const KeptEntry e = entry(i);
@@ -853,21 +858,48 @@ __device__ __forceinline__ void merge_row_partials(const PartialFull* pp, int32_
     *s_out = wave_sum_dpp(s);
 }
 
+// The accept test of guess k (id x, logits lt / ld at it, uniform u):
+// p(x) and q(x) in fp64, accepted when u < min(1, p / q); a rejection lowers
+// n to k, a bad id sets bad.
+__device__ __forceinline__ void accept_one(const VerifyArgs& a, int32_t k, int32_t x, float lt, float ld,
+                                           const RowLds& rt, const RowLds& rd, double u, int32_t drow0,
+                                           bool write_probs, int32_t& n, int32_t& bad)
+{
+    if (x < 0 || x >= a.vocab) {
+        atomicOr(&bad, 1);
+        return;
+    }
+    const double cd = (double)a.c;
+    const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
+    const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
+    if (write_probs && a.out_probs != nullptr) {
+        a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
+        a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
+    }
+    const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+    if (!(u < ratio)) atomicMin(&n, k);
+}
+
 template <int DT, bool FROM_DESC, int NT>
 __device__ __forceinline__ int32_t verify_accept(const VerifyArgs& a, int32_t b, int32_t k0, int32_t kb,
                                                  VerifyLds<NT>& S, bool write_probs)
 {
+    static_assert(NT >= kMaxDraft, "one guess per thread");
     const int32_t trow0 = k0 + b;  // first target row of the sequence
     const int32_t drow0 = k0;      // first draft row
     const int32_t nrows = 2 * kb + 1;
+    // with row descriptors (one small load round), thread k's guess is
+    // loaded with them, which saves the accept test a dependent round; over
+    // full rows it is loaded with the accept test (measured faster there)
+    const int32_t xk = FROM_DESC && (int32_t)threadIdx.x < kb ? a.ids[drow0 + threadIdx.x] : 0;
 
     if (threadIdx.x == 0) {
         S.n = kb;
         S.bad = 0;
     }
     // every uniform the step can use, computed while the first loads are in
-    // flight: thread k holds U(b, k, 0) (positions past NT compute their own);
-    // S.udraw[k] = U(b, k, 1), S.udraw[kb] = U(b, kb, 2)
+    // flight: thread k holds U(b, k, 0); S.udraw[k] = U(b, k, 1),
+    // S.udraw[kb] = U(b, kb, 2)
     const int32_t tk = threadIdx.x;
     const double u_acc = uniform24(a.seed, (uint32_t)b, (uint32_t)tk, 0u, a.offset);
     for (int32_t t = tk; t <= kb; t += NT)
@@ -918,26 +950,24 @@ __device__ __forceinline__ int32_t verify_accept(const VerifyArgs& a, int32_t b,
     // ---- B: accept test at every draft position
     const char* tbase = a.rs.tgt;
     const char* dbase = a.rs.drf;
-    for (int32_t k = threadIdx.x; k < kb; k += NT) {
+    const int32_t k = threadIdx.x;
+    if constexpr (FROM_DESC) {
+        if (kb == 0) return S.n;
+        // thread k's two logits at its guess; lanes past kb and a bad id load
+        // a clamped element that is not used, so that the loads are unconditional
+        const int32_t kc = min(k, kb - 1);
+        const int32_t xc = min(max(xk, 0), a.vocab - 1);
+        const float lt = load_one<DT>(tbase + (int64_t)(trow0 + kc) * a.rs.t_stride_bytes, xc);
+        const float ld = load_one<DT>(dbase + (int64_t)(drow0 + kc) * a.rs.d_stride_bytes, xc);
+        if (k < kb) accept_one(a, k, xk, lt, ld, S.row[k], S.row[kb + 1 + k], u_acc, drow0, write_probs, S.n, S.bad);
+    } else if (k < kb) {
         const int32_t x = a.ids[drow0 + k];
-        if (x < 0 || x >= a.vocab) {
-            atomicOr(&S.bad, 1);
-            continue;
+        float lt = 0.0f, ld = 0.0f;
+        if (x >= 0 && x < a.vocab) {
+            lt = load_one<DT>(tbase + (int64_t)(trow0 + k) * a.rs.t_stride_bytes, x);
+            ld = load_one<DT>(dbase + (int64_t)(drow0 + k) * a.rs.d_stride_bytes, x);
         }
-        const float lt = load_one<DT>(tbase + (int64_t)(trow0 + k) * a.rs.t_stride_bytes, x);
-        const float ld = load_one<DT>(dbase + (int64_t)(drow0 + k) * a.rs.d_stride_bytes, x);
-        const RowLds& rt = S.row[k];
-        const RowLds& rd = S.row[kb + 1 + k];
-        const double cd = (double)a.c;
-        const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
-        const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
-        if (write_probs && a.out_probs != nullptr) {
-            a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
-            a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
-        }
-        const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-        const double u = k == tk ? u_acc : uniform24(a.seed, (uint32_t)b, (uint32_t)k, 0u, a.offset);
-        if (!(u < ratio)) atomicMin(&S.n, k);
+        accept_one(a, k, x, lt, ld, S.row[k], S.row[kb + 1 + k], u_acc, drow0, write_probs, S.n, S.bad);
     }
     __syncthreads();
     return S.bad != 0 ? -1 : S.n;
