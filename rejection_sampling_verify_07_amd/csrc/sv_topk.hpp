@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void topk_cand_kernel(
                 wave_umax_umin_dpp(kmax, kmin);
                 const uint32_t diff = kmax ^ kmin;
                 const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
-                uint32_t hs = kmax & ~((2u << top) - 1u);  // the common prefix
+                uint32_t hs = top >= 0 ? kmax & ~((2u << top) - 1u) : kmax;  // the common prefix
                 for (int bit = top; bit >= 0; --bit) {
                     const uint32_t cand = hs | (1u << bit);
                     int cnt = 0;
