@@ -329,8 +329,8 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
                           (int32_t)kXcds);
         }
         if (launch_status() != SV_OK) return SV_ERR_HIP;
-        // one wave per row; rows whose chunks overflowed take the exact path inside
-        hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kWave), 0, stream, rs,
+        // one workgroup per row; rows whose chunks overflowed take the exact path inside
+        hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kSelWaves * sv::kWave), 0, stream, rs,
                            sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, descs, kept);
     } else {
         hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,

@@ -273,51 +273,67 @@ __device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t 
     select_tail<DT>(row, top_k, c, descs, kept, L, e, nj);
 }
 
-// Speculative path.  Every chunk bound is a lower bound of the row's tau, so
-// only candidates >= their maximum can be kept; those few are compacted (in
-// LDS, in chunk order) before the select.  The counts and bounds are read
-// first (one lane per chunk, 64 chunks per round); the candidate slots then
-// follow in batches of kSpecChunks chunks, the first kSpecSlots * 64 slots
-// of each chunk loaded at once (a row of at most kSpecChunks chunks whose
-// counts fit those slots takes a single batch), and the rare slots past them
-// one load round at a time.  Returns false, having written nothing, when a
-// chunk overflowed or the survivors do not fit the kept list.
-constexpr int kSpecChunks = 16;
+// Speculative path, kSelWaves waves per row.  Every chunk bound is a lower
+// bound of the row's tau, so only candidates >= their maximum can be kept.
+// Each wave reads every count and bound itself (one lane per chunk, 64
+// chunks per round), so each knows the largest bound and whether a chunk
+// overflowed; wave w then takes the contiguous chunks [w C, (w + 1) C),
+// C = ceil(nchunk / kSelWaves), kSpecChunks at a time with the first
+// kSpecSlots * 64 slots of each loaded at once (the first batch in flight
+// with the counts and bounds) and the rare slots past them kSpecExtra rounds
+// at a time, and compacts its survivors in chunk order into its own part of
+// the LDS list.  Region after region, that is the row's chunk order.  After
+// one barrier wave 0 runs the select over them.  Returns false (the same in
+// every wave), having written nothing, when a chunk overflowed or the
+// survivors do not fit the kept list.
+constexpr int kSelWaves = 4;
+constexpr int kSelRegion = kKeepCapList / kSelWaves;  // survivors a wave can hold
+constexpr int kSpecChunks = 4;
 constexpr int kSpecSlots = 2;
 constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (512 slots: all of them)
 
-// The select over n candidates staged in L.kidx / L.kval (n <= NJ * 64).
+// The select over the n survivors held in the waves' LDS regions (region v
+// holds off[v + 1] - off[v] of them), in region order; n <= NJ * 64.
 template <int DT, int NJ>
-__device__ __forceinline__ void select_from_lds(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
-                                KeptEntry* __restrict__ kept, WaveSelLds& L, int32_t n)
+__device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+                                                    KeptEntry* __restrict__ kept, WaveSelLds& L,
+                                                    const int32_t* off, int32_t n)
 {
     KeptEntry r[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int32_t i = lane_id() + j * kWave;
-        r[j] = i < n ? KeptEntry{L.kidx[i], L.kval[i]} : KeptEntry{INT32_MAX, neg_inf()};
+        int32_t at = i;  // region 0
+#pragma unroll
+        for (int u = 1; u < kSelWaves; ++u)
+            if (i >= off[u]) at = u * kSelRegion + (i - off[u]);
+        r[j] = i < n ? KeptEntry{L.kidx[at], L.kval[at]} : KeptEntry{INT32_MAX, neg_inf()};
     }
     __builtin_amdgcn_wave_barrier();
     select_tail_n<DT, NJ>(row, top_k, c, descs, kept, L, r);
 }
 
 template <int DT>
-__device__ __forceinline__ bool wave_select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
-                                 const int32_t* __restrict__ counts, const float* __restrict__ bounds,
-                                 const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
-                                 KeptEntry* __restrict__ kept, WaveSelLds& L)
+__device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+                                            const int32_t* __restrict__ counts, const float* __restrict__ bounds,
+                                            const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
+                                            KeptEntry* __restrict__ kept, WaveSelLds& L, int32_t* s_wn)
 {
     const int lane = lane_id();
+    const int w = wave_id();
     const int64_t t0 = (int64_t)row * nchunk;
+    const int32_t C = (nchunk + kSelWaves - 1) / kSelWaves;
+    const int32_t cb = min(nchunk, w * C), ce = min(nchunk, cb + C);  // this wave's chunks
     int32_t cnt_l = lane < nchunk ? counts[t0 + lane] : 0;  // chunk `lane` of the first 64
     float bnd_l = lane < nchunk ? bounds[t0 + lane] : neg_inf();
-    // the first batch of candidate slots in flight with the counts and bounds
+    // the first batch of this wave's candidate slots in flight with the counts and bounds
     KeptEntry e[kSpecChunks][kSpecSlots];
+    int32_t cnt_b = lane < kSpecChunks && cb + lane < ce ? counts[t0 + cb + lane] : 0;  // lane ch: chunk c0 + ch
 #pragma unroll
     for (int ch = 0; ch < kSpecChunks; ++ch) {
 #pragma unroll
         for (int q = 0; q < kSpecSlots; ++q) {
-            e[ch][q] = ch < nchunk ? cands[(t0 + ch) * cap + q * kWave + lane] : KeptEntry{INT32_MAX, neg_inf()};
+            e[ch][q] = cb + ch < ce ? cands[(t0 + cb + ch) * cap + q * kWave + lane] : KeptEntry{INT32_MAX, neg_inf()};
         }
     }
     bool over = cnt_l > cap;
@@ -331,36 +347,37 @@ __device__ __forceinline__ bool wave_select_spec(int32_t row, int32_t nchunk, in
     if (__ballot(over) != 0) return false;
     const float bmax = wave_max_dpp(bnd_l);
 
-    // survivors (candidate >= the largest chunk bound), compacted in chunk order
+    // survivors (candidate >= the largest chunk bound) of this wave's chunks,
+    // compacted in chunk order into region w
+    const int32_t rbase = w * kSelRegion;
     int32_t ns = 0;
     auto keep = [&](const KeptEntry& x, bool valid) {
         const bool pred = valid && x.val >= bmax;
         const uint64_t m = __ballot(pred);
         if (m != 0) {
             const int32_t pos = ns + lanes_below(m);
-            if (pred && pos < kKeepCapList) {
-                L.kidx[pos] = x.idx;
-                L.kval[pos] = x.val;
+            if (pred && pos < kSelRegion) {
+                L.kidx[rbase + pos] = x.idx;
+                L.kval[rbase + pos] = x.val;
             }
             ns += (int32_t)__popcll(m);
         }
     };
-    int32_t cnt_b = cnt_l;  // lane ch: the count of chunk c0 + ch
-    for (int32_t c0 = 0; c0 < nchunk; c0 += kSpecChunks) {
-        if (c0 > 0) {
+    for (int32_t c0 = cb; c0 < ce; c0 += kSpecChunks) {
+        if (c0 > cb) {
 #pragma unroll
             for (int ch = 0; ch < kSpecChunks; ++ch) {
 #pragma unroll
                 for (int q = 0; q < kSpecSlots; ++q) {
-                    e[ch][q] = c0 + ch < nchunk ? cands[(t0 + c0 + ch) * cap + q * kWave + lane]
-                                                : KeptEntry{INT32_MAX, neg_inf()};
+                    e[ch][q] = c0 + ch < ce ? cands[(t0 + c0 + ch) * cap + q * kWave + lane]
+                                            : KeptEntry{INT32_MAX, neg_inf()};
                 }
             }
-            cnt_b = lane < kSpecChunks && c0 + lane < nchunk ? counts[t0 + c0 + lane] : 0;
+            cnt_b = lane < kSpecChunks && c0 + lane < ce ? counts[t0 + c0 + lane] : 0;
         }
 #pragma unroll
         for (int ch = 0; ch < kSpecChunks; ++ch) {
-            if (c0 + ch < nchunk) {
+            if (c0 + ch < ce) {
                 const int32_t cnt = __builtin_amdgcn_readlane(cnt_b, ch);
 #pragma unroll
                 for (int q = 0; q < kSpecSlots; ++q) keep(e[ch][q], q * kWave + lane < cnt);
@@ -379,19 +396,31 @@ __device__ __forceinline__ bool wave_select_spec(int32_t row, int32_t nchunk, in
             }
         }
     }
-    if (ns < top_k || ns > kKeepCapList) return false;
-    __builtin_amdgcn_wave_barrier();
-    const int32_t nj = (ns + kWave - 1) / kWave;
+    if (lane == 0) s_wn[w] = ns;
+    __syncthreads();
+    int32_t off[kSelWaves + 1];
+    int32_t tot = 0;
+    bool fit = true;
+#pragma unroll
+    for (int v = 0; v < kSelWaves; ++v) {
+        off[v] = tot;
+        tot += s_wn[v];
+        fit = fit && s_wn[v] <= kSelRegion;
+    }
+    off[kSelWaves] = tot;
+    if (!fit || tot < top_k || tot > kKeepCapList) return false;
+    if (w != 0) return true;
+    const int32_t nj = (tot + kWave - 1) / kWave;
     if (nj <= 1) {
-        select_from_lds<DT, 1>(row, top_k, c, descs, kept, L, ns);
+        select_from_regions<DT, 1>(row, top_k, c, descs, kept, L, off, tot);
     } else if (nj <= 2) {
-        select_from_lds<DT, 2>(row, top_k, c, descs, kept, L, ns);
+        select_from_regions<DT, 2>(row, top_k, c, descs, kept, L, off, tot);
     } else if (nj <= 4) {
-        select_from_lds<DT, 4>(row, top_k, c, descs, kept, L, ns);
+        select_from_regions<DT, 4>(row, top_k, c, descs, kept, L, off, tot);
     } else if (nj <= 8) {
-        select_from_lds<DT, 8>(row, top_k, c, descs, kept, L, ns);
+        select_from_regions<DT, 8>(row, top_k, c, descs, kept, L, off, tot);
     } else {
-        select_from_lds<DT, kSelPer>(row, top_k, c, descs, kept, L, ns);
+        select_from_regions<DT, kSelPer>(row, top_k, c, descs, kept, L, off, tot);
     }
     return true;
 }
@@ -548,9 +577,12 @@ __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, i
                                 int32_t cap, float c, const int32_t* __restrict__ counts,
                                 const float* __restrict__ bounds, const KeptEntry* __restrict__ cands,
                                 RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
-                                int32_t* s_choff)
+                                int32_t* s_choff, int32_t* s_wn)
 {
-    if (wave_select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L)) return;
+    if (select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L, s_wn)) return;
+    if (wave_id() != 0) return;  // the paths below are one wave's
+    // every wave has passed the barrier of the speculative path (or none has),
+    // so wave 0 alone may reuse the LDS from here
     int32_t base = 0, bad = 0;
     for (int32_t g = 0; g < nchunk; g += kWave) {
         const int32_t ch = g + lane_id();
@@ -570,9 +602,10 @@ __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, i
     wave_select_exact<DT>(row, row_ptr(rs, row), vocab, top_k, c, descs, kept, L);
 }
 
-// One wave per row, over the candidates of the top-k streaming pass.
+// One workgroup of kSelWaves waves per row, over the candidates of the top-k
+// streaming pass.
 template <int DT>
-__global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
+__global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                                  int32_t top_k, int32_t cap, float c,
                                                                  const int32_t* __restrict__ counts,
                                                                  const float* __restrict__ bounds,
@@ -582,8 +615,9 @@ __global__ __launch_bounds__(kWave) void topk_select_wave_kernel(RowSet rs, int3
 {
     __shared__ WaveSelLds L;
     __shared__ int32_t s_choff[kMaxChunks + 1];
+    __shared__ int32_t s_wn[kSelWaves];
     select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L,
-                        s_choff);
+                        s_choff, s_wn);
 }
 
 }  // namespace sv
