@@ -858,9 +858,15 @@ __device__ __forceinline__ void merge_row_partials(const PartialFull* pp, int32_
     *s_out = wave_sum_dpp(s);
 }
 
-// The accept test of guess k (id x, logits lt / ld at it, uniform u):
-// p(x) and q(x) in fp64, accepted when u < min(1, p / q); a rejection lowers
-// n to k, a bad id sets bad.
+// The accept test of guess k (id x, logits lt / ld at it, uniform u): accepted
+// when u < min(1, p / q) with p(x) and q(x) in fp64.  The same test in fp32
+// decides first: with both exponents within 64 of the row maxima, fp32 p and
+// q are within 3e-6 of the fp64 ones (the exponent's rounding, 2^-24 of at
+// most 64, times ln 2, plus three roundings) and their ratio within 6e-6, so
+// a u farther than 2^-12 of the ratio (relative) gets the fp64 test's answer;
+// only the rest (about 5e-4 of the draws) take the fp64 test.  p and q are
+// reported from whichever precision decided.  A rejection lowers n to k, a
+// bad id sets bad.
 __device__ __forceinline__ void accept_one(const VerifyArgs& a, int32_t k, int32_t x, float lt, float ld,
                                            const RowLds& rt, const RowLds& rd, double u, int32_t drow0,
                                            bool write_probs, int32_t& n, int32_t& bad)
@@ -869,15 +875,37 @@ __device__ __forceinline__ void accept_one(const VerifyArgs& a, int32_t k, int32
         atomicOr(&bad, 1);
         return;
     }
-    const double cd = (double)a.c;
-    const double p = lt >= rt.tau ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
-    const double q = ld >= rd.tau ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
-    if (write_probs && a.out_probs != nullptr) {
-        a.out_probs[2 * (int64_t)(drow0 + k)] = (float)p;
-        a.out_probs[2 * (int64_t)(drow0 + k) + 1] = (float)q;
+    const bool pin = lt >= rt.tau, qin = ld >= rd.tau;  // kept by the filters
+    const float at = __builtin_fmaf(lt, a.c, -rt.mcc), ad = __builtin_fmaf(ld, a.c, -rd.mcc);
+    const float p32 = pin ? __builtin_amdgcn_exp2f(at) * rt.inv_s : 0.0f;
+    const float q32 = qin ? __builtin_amdgcn_exp2f(ad) * rd.inv_s : 0.0f;
+    constexpr float kMargin = 1.0f / 4096.0f;
+    const float uf = (float)u;  // exact: u has 24 bits
+    int dec = -1;               // 1 accept, 0 reject, -1 undecided
+    if (!qin) {
+        dec = pin ? 1 : 0;  // ratio 1 when p > 0, else 0 (u >= 0 never passes)
+    } else if (!pin) {
+        dec = 0;
+    } else if (fabsf(at) <= 64.0f && fabsf(ad) <= 64.0f) {
+        const float r32 = p32 / q32;
+        if (r32 >= 1.0f + kMargin || uf < r32 * (1.0f - kMargin)) dec = 1;  // u < 1 <= p / q, or u clearly below
+        else if (uf > r32 * (1.0f + kMargin)) dec = 0;
     }
-    const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
-    if (!(u < ratio)) atomicMin(&n, k);
+    float pw = p32, qw = q32;
+    if (dec < 0) {
+        const double cd = (double)a.c;
+        const double p = exp2((double)lt * cd - (double)rt.mcc) / rt.s;
+        const double q = exp2((double)ld * cd - (double)rd.mcc) / rd.s;
+        const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
+        dec = u < ratio ? 1 : 0;
+        pw = (float)p;
+        qw = (float)q;
+    }
+    if (write_probs && a.out_probs != nullptr) {
+        a.out_probs[2 * (int64_t)(drow0 + k)] = pw;
+        a.out_probs[2 * (int64_t)(drow0 + k) + 1] = qw;
+    }
+    if (dec == 0) atomicMin(&n, k);
 }
 
 template <int DT, bool FROM_DESC, int NT>
