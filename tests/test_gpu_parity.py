@@ -215,6 +215,67 @@ def test_draft_equals_target_accepts_all():
     compare_sample(w, g, _oracle(w))
 
 
+@pytest.mark.parametrize("top_k", [0, 50])
+def test_accept_ratio_near_the_uniform(top_k):
+    """Guesses whose p/q lies just above or below its accept uniform.
+
+    The kernel decides the accept test in fp32 unless u lies within 2^-12
+    (relative) of the fp32 ratio, and in fp64 there; these guesses put the
+    ratio at u * (1 + rel) for rel from -3e-3 to 3e-3, on both sides of that
+    margin.  Each sequence has one guess.  In the sequences whose u lies in
+    [0.2, 0.95] the draft row is random with the guess on top, and the target
+    row equals it except at the guess, whose logit is solved (by bisection on
+    the oracle's own probabilities) so that the ratio lands on its mark; the
+    other sequences keep their random rows.  Every placed decision must be
+    the one its offset fixes (accept above u, reject below), on the GPU and
+    in the oracle."""
+    rels = [-3e-3, -4e-4, -2e-4, -5e-5, -1e-5, 1e-5, 5e-5, 2e-4, 4e-4, 3e-3]
+    B, V, T = 96, 3000, 0.5
+    w = W.make_workload(_spec(vocab=V, batch=B, k=1, dtype="f32", temperature=T, top_k=top_k), gen_seed=21)
+    rng = np.random.default_rng(5)
+    target, draft, ids = w.target.copy(), w.draft.copy(), w.draft_ids.copy()
+    want = {}
+    for b in range(B):
+        u = oracle.uniform(w.seed, b, 0, 0, w.offset)
+        if not 0.2 <= u <= 0.95:
+            continue
+        mark = u * (1.0 + rels[len(want) % len(rels)])
+        want[b] = int(u < mark)
+        d = rng.normal(0.0, 1.0, V).astype(np.float32)
+        x = int(rng.integers(V))
+        d[x] = np.float32(d.max() + 1.0)  # the guess tops the draft row (kept by any top-k)
+        q = oracle.row_probs(d, "f32", T, top_k)[0][x]
+
+        def ratio(delta):
+            t = d.copy()
+            t[x] = np.float32(d[x] + delta)
+            return oracle.row_probs(t, "f32", T, top_k)[0][x] / q, t
+
+        lo, hi = -2.0, 1.0
+        assert ratio(lo)[0] < mark < ratio(hi)[0]
+        for _ in range(60):
+            mid = 0.5 * (lo + hi)
+            if ratio(mid)[0] < mark:
+                lo = mid
+            else:
+                hi = mid
+        (rl, tl), (rh, th) = ratio(lo), ratio(hi)
+        r, t = (rl, tl) if abs(rl - mark) < abs(rh - mark) else (rh, th)
+        assert abs(r / mark - 1.0) < 2e-6
+        target[int(w.cu_draft[b]) + b] = t
+        draft[int(w.cu_draft[b])] = d
+        ids[int(w.cu_draft[b])] = x
+    assert len(want) >= 3 * len(rels)
+    w = dataclasses.replace(w, target=target, draft=draft, draft_ids=ids)
+    o = _oracle(w)
+    g = gpu_sample(w)
+    for b, a in want.items():
+        assert int(o["num_accepted"][b]) == a, f"oracle, sequence {b}"
+        assert int(g["num_accepted"][b]) == a, f"GPU, sequence {b}"
+    rep = compare_sample(w, g, o)
+    note(f"accept near the uniform (top_k {top_k}, {len(want)} placed): {rep}")
+
+
 def test_strided_and_offset_rows():
     """Rows with a padded stride and a start offset (not 16-byte aligned)."""
     w = W.make_workload(_spec(vocab=2000, batch=5, k=3, dtype="bf16", top_k=40), gen_seed=8)
