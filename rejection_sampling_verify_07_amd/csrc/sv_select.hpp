@@ -281,13 +281,20 @@ __device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t 
 // C = ceil(nchunk / kSelWaves), kSpecChunks at a time with the first
 // kSpecSlots * 64 slots of each loaded at once (the first batch in flight
 // with the counts and bounds) and the rare slots past them kSpecExtra rounds
-// at a time, and compacts its survivors in chunk order into its own part of
-// the LDS list.  Region after region, that is the row's chunk order.  After
-// one barrier wave 0 runs the select over them.  Returns false (the same in
-// every wave), having written nothing, when a chunk overflowed or the
-// survivors do not fit the kept list.
+// at a time, and compacts its survivors in chunk order into an LDS region
+// of its own, which holds a whole kept list (survivors need not spread
+// evenly over the waves).  Region after region, that is the row's
+// chunk order.  After one barrier wave 0 runs the select over them.  Returns
+// false (the same in every wave), having written nothing, when a chunk
+// overflowed or the survivors do not fit the kept list.
 constexpr int kSelWaves = 4;
-constexpr int kSelRegion = kKeepCapList / kSelWaves;  // survivors a wave can hold
+constexpr int kSelRegion = kKeepCapList;  // survivors a wave can hold
+
+// Survivor regions of the speculative path (32 KB).
+struct SpecLds {
+    int32_t idx[kSelWaves * kSelRegion];
+    float val[kSelWaves * kSelRegion];
+};
 constexpr int kSpecChunks = 4;
 constexpr int kSpecSlots = 2;
 constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (512 slots: all of them)
@@ -296,7 +303,7 @@ constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (51
 // holds off[v + 1] - off[v] of them), in region order; n <= NJ * 64.
 template <int DT, int NJ>
 __device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
-                                                    KeptEntry* __restrict__ kept, WaveSelLds& L,
+                                                    KeptEntry* __restrict__ kept, WaveSelLds& L, const SpecLds& R,
                                                     const int32_t* off, int32_t n)
 {
     KeptEntry r[NJ];
@@ -307,9 +314,8 @@ __device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, 
 #pragma unroll
         for (int u = 1; u < kSelWaves; ++u)
             if (i >= off[u]) at = u * kSelRegion + (i - off[u]);
-        r[j] = i < n ? KeptEntry{L.kidx[at], L.kval[at]} : KeptEntry{INT32_MAX, neg_inf()};
+        r[j] = i < n ? KeptEntry{R.idx[at], R.val[at]} : KeptEntry{INT32_MAX, neg_inf()};
     }
-    __builtin_amdgcn_wave_barrier();
     select_tail_n<DT, NJ>(row, top_k, c, descs, kept, L, r);
 }
 
@@ -317,7 +323,7 @@ template <int DT>
 __device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
                                             const int32_t* __restrict__ counts, const float* __restrict__ bounds,
                                             const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
-                                            KeptEntry* __restrict__ kept, WaveSelLds& L, int32_t* s_wn)
+                                            KeptEntry* __restrict__ kept, WaveSelLds& L, SpecLds& R, int32_t* s_wn)
 {
     const int lane = lane_id();
     const int w = wave_id();
@@ -357,8 +363,8 @@ __device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t
         if (m != 0) {
             const int32_t pos = ns + lanes_below(m);
             if (pred && pos < kSelRegion) {
-                L.kidx[rbase + pos] = x.idx;
-                L.kval[rbase + pos] = x.val;
+                R.idx[rbase + pos] = x.idx;
+                R.val[rbase + pos] = x.val;
             }
             ns += (int32_t)__popcll(m);
         }
@@ -412,15 +418,15 @@ __device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t
     if (w != 0) return true;
     const int32_t nj = (tot + kWave - 1) / kWave;
     if (nj <= 1) {
-        select_from_regions<DT, 1>(row, top_k, c, descs, kept, L, off, tot);
+        select_from_regions<DT, 1>(row, top_k, c, descs, kept, L, R, off, tot);
     } else if (nj <= 2) {
-        select_from_regions<DT, 2>(row, top_k, c, descs, kept, L, off, tot);
+        select_from_regions<DT, 2>(row, top_k, c, descs, kept, L, R, off, tot);
     } else if (nj <= 4) {
-        select_from_regions<DT, 4>(row, top_k, c, descs, kept, L, off, tot);
+        select_from_regions<DT, 4>(row, top_k, c, descs, kept, L, R, off, tot);
     } else if (nj <= 8) {
-        select_from_regions<DT, 8>(row, top_k, c, descs, kept, L, off, tot);
+        select_from_regions<DT, 8>(row, top_k, c, descs, kept, L, R, off, tot);
     } else {
-        select_from_regions<DT, kSelPer>(row, top_k, c, descs, kept, L, off, tot);
+        select_from_regions<DT, kSelPer>(row, top_k, c, descs, kept, L, R, off, tot);
     }
     return true;
 }
@@ -577,9 +583,9 @@ __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, i
                                 int32_t cap, float c, const int32_t* __restrict__ counts,
                                 const float* __restrict__ bounds, const KeptEntry* __restrict__ cands,
                                 RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
-                                int32_t* s_choff, int32_t* s_wn)
+                                SpecLds& R, int32_t* s_choff, int32_t* s_wn)
 {
-    if (select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L, s_wn)) return;
+    if (select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L, R, s_wn)) return;
     if (wave_id() != 0) return;  // the paths below are one wave's
     // every wave has passed the barrier of the speculative path (or none has),
     // so wave 0 alone may reuse the LDS from here
@@ -615,9 +621,10 @@ __global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(Row
 {
     __shared__ WaveSelLds L;
     __shared__ int32_t s_choff[kMaxChunks + 1];
+    __shared__ SpecLds R;
     __shared__ int32_t s_wn[kSelWaves];
     select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L,
-                        s_choff, s_wn);
+                        R, s_choff, s_wn);
 }
 
 }  // namespace sv
