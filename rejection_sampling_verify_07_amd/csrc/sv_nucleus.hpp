@@ -613,8 +613,14 @@ struct NucStage {
 template <int DT>
 __device__ __forceinline__ uint32_t key16(float v)
 {
-    if constexpr (DT == DT_F16) return SelKey<DT_F16>::of(v);
-    else return order_key(v) >> 16;
+    if constexpr (DT == DT_F16) {
+        return SelKey<DT_F16>::of(v);
+    } else {
+        // order_key(v) >> 16, with the flip mask from an arithmetic shift
+        // (no compare and select: this runs once per block of the first read)
+        const uint32_t b = __float_as_uint(v);
+        return (b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u)) >> 16;
+    }
 }
 
 template <int DT, int NT>
@@ -716,14 +722,17 @@ struct Walk1 {
     {
         const int32_t G = 1 << lg_g;
         const int32_t jlo = r * U * NT, jhi = (r + 1) * U * NT;  // the round's blocks [jlo, jhi)
-        if (jlo * VEC < rb.mis || jhi * VEC > rb.mis + vocab) {
+        const bool edge = jlo * VEC < rb.mis || jhi * VEC > rb.mis + vocab;  // uniform
+        if (edge) {
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 fill_edge<DT>(raw[u], ((r * U + u) * NT + (int32_t)threadIdx.x) * VEC - rb.mis, vocab);
         }
         // one pass over the round: block maxima and the exp2 terms against
         // the reference the lane had before it (a term exceeds 1 when the
-        // round raises the maximum; the sum is rescaled below)
+        // round raises the maximum; the sum is rescaled below).  Logits are
+        // finite or -inf (the edge fill is -inf), so the maxima take v_max3
+        // on the values as they are, with no NaN quieting.
         const float ref = lref;
         float rm = neg_inf(), t = 0.0f;
 #pragma unroll
@@ -733,14 +742,16 @@ struct Walk1 {
             unpack<DT>(raw[u], f);
             float bm = f[0];
 #pragma unroll
-            for (int e = 1; e < VEC; ++e) bm = fmaxf(bm, f[e]);
-            rm = fmaxf(rm, bm);
+            for (int e = 1; e < VEC; e += 2) bm = max3_quiet(bm, f[e], e + 1 < VEC ? f[e + 1] : f[e]);
+            rm = max3_quiet(rm, bm, bm);
             uint32_t k = key16<DT>(bm);
-            for (int o = 1; o < G; o <<= 1) k = max(k, (uint32_t)__shfl_xor((int)k, o, kWave));
-            if (j < rb.nblk) {
-                if ((j & (G - 1)) == 0) gmax[j >> lg_g] = (uint16_t)k;
-                if ((j & ((1 << lg_s) - 1)) == 0) sub[j >> lg_s] = raw[u];
+            if (G == 1 && !edge) {
+                gmax[j] = (uint16_t)k;  // one block per group, every block of the round inside the row
+            } else {
+                for (int o = 1; o < G; o <<= 1) k = max(k, (uint32_t)__shfl_xor((int)k, o, kWave));
+                if (j < rb.nblk && (j & (G - 1)) == 0) gmax[j >> lg_g] = (uint16_t)k;
             }
+            if (j < rb.nblk && (j & ((1 << lg_s) - 1)) == 0) sub[j >> lg_s] = raw[u];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -ref));
         }
