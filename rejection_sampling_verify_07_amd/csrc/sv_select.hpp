@@ -1,4 +1,6 @@
-// Per-row top-k selection by one wave (64 threads, no workgroup barriers).
+// Per-row top-k selection, one workgroup of four waves per row: the four
+// waves share the speculative path's survivor pass (one barrier), and every
+// other step runs in one wave with no workgroup barrier.
 //
 // Input: the candidates the streaming pass wrote for each (row, chunk) (every
 // chunk element >= a lower bound of the row's tau, so the candidate set holds
@@ -8,11 +10,13 @@
 // set) and the kept list sorted by id, or kept = -1 ("full row masked by
 // tau") when the kept set is larger than the list capacity.
 //
-// Fast path (no chunk overflowed, top_k <= candidates <= kKeepCapList):
-// candidates go to registers (16 per lane), a ballot radix select over the
-// top key bits finds tau without LDS atomics, the kept entries are
-// compacted with ballots and sorted by id (a register bitonic network when
-// at most 64 are kept, an LDS network otherwise).
+// Speculative path (every row of a typical call): only candidates >= the
+// largest chunk bound can be kept; the four waves compact those survivors,
+// then a ballot radix select over the top key bits finds tau without LDS
+// atomics, and the kept entries are compacted with ballots, placed by rank
+// (at most 64) or sorted by id with a register bitonic network.
+// Chunk-list path (no chunk overflowed, top_k <= candidates <= kKeepCapList):
+// the same select over every candidate, found by position.
 // Exact path: the same radix select with one pass over the whole row per
 // 8-bit digit, then an ordered compaction of the row.
 #pragma once
