@@ -882,20 +882,19 @@ __device__ __forceinline__ void accept_one(const VerifyArgs& a, int32_t k, int32
     constexpr float kMargin = 1.0f / 4096.0f;
     const float uf = (float)u;  // exact: u has 24 bits
     int dec = -1;               // 1 accept, 0 reject, -1 undecided
-    if (!qin) {
-        dec = pin ? 1 : 0;  // ratio 1 when p > 0, else 0 (u >= 0 never passes)
-    } else if (!pin) {
-        dec = 0;
-    } else if (fabsf(at) <= 64.0f && fabsf(ad) <= 64.0f) {
+    if (!pin) {
+        dec = 0;  // p = 0: the ratio is 0 whatever q is, and u >= 0 never passes
+    } else if (qin && fabsf(at) <= 64.0f && fabsf(ad) <= 64.0f) {
         const float r32 = p32 / q32;
         if (r32 >= 1.0f + kMargin || uf < r32 * (1.0f - kMargin)) dec = 1;  // u < 1 <= p / q, or u clearly below
         else if (uf > r32 * (1.0f + kMargin)) dec = 0;
     }
     float pw = p32, qw = q32;
     if (dec < 0) {
+        // (q = 0 lands here too: the ratio is then 1 exactly when p > 0 in fp64)
         const double cd = (double)a.c;
-        const double p = exp2((double)lt * cd - (double)rt.mcc) / rt.s;
-        const double q = exp2((double)ld * cd - (double)rd.mcc) / rd.s;
+        const double p = pin ? exp2((double)lt * cd - (double)rt.mcc) / rt.s : 0.0;
+        const double q = qin ? exp2((double)ld * cd - (double)rd.mcc) / rd.s : 0.0;
         const double ratio = q > 0.0 ? fmin(1.0, p / q) : (p > 0.0 ? 1.0 : 0.0);
         dec = u < ratio ? 1 : 0;
         pw = (float)p;

@@ -276,6 +276,35 @@ def test_accept_ratio_near_the_uniform(top_k):
     note(f"accept near the uniform (top_k {top_k}, {len(want)} placed): {rep}")
 
 
+def test_guess_outside_both_supports_is_rejected():
+    """A guess whose target logit is -inf in a row with fewer finite logits
+    than top_k (so tau = -inf keeps it, with p = 0) and which the draft's
+    top-k drops (q = 0): the ratio is 0 and the guess must be rejected.  The
+    accept test's fp32 shortcut must not read "kept by the filter" as p > 0."""
+    V, K, B = 64, 2, 8
+    w = W.make_workload(_spec(vocab=V, batch=B, k=K, dtype="f32", temperature=1.0, top_k=50), gen_seed=31)
+    rng = np.random.default_rng(9)
+    target, draft, ids = w.target.copy(), w.draft.copy(), w.draft_ids.copy()
+    for b in range(B):
+        t0, d0 = int(w.cu_draft[b]) + b, int(w.cu_draft[b])
+        for k in range(K):
+            row_t = np.full(V, -np.inf, np.float32)
+            live = rng.choice(V, size=10, replace=False)
+            row_t[live] = rng.normal(0.0, 1.0, 10).astype(np.float32)  # 10 finite: tau = -inf
+            row_d = rng.normal(0.0, 1.0, V).astype(np.float32)
+            dead = [v for v in range(V) if v not in set(live.tolist())]
+            x = int(dead[b % len(dead)])
+            row_d[x] = np.float32(row_d.min() - 5.0)  # outside the draft's top 50: q(x) = 0
+            target[t0 + k], draft[d0 + k], ids[d0 + k] = row_t, row_d, x
+        target[t0 + K] = rng.normal(0.0, 1.0, V).astype(np.float32)
+    w = dataclasses.replace(w, target=target, draft=draft, draft_ids=ids)
+    o = _oracle(w)
+    g = gpu_sample(w)
+    assert np.all(o["num_accepted"] == 0)
+    assert np.all(g["num_accepted"] == 0)
+    compare_sample(w, g, o)
+
+
 def test_strided_and_offset_rows():
     """Rows with a padded stride and a start offset (not 16-byte aligned)."""
     w = W.make_workload(_spec(vocab=2000, batch=5, k=3, dtype="bf16", top_k=40), gen_seed=8)
