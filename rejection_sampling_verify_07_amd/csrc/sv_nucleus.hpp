@@ -684,8 +684,9 @@ __device__ __forceinline__ void fill_edge(u32x4& w, int32_t r0, int32_t vocab)
 }
 
 // Walk 1.  Per thread: the running maximum lm of its blocks and the sum, in
-// fp64, of exp2(fma(l, c, -fl32(lm c))) over them (fp32 terms per round of
-// U blocks, rescaled in fp64 when the maximum grows); per group of
+// fp64, of exp2(fma(l, c, -lref)) over them, lref = ceil(lm c) as of the
+// round that last raised lm (fp32 terms per round of U blocks, the fp64 sum
+// rescaled by a power of two when lref moves up); per group of
 // G = 2^lg_g blocks (G <= 64: adjacent lanes) its maximum's 16-bit key into
 // gmax; every 2^lg_s-th block into sub.  Block j of round r is
 // (r U + u) NT + tid.  Two rounds of loads are in flight: round r + 1 is
@@ -728,21 +729,20 @@ struct Walk1 {
             for (int u = 0; u < U; ++u)
                 fill_edge<DT>(raw[u], ((r * U + u) * NT + (int32_t)threadIdx.x) * VEC - rb.mis, vocab);
         }
-        // one pass over the round: block maxima and the exp2 terms against
-        // the reference the lane had before it (a term exceeds 1 when the
-        // round raises the maximum; the sum is rescaled below).  Logits are
-        // finite or -inf (the edge fill is -inf), so the maxima take v_max3
-        // on the values as they are, with no NaN quieting.
-        const float ref = lref;
-        float rm = neg_inf(), t = 0.0f;
+        // block maxima first (logits are finite or -inf, the edge fill is
+        // -inf, so v_max3 takes the values as they are, with no NaN
+        // quieting); a round that raises the lane's maximum moves the
+        // reference up first, an exact power-of-two rescale of the sum, so
+        // the round's terms are taken once, against the new reference
+        float rm = neg_inf();
+        float f[U][VEC];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int32_t j = (r * U + u) * NT + (int32_t)threadIdx.x;
-            float f[VEC];
-            unpack<DT>(raw[u], f);
-            float bm = f[0];
+            unpack<DT>(raw[u], f[u]);
+            float bm = f[u][0];
 #pragma unroll
-            for (int e = 1; e < VEC; e += 2) bm = max3_quiet(bm, f[e], e + 1 < VEC ? f[e + 1] : f[e]);
+            for (int e = 1; e < VEC; e += 2) bm = max3_quiet(bm, f[u][e], e + 1 < VEC ? f[u][e + 1] : f[u][e]);
             rm = max3_quiet(rm, bm, bm);
             uint32_t k = key16<DT>(bm);
             if (G == 1 && !edge) {
@@ -752,32 +752,21 @@ struct Walk1 {
                 if (j < rb.nblk && (j & (G - 1)) == 0) gmax[j >> lg_g] = (uint16_t)k;
             }
             if (j < rb.nblk && (j & ((1 << lg_s) - 1)) == 0) sub[j >> lg_s] = raw[u];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -ref));
         }
         if (rm > lm) {
             const float nref = ceilf(rm * c);
-            if (!(nref - ref <= 64.0f)) {
-                // no finite reference yet (ref = -inf), or a rise of more than
-                // 64 bits: the terms above are unusable, sum again against nref
-                t = 0.0f;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float f[VEC];
-                    unpack<DT>(raw[u], f);
-#pragma unroll
-                    for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[e], c, -nref));
-                }
-                // (a shift below -2000 leaves no double bits; the clamp keeps the cast defined)
-                ls = (lm == neg_inf() ? 0.0 : ldexp(ls, (int)fmaxf(ref - nref, -2000.0f))) + (double)t;
-            } else {
-                ls = ldexp(ls + (double)t, (int)(ref - nref));
-            }
+            // (no finite reference yet: nothing to rescale; a shift below
+            // -2000 leaves no double bits, and the clamp keeps the cast defined)
+            ls = lm == neg_inf() ? 0.0 : ldexp(ls, (int)fmaxf(lref - nref, -2000.0f));
             lm = rm;
             lref = nref;
-        } else if (lm != neg_inf()) {
-            ls += (double)t;
         }
+        float t = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) t += __builtin_amdgcn_exp2f(__builtin_fmaf(f[u][e], c, -lref));
+        if (lm != neg_inf()) ls += (double)t;  // (with lm = -inf every term is NaN: there is nothing to add)
     }
 
     // every load is issued unconditionally (rounds past the row reload its
