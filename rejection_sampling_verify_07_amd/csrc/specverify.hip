@@ -25,6 +25,7 @@ static_assert(SV_MAX_VOCAB == sv::kMaxSeg * sv::kSeg, "vocab limit mismatch");
 static_assert(sv::kKeepCap == sv::kKeepCapList, "kept-list capacity mismatch");
 // the per-row top-p kernel groups a row's 16-byte blocks by at most 64 (adjacent lanes)
 static_assert((int64_t)sv::kNucGroups * 64 >= SV_MAX_VOCAB / 4 + 2, "top-p block groups too small for the largest row");
+static_assert((int64_t)sv::NucRowSize<true>::kGroups * 64 >= SV_MAX_VOCAB / 4 + 2, "top-p block groups too small for the largest row");
 
 namespace {
 
@@ -353,8 +354,13 @@ sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs,
         // reads every row, so it is the timed streaming pass)
         const sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p,
                              ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};
-        launch_stream_nt(prof, sv::nucleus_row_kernel<DT, sv::kNucRowThreads>, (uint32_t)p.rows,
-                         (uint32_t)sv::kNucRowThreads, stream, na);
+        // (+1: a row that starts inside a block covers one more)
+        if ((int64_t)sh->vocab <= (int64_t)(sv::kNucSmallBlocks - 1) * sv::Dt<DT>::kVec)
+            launch_stream_nt(prof, sv::nucleus_row_kernel<DT, sv::kNucRowThreads, true>, (uint32_t)p.rows,
+                             (uint32_t)sv::kNucRowThreads, stream, na);
+        else
+            launch_stream_nt(prof, sv::nucleus_row_kernel<DT, sv::kNucRowThreads, false>, (uint32_t)p.rows,
+                             (uint32_t)sv::kNucRowThreads, stream, na);
         va.descs = na.descs;
         va.kept = na.kept;
         return launch_status();

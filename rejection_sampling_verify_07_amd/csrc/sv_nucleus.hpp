@@ -550,7 +550,8 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
 
 // ---------------------------------------------------------------------------
 // Full rows with no top-k: statistics and cut in one kernel, one row per
-// workgroup of kNucRowThreads threads (two per CU).
+// workgroup of kNucRowThreads threads (two per CU; three for rows of at most
+// kNucSmallBlocks blocks, with the smaller LDS layout).
 //
 //  1. One read of the row (from HBM): the maximum m and S = sum of
 //     exp2(fma(l, c, -fl32(m c))), the maximum of every group of G 16-byte
@@ -573,10 +574,20 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
 // ---------------------------------------------------------------------------
 constexpr int kNucRowThreads = 512;
 constexpr int kNucRowUnroll = 4;        // 16-byte loads per thread per round of the first read (two in flight)
+constexpr int kNucRowUnrollSmall = 2;   // ... in the smaller layout (fewer registers: six waves per SIMD)
 constexpr int kNucHitUnroll = 8;        // ... in the re-read of the groups that reach l_low
 constexpr int kNucListUnroll = 4;       // ... in the exact path and the kept-list walk
 constexpr int kNucGroups = 16384;       // group-maximum slots (16-bit keys)
 constexpr int kNucStageBytes = 32768;   // staged keys: 16 bits (16-bit types) or 32 bits (fp32)
+// Rows of at most kNucSmallBlocks 16-byte blocks take a smaller LDS layout
+// (8192 group slots, a 20 KB stage: about 50 KB in all), so that three
+// workgroups share a CU instead of two; any row size is still correct there.
+constexpr int kNucSmallBlocks = 8190;
+template <bool SMALL>
+struct NucRowSize {
+    static constexpr int kGroups = SMALL ? 8192 : kNucGroups;
+    static constexpr int kStageBytes = SMALL ? 20480 : kNucStageBytes;
+};
 constexpr int kNucSubMax = 1024;        // subsample blocks kept in LDS
 constexpr int kNucSubStrideMin = 16;    // the subsample takes at most every 16th block
 // The predicted cut leaves this share of the estimated tail mass (1 - top_p)
@@ -585,10 +596,10 @@ constexpr int kNucSubStrideMin = 16;    // the subsample takes at most every 16t
 constexpr double kNucTailKeep = 0.75;
 constexpr double kNucStageFill = 0.7;
 
-template <int DT>
+template <int DT, int STAGE_BYTES>
 struct NucStage {
     using T = typename std::conditional<Dt<DT>::kSize == 2, uint16_t, uint32_t>::type;
-    static constexpr int kCap = kNucStageBytes / (int)sizeof(T);
+    static constexpr int kCap = STAGE_BYTES / (int)sizeof(T);
     // a logit is staged as its raw bits: element e of a 16-byte block
     __device__ __forceinline__ static T raw(const u32x4& w, int e)
     {
@@ -623,10 +634,12 @@ __device__ __forceinline__ uint32_t key16(float v)
     }
 }
 
-template <int DT, int NT>
+template <int DT, int NT, bool SMALL>
 struct NucRowLds {
+    using Sz = NucRowSize<SMALL>;
+    using St = NucStage<DT, Sz::kStageBytes>;
     union {
-        uint16_t gmax[kNucGroups];  // walks 1-3: group maxima, then each wave's hit list
+        uint16_t gmax[Sz::kGroups];  // walks 1-3: group maxima, then each wave's hit list
         struct {
             uint32_t ck[kNucCap];   // step 4: the crossing bucket's entries
             uint64_t cw[kNucCap];
@@ -635,7 +648,7 @@ struct NucRowLds {
     } a;
     union {
         u32x4 sub[kNucSubMax];                                  // walks 1-2: the subsample
-        typename NucStage<DT>::T stage[NucStage<DT>::kCap];    // walk 3 on: the staged keys
+        typename St::T stage[St::kCap];  // walk 3 on: the staged keys
     } b;
     uint64_t hist[256];
     uint64_t hstage[256];  // the staged logits' fixed-point weights per log-weight bucket
@@ -788,29 +801,31 @@ struct Walk1 {
     }
 };
 
-template <int DT, int NT>
-__global__ __launch_bounds__(NT) void nucleus_row_kernel(NucArgs a)
+template <int DT, int NT, bool SMALL>
+__global__ __launch_bounds__(NT, SMALL ? 6 : 1) void nucleus_row_kernel(NucArgs a)
 {
     constexpr int VEC = Dt<DT>::kVec;
     constexpr int LOW = Dt<DT>::kSize == 2 ? 16 : 0;
     constexpr int NW = NT / kWave;
-    constexpr int U = kNucRowUnroll;
+    constexpr int U = SMALL ? kNucRowUnrollSmall : kNucRowUnroll;
     constexpr int UH = kNucHitUnroll;
     constexpr int UL = kNucListUnroll;
-    using St = NucStage<DT>;
+    using Lds = NucRowLds<DT, NT, SMALL>;
+    using St = typename Lds::St;
     constexpr int SLICE = St::kCap / NW;  // stage entries per wave
-    __shared__ NucRowLds<DT, NT> S;
+    static_assert(St::kCap % NW == 0, "stage slices");
+    __shared__ Lds S;
     const int32_t row = blockIdx.x;
     const char* rowp = row_ptr(a.rs, row);
     const RowBlocks<DT> rb(rowp, a.vocab);
     const float c = a.c;
     const int lane = lane_id(), wv = wave_id();
     for (int i = threadIdx.x; i < kNucBuckets; i += NT) S.hstage[i] = 0;  // (published by walk 1's barriers)
-    // group size G = 2^lg_g: the smallest with nblk / G <= kNucGroups (G <= 64
+    // group size G = 2^lg_g: the smallest with nblk / G <= the group slots (G <= 64
     // for any row the ABI takes); subsample stride 2^lg_s: the smallest
     // >= kNucSubStrideMin with nblk / stride <= kNucSubMax
     int lg_g = 0, lg_s = 0;
-    while (((int64_t)1 << lg_g) * kNucGroups < rb.nblk) ++lg_g;
+    while (((int64_t)1 << lg_g) * Lds::Sz::kGroups < rb.nblk) ++lg_g;
     while ((1 << lg_s) < kNucSubStrideMin || ((int64_t)1 << lg_s) * kNucSubMax < rb.nblk) ++lg_s;
     const int32_t G = 1 << lg_g;
     const int32_t ngroups = (rb.nblk + G - 1) >> lg_g;
