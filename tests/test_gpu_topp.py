@@ -112,6 +112,14 @@ EDGE = {
     # the cut falls in a bucket of 3000 tied logits: more crossing entries
     # than the per-wave regions hold (the radix then runs over the staged set)
     "crossing_bucket_of_3000_ties": (_spec(vocab=30000), lambda x: _tied_crossing(x)),
+    # the per-row kernel's two LDS layouts meet at rows of 8190 16-byte blocks
+    # (one more for a row that starts inside a block): the largest rows of the
+    # smaller layout and the smallest of the larger one, aligned and not
+    "small_layout_largest_bf16": (_spec(vocab=65512, batch=2), None),
+    "small_layout_misaligned_bf16": (_spec(vocab=65511, batch=2), None),
+    "large_layout_smallest_bf16": (_spec(vocab=65513, batch=2), None),
+    "small_layout_largest_f32": (_spec(vocab=32756, batch=2, dtype="f32"), None),
+    "large_layout_smallest_f32": (_spec(vocab=32757, batch=2, dtype="f32"), None),
 }
 
 
