@@ -331,8 +331,14 @@ sv_status_t run_stats_topk(const sv_shape_t* sh, const Plan& p, const sv::RowSet
         }
         if (launch_status() != SV_OK) return SV_ERR_HIP;
         // one workgroup per row; rows whose chunks overflowed take the exact path inside
-        hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT>), dim3(p.rows), dim3(sv::kSelWaves * sv::kWave), 0, stream, rs,
-                           sh->vocab, p.nchunk, top_k, kCandCap, c, counts, bounds, cands, descs, kept);
+        if (p.topp)
+            hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT, true>), dim3(p.rows), dim3(sv::kSelWaves * sv::kWave), 0,
+                               stream, rs, sh->vocab, p.nchunk, top_k, kCandCap, c, p.top_p, counts, bounds, cands, descs,
+                               kept);
+        else
+            hipLaunchKernelGGL((sv::topk_select_wave_kernel<DT, false>), dim3(p.rows), dim3(sv::kSelWaves * sv::kWave), 0,
+                               stream, rs, sh->vocab, p.nchunk, top_k, kCandCap, c, 1.0f, counts, bounds, cands, descs,
+                               kept);
     } else {
         hipLaunchKernelGGL((sv::topk_select_kernel<DT>), dim3(p.rows), dim3(sv::kThreads), 0, stream, rs, sh->vocab,
                            top_k, c, (int32_t)sv::kKeepCap, descs, kept);

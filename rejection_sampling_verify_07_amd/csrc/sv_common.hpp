@@ -430,9 +430,11 @@ struct RowDesc {
     float mcc;      // fl32(m * c), c = log2(e) / T in fp32
     int32_t kept;   // >= 0: number of entries in the row's kept list; -1: full row masked by tau
     double s;       // sum over kept v of exp2(fl32(l_v * c - mcc))
-    int32_t flags;  // bit 0: candidate overflow took the exact full-row path
+    int32_t flags;  // bit 0: candidate overflow took the exact full-row path; bit 1 (kDescTopP): top-p applied
     int32_t pad;
 };
+
+constexpr int32_t kDescTopP = 2;  // RowDesc.flags: the select already narrowed the kept set by top-p
 
 struct KeptEntry {
     int32_t idx;

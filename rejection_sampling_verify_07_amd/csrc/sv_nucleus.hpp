@@ -537,6 +537,7 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
     if (threadIdx.x == 0) s_desc = a.descs[row];
     __syncthreads();
     const RowDesc d = s_desc;
+    if (d.flags & kDescTopP) return;  // the select narrowed this row's kept list already
     if (!(d.s > 0.0)) {  // no finite kept logit: the consumers report the row
         if (threadIdx.x == 0) a.descs[row] = d;
         return;

@@ -149,7 +149,7 @@ __device__ __forceinline__ double sort_write_kept(WaveSelLds& L, int32_t nk, Kep
 // NJ is a template argument so that every per-slot loop is unrolled without
 // branches; select_tail picks the smallest NJ that holds the candidates.
 template <int DT, int NJ>
-__device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+__device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float c, float top_p, RowDesc* __restrict__ descs,
                               KeptEntry* __restrict__ kept, WaveSelLds& L, const KeptEntry* e)
 {
     using K = SelKey<DT>;
@@ -167,6 +167,43 @@ __device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float 
 #pragma unroll
         for (int j = 0; j < NJ; ++j) cnt += (int)__popcll(__ballot(key[j] >= cand));
         h = cnt >= top_k ? cand : h;
+    }
+
+    // top-p after top-k: among the top-k set (key >= h), the largest key hp
+    // whose entries at or above it hold top_p of the set's mass, by the same
+    // bitwise search, fp32 weights and fp64 wave sums as the kept-list path
+    // of the nucleus kernel (which then leaves the row alone).  The row's
+    // maximum stays kept, so its reference mcc is the top-k set's.  A set
+    // with no finite logit is left unfiltered, for the consumers to report.
+    bool nucleus = false;
+    float m0 = neg_inf();
+    if (top_p < 1.0f) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (key[j] >= h && e[j].idx != INT32_MAX) m0 = fmaxf(m0, e[j].val);
+        m0 = wave_max_dpp(m0);
+        nucleus = m0 != neg_inf();
+    }
+    if (nucleus) {
+        const float mcc0 = m0 * c;
+        float w[NJ];
+        double s0 = 0.0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            w[j] = (key[j] >= h && e[j].idx != INT32_MAX) ? __builtin_amdgcn_exp2f(__builtin_fmaf(e[j].val, c, -mcc0))
+                                                          : 0.0f;
+            s0 += (double)w[j];
+        }
+        const double target = (double)top_p * wave_sum_dpp(s0);
+        uint32_t hp = 0;
+        for (int bit = K::kBits - 1; bit >= 0; --bit) {
+            const uint32_t cand = hp | (1u << bit);
+            double ls = 0.0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ls += key[j] >= cand ? (double)w[j] : 0.0;
+            if (wave_sum_dpp(ls) >= target) hp = cand;
+        }
+        h = hp;  // >= the top-k h: the whole set's mass reaches the target
     }
 
     // kept entries (key >= h), compacted in candidate order
@@ -226,7 +263,7 @@ __device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float 
         d.mcc = mcc;
         d.kept = nk;
         d.s = ls;
-        d.flags = 0;
+        d.flags = nucleus ? kDescTopP : 0;
         d.pad = 0;
         descs[row] = d;
     }
@@ -234,19 +271,19 @@ __device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float 
 
 // e[0 .. nj) hold the candidates (nj wave-uniform, at most kSelPer).
 template <int DT>
-__device__ void select_tail(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+__device__ void select_tail(int32_t row, int32_t top_k, float c, float top_p, RowDesc* __restrict__ descs,
                             KeptEntry* __restrict__ kept, WaveSelLds& L, const KeptEntry* e, int32_t nj)
 {
     if (nj <= 1) {
-        select_tail_n<DT, 1>(row, top_k, c, descs, kept, L, e);
+        select_tail_n<DT, 1>(row, top_k, c, top_p, descs, kept, L, e);
     } else if (nj <= 2) {
-        select_tail_n<DT, 2>(row, top_k, c, descs, kept, L, e);
+        select_tail_n<DT, 2>(row, top_k, c, top_p, descs, kept, L, e);
     } else if (nj <= 4) {
-        select_tail_n<DT, 4>(row, top_k, c, descs, kept, L, e);
+        select_tail_n<DT, 4>(row, top_k, c, top_p, descs, kept, L, e);
     } else if (nj <= 8) {
-        select_tail_n<DT, 8>(row, top_k, c, descs, kept, L, e);
+        select_tail_n<DT, 8>(row, top_k, c, top_p, descs, kept, L, e);
     } else {
-        select_tail_n<DT, kSelPer>(row, top_k, c, descs, kept, L, e);
+        select_tail_n<DT, kSelPer>(row, top_k, c, top_p, descs, kept, L, e);
     }
 }
 
@@ -254,7 +291,7 @@ __device__ void select_tail(int32_t row, int32_t top_k, float c, RowDesc* __rest
 // each, choff their exclusive prefix sums (in LDS); candidate i is found by a
 // binary search over choff.
 template <int DT>
-__device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+__device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c, float top_p,
                                  const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
                                  KeptEntry* __restrict__ kept, WaveSelLds& L, const int32_t* choff, int32_t total)
 {
@@ -274,7 +311,7 @@ __device__ __attribute__((noinline)) void wave_select_fast(int32_t row, int32_t 
             e[j] = cands[((int64_t)row * nchunk + lo) * cap + (i - choff[lo])];
         }
     }
-    select_tail<DT>(row, top_k, c, descs, kept, L, e, nj);
+    select_tail<DT>(row, top_k, c, top_p, descs, kept, L, e, nj);
 }
 
 // Speculative path, kSelWaves waves per row.  Every chunk bound is a lower
@@ -306,7 +343,7 @@ constexpr int kSpecExtra = 6;  // slot rounds past kSpecSlots loaded at once (51
 // The select over the n survivors held in the waves' LDS regions (region v
 // holds off[v + 1] - off[v] of them), in region order; n <= NJ * 64.
 template <int DT, int NJ>
-__device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, float c, RowDesc* __restrict__ descs,
+__device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, float c, float top_p, RowDesc* __restrict__ descs,
                                                     KeptEntry* __restrict__ kept, WaveSelLds& L, const SpecLds& R,
                                                     const int32_t* off, int32_t n)
 {
@@ -320,11 +357,11 @@ __device__ __forceinline__ void select_from_regions(int32_t row, int32_t top_k, 
             if (i >= off[u]) at = u * kSelRegion + (i - off[u]);
         r[j] = i < n ? KeptEntry{R.idx[at], R.val[at]} : KeptEntry{INT32_MAX, neg_inf()};
     }
-    select_tail_n<DT, NJ>(row, top_k, c, descs, kept, L, r);
+    select_tail_n<DT, NJ>(row, top_k, c, top_p, descs, kept, L, r);
 }
 
 template <int DT>
-__device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c,
+__device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t top_k, int32_t cap, float c, float top_p,
                                             const int32_t* __restrict__ counts, const float* __restrict__ bounds,
                                             const KeptEntry* __restrict__ cands, RowDesc* __restrict__ descs,
                                             KeptEntry* __restrict__ kept, WaveSelLds& L, SpecLds& R, int32_t* s_wn)
@@ -422,15 +459,15 @@ __device__ __forceinline__ bool select_spec(int32_t row, int32_t nchunk, int32_t
     if (w != 0) return true;
     const int32_t nj = (tot + kWave - 1) / kWave;
     if (nj <= 1) {
-        select_from_regions<DT, 1>(row, top_k, c, descs, kept, L, R, off, tot);
+        select_from_regions<DT, 1>(row, top_k, c, top_p, descs, kept, L, R, off, tot);
     } else if (nj <= 2) {
-        select_from_regions<DT, 2>(row, top_k, c, descs, kept, L, R, off, tot);
+        select_from_regions<DT, 2>(row, top_k, c, top_p, descs, kept, L, R, off, tot);
     } else if (nj <= 4) {
-        select_from_regions<DT, 4>(row, top_k, c, descs, kept, L, R, off, tot);
+        select_from_regions<DT, 4>(row, top_k, c, top_p, descs, kept, L, R, off, tot);
     } else if (nj <= 8) {
-        select_from_regions<DT, 8>(row, top_k, c, descs, kept, L, R, off, tot);
+        select_from_regions<DT, 8>(row, top_k, c, top_p, descs, kept, L, R, off, tot);
     } else {
-        select_from_regions<DT, kSelPer>(row, top_k, c, descs, kept, L, R, off, tot);
+        select_from_regions<DT, kSelPer>(row, top_k, c, top_p, descs, kept, L, R, off, tot);
     }
     return true;
 }
@@ -584,12 +621,12 @@ __device__ __attribute__((noinline)) void wave_select_exact(int32_t row, const c
 // chunk-list path, else the exact path over the full row.
 template <int DT>
 __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, int32_t vocab, int32_t nchunk, int32_t top_k,
-                                int32_t cap, float c, const int32_t* __restrict__ counts,
+                                int32_t cap, float c, float top_p, const int32_t* __restrict__ counts,
                                 const float* __restrict__ bounds, const KeptEntry* __restrict__ cands,
                                 RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
                                 SpecLds& R, int32_t* s_choff, int32_t* s_wn)
 {
-    if (select_spec<DT>(row, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L, R, s_wn)) return;
+    if (select_spec<DT>(row, nchunk, top_k, cap, c, top_p, counts, bounds, cands, descs, kept, L, R, s_wn)) return;
     if (wave_id() != 0) return;  // the paths below are one wave's
     // every wave has passed the barrier of the speculative path (or none has),
     // so wave 0 alone may reuse the LDS from here
@@ -606,17 +643,18 @@ __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, i
     if (lane_id() == 0) s_choff[nchunk] = base;
     __builtin_amdgcn_wave_barrier();
     if (__ballot(bad != 0) == 0 && base >= top_k && base <= kKeepCapList) {
-        wave_select_fast<DT>(row, nchunk, top_k, cap, c, cands, descs, kept, L, s_choff, base);
+        wave_select_fast<DT>(row, nchunk, top_k, cap, c, top_p, cands, descs, kept, L, s_choff, base);
         return;
     }
     wave_select_exact<DT>(row, row_ptr(rs, row), vocab, top_k, c, descs, kept, L);
 }
 
 // One workgroup of kSelWaves waves per row, over the candidates of the top-k
-// streaming pass.
-template <int DT>
+// streaming pass.  TOPP: top_p < 1 narrows the kept sets it writes (without
+// it the top-p code is compiled out).
+template <int DT, bool TOPP>
 __global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
-                                                                 int32_t top_k, int32_t cap, float c,
+                                                                 int32_t top_k, int32_t cap, float c, float top_p,
                                                                  const int32_t* __restrict__ counts,
                                                                  const float* __restrict__ bounds,
                                                                  const KeptEntry* __restrict__ cands,
@@ -627,8 +665,8 @@ __global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(Row
     __shared__ int32_t s_choff[kMaxChunks + 1];
     __shared__ SpecLds R;
     __shared__ int32_t s_wn[kSelWaves];
-    select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, counts, bounds, cands, descs, kept, L,
-                        R, s_choff, s_wn);
+    select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, TOPP ? top_p : 1.0f, counts, bounds, cands,
+                        descs, kept, L, R, s_choff, s_wn);
 }
 
 }  // namespace sv
