@@ -527,7 +527,8 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
 }
 
 // Top-k rows narrowed by top-p: the select's descriptor and kept list in,
-// the nucleus's out.
+// the nucleus's out.  Rows the select has narrowed already (kDescTopP) are
+// left as they are; the rest come from the select's exact paths.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
 {

@@ -17,6 +17,9 @@
 // (at most 64) or sorted by id with a register bitonic network.
 // Chunk-list path (no chunk overflowed, top_k <= candidates <= kKeepCapList):
 // the same select over every candidate, found by position.
+// With top-p (top_p < 1) both paths also narrow the top-k set to its nucleus
+// before writing it, and mark the descriptor (kDescTopP) so that the nucleus
+// kernel leaves the row alone.
 // Exact path: the same radix select with one pass over the whole row per
 // 8-bit digit, then an ordered compaction of the row.
 #pragma once
