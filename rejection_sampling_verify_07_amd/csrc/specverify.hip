@@ -372,7 +372,8 @@ sv_status_t run_stats(const sv_shape_t* sh, const Plan& p, const sv::RowSet& rs,
         return launch_status();
     }
     if (run_stats_topk<DT>(sh, p, rs, c, ws, stream, va, prof) != SV_OK) return SV_ERR_HIP;
-    if (!p.topp) return SV_OK;
+    // (the candidate path's select narrows its rows by top-p itself)
+    if (!p.topp || p.mode == PLAN_TOPK_FAST) return SV_OK;
     // a top-k row's kept list (or a kept set that outgrew it) narrowed by top-p
     const sv::NucArgs na{rs, sh->vocab, p.rows, c, p.top_p,
                          ws_at<sv::RowDesc>(ws, p.off_descs), ws_at<sv::KeptEntry>(ws, p.off_kept)};

@@ -526,21 +526,27 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
     nucleus_write_list<DT, NT, U>(a, row, d, tau_p, S.w, S.d);
 }
 
-// Top-k rows narrowed by top-p: the select's descriptor and kept list in,
-// the nucleus's out.  Rows the select has narrowed already (kDescTopP) are
-// left as they are; the rest come from the select's exact paths.
+// A top-k row narrowed by top-p: the select's descriptor and kept list in,
+// the nucleus's out, by kThreads threads.  A row the select has narrowed
+// already (kDescTopP) is left as it is.  Out of line: inside the select
+// kernel it serves only the rows of its exact path, and inlined it would
+// raise the registers of every path there.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
+__device__ __attribute__((noinline)) void nucleus_topk_row(const RowSet& rs, int32_t vocab, float c, float top_p,
+                                                           RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept,
+                                                           int32_t row, void* lds)
 {
-    __shared__ NucLds<kThreads> s_nuc;
+    static_assert(sizeof(NucLds<kThreads>) <= sizeof(SpecLds) && kSelWaves * kWave == kThreads,
+                  "the select kernel's LDS holds the nucleus's");
+    NucLds<kThreads>& s_nuc = *static_cast<NucLds<kThreads>*>(lds);
     __shared__ RowDesc s_desc;
-    const int32_t row = blockIdx.x;
-    if (threadIdx.x == 0) s_desc = a.descs[row];
+    const NucArgs a{rs, vocab, 0, c, top_p, descs, kept};
+    if (threadIdx.x == 0) s_desc = descs[row];
     __syncthreads();
     const RowDesc d = s_desc;
-    if (d.flags & kDescTopP) return;  // the select narrowed this row's kept list already
+    if (d.flags & kDescTopP) return;
     if (!(d.s > 0.0)) {  // no finite kept logit: the consumers report the row
-        if (threadIdx.x == 0) a.descs[row] = d;
+        if (threadIdx.x == 0) descs[row] = d;
         return;
     }
     if (d.kept >= 0) {
@@ -548,6 +554,14 @@ __global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
     } else {
         nucleus_full<DT, kThreads, kRowUnroll>(a, row, d, s_nuc);
     }
+}
+
+// Top-k rows from the workgroup-per-row exact select, narrowed by top-p.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void nucleus_kernel(NucArgs a)
+{
+    __shared__ SpecLds s_lds;
+    nucleus_topk_row<DT>(a.rs, a.vocab, a.c, a.top_p, a.descs, a.kept, (int32_t)blockIdx.x, &s_lds);
 }
 
 // ---------------------------------------------------------------------------

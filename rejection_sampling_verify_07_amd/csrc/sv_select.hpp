@@ -198,15 +198,21 @@ __device__ __forceinline__ void select_tail_n(int32_t row, int32_t top_k, float 
             s0 += (double)w[j];
         }
         const double target = (double)top_p * wave_sum_dpp(s0);
-        uint32_t hp = 0;
-        for (int bit = K::kBits - 1; bit >= 0; --bit) {
-            const uint32_t cand = hp | (1u << bit);
-            double ls = 0.0;
+        // the cut lies in [h, key of the maximum]: the bits above the highest
+        // one where those two differ are the cut's too
+        const uint32_t kmax = K::of(m0);
+        if (kmax != h) {
+            const int top = 31 - __builtin_clz(kmax ^ h);
+            uint32_t hp = h & ~((2u << top) - 1u);
+            for (int bit = top; bit >= 0; --bit) {
+                const uint32_t cand = hp | (1u << bit);
+                double ls = 0.0;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) ls += key[j] >= cand ? (double)w[j] : 0.0;
-            if (wave_sum_dpp(ls) >= target) hp = cand;
+                for (int j = 0; j < NJ; ++j) ls += key[j] >= cand ? (double)w[j] : 0.0;
+                if (wave_sum_dpp(ls) >= target) hp = cand;
+            }
+            h = hp;  // >= the top-k h: the whole set's mass reaches the target
         }
-        h = hp;  // >= the top-k h: the whole set's mass reaches the target
     }
 
     // kept entries (key >= h), compacted in candidate order
@@ -335,7 +341,7 @@ constexpr int kSelWaves = 4;
 constexpr int kSelRegion = kKeepCapList;  // survivors a wave can hold
 
 // Survivor regions of the speculative path (32 KB).
-struct SpecLds {
+struct alignas(16) SpecLds {
     int32_t idx[kSelWaves * kSelRegion];
     float val[kSelWaves * kSelRegion];
 };
@@ -621,16 +627,18 @@ __device__ __attribute__((noinline)) void wave_select_exact(int32_t row, const c
 }
 
 // The select of one row by one wave: the speculative path, else the
-// chunk-list path, else the exact path over the full row.
+// chunk-list path, else the exact path over the full row.  Returns true (in
+// every wave) when the speculative path wrote the row; false when wave 0
+// took one of the others (the other waves return at once).
 template <int DT>
-__device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, int32_t vocab, int32_t nchunk, int32_t top_k,
+__device__ __forceinline__ bool select_row_wave(const RowSet& rs, int32_t row, int32_t vocab, int32_t nchunk, int32_t top_k,
                                 int32_t cap, float c, float top_p, const int32_t* __restrict__ counts,
                                 const float* __restrict__ bounds, const KeptEntry* __restrict__ cands,
                                 RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept, WaveSelLds& L,
                                 SpecLds& R, int32_t* s_choff, int32_t* s_wn)
 {
-    if (select_spec<DT>(row, nchunk, top_k, cap, c, top_p, counts, bounds, cands, descs, kept, L, R, s_wn)) return;
-    if (wave_id() != 0) return;  // the paths below are one wave's
+    if (select_spec<DT>(row, nchunk, top_k, cap, c, top_p, counts, bounds, cands, descs, kept, L, R, s_wn)) return true;
+    if (wave_id() != 0) return false;  // the paths below are one wave's
     // every wave has passed the barrier of the speculative path (or none has),
     // so wave 0 alone may reuse the LDS from here
     int32_t base = 0, bad = 0;
@@ -647,14 +655,25 @@ __device__ __forceinline__ void select_row_wave(const RowSet& rs, int32_t row, i
     __builtin_amdgcn_wave_barrier();
     if (__ballot(bad != 0) == 0 && base >= top_k && base <= kKeepCapList) {
         wave_select_fast<DT>(row, nchunk, top_k, cap, c, top_p, cands, descs, kept, L, s_choff, base);
-        return;
+        return false;
     }
     wave_select_exact<DT>(row, row_ptr(rs, row), vocab, top_k, c, descs, kept, L);
+    return false;
 }
+
+// The top-p narrowing of one top-k row by kThreads threads (the nucleus
+// kernel's per-row steps; defined with them).  lds: at least the nucleus's
+// LDS, 16-byte aligned.
+template <int DT>
+__device__ __attribute__((noinline)) void nucleus_topk_row(const RowSet& rs, int32_t vocab, float c, float top_p,
+                                                           RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept,
+                                                           int32_t row, void* lds);
 
 // One workgroup of kSelWaves waves per row, over the candidates of the top-k
 // streaming pass.  TOPP: top_p < 1 narrows the kept sets it writes (without
-// it the top-p code is compiled out).
+// it the top-p code is compiled out): the speculative and chunk-list paths
+// do it on the set in registers; a row the exact path wrote is narrowed
+// after it by the whole workgroup, in the speculative path's LDS.
 template <int DT, bool TOPP>
 __global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(RowSet rs, int32_t vocab, int32_t nchunk,
                                                                  int32_t top_k, int32_t cap, float c, float top_p,
@@ -668,8 +687,13 @@ __global__ __launch_bounds__(kSelWaves * kWave) void topk_select_wave_kernel(Row
     __shared__ int32_t s_choff[kMaxChunks + 1];
     __shared__ SpecLds R;
     __shared__ int32_t s_wn[kSelWaves];
-    select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, TOPP ? top_p : 1.0f, counts, bounds, cands,
-                        descs, kept, L, R, s_choff, s_wn);
+    const bool spec = select_row_wave<DT>(rs, (int32_t)blockIdx.x, vocab, nchunk, top_k, cap, c, TOPP ? top_p : 1.0f,
+                                          counts, bounds, cands, descs, kept, L, R, s_choff, s_wn);
+    if constexpr (TOPP) {
+        if (spec) return;  // (the same in every wave)
+        __syncthreads();   // wave 0's descriptor and kept list are written
+        nucleus_topk_row<DT>(rs, vocab, c, top_p, descs, kept, (int32_t)blockIdx.x, &R);
+    }
 }
 
 }  // namespace sv
