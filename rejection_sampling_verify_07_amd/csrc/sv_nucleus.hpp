@@ -530,9 +530,10 @@ __device__ void nucleus_full(const NucArgs& a, int32_t row, const RowDesc& d, Nu
 // the nucleus's out, by kThreads threads.  A row the select has narrowed
 // already (kDescTopP) is left as it is.  Out of line: inside the select
 // kernel it serves only the rows of its exact path, and inlined it would
-// raise the registers of every path there.
+// raise the registers of every path there.  The row set comes by value: by
+// reference, the select kernel stored it to scratch at every launch.
 template <int DT>
-__device__ __attribute__((noinline)) void nucleus_topk_row(const RowSet& rs, int32_t vocab, float c, float top_p,
+__device__ __attribute__((noinline)) void nucleus_topk_row(RowSet rs, int32_t vocab, float c, float top_p,
                                                            RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept,
                                                            int32_t row, void* lds)
 {

@@ -665,7 +665,7 @@ __device__ __forceinline__ bool select_row_wave(const RowSet& rs, int32_t row, i
 // kernel's per-row steps; defined with them).  lds: at least the nucleus's
 // LDS, 16-byte aligned.
 template <int DT>
-__device__ __attribute__((noinline)) void nucleus_topk_row(const RowSet& rs, int32_t vocab, float c, float top_p,
+__device__ __attribute__((noinline)) void nucleus_topk_row(RowSet rs, int32_t vocab, float c, float top_p,
                                                            RowDesc* __restrict__ descs, KeptEntry* __restrict__ kept,
                                                            int32_t row, void* lds);
 
