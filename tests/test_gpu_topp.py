@@ -112,6 +112,13 @@ EDGE = {
     # the cut falls in a bucket of 3000 tied logits: more crossing entries
     # than the per-wave regions hold (the radix then runs over the staged set)
     "crossing_bucket_of_3000_ties": (_spec(vocab=30000), lambda x: _tied_crossing(x)),
+    # top-k rows whose candidates overflow a chunk take the select's exact
+    # path, and its kernel then applies top-p itself: a kept list (700 ids
+    # tied at the top, all in the first chunk) and a kept set past the list
+    # (every logit equal)
+    "tied_peak_overflows_top50_then_top_p": (_spec(vocab=20000, top_k=50, top_p=0.7),
+                                             lambda x: _tied_peak(x)),
+    "flat_rows_top50_then_top_p": (_spec(kind="flat", vocab=5000, top_k=50, top_p=0.5), None),
     # the per-row kernel's two LDS layouts meet at rows of 8190 16-byte blocks
     # (one more for a row that starts inside a block): the largest rows of the
     # smaller layout and the smallest of the larger one, aligned and not
@@ -121,6 +128,12 @@ EDGE = {
     "small_layout_largest_f32": (_spec(vocab=32756, batch=2, dtype="f32"), None),
     "large_layout_smallest_f32": (_spec(vocab=32757, batch=2, dtype="f32"), None),
 }
+
+
+def _tied_peak(x):
+    """Ids 100..799 at 5 and every other logit at most 4 (every row)."""
+    ids = np.arange(x.shape[1])
+    return np.where((ids >= 100) & (ids < 800), 5.0, np.minimum(x, 4.0)).astype(x.dtype)
 
 
 def _tied_crossing(x):
